@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Throughput of the int8 mixed-precision linear (LLM.int8()) on one MI355X.
+
+A step is one pass of the whole hot path (outlier detection + calibration +
+quantization, extraction, int8 MFMA GEMM with the fused dequant / outlier /
+bias epilogue) over every layer of the workload, each layer on its own seeded
+synthetic input.  Inputs and weights are resident in HBM before timing starts;
+weight quantization (offline in the method) is done once, untimed.  Inputs,
+weights, workspaces and outputs are rotated over enough copies that the
+working set exceeds the last-level caches.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "int8 linear TOPS & % int8-MFMA peak (prefill); GB/s & % HBM peak (decode)"
+PEAK_INT8_OPS = 5.0e15     # MI355X dense int8 MFMA
+PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
+DEFAULT_WORKLOAD = "opt350m_mlp_pair_m512"
+GEMM_SRC = os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def workload_specs(name: str):
+    from synth import layer_specs
+    if name.startswith("llama13b_decode_m"):
+        m = int(name.rsplit("_m", 1)[1])
+        specs = [s for s in layer_specs("llama13b_decode") if s.name.endswith(f"_m{m}_o8")]
+        if not specs:
+            raise SystemExit(f"unknown decode batch in {name}")
+        return specs, "decode"
+    specs = layer_specs(name)
+    kind = "prefill"
+    return specs, kind
+
+
+def alg_bytes(s) -> int:
+    """Bytes the method itself must move for one layer: x, w_q, w_absmax, out (+ bias)."""
+    b = 2 * s.m * s.k + s.n * s.k + 4 * s.n + 2 * s.m * s.n
+    if s.bias_std is not None:
+        b += 2 * s.n
+    return b
+
+
+def gemm_alg_bytes(s) -> int:
+    """Bytes of the fused GEMM kernel alone: codes, w_q, both absmax vectors, out (+ bias)."""
+    b = s.m * s.k + s.n * s.k + 4 * (s.m + s.n) + 2 * s.m * s.n
+    if s.bias_std is not None:
+        b += 2 * s.n
+    return b
+
+
+def src_sha() -> str:
+    h = hashlib.sha256()
+    h.update(open(GEMM_SRC, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("gemm_source_sha") != src_sha():
+        return None
+    return d.get("per_launch_bytes", {}).get(workload)
+
+
+def cpu_baseline(specs, kind: str, budget_s: float):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import oracle  # only this leg of the benchmark touches the oracle
+    from synth import make_layer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas")
+    except Exception:  # pragma: no cover
+        threads = 1
+    threads = max(threads, 1)
+    rows_cap = 256 if kind == "prefill" else None
+    prepared = []
+    for s in specs:
+        m = s.m if rows_cap is None else min(s.m, rows_cap)
+        L = make_layer(s, m=m)
+        wq, ws = oracle.quantize_weight(L.w)  # offline weight quantization: untimed
+        prepared.append((s, m, L, wq, ws))
+    done_units = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for s, m, L, wq, ws in prepared:
+            oracle.linear_forward(L.x, wq, ws, L.bias, s.tau)
+            if kind == "prefill":
+                done_units += 2.0 * m * s.n * s.k
+            else:
+                done_units += alg_bytes(s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    if kind == "prefill":
+        value, unit = done_units / el / 1e12, "TOPS"
+        rows = ", ".join(f"{s.name}: {m} of {s.m} rows" for s, m, *_ in prepared)
+        sample = f"{reps} passes over the workload's layers ({rows}; outlier set from the sampled rows)"
+    else:
+        value, unit = done_units / el / 1e9, "GB/s"
+        sample = f"{reps} passes over the workload's layers (full size)"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds": round(el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cap", type=int, default=256)
+    ap.add_argument("--rotate-mb", type=float, default=1024.0)
+    ap.add_argument("--graph", choices=("on", "off"), default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the multi-GPU path is not built (one GPU per box); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+    from synth import make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs, kind = workload_specs(args.workload)
+    cap = args.cap
+
+    # ---- inputs resident in HBM, weights quantized once (untimed) -----------------
+    base = []
+    per_copy = 0
+    for s in specs:
+        log(f"layer {s.name}: m={s.m} k={s.k} n={s.n} outliers={s.n_outlier}")
+        L = make_layer(s)
+        x = torch.from_numpy(L.x).to(dev)
+        w = torch.from_numpy(L.w).to(dev)
+        wq, wabs = i8.quantize_weight(w)
+        del w
+        b = torch.from_numpy(L.bias).to(dev) if L.bias is not None else None
+        ws = i8.LinearWorkspace.create(s.m, s.n, s.k, cap, dev)
+        base.append((s, x, wq, wabs, b))
+        per_copy += x.numel() * 2 + wq.numel() + ws.buf.numel() + s.m * s.n * 2
+    copies = int(min(64, max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))))
+    log(f"rotation copies: {copies} ({per_copy / 2**20:.1f} MiB each)")
+    sets = []
+    for c in range(copies):
+        layer_sets = []
+        for s, x, wq, wabs, b in base:
+            if c == 0:
+                xc, wqc, wac = x, wq, wabs
+            else:
+                xc, wqc, wac = x.clone(), wq.clone(), wabs.clone()
+            ws = i8.LinearWorkspace.create(s.m, s.n, s.k, cap, dev)
+            out = torch.empty((s.m, s.n), dtype=torch.float16, device=dev)
+            layer_sets.append((s, xc, wqc, wac, b, ws, out))
+        sets.append(layer_sets)
+    torch.cuda.synchronize()
+
+    def step(c: int) -> None:
+        for s, xc, wqc, wac, b, ws, out in sets[c]:
+            i8.linear(xc, wqc, wac, b, s.tau, cap, ws, out)
+
+    # first call: check for outlier-capacity overflow once (outside timing)
+    for c in range(copies):
+        step(c)
+    torch.cuda.synchronize()
+    for s, xc, wqc, wac, b, ws, out in sets[0]:
+        if ws.outlier_overflow():
+            raise SystemExit(f"layer {s.name}: more outlier columns than cap={cap}")
+
+    # ---- eager timing ------------------------------------------------------------
+    def timed(run, steps, warmup):
+        for i in range(warmup):
+            run(i % copies)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            run(i % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    eager_ms, _ = timed(step, args.steps, args.warmup)
+    log(f"eager: {eager_ms * 1e3:.2f} us/step")
+
+    ms = eager_ms
+    launch = "eager"
+    graph_ms = None
+    if args.graph == "on":
+        graphs = []
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    step(c)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        graph_ms, _ = timed(lambda c: graphs[c].replay(), args.steps, args.warmup)
+        log(f"graph replay: {graph_ms * 1e3:.2f} us/step")
+        if graph_ms < ms:
+            ms, launch = graph_ms, "hipGraph replay"
+
+    # ---- dominant kernel: the fused GEMM, timed alone with events on its stream -----
+    stream = torch.cuda.current_stream()
+    for c in range(copies):
+        for s, xc, wqc, wac, b, ws, out in sets[c]:
+            i8.linear_quantize(xc, ws, s.tau)
+    torch.cuda.synchronize()
+    gemm_us = {}
+    for li, s in enumerate(specs):
+        reps = max(args.steps, 50)
+        for i in range(10):
+            _, _, wqc, wac, b, ws, out = sets[i % copies][li]
+            i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            _, _, wqc, wac, b, ws, out = sets[i % copies][li]
+            i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_us[s.name] = e0.elapsed_time(e1) * 1e3 / reps
+        log(f"gemm {s.name}: {gemm_us[s.name]:.2f} us/launch")
+
+    ops = sum(2 * s.m * s.n * s.k for s in specs)
+    byts = sum(alg_bytes(s) for s in specs)
+    if kind == "prefill":
+        value, unit = ops / (ms * 1e-3) / 1e12, "TOPS"
+    else:
+        value, unit = byts / (ms * 1e-3) / 1e9, "GB/s"
+
+    # roofline of the fused GEMM kernel over the step's launches
+    g_ops = sum(2 * s.m * s.n * s.k for s in specs)
+    g_bytes = sum(gemm_alg_bytes(s) for s in specs)
+    g_time = sum(gemm_us[s.name] for s in specs) * 1e-6
+    t_mfma = g_ops / PEAK_INT8_OPS
+    t_hbm = g_bytes / PEAK_HBM
+    if t_mfma >= t_hbm:
+        achieved = g_ops / g_time / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_OPS / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / (PEAK_INT8_OPS / 1e12), 4)}
+    else:
+        achieved = g_bytes / g_time / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
+    roof["kernel"] = "i8mp::gemm_kernel (fused dequant epilogue)"
+    roof["per_launch_us"] = {k: round(v, 3) for k, v in gemm_us.items()}
+    roof["traffic"] = read_traffic(args.workload)
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"cpu oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(specs, kind, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+f16",
+        "data": "synthetic (seeded layers; no datasets or trained weights)",
+        "config": {
+            "workload": args.workload,
+            "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n, "outlier_cols": s.n_outlier,
+                        "bias": s.bias_std is not None} for s in specs],
+            "threshold": specs[0].tau,
+            "cap": cap,
+            "launch": launch,
+            "eager_ms_per_step": round(eager_ms, 6),
+            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
+            "rotation_copies": copies,
+            "device": torch.cuda.get_device_name(dev),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

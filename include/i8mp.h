@@ -1,0 +1,222 @@
+/*
+ * i8mp.h - C ABI of libi8mp.so, the LLM.int8() vector-wise mixed-precision
+ * linear for AMD Instinct MI355X (gfx950).
+ *
+ * The method (transformers PR "`bitsandbytes` - `Linear8bitLt` integration
+ * into `transformers` models", section "About the mixed quantization method in
+ * few words"): the matmul over outlier feature columns runs in fp16, the rest
+ * in int8.  The ops follow the names of the bitsandbytes PR "LLM.int8()
+ * Refactoring: Part 1" (sections "Enhancements", "Deprecations", "Next steps"):
+ * int8_vectorwise_quant, extract_outliers, int8_linear_matmul, int8_mm_dequant
+ * and the sparse decomposition, on row-major data only, on an explicit stream,
+ * with NULL allowed for optional arguments, for any shape, and capturable in a
+ * graph.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, except
+ *    where a comment says "host".  fp16 tensors are IEEE binary16 bit patterns
+ *    passed as void*.  Matrices are row-major with an explicit leading
+ *    dimension in elements (ld >= number of columns).
+ *  - The caller owns every buffer.  The library allocates nothing, never
+ *    synchronizes, never reads device memory back to the host and keeps no
+ *    state besides loaded code and a per-device architecture check.  All work
+ *    is enqueued on `stream` (0 = the null stream), so every call can be
+ *    captured into a HIP graph.
+ *  - Errors are returned, never thrown or aborted on.  Arguments are checked
+ *    before anything is enqueued; on a non-OK status nothing was enqueued,
+ *    except for I8MP_ELAUNCH (a launch failed; earlier kernels of the same call
+ *    may have been enqueued).
+ *  - Sizes: m, n >= 0, k >= 1; k <= I8MP_MAX_K so that int32 accumulation of
+ *    int8 products is exact.  m == 0 or n == 0 is a valid empty call.
+ *  - Calls that share a workspace or outputs and overlap in time race; calls
+ *    on one stream are ordered.
+ *
+ * Numerics (the readings of the pages; the pages print no formula):
+ *  - outlier columns O = { j : |x[i,j]| >= threshold for some row i }, with
+ *    threshold <= 0 meaning "no outlier handling" (pure int8; also used to
+ *    quantize weights);
+ *  - absmax[i] = max over j not in O of |x[i,j]| (fp32, exact), 0 if none;
+ *  - q[i,j] = clamp(rne(fl32(x[i,j] * fl32(127 / absmax[i]))), -127, 127), all in
+ *    IEEE binary32; 0 in outlier columns and in rows with absmax 0;
+ *  - out[i,n] = fp16( (w_absmax[n]/127) * (C[i,n] * absmax[i]/127 + P[i,n]) + bias[n] )
+ *    with C = q . w_q^T exact in int32 and P[i,n] = sum_{j in O} x[i,j] * w_q[n,j]
+ *    (the int8 weights, widened exactly), computed in fp32.
+ */
+#ifndef I8MP_H
+#define I8MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t i8mp_status;
+
+#define I8MP_OK 0
+#define I8MP_EINVAL -1     /* NULL required pointer, bad size, ld too small, bad cap */
+#define I8MP_ERANGE -2     /* k > I8MP_MAX_K: int32 accumulation could overflow   */
+#define I8MP_EWORKSPACE -3 /* workspace NULL or smaller than the query returned   */
+#define I8MP_EDEVICE -4    /* current device is not gfx950, or no device          */
+#define I8MP_ELAUNCH -5    /* a kernel launch failed (hipGetLastError)            */
+
+/* floor((2^31 - 1) / 127^2): largest k whose worst-case int8 dot product fits int32. */
+#define I8MP_MAX_K 133144
+
+/* Host.  Static English text for a status code (never NULL). */
+const char* i8mp_status_string(i8mp_status s);
+
+/* Host.  ABI version of this header: (major << 16) | minor. */
+int32_t i8mp_abi_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* int8_vectorwise_quant: outlier-column detection + row-scale calibration +
+ * int8 quantization in one op (bitsandbytes PR "LLM.int8() Refactoring:
+ * Part 1", "Enhancements": fused activation scale calibration and
+ * quantization; the outlier columns of the sparse decomposition).
+ *
+ *   x            fp16 [m x k], leading dimension ldx >= k (elements)
+ *   threshold    outlier magnitude; <= 0 disables outlier handling
+ *   q            int8 [m x ldq] output codes, ldq >= k; only columns [0, k) are written
+ *   absmax       fp32 [m] output row absmax over non-outlier columns
+ *   outlier_bitmap  optional uint32 [ceil(k/32)] output, bit (j % 32) of word
+ *                j / 32 set iff column j is an outlier; may be NULL
+ *   workspace    device scratch of at least i8mp_quant_workspace_bytes(m, k)
+ *                bytes (per-row-block partial outlier bitmaps); contents on
+ *                entry are ignored; may be NULL iff that query returns 0
+ *
+ * Weight quantization is this op with threshold <= 0 on the fp16 weight
+ * [n x k]: q is the int8 weight state and absmax its per-row statistics.
+ */
+size_t i8mp_quant_workspace_bytes(int64_t m, int64_t k);
+
+i8mp_status i8mp_int8_vectorwise_quant(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                       float threshold, int8_t* q, int64_t ldq, float* absmax,
+                                       uint32_t* outlier_bitmap, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* extract_outliers: the fp16 columns X[:, O] and the sorted outlier index list
+ * (bitsandbytes PR "LLM.int8() Refactoring: Part 1", "Deprecations":
+ * extract_outliers; the index list the autograd function keeps for the
+ * outlier columns).
+ *
+ *   x               fp16 [m x k], ldx >= k
+ *   outlier_bitmap  uint32 [ceil(k/32)] as written by i8mp_int8_vectorwise_quant
+ *   cap             capacity (>= 0) of idx and of the columns of x_out
+ *   idx             int32 [cap] output: ascending outlier columns, -1 past the count
+ *   count           int32 [1] output: the number of outlier columns (may exceed cap;
+ *                   then only the first cap columns are listed and gathered)
+ *   x_out           optional fp16 [m x ldo] output, ldo >= cap: x_out[i, s] =
+ *                   x[i, idx[s]] for s < min(count, cap), 0 for the other s < cap
+ */
+i8mp_status i8mp_outlier_extract(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                 const uint32_t* outlier_bitmap, int32_t cap, int32_t* idx,
+                                 int32_t* count, void* x_out, int64_t ldo, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* int8_linear_matmul (replacement of igemmlt in the bitsandbytes PR,
+ * "Deprecations"): C = A . B^T exactly, int32.
+ *
+ *   a  int8 [m x lda], lda >= k      (activations, row-major, K contiguous)
+ *   b  int8 [n x ldb], ldb >= k      (weights, nn.Linear orientation)
+ *   c  int32 [m x ldc] output, ldc >= n
+ * Any m, n >= 0 and 1 <= k <= I8MP_MAX_K.
+ */
+i8mp_status i8mp_int8_linear_matmul(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                                    int64_t m, int64_t n, int64_t k, int32_t* c, int64_t ldc,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* int8_mm_dequant with the sparse-decomposition term (bitsandbytes PR,
+ * "Deprecations": mm_dequant and vectorwise_mm_dequant replaced by
+ * int8_mm_dequant; "Next steps": sparse decomposition):
+ *
+ *   out[i,n] = fp16( (col_absmax[n]/127) * (C[i,n]*row_absmax[i]/127 + P[i,n]) + bias[n] )
+ *   P[i,n]   = sum_{s < min(count, cap)} x_out[i,s] * b[n, idx[s]]   (fp32)
+ *
+ *   c           int32 [m x ldc], ldc >= n
+ *   row_absmax  fp32 [m];  col_absmax fp32 [n]
+ *   bias        optional fp16 [n] (NULL = no bias)
+ *   x_out, idx, count, b   optional outlier term (all NULL, or all non-NULL):
+ *               x_out fp16 [m x ldo] and idx int32 [cap] / count int32 [1] as
+ *               written by i8mp_outlier_extract; b int8 [n x ldb] the int8
+ *               weight with k columns (idx entries must be < k)
+ *   out         fp16 [m x ldout] output, ldout >= n
+ */
+i8mp_status i8mp_int8_mm_dequant(const int32_t* c, int64_t ldc, const float* row_absmax,
+                                 const float* col_absmax, const void* bias, int64_t m, int64_t n,
+                                 const void* x_out, int64_t ldo, const int32_t* idx,
+                                 const int32_t* count, int32_t cap, const int8_t* b, int64_t ldb,
+                                 int64_t k, void* out, int64_t ldout, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* The whole mixed-precision linear, fused: quantize + detect, extract, int8
+ * MFMA GEMM with the dequant, outlier sub-matmul and bias in its epilogue.
+ *
+ *   x          fp16 [m x k], ldx >= k
+ *   w_q        int8 [n x ldw], ldw >= k   (from i8mp_int8_vectorwise_quant, threshold <= 0)
+ *   w_absmax   fp32 [n]
+ *   bias       optional fp16 [n]
+ *   threshold  outlier threshold (<= 0: pure int8)
+ *   cap        outlier capacity (>= 0).  If the call finds more than cap outlier
+ *              columns, only the first cap take the fp16 path and the others are
+ *              dropped from both parts: out is then NOT the method's result.  The
+ *              true count is left in the workspace (see the layout query).
+ *   out        fp16 [m x ldout] output, ldout >= n
+ *   workspace  at least i8mp_linear_workspace(...).bytes bytes; contents on entry
+ *              are ignored; after the call it holds the intermediates at the
+ *              offsets the layout query reports.
+ */
+typedef struct i8mp_linear_workspace {
+    size_t bytes;          /* total size needed                                   */
+    size_t q_offset;       /* int8 codes [m x ldq], zero-padded to ldq            */
+    int64_t ldq;           /* leading dimension of the codes                      */
+    size_t absmax_offset;  /* fp32 [m] row absmax                                 */
+    size_t bitmap_offset;  /* uint32 [ceil(k/32)] outlier bitmap                  */
+    size_t idx_offset;     /* int32 [cap_pad] outlier columns, -1 past the count  */
+    size_t count_offset;   /* int32 [1] outlier count                             */
+    size_t xo_offset;      /* fp16 [m x cap_pad] gathered outlier columns         */
+    int32_t cap_pad;       /* cap rounded up to the fp16 MFMA depth               */
+    size_t partial_offset; /* private: per-row-block partial bitmaps              */
+    size_t partial_bytes;
+} i8mp_linear_workspace;
+
+i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
+                                        i8mp_linear_workspace* layout /* host */);
+
+/* The two halves of i8mp_linear_forward, for callers that schedule them
+ * separately (e.g. to quantize the next layer's input while this one's GEMM
+ * runs on another stream, or to time the GEMM alone).  Calling
+ * i8mp_linear_quantize then i8mp_linear_matmul_dequant on one stream with the
+ * same workspace is exactly i8mp_linear_forward.
+ *
+ * i8mp_linear_quantize: outlier detection, row calibration, quantization and
+ * outlier extraction of x into the workspace (arguments as for the forward).
+ * i8mp_linear_matmul_dequant: the int8 MFMA GEMM of the workspace codes with
+ * w_q and the fused epilogue (row/column absmax, outlier sub-matmul, bias);
+ * m, k and cap must be those of the i8mp_linear_quantize call that filled the
+ * workspace. */
+i8mp_status i8mp_linear_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
+                                 int32_t cap, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+i8mp_status i8mp_linear_matmul_dequant(const void* workspace, size_t workspace_bytes, int64_t m,
+                                       int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
+                                       const float* w_absmax, int64_t n, const void* bias, void* out,
+                                       int64_t ldout, hipStream_t stream);
+
+i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+                                const void* bias, float threshold, int32_t cap, void* out,
+                                int64_t ldout, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8MP_H */

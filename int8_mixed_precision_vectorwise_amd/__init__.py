@@ -1,0 +1,292 @@
+"""LLM.int8() vector-wise mixed-precision linear for AMD MI355X (gfx950).
+
+Thin Python binding of libi8mp.so.  Every step of the computation runs in the
+library's HIP kernels; this module checks devices, dtypes and layouts (all
+non-None tensors on one GPU, as the bitsandbytes pre-call check requires),
+allocates outputs and workspaces with PyTorch, and passes the current stream.
+There is no CPU fallback: calling an op without the built library, or on
+tensors that are not on a GPU, raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    I8MP_MAX_K,
+    I8mpError,
+    LinearWorkspaceLayout,
+    check,
+    lib,
+    status_string,
+)
+
+__all__ = [
+    "quantize_weight",
+    "vectorwise_quant",
+    "outlier_extract",
+    "linear_matmul",
+    "mm_dequant",
+    "linear",
+    "linear_quantize",
+    "linear_matmul_dequant",
+    "LinearWorkspace",
+    "I8mpError",
+]
+
+DEFAULT_THRESHOLD = 6.0
+DEFAULT_CAP = 256
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _device_of(*tensors) -> torch.device:
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU (got {dev}); there is no CPU path")
+    return dev
+
+
+def _rowmajor(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    """Leading dimension of a row-major 2-D tensor with unit column stride."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def _vec(t: torch.Tensor, name: str, dtype: torch.dtype, n: int) -> None:
+    if t.dtype != dtype or t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous {dtype} vector of length {n}")
+
+
+def vectorwise_quant(x: torch.Tensor, threshold: float = DEFAULT_THRESHOLD,
+                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """int8_vectorwise_quant: (codes int8 [m,k], row absmax fp32 [m], outlier bitmap uint32-as-int32)."""
+    dev = _device_of(x)
+    ldx = _rowmajor(x, "x", torch.float16)
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    absmax = torch.empty(m, dtype=torch.float32, device=dev)
+    bitmap = torch.empty((k + 31) // 32, dtype=torch.int32, device=dev)
+    L = lib()
+    wsb = L.i8mp_quant_workspace_bytes(m, k) if threshold > 0 else 0
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        check(L.i8mp_int8_vectorwise_quant(_ptr(x), m, k, ldx, threshold, _ptr(q), k, _ptr(absmax),
+                                           _ptr(bitmap), _ptr(ws), wsb, _stream(dev)),
+              "i8mp_int8_vectorwise_quant")
+    return q, absmax, bitmap
+
+
+def quantize_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Row-wise int8 weight state (codes, per-row absmax) of an fp16 weight [n, k]."""
+    q, absmax, _ = vectorwise_quant(w, 0.0)
+    return q, absmax
+
+
+def outlier_extract(x: torch.Tensor, bitmap: torch.Tensor, cap: int
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """extract_outliers: (idx int32 [cap], count int32 [1], x_out fp16 [m, cap])."""
+    dev = _device_of(x, bitmap)
+    ldx = _rowmajor(x, "x", torch.float16)
+    m, k = x.shape
+    _vec(bitmap, "bitmap", torch.int32, (k + 31) // 32)
+    idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    xo = torch.empty((m, max(cap, 1)), dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_outlier_extract(_ptr(x), m, k, ldx, _ptr(bitmap), cap, _ptr(idx), _ptr(count),
+                                         _ptr(xo), max(cap, 1), _stream(dev)),
+              "i8mp_outlier_extract")
+    return idx[:cap], count, xo[:, :cap]
+
+
+def linear_matmul(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """int8_linear_matmul: C = A . B^T, exact int32 [m, n]."""
+    dev = _device_of(a, b)
+    lda = _rowmajor(a, "a", torch.int8)
+    ldb = _rowmajor(b, "b", torch.int8)
+    m, k = a.shape
+    n, kb = b.shape
+    if kb != k:
+        raise ValueError("inner dimensions differ")
+    c = torch.empty((m, n), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_int8_linear_matmul(_ptr(a), lda, _ptr(b), ldb, m, n, k, _ptr(c), max(n, 1),
+                                            _stream(dev)),
+              "i8mp_int8_linear_matmul")
+    return c
+
+
+def mm_dequant(c: torch.Tensor, row_absmax: torch.Tensor, col_absmax: torch.Tensor,
+               bias: Optional[torch.Tensor] = None,
+               outliers: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               ) -> torch.Tensor:
+    """int8_mm_dequant (+ bias, + the sparse-decomposition term).
+
+    ``outliers`` = (x_out fp16 [m, cap], idx int32 [cap], count int32 [1], w_q int8 [n, k]).
+    """
+    xo = idx = count = wq = None
+    if outliers is not None:
+        xo, idx, count, wq = outliers
+    dev = _device_of(c, row_absmax, col_absmax, bias, xo, idx, count, wq)
+    ldc = _rowmajor(c, "c", torch.int32)
+    m, n = c.shape
+    _vec(row_absmax, "row_absmax", torch.float32, m)
+    _vec(col_absmax, "col_absmax", torch.float32, n)
+    if bias is not None:
+        _vec(bias, "bias", torch.float16, n)
+    cap, ldo, ldb, k = 0, 0, 0, 1
+    if outliers is not None:
+        ldo = _rowmajor(xo, "x_out", torch.float16)
+        cap = xo.shape[1]
+        ldb = _rowmajor(wq, "w_q", torch.int8)
+        k = wq.shape[1]
+    out = torch.empty((m, n), dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_int8_mm_dequant(_ptr(c), ldc, _ptr(row_absmax), _ptr(col_absmax), _ptr(bias), m, n,
+                                         _ptr(xo), ldo, _ptr(idx), _ptr(count), cap, _ptr(wq), ldb, k,
+                                         _ptr(out), max(n, 1), _stream(dev)),
+              "i8mp_int8_mm_dequant")
+    return out
+
+
+@dataclass
+class LinearWorkspace:
+    """Device workspace of i8mp_linear_forward plus views of its intermediates."""
+
+    m: int
+    n: int
+    k: int
+    cap: int
+    layout: LinearWorkspaceLayout
+    buf: torch.Tensor
+
+    @classmethod
+    def create(cls, m: int, n: int, k: int, cap: int, device) -> "LinearWorkspace":
+        L = LinearWorkspaceLayout()
+        check(lib().i8mp_linear_workspace_query(m, n, k, cap, ctypes.byref(L)), "i8mp_linear_workspace_query")
+        buf = torch.empty(max(L.bytes, 1), dtype=torch.uint8, device=device)
+        return cls(m, n, k, cap, L, buf)
+
+    def fits(self, m: int, n: int, k: int, cap: int) -> bool:
+        L = LinearWorkspaceLayout()
+        check(lib().i8mp_linear_workspace_query(m, n, k, cap, ctypes.byref(L)), "i8mp_linear_workspace_query")
+        return L.bytes <= self.buf.numel() and (m, k, cap) == (self.m, self.k, self.cap)
+
+    def _view(self, off: int, count: int, dtype: torch.dtype) -> torch.Tensor:
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return self.buf[off:off + nbytes].view(dtype)
+
+    # intermediates left by the last forward call (for tests and inspection)
+    def codes(self) -> torch.Tensor:
+        return self._view(self.layout.q_offset, self.m * self.layout.ldq, torch.int8).view(
+            self.m, self.layout.ldq)[:, : self.k]
+
+    def absmax(self) -> torch.Tensor:
+        return self._view(self.layout.absmax_offset, self.m, torch.float32)
+
+    def bitmap(self) -> torch.Tensor:
+        return self._view(self.layout.bitmap_offset, (self.k + 31) // 32, torch.int32)
+
+    def idx(self) -> torch.Tensor:
+        return self._view(self.layout.idx_offset, max(self.layout.cap_pad, 1), torch.int32)[: self.cap]
+
+    def count(self) -> torch.Tensor:
+        return self._view(self.layout.count_offset, 1, torch.int32)
+
+    def x_out(self) -> torch.Tensor:
+        cp = self.layout.cap_pad
+        return self._view(self.layout.xo_offset, self.m * cp, torch.float16).view(self.m, cp)[:, : self.cap]
+
+    def outlier_overflow(self) -> bool:
+        """True if the last call found more outlier columns than cap (synchronizes)."""
+        return int(self.count().item()) > self.cap
+
+
+def linear(x: torch.Tensor, w_q: torch.Tensor, w_absmax: torch.Tensor,
+           bias: Optional[torch.Tensor] = None, threshold: float = DEFAULT_THRESHOLD,
+           cap: int = DEFAULT_CAP, workspace: Optional[LinearWorkspace] = None,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The fused mixed-precision linear: fp16 out [m, n] = x . dequant(w)^T + bias."""
+    dev = _device_of(x, w_q, w_absmax, bias, out)
+    ldx = _rowmajor(x, "x", torch.float16)
+    ldw = _rowmajor(w_q, "w_q", torch.int8)
+    m, k = x.shape
+    n, kw = w_q.shape
+    if kw != k:
+        raise ValueError("x and w_q differ in k")
+    _vec(w_absmax, "w_absmax", torch.float32, n)
+    if bias is not None:
+        _vec(bias, "bias", torch.float16, n)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=dev)
+    ldout = _rowmajor(out, "out", torch.float16)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = LinearWorkspace.create(m, n, k, cap, dev)
+    elif not workspace.fits(m, n, k, cap):
+        raise ValueError("workspace was created for another shape or capacity")
+    with torch.cuda.device(dev):
+        check(lib().i8mp_linear_forward(_ptr(x), m, k, ldx, _ptr(w_q), ldw, _ptr(w_absmax), n, _ptr(bias),
+                                        threshold, cap, _ptr(out), ldout, _ptr(workspace.buf),
+                                        workspace.buf.numel(), _stream(dev)),
+              "i8mp_linear_forward")
+    return out
+
+
+def linear_quantize(x: torch.Tensor, workspace: LinearWorkspace,
+                    threshold: float = DEFAULT_THRESHOLD) -> None:
+    """First half of ``linear``: detect, calibrate, quantize and extract into the workspace."""
+    dev = _device_of(x, workspace.buf)
+    ldx = _rowmajor(x, "x", torch.float16)
+    m, k = x.shape
+    if (m, k) != (workspace.m, workspace.k):
+        raise ValueError("workspace was created for another shape")
+    with torch.cuda.device(dev):
+        check(lib().i8mp_linear_quantize(_ptr(x), m, k, ldx, threshold, workspace.cap, _ptr(workspace.buf),
+                                         workspace.buf.numel(), _stream(dev)),
+              "i8mp_linear_quantize")
+
+
+def linear_matmul_dequant(workspace: LinearWorkspace, w_q: torch.Tensor, w_absmax: torch.Tensor,
+                          bias: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Second half of ``linear``: fused int8 GEMM + dequant epilogue from the workspace."""
+    dev = _device_of(workspace.buf, w_q, w_absmax, bias, out)
+    ldw = _rowmajor(w_q, "w_q", torch.int8)
+    n, k = w_q.shape
+    if k != workspace.k:
+        raise ValueError("w_q and the workspace differ in k")
+    _vec(w_absmax, "w_absmax", torch.float32, n)
+    if bias is not None:
+        _vec(bias, "bias", torch.float16, n)
+    m = workspace.m
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=dev)
+    ldout = _rowmajor(out, "out", torch.float16)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_linear_matmul_dequant(_ptr(workspace.buf), workspace.buf.numel(), m, k, workspace.cap,
+                                               _ptr(w_q), ldw, _ptr(w_absmax), n, _ptr(bias), _ptr(out),
+                                               ldout, _stream(dev)),
+              "i8mp_linear_matmul_dequant")
+    return out

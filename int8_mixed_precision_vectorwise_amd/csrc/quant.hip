@@ -1,0 +1,350 @@
+// Outlier-column detection and fused row calibration + int8 quantization +
+// outlier extraction for gfx950.
+//
+// The method keeps outlier feature columns in fp16 and quantizes the rest of
+// each row to int8 with its own absmax (transformers PR "`bitsandbytes` -
+// `Linear8bitLt` integration into `transformers` models", "About the mixed
+// quantization method in few words"; bitsandbytes PR "LLM.int8() Refactoring:
+// Part 1", "Enhancements": calibration and quantization fused in one op).
+//
+// Because a row's scale excludes every outlier column, and the outlier set is
+// a property of all rows, the work is split at the one point that needs a
+// global view:
+//   detect_kernel  one pass over X: per (row block, 256-column block) a word
+//                  of the partial outlier bitmap (no atomics, no zeroing: every
+//                  word of every partial is written);
+//   quant_kernel   ORs the partial bitmaps into LDS, then per row: coalesced
+//                  16-byte loads, wavefront-shuffle + LDS absmax over the
+//                  non-outlier columns, IEEE fp32 quantization, 8-byte code
+//                  stores, gather of the outlier values into the compact fp16
+//                  matrix.  Workgroup 0 also writes the bitmap, the ascending
+//                  index list and the count.
+#include "common.h"
+
+namespace i8mp {
+
+namespace {
+
+__device__ inline float h2f(half_bits h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ inline uint32_t outlier_bits8(const uint4& v, float tau) {
+    uint32_t m = 0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float lo = h2f((half_bits)(w[i] & 0x7fffu));
+        float hi = h2f((half_bits)((w[i] >> 16) & 0x7fffu));
+        m |= (lo >= tau ? 1u : 0u) << (2 * i);
+        m |= (hi >= tau ? 1u : 0u) << (2 * i + 1);
+    }
+    return m;
+}
+
+// 8 fp16 values starting at column col of a row; columns >= k read as 0.
+template <bool kVec>
+__device__ inline uint4 load8(const half_bits* __restrict__ row, int64_t col, int64_t k) {
+    if (kVec && col + 8 <= k) return *reinterpret_cast<const uint4*>(row + col);
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (col + e < k) w[e >> 1] |= (uint32_t)row[col + e] << (16 * (e & 1));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ inline half_bits half_at(const uint4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (half_bits)((w >> (16 * (e & 1))) & 0xffffu);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// One int8 code per the method's reading: 0 for outlier columns and for rows
+// without a non-outlier magnitude, else clamp(rne(fl32(x * inv)), -127, 127).
+__device__ inline uint32_t code_byte(float x, float inv, bool zero) {
+    float q = __builtin_rintf(x * inv);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    int iq = zero ? 0 : (int)q;
+    return (uint32_t)iq & 0xffu;
+}
+
+}  // namespace
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void detect_kernel(const half_bits* __restrict__ x, int64_t m,
+                                                     int64_t k, int64_t ldx, float tau,
+                                                     int64_t rows_per_block, int64_t words,
+                                                     uint32_t* __restrict__ partial) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cg = tid & 31;  // group of 8 columns
+    const int rsub = tid >> 5;
+    const int64_t col0 = (int64_t)blockIdx.x * kDetectCols + cg * 8;
+    const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
+    int64_t r_end = r_begin + rows_per_block;
+    if (r_end > m) r_end = m;
+
+    uint32_t mask = 0;
+    if (col0 < k) {
+        if (kVec && col0 + 8 <= k) {
+#pragma unroll 8
+            for (int64_t r = r_begin + rsub; r < r_end; r += 8) {
+                uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + col0);
+                mask |= outlier_bits8(v, tau);
+            }
+        } else {
+            for (int64_t r = r_begin + rsub; r < r_end; r += 8) {
+                uint4 v = load8<false>(x + r * ldx, col0, k);
+                mask |= outlier_bits8(v, tau);
+            }
+        }
+    }
+    mask |= __shfl_xor(mask, 32, 64);  // lanes l and l^32 hold the same columns
+    __shared__ uint32_t red[4][32];
+    if (lane < 32) red[wave][lane] = mask;
+    __syncthreads();
+    if (tid < 8) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int g = tid * 4 + q4;
+            const uint32_t mm = red[0][g] | red[1][g] | red[2][g] | red[3][g];
+            word |= (mm & 0xffu) << (8 * q4);
+        }
+        const int64_t w = (int64_t)blockIdx.x * 8 + tid;
+        if (w < words) partial[(int64_t)blockIdx.y * words + w] = word;
+    }
+}
+
+// NCH > 0: each thread keeps NCH chunks of 8 columns of the row in registers
+// (k <= NCH * 2048); NCH == 0: the row is streamed twice (any k).
+template <int NCH, bool kVec>
+__global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* bm = smem;                                       // [words]
+    int32_t* pre = reinterpret_cast<int32_t*>(smem + a.words);  // [words]
+    __shared__ float red[4];
+    __shared__ int32_t wave_tot[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const bool outl = a.partial != nullptr;
+    const bool need_prefix = outl && (a.x_out || a.idx_out || a.count_out);
+
+    // 1. the final outlier bitmap: OR of the per-row-block partials
+    if (outl) {
+        for (int64_t w = tid; w < a.words; w += 256) {
+            uint32_t v = 0;
+            for (int64_t r = 0; r < a.row_blocks; ++r) v |= a.partial[r * a.words + w];
+            if (w == a.words - 1 && (a.k & 31)) v &= (1u << (a.k & 31)) - 1u;
+            bm[w] = v;
+        }
+    }
+    __syncthreads();
+
+    // 2. exclusive prefix of the per-word popcounts (slot of each outlier column)
+    int32_t total = 0;
+    if (need_prefix) {
+        const int64_t per = (a.words + 255) / 256;
+        const int64_t w0 = (int64_t)tid * per;
+        int64_t w1 = w0 + per;
+        if (w1 > a.words) w1 = a.words;
+        int32_t s = 0;
+        for (int64_t w = w0; w < w1; ++w) s += __popc(bm[w]);
+        int32_t incl = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int32_t t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) wave_tot[wave] = incl;
+        __syncthreads();
+        int32_t off = 0;
+        for (int i = 0; i < 4; ++i) {
+            if (i < wave) off += wave_tot[i];
+            total += wave_tot[i];
+        }
+        int32_t run = off + incl - s;
+        for (int64_t w = w0; w < w1; ++w) {
+            pre[w] = run;
+            run += __popc(bm[w]);
+        }
+        __syncthreads();
+    }
+    const int32_t kept = total < a.cap ? total : a.cap;
+
+    // 3. workgroup 0 publishes the bitmap, the index list and the count
+    if (blockIdx.x == 0) {
+        if (a.bitmap_out)
+            for (int64_t w = tid; w < a.words; w += 256) a.bitmap_out[w] = outl ? bm[w] : 0u;
+        if (a.count_out && tid == 0) *a.count_out = total;
+        if (a.idx_out) {
+            for (int32_t s = tid; s < a.idx_len; s += 256)
+                if (s >= kept) a.idx_out[s] = -1;
+            if (outl) {
+                for (int64_t w = tid; w < a.words; w += 256) {
+                    uint32_t v = bm[w];
+                    int32_t slot = pre[w];
+                    while (v) {
+                        const int b = __ffs(v) - 1;
+                        if (slot < a.cap) a.idx_out[slot] = (int32_t)(w * 32 + b);
+                        ++slot;
+                        v &= v - 1u;
+                    }
+                }
+            }
+        }
+    }
+
+    // 4. rows
+    const int64_t nchunks = (a.k + 7) / 8;
+    const bool vec_q = a.q && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
+    for (int64_t rr = 0; rr < a.rows_per_block; ++rr) {
+        const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
+        if (r >= a.m) break;
+        const half_bits* __restrict__ xr = a.x + r * a.ldx;
+        constexpr int RC = NCH > 0 ? NCH : 1;
+        uint4 v[RC];
+        uint32_t ob[RC];
+
+        // 4a. absmax over the non-outlier columns
+        float mx = 0.0f;
+        auto chunk_max = [&](const uint4& vv, uint32_t obits) {
+            float t = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = fabsf(h2f(half_at(vv, e)));
+                t = ((obits >> e) & 1u) ? t : fmaxf(t, f);
+            }
+            return t;
+        };
+        auto obyte = [&](int64_t col) -> uint32_t {
+            return outl ? (bm[col >> 5] >> (col & 31)) & 0xffu : 0u;
+        };
+        if (NCH > 0) {
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                const int64_t col = ((int64_t)tid + 256 * c) * 8;
+                if (col < a.k) {
+                    v[c] = load8<kVec>(xr, col, a.k);
+                    ob[c] = obyte(col);
+                } else {
+                    v[c] = make_uint4(0, 0, 0, 0);
+                    ob[c] = 0;
+                }
+                mx = fmaxf(mx, chunk_max(v[c], ob[c]));
+            }
+        } else {
+            for (int64_t ch = tid; ch < nchunks; ch += 256) {
+                const int64_t col = ch * 8;
+                mx = fmaxf(mx, chunk_max(load8<kVec>(xr, col, a.k), obyte(col)));
+            }
+        }
+        mx = wave_max(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+
+        // 4b. codes, 4c. outlier gather
+        const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
+        const bool zero_row = !(s > 0.0f);
+        auto emit = [&](const uint4& vv, uint32_t obits, int64_t col) {
+            if (a.q) {
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t b =
+                        code_byte(h2f(half_at(vv, e)), inv, zero_row || ((obits >> e) & 1u));
+                    if (e < 4) lo |= b << (8 * e);
+                    else hi |= b << (8 * (e - 4));
+                }
+                int8_t* qr = a.q + r * a.ldq + col;
+                if (vec_q && col + 8 <= a.k) {
+                    *reinterpret_cast<uint2*>(qr) = make_uint2(lo, hi);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < a.k)
+                            qr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+                }
+            }
+            if (a.x_out && obits) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((obits >> e) & 1u) {
+                        const int64_t j = col + e;
+                        const int64_t w = j >> 5;
+                        const uint32_t below = bm[w] & ((1u << (j & 31)) - 1u);
+                        const int32_t slot = pre[w] + __popc(below);
+                        if (slot < a.cap) a.x_out[r * a.ldo + slot] = half_at(vv, e);
+                    }
+                }
+            }
+        };
+        if (NCH > 0) {
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                const int64_t col = ((int64_t)tid + 256 * c) * 8;
+                if (col < a.k) emit(v[c], ob[c], col);
+            }
+        } else {
+            for (int64_t ch = tid; ch < nchunks; ch += 256) {
+                const int64_t col = ch * 8;
+                emit(load8<kVec>(xr, col, a.k), obyte(col), col);
+            }
+        }
+        if (a.q) {
+            for (int64_t j = a.k + tid; j < a.kpad; j += 256) a.q[r * a.ldq + j] = 0;
+            if (tid == 0) a.absmax[r] = s;
+        }
+        if (a.x_out)
+            for (int32_t t = kept + tid; t < a.xo_cols; t += 256) a.x_out[r * a.ldo + t] = 0;
+    }
+}
+
+hipError_t launch_detect(const half_bits* x, int64_t m, int64_t k, int64_t ldx, float threshold,
+                         const QuantPlan& plan, uint32_t* partial, hipStream_t stream) {
+    const bool vec = ((ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    dim3 grid((unsigned)plan.detect_gx, (unsigned)plan.row_blocks);
+    if (vec)
+        hipLaunchKernelGGL(detect_kernel<true>, grid, dim3(256), 0, stream, x, m, k, ldx, threshold,
+                           plan.rows_per_detect_block, plan.words, partial);
+    else
+        hipLaunchKernelGGL(detect_kernel<false>, grid, dim3(256), 0, stream, x, m, k, ldx,
+                           threshold, plan.rows_per_detect_block, plan.words, partial);
+    return hipGetLastError();
+}
+
+template <int NCH>
+static void launch_quant_n(const QuantArgs& a, dim3 grid, size_t lds, bool vec, hipStream_t s) {
+    if (vec)
+        hipLaunchKernelGGL((quant_kernel<NCH, true>), grid, dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL((quant_kernel<NCH, false>), grid, dim3(256), lds, s, a);
+}
+
+hipError_t launch_quant(const QuantArgs& a, hipStream_t stream) {
+    const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+    int64_t blocks = a.m > 0 ? ceil_div(a.m, a.rows_per_block) : 1;
+    dim3 grid((unsigned)blocks);
+    const size_t lds = (size_t)a.words * 2 * sizeof(uint32_t);
+    const int64_t per = ceil_div(ceil_div(a.k, 8), 256);
+    if (per <= 1) launch_quant_n<1>(a, grid, lds, vec, stream);
+    else if (per <= 2) launch_quant_n<2>(a, grid, lds, vec, stream);
+    else if (per <= 4) launch_quant_n<4>(a, grid, lds, vec, stream);
+    else if (per <= 8) launch_quant_n<8>(a, grid, lds, vec, stream);
+    else if (per <= 12) launch_quant_n<12>(a, grid, lds, vec, stream);
+    else launch_quant_n<0>(a, grid, lds, vec, stream);
+    return hipGetLastError();
+}
+
+}  // namespace i8mp

@@ -1,0 +1,179 @@
+"""The C-ABI library loads, exports what include/i8mp.h declares, and rejects
+bad arguments with the documented status codes before touching a device.
+
+No compute calls are made here: every call below fails validation (or, on a
+machine without a GPU, the device check) before anything is enqueued.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_mixed_precision_vectorwise_amd as i8
+from int8_mixed_precision_vectorwise_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i8mp.h")
+
+OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(i8mp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libi8mp.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_exports_match_header(L):
+    declared = _header_functions()
+    assert declared == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in (OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE, -5):
+        assert len(L.i8mp_status_string(s)) > 0
+    assert L.i8mp_abi_version() >> 16 == 1
+
+
+def test_workspace_queries(L):
+    assert L.i8mp_quant_workspace_bytes(2048, 4096) > 0
+    assert L.i8mp_quant_workspace_bytes(0, 4096) == 0
+    assert L.i8mp_quant_workspace_bytes(16, 133145) == 0
+    lay = _lib.LinearWorkspaceLayout()
+    assert L.i8mp_linear_workspace_query(2048, 4096, 4096, 20, ctypes.byref(lay)) == OK
+    assert lay.ldq % 128 == 0 and lay.ldq >= 4096
+    assert lay.cap_pad == 32
+    offs = [lay.partial_offset, lay.bitmap_offset, lay.idx_offset, lay.count_offset,
+            lay.absmax_offset, lay.q_offset, lay.xo_offset]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.bytes >= lay.xo_offset + 2048 * 32 * 2
+    assert lay.q_offset + 2048 * lay.ldq <= lay.xo_offset
+    assert L.i8mp_linear_workspace_query(16, 16, 133145, 8, ctypes.byref(lay)) == ERANGE
+    assert L.i8mp_linear_workspace_query(16, 16, 0, 8, ctypes.byref(lay)) == EINVAL
+    assert L.i8mp_linear_workspace_query(16, 16, 64, -1, ctypes.byref(lay)) == EINVAL
+    assert L.i8mp_linear_workspace_query(16, 16, 64, 8, None) == EINVAL
+
+
+def test_quant_validation(L):
+    q = L.i8mp_int8_vectorwise_quant
+    assert q(None, 4, 64, 64, 6.0, FAKE, 64, FAKE, None, FAKE, 1 << 20, None) == EINVAL
+    assert q(FAKE, 4, 64, 32, 6.0, FAKE, 64, FAKE, None, FAKE, 1 << 20, None) == EINVAL   # ldx < k
+    assert q(FAKE, 4, 64, 64, 6.0, FAKE, 63, FAKE, None, FAKE, 1 << 20, None) == EINVAL   # ldq < k
+    assert q(FAKE, -1, 64, 64, 6.0, FAKE, 64, FAKE, None, FAKE, 1 << 20, None) == EINVAL
+    assert q(FAKE, 4, 0, 64, 6.0, FAKE, 64, FAKE, None, FAKE, 1 << 20, None) == EINVAL
+    assert q(FAKE, 4, 133145, 133145, 6.0, FAKE, 133145, FAKE, None, FAKE, 1 << 30, None) == ERANGE
+    assert q(FAKE, 4, 64, 64, 6.0, FAKE, 64, FAKE, None, None, 0, None) == EWORKSPACE
+    need = L.i8mp_quant_workspace_bytes(4, 64)
+    assert q(FAKE, 4, 64, 64, 6.0, FAKE, 64, FAKE, None, FAKE, need - 1, None) == EWORKSPACE
+    assert q(FAKE, 0, 64, 64, 6.0, None, 64, None, None, None, 0, None) == OK  # empty
+
+
+def test_extract_validation(L):
+    e = L.i8mp_outlier_extract
+    assert e(FAKE, 4, 64, 64, None, 8, FAKE, FAKE, FAKE, 8, None) == EINVAL     # no bitmap
+    assert e(FAKE, 4, 64, 64, FAKE, -1, FAKE, FAKE, FAKE, 8, None) == EINVAL    # cap < 0
+    assert e(FAKE, 4, 64, 64, FAKE, 8, FAKE, FAKE, FAKE, 7, None) == EINVAL     # ldo < cap
+    assert e(FAKE, 4, 64, 64, FAKE, 8, None, FAKE, FAKE, 8, None) == EINVAL     # no idx
+    assert e(FAKE, 4, 64, 64, FAKE, 8, FAKE, None, FAKE, 8, None) == EINVAL     # no count
+
+
+def test_matmul_validation(L):
+    mm = L.i8mp_int8_linear_matmul
+    assert mm(FAKE, 63, FAKE, 64, 4, 4, 64, FAKE, 4, None) == EINVAL   # lda < k
+    assert mm(FAKE, 64, FAKE, 63, 4, 4, 64, FAKE, 4, None) == EINVAL   # ldb < k
+    assert mm(FAKE, 64, FAKE, 64, 4, 4, 64, FAKE, 3, None) == EINVAL   # ldc < n
+    assert mm(None, 64, FAKE, 64, 4, 4, 64, FAKE, 4, None) == EINVAL
+    assert mm(FAKE, 64, FAKE, 64, 4, 4, 0, FAKE, 4, None) == EINVAL
+    k = 133145
+    assert mm(FAKE, k, FAKE, k, 1, 1, k, FAKE, 1, None) == ERANGE
+    assert mm(None, 64, None, 64, 0, 4, 64, None, 4, None) == OK      # empty m
+    assert mm(None, 64, None, 64, 4, 0, 64, None, 0, None) == OK      # empty n
+
+
+def test_dequant_validation(L):
+    d = L.i8mp_int8_mm_dequant
+    # outlier arguments must be all NULL or all set
+    assert d(FAKE, 4, FAKE, FAKE, None, 4, 4, FAKE, 8, None, FAKE, 8, FAKE, 64, 64, FAKE, 4, None) == EINVAL
+    assert d(FAKE, 3, FAKE, FAKE, None, 4, 4, None, 0, None, None, 0, None, 0, 1, FAKE, 4, None) == EINVAL
+    assert d(None, 4, FAKE, FAKE, None, 4, 4, None, 0, None, None, 0, None, 0, 1, FAKE, 4, None) == EINVAL
+    assert d(FAKE, 4, FAKE, FAKE, None, 4, 4, FAKE, 7, FAKE, FAKE, 8, FAKE, 64, 64, FAKE, 4, None) == EINVAL
+
+
+def test_forward_validation(L):
+    f = L.i8mp_linear_forward
+    lay = _lib.LinearWorkspaceLayout()
+    assert L.i8mp_linear_workspace_query(16, 32, 64, 8, ctypes.byref(lay)) == OK
+    args = dict(x=FAKE, m=16, k=64, ldx=64, w=FAKE, ldw=64, sw=FAKE, n=32, b=None, t=6.0, cap=8,
+                out=FAKE, ldo=32, ws=FAKE, wsb=lay.bytes)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["m"], a["k"], a["ldx"], a["w"], a["ldw"], a["sw"], a["n"], a["b"], a["t"],
+                 a["cap"], a["out"], a["ldo"], a["ws"], a["wsb"], None)
+
+    assert call(x=None) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(sw=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(ldx=63) == EINVAL
+    assert call(ldw=63) == EINVAL
+    assert call(ldo=31) == EINVAL
+    assert call(cap=-1) == EINVAL
+    assert call(k=133145, ldx=133145, ldw=133145) == ERANGE
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=lay.bytes - 1) == EWORKSPACE
+    assert call(m=0) == OK
+    assert call(n=0) == OK
+
+    qz = L.i8mp_linear_quantize
+    assert qz(None, 16, 64, 64, 6.0, 8, FAKE, lay.bytes, None) == EINVAL
+    assert qz(FAKE, 16, 64, 63, 6.0, 8, FAKE, lay.bytes, None) == EINVAL
+    assert qz(FAKE, 16, 64, 64, 6.0, -1, FAKE, lay.bytes, None) == EINVAL
+    assert qz(FAKE, 16, 64, 64, 6.0, 8, FAKE, lay.bytes - 1, None) == EWORKSPACE
+    assert qz(FAKE, 16, 133145, 133145, 6.0, 8, FAKE, 1 << 40, None) == ERANGE
+    assert qz(None, 0, 64, 64, 6.0, 8, None, 0, None) == OK
+    md = L.i8mp_linear_matmul_dequant
+    assert md(FAKE, lay.bytes, 16, 64, 8, None, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL
+    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 63, FAKE, 32, None, FAKE, 32, None) == EINVAL
+    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 31, None) == EINVAL
+    assert md(None, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
+    assert md(FAKE, lay.bytes - 1, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
+    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 0, None, FAKE, 32, None) == OK
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="device check only observable without a GPU")
+def test_no_device_reported(L):
+    lay = _lib.LinearWorkspaceLayout()
+    L.i8mp_linear_workspace_query(16, 32, 64, 8, ctypes.byref(lay))
+    st = L.i8mp_linear_forward(FAKE, 16, 64, 64, FAKE, 64, FAKE, 32, None, 6.0, 8, FAKE, 32, FAKE,
+                               lay.bytes, None)
+    assert st == EDEVICE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        i8.vectorwise_quant(x, 6.0)
+    with pytest.raises(ValueError, match="GPU"):
+        i8.linear(x, torch.zeros(8, 64, dtype=torch.int8), torch.ones(8))

@@ -1,0 +1,305 @@
+"""GPU parity: every entry point of libi8mp.so against the CPU oracle.
+
+Bit-exact: codes, row absmax, outlier bitmap / indices / count, gathered
+outlier values, int32 accumulators, weight codes and statistics.
+Tolerance (fp16 outputs, fp32 epilogue arithmetic): |gpu - oracle| <=
+1e-3 + 1e-2 |oracle| per element.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_mixed_precision_vectorwise_amd as i8
+import oracle
+from gpu_util import assert_equal, assert_fp16_close, dev, host, say
+from synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TAU = 6.0
+
+QUANT_CASES = [
+    # m, k, n_outlier, row_frac, tau
+    (1, 1, 0, 1.0, TAU),
+    (1, 7, 1, 1.0, TAU),
+    (3, 33, 2, 1.0, TAU),
+    (5, 257, 3, 0.5, TAU),
+    (16, 1024, 4, 1.0, TAU),
+    (17, 1000, 6, 0.2, TAU),
+    (64, 2049, 9, 0.05, TAU),
+    (130, 4096, 7, 1.0, TAU),
+    (9, 20000, 20, 0.3, TAU),      # register-resident chunks, largest bucket
+    (4, 40000, 5, 1.0, TAU),       # streamed rows
+    (33, 300, 0, 1.0, 0.0),        # threshold off
+    (8, 96, 96, 1.0, TAU),         # every column an outlier
+]
+
+
+def _quant_layer(m, k, o, frac, seed):
+    return make_inputs(m, k, 1, n_outlier=o, lo=6.0, hi=60.0, seed=(70, seed, 0), outlier_row_frac=frac,
+                       with_weight=False)
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "m%d_k%d_o%d_f%g_t%g" % c)
+def test_vectorwise_quant_bit_exact(case):
+    m, k, o, frac, tau = case
+    L = _quant_layer(m, k, o, frac, hash(case) % 1000)
+    x = L.x.copy()
+    if m > 2:
+        x[1] = 0  # a zero row
+    say(f"vectorwise_quant m={m} k={k} o={o} tau={tau}")
+    q, s, bm = i8.vectorwise_quant(dev(x), tau)
+    torch.cuda.synchronize()
+    ref = oracle.vectorwise_quant(x, tau)
+    assert_equal(q, ref.q, "codes")
+    assert_equal(s, ref.absmax, "absmax")
+    assert_equal(bm.view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+
+
+def test_vectorwise_quant_unaligned_rows():
+    m, k = 37, 301
+    L = _quant_layer(m, k + 3, 4, 0.7, 5)
+    full = dev(L.x)
+    x = full[:, 1:k + 1]             # odd element offset, ld = k + 3
+    say("vectorwise_quant unaligned view")
+    q, s, bm = i8.vectorwise_quant(x, TAU)
+    torch.cuda.synchronize()
+    ref = oracle.vectorwise_quant(np.ascontiguousarray(L.x[:, 1:k + 1]), TAU)
+    assert_equal(q, ref.q, "codes")
+    assert_equal(s, ref.absmax, "absmax")
+    assert_equal(bm.view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 33), (300, 1000), (4096, 1024), (64, 13824)])
+def test_weight_quant_bit_exact(n, k):
+    w = (np.random.default_rng([71, n, k]).standard_normal((n, k)) * 0.02).astype(np.float16)
+    say(f"quantize_weight n={n} k={k}")
+    wq, ws = i8.quantize_weight(dev(w))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_weight(w)
+    assert_equal(wq, rq, "weight codes")
+    assert_equal(ws, rs, "weight absmax")
+
+
+@pytest.mark.parametrize("m,k,o,cap", [(5, 100, 3, 8), (64, 4096, 7, 32), (16, 1024, 0, 8),
+                                       (4, 200, 12, 5), (1, 70, 2, 0)])
+def test_outlier_extract_bit_exact(m, k, o, cap):
+    L = _quant_layer(m, k, o, 0.6, 9)
+    say(f"outlier_extract m={m} k={k} o={o} cap={cap}")
+    xd = dev(L.x)
+    _, _, bm = i8.vectorwise_quant(xd, TAU)
+    idx, count, xo = i8.outlier_extract(xd, bm, cap)
+    torch.cuda.synchronize()
+    ref = oracle.vectorwise_quant(L.x, TAU)
+    ridx, rcount, rxo = oracle.outlier_extract(L.x, ref.cols, cap)
+    assert int(host(count)[0]) == rcount
+    assert_equal(idx, ridx, "idx")
+    assert_equal(xo.view(torch.int16), rxo.view(np.int16), "x_out")
+
+
+MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128), (300, 600, 300),
+             (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100)]
+
+
+@pytest.mark.parametrize("m,n,k", MM_SHAPES)
+def test_linear_matmul_bit_exact(m, n, k):
+    rng = np.random.default_rng([72, m, n, k])
+    a = rng.integers(-128, 128, (m, k), dtype=np.int16).astype(np.int8)
+    b = rng.integers(-128, 128, (n, k), dtype=np.int16).astype(np.int8)
+    say(f"linear_matmul m={m} n={n} k={k}")
+    c = i8.linear_matmul(dev(a), dev(b))
+    torch.cuda.synchronize()
+    ref = a.astype(np.int64) @ b.astype(np.int64).T
+    assert_equal(c, oracle.int8_linear_matmul(a, b), "C")
+    assert np.array_equal(host(c).astype(np.int64), ref)
+
+
+def test_linear_matmul_unaligned_and_strided():
+    rng = np.random.default_rng(73)
+    m, n, k = 70, 90, 203
+    a_full = rng.integers(-127, 128, (m, k + 5), dtype=np.int16).astype(np.int8)
+    b_full = rng.integers(-127, 128, (n, k + 3), dtype=np.int16).astype(np.int8)
+    say("linear_matmul unaligned")
+    c = i8.linear_matmul(dev(a_full)[:, 1:k + 1], dev(b_full)[:, 2:k + 2])
+    torch.cuda.synchronize()
+    assert_equal(c, oracle.int8_linear_matmul(np.ascontiguousarray(a_full[:, 1:k + 1]),
+                                              np.ascontiguousarray(b_full[:, 2:k + 2])), "C")
+
+
+def test_linear_matmul_int32_extreme():
+    k = 8192
+    a = np.full((3, k), 127, np.int8)
+    a[1] = -127
+    b = np.full((2, k), 127, np.int8)
+    b[1, ::2] = -128
+    say("linear_matmul extremes")
+    c = i8.linear_matmul(dev(a), dev(b))
+    torch.cuda.synchronize()
+    assert_equal(c, oracle.int8_linear_matmul(a, b), "C")
+
+
+@pytest.mark.parametrize("m,n,k,o,bias", [(16, 1024, 1024, 4, True), (70, 300, 513, 9, False),
+                                          (33, 65, 200, 0, True), (5, 40, 64, 40, True)])
+def test_mm_dequant_parity(m, n, k, o, bias):
+    L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01 if bias else None, seed=(74, m, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    cap = max(o, 1)
+    ridx, rcount, rxo = oracle.outlier_extract(L.x, ref.quant.cols, cap)
+    say(f"mm_dequant m={m} n={n} k={k} o={o}")
+    count = torch.tensor([rcount], dtype=torch.int32, device="cuda")
+    out = i8.mm_dequant(dev(ref.c), dev(ref.quant.absmax), dev(ws), dev(L.bias) if bias else None,
+                        (dev(rxo), dev(ridx), count, dev(wq)))
+    out_plain = i8.mm_dequant(dev(ref.c), dev(ref.quant.absmax), dev(ws), dev(L.bias) if bias else None)
+    torch.cuda.synchronize()
+    assert_fp16_close(out, ref.out)
+    no_outl = oracle.mm_dequant(ref.c, ref.quant.absmax, ws, L.bias)
+    assert_fp16_close(out_plain, no_outl, "out without outlier term")
+
+
+FWD_CASES = [
+    # m, k, n, o, frac, bias, tau, cap
+    (16, 1024, 1024, 4, 1.0, True, TAU, 256),     # tiny workload shape
+    (1, 64, 32, 1, 1.0, False, TAU, 8),
+    (3, 33, 5, 2, 1.0, True, TAU, 8),
+    (300, 520, 600, 11, 0.3, True, TAU, 64),
+    (257, 1000, 259, 5, 1.0, False, TAU, 32),
+    (64, 256, 512, 0, 1.0, True, TAU, 32),        # no outliers present
+    (40, 300, 100, 3, 1.0, True, 0.0, 32),        # threshold off
+    (12, 96, 70, 96, 1.0, True, TAU, 96),         # every column an outlier
+    (4, 5120, 1000, 8, 1.0, False, TAU, 256),     # decode-shaped
+    (16, 2048, 512, 40, 0.5, False, TAU, 64),     # more outliers than one fp16 MFMA step
+]
+
+
+def _check_forward(L, wq, ws, tau, cap, what):
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, tau)
+    m, k = L.x.shape
+    n = wq.shape[0]
+    say(f"linear_forward {what}")
+    wsp = i8.LinearWorkspace.create(m, n, k, cap, "cuda")
+    out = i8.linear(dev(L.x), dev(wq), dev(ws), dev(L.bias) if L.bias is not None else None, tau, cap, wsp)
+    torch.cuda.synchronize()
+    assert_equal(wsp.codes(), ref.quant.q, "codes")
+    assert_equal(wsp.absmax(), ref.quant.absmax, "absmax")
+    assert_equal(wsp.bitmap().view(torch.int32), ref.quant.bitmap.view(np.int32), "bitmap")
+    assert int(host(wsp.count())[0]) == ref.quant.cols.size
+    ridx, _, rxo = oracle.outlier_extract(L.x, ref.quant.cols, cap)
+    assert_equal(wsp.idx(), ridx, "idx")
+    assert_equal(wsp.x_out().contiguous().view(torch.int16), rxo.view(np.int16), "x_out")
+    assert_fp16_close(out, ref.out)
+    return out, ref
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "m%d_k%d_n%d_o%d_f%g_b%d_t%g_c%d" % c)
+def test_linear_forward_parity(case):
+    m, k, n, o, frac, bias, tau, cap = case
+    L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01 if bias else None, seed=(75, m, k),
+                    outlier_row_frac=frac)
+    wq, ws = oracle.quantize_weight(L.w)
+    _check_forward(L, wq, ws, tau, cap, str(case))
+
+
+def test_linear_forward_gpu_quantized_weights():
+    """Weights quantized on the GPU are the oracle's, so the whole path can run
+    from the fp16 weight without touching the oracle."""
+    L = make_inputs(48, 700, 333, n_outlier=3, bias_std=0.01, seed=(76, 0, 0))
+    say("forward from GPU-quantized weights")
+    wq_g, ws_g = i8.quantize_weight(dev(L.w))
+    out = i8.linear(dev(L.x), wq_g, ws_g, dev(L.bias), TAU, 32)
+    torch.cuda.synchronize()
+    wq, ws = oracle.quantize_weight(L.w)
+    assert_equal(wq_g, wq, "weight codes")
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_fp16_close(out, ref.out)
+
+
+def test_linear_forward_zero_rows_and_zero_input():
+    L = make_inputs(20, 256, 130, n_outlier=2, bias_std=0.01, seed=(77, 0, 0))
+    L.x[[0, 7, 19]] = 0
+    wq, ws = oracle.quantize_weight(L.w)
+    _check_forward(L, wq, ws, TAU, 32, "zero rows")
+    L.x[:] = 0
+    out, ref = _check_forward(L, wq, ws, TAU, 32, "zero input")
+    assert np.array_equal(host(out), np.repeat(L.bias[None, :], 20, 0))
+
+
+def test_linear_forward_capacity_overflow_reports_count():
+    L = make_inputs(8, 512, 64, n_outlier=12, seed=(78, 0, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    say("forward cap overflow")
+    wsp = i8.LinearWorkspace.create(8, 64, 512, 4, "cuda")
+    i8.linear(dev(L.x), dev(wq), dev(ws), None, TAU, 4, wsp)
+    torch.cuda.synchronize()
+    assert int(host(wsp.count())[0]) == 12
+    assert wsp.outlier_overflow()
+    ref = oracle.vectorwise_quant(L.x, TAU)
+    assert_equal(wsp.idx(), ref.cols[:4].astype(np.int32), "first cap indices")
+
+
+def test_empty_calls_are_noops():
+    say("empty calls")
+    x = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    q, s, bm = i8.vectorwise_quant(x, TAU)
+    assert q.shape == (0, 64)
+    c = i8.linear_matmul(torch.empty((0, 64), dtype=torch.int8, device="cuda"),
+                         torch.zeros((5, 64), dtype=torch.int8, device="cuda"))
+    assert c.shape == (0, 5)
+    out = i8.linear(x, torch.zeros((5, 64), dtype=torch.int8, device="cuda"),
+                    torch.ones(5, device="cuda"), None, TAU, 8)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 5)
+    assert not host(bm).any()
+
+
+def test_deterministic_repeat():
+    L = make_inputs(300, 1024, 700, n_outlier=6, bias_std=0.01, seed=(79, 0, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
+    say("determinism")
+    o1 = i8.linear(x, w, s, b, TAU, 32).clone()
+    o2 = i8.linear(x, w, s, b, TAU, 32).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_non_default_stream():
+    L = make_inputs(64, 512, 256, n_outlier=3, bias_std=0.01, seed=(80, 0, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
+    torch.cuda.synchronize()
+    say("side stream")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        out = i8.linear(x, w, s, b, TAU, 32)
+    st.synchronize()
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_fp16_close(out, ref.out)
+
+
+def test_graph_capture_replays_match_eager():
+    L = make_inputs(128, 1024, 512, n_outlier=5, bias_std=0.01, seed=(81, 0, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
+    wsp = i8.LinearWorkspace.create(128, 512, 1024, 32, "cuda")
+    out = torch.empty((128, 512), dtype=torch.float16, device="cuda")
+    say("graph capture")
+    eager = i8.linear(x, w, s, b, TAU, 32, wsp).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            i8.linear(x, w, s, b, TAU, 32, wsp, out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(0)
+        wsp.buf.fill_(0x5a)      # the replay must not depend on workspace contents
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_fp16_close(out, ref.out)
