@@ -254,6 +254,7 @@ i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* w
     GemmArgs g{};
     g.a = reinterpret_cast<const int8_t*>(ws + L.q_offset);
     g.lda = L.ldq;
+    g.a_zero_padded = true;
     g.b = w_q;
     g.ldb = ldw;
     g.m = m;

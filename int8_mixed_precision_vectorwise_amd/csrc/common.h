@@ -19,7 +19,6 @@ typedef uint16_t half_bits;
 // ---- outlier detection / quantization plan ---------------------------------
 constexpr int kQuantThreads = 256;
 constexpr int kDetectCols = 256;      // columns per detect workgroup (32 lanes x 8 fp16)
-constexpr int kMaxPartialWordsPerWG = 8192;  // bound on partial-bitmap words a quant WG ORs
 
 struct QuantPlan {
     int64_t words;        // ceil(k / 32)
@@ -37,30 +36,33 @@ inline QuantPlan make_quant_plan(int64_t m, int64_t k, bool detect) {
     QuantPlan p{};
     p.words = ceil_div(k, 32);
     p.detect_gx = ceil_div(k, kDetectCols);
+    // rows per quant workgroup: 4 waves, one row per wave at a time; enough
+    // workgroups to cover the CUs twice before giving a wave more rows
+    auto quant_rows = [&](int64_t r) {
+        int64_t rpb = 4 * ceil_div(r, 8);            // amortize the partial-bitmap OR
+        if (rpb < 4) rpb = 4;
+        while (rpb > 4 && ceil_div(m, rpb) < 512) rpb -= 4;
+        return rpb;
+    };
     if (!detect || m <= 0) {
         p.row_blocks = 0;
         p.rows_per_detect_block = 0;
-        p.rows_per_quant_block = m >= 2048 ? 4 : 1;
+        p.rows_per_quant_block = quant_rows(0);
         p.partial_bytes = 0;
         return p;
     }
-    int64_t r_max = kMaxPartialWordsPerWG / p.words;
-    if (r_max < 1) r_max = 1;
-    int64_t r_want = ceil_div(2048, p.detect_gx);
-    int64_t r = r_want < r_max ? r_want : r_max;
-    int64_t r_rows = ceil_div(m, 8);
+    // row blocks of the detect grid: about 1024 workgroups, at least 8 rows each,
+    // at most 32 partials (the OR every quant workgroup does is R words per word)
+    int64_t r = ceil_div(1024, p.detect_gx);
+    if (r > 32) r = 32;
+    const int64_t r_rows = ceil_div(m, 8);
     if (r > r_rows) r = r_rows;
     if (r < 1) r = 1;
-    int64_t rb = round_up(ceil_div(m, r), 8);
+    const int64_t rb = round_up(ceil_div(m, r), 8);
     r = ceil_div(m, rb);
     p.row_blocks = r;
     p.rows_per_detect_block = rb;
-    // Each quant workgroup ORs r partial words per bitmap word; give it enough
-    // rows that this stays small next to the rows it reads.
-    int64_t rpb = ceil_div(r, 2);
-    if (rpb < 1) rpb = 1;
-    if (rpb > 16) rpb = 16;
-    p.rows_per_quant_block = rpb;
+    p.rows_per_quant_block = quant_rows(r);
     p.partial_bytes = (size_t)(r * p.words) * sizeof(uint32_t);
     return p;
 }
@@ -96,6 +98,7 @@ struct GemmArgs {
     const int8_t* a; int64_t lda;
     const int8_t* b; int64_t ldb;
     int64_t m, n, k;
+    bool a_zero_padded;                  // A rows hold zeros from k to a multiple of 128
     int32_t* c; int64_t ldc;             // int32 output (unfused)
     // fused epilogue
     const float* row_absmax;

@@ -10,12 +10,19 @@
 //
 // Design (CDNA4): 256 threads = 4 wave64 in a 2 x 2 grid; each wave owns a
 // (BM/2) x (BN/2) block of 32x32 accumulators fed by v_mfma_i32_32x32x32_i8.
-// K advances in 128-byte tiles staged through LDS, double-buffered, loaded
-// with 16-byte global loads into registers one tile ahead.  LDS rows are
-// 128 bytes with the 16-byte chunk index XOR-swizzled by (row & 7), so the
-// 16-byte fragment reads of 8 consecutive lanes hit distinct banks.  The
-// contraction order inside an MFMA does not matter: A and B fragments use the
-// same lane -> k mapping, and integer sums are exact in any order.
+// K advances in 128-byte tiles staged through LDS, double-buffered; the next
+// tile is fetched into registers with 16-byte buffer loads while the current
+// one is multiplied.  Buffer loads return 0 past the end of the matrix, so
+// rows beyond m or n need no branches; only the last K tile of an operand
+// whose rows are not zero-padded is masked.  LDS rows are 128 bytes with the
+// 16-byte chunk index XOR-swizzled (swz) so that fragment reads are free of
+// bank conflicts.  The contraction order inside an
+// MFMA does not matter: A and B fragments use the same lane -> k mapping, and
+// integer sums are exact in any order.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
+// remapped so that each XCD works on a contiguous run of tiles (sharing
+// operand rows in its own L2), walked in groups of kGroupM tile rows.
 #include "common.h"
 
 namespace i8mp {
@@ -24,135 +31,72 @@ namespace {
 
 constexpr int BK = 128;
 constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ inline float h2f(half_bits h) {
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-__device__ inline half_bits f2h(float f) {
-    return __builtin_bit_cast(half_bits, (_Float16)f);
+__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, (_Float16)f); }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+    if (bytes < 0) bytes = 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
-// 16 bytes of row `row` at byte offset `col` (k-relative), zero past k.
-template <bool kAligned>
-__device__ inline v4i load16(const int8_t* __restrict__ base, int64_t ld, int64_t row, int64_t nrows,
-                             int64_t col, int64_t k) {
+// 128-byte LDS rows.  A wave's 16-byte LDS accesses are served 16 lanes
+// (256 bytes) at a time; lanes 0-15 of an MFMA fragment read rows r..r+15 at
+// the same K chunk, so the chunk is XOR-ed with (row >> 1) & 7: the 16 rows
+// then cover all 16 distinct 16-byte bank groups of a 256-byte bank line.
+__device__ inline int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// zero the bytes of a 16-byte chunk at or beyond `valid` (0..16)
+__device__ inline v4i mask_tail(v4i v, int valid) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        int nb = valid - 4 * d;
+        nb = nb < 0 ? 0 : (nb > 4 ? 4 : nb);
+        const uint32_t m = nb >= 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+        v[d] = (int)((uint32_t)v[d] & m);
+    }
+    return v;
+}
+
+// Unaligned operands (leading dimension or base not 16-byte aligned): bytes.
+__device__ inline v4i load16_bytes(const int8_t* __restrict__ base, int64_t ld, int64_t row,
+                                   int64_t nrows, int64_t col, int64_t k) {
     v4i r = {0, 0, 0, 0};
-    if (row >= nrows || col >= k) return r;
+    if (row >= nrows) return r;
     const int8_t* p = base + row * ld + col;
-    if (kAligned && col + 16 <= k) return *reinterpret_cast<const v4i*>(p);
-    uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-        if (col + e < k) w[e >> 2] |= ((uint32_t)(uint8_t)p[e]) << (8 * (e & 3));
-    r[0] = (int)w[0];
-    r[1] = (int)w[1];
-    r[2] = (int)w[2];
-    r[3] = (int)w[3];
+        if (col + e < k) r[e >> 2] |= (int)(((uint32_t)(uint8_t)p[e]) << (8 * (e & 3)));
     return r;
 }
 
-__device__ inline int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
-
-}  // namespace
-
-template <int BM, int BN, bool kFused, bool kAligned>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int A_CH = BM * BK / 16 / 256;
-    constexpr int B_CH = BN * BK / 16 / 256;
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // grouped tile order: kGroupM tile rows walk the N tiles together
-    const int64_t tiles_m = (g.m + BM - 1) / BM;
-    const int64_t tiles_n = (g.n + BN - 1) / BN;
-    const int64_t bid = blockIdx.x;
+__device__ inline void tile_coords(int64_t bid, int64_t nblocks, int64_t tiles_m, int64_t tiles_n,
+                                   int64_t& tm, int64_t& tn) {
+    const int64_t full = (nblocks / kXcds) * kXcds;
+    int64_t t = bid;
+    if (bid < full) t = (bid % kXcds) * (full / kXcds) + bid / kXcds;
     const int64_t in_group = (int64_t)kGroupM * tiles_n;
-    const int64_t group = bid / in_group;
+    const int64_t group = t / in_group;
     const int64_t first_m = group * kGroupM;
     int64_t gsize = tiles_m - first_m;
     if (gsize > kGroupM) gsize = kGroupM;
-    const int64_t tm = first_m + (bid % in_group) % gsize;
-    const int64_t tn = (bid % in_group) / gsize;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    tm = first_m + (t % in_group) % gsize;
+    tn = (t % in_group) / gsize;
+}
 
-    v16i acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+}  // namespace
 
-    v4i ra[A_CH], rb[B_CH];
-    const int64_t ktiles = (g.k + BK - 1) / BK;
-
-    auto gload = [&](int64_t kt) {
-#pragma unroll
-        for (int p = 0; p < A_CH; ++p) {
-            const int id = p * 256 + tid;
-            ra[p] = load16<kAligned>(g.a, g.lda, m0 + (id >> 3), g.m, kt * BK + (id & 7) * 16, g.k);
-        }
-#pragma unroll
-        for (int p = 0; p < B_CH; ++p) {
-            const int id = p * 256 + tid;
-            rb[p] = load16<kAligned>(g.b, g.ldb, n0 + (id >> 3), g.n, kt * BK + (id & 7) * 16, g.k);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < A_CH; ++p) {
-            const int id = p * 256 + tid;
-            *reinterpret_cast<v4i*>(&As[buf][swz(id >> 3, id & 7)]) = ra[p];
-        }
-#pragma unroll
-        for (int p = 0; p < B_CH; ++p) {
-            const int id = p * 256 + tid;
-            *reinterpret_cast<v4i*>(&Bs[buf][swz(id >> 3, id & 7)]) = rb[p];
-        }
-    };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < ktiles) gload(kt + 1);
-#pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            v4i af[FM], bf[FN];
-            const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * WM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const v4i*>(&As[buf][swz(row, ch)]);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * WN + j * 32 + (lane & 31);
-                bf[j] = *reinterpret_cast<const v4i*>(&Bs[buf][swz(row, ch)]);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < ktiles) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // accumulator (i, j, r) of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
-    // column l%32 of the 32x32 block (i, j)
-    const int64_t wrow0 = m0 + wm * WM + 4 * (lane >> 5);
-    const int64_t wcol0 = n0 + wn * WN + (lane & 31);
-
+// Epilogue shared by both GEMM kernels.  Accumulator (i, j, r) of lane l
+// holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of 32x32 block (i, j);
+// wrow0 / wcol0 are this lane's first row and column.
+template <int BM, int BN, bool kFused>
+__device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[BM / 64][BN / 64], int64_t m0, int64_t wrow0,
+                                int64_t wcol0, int lane, int wm) {
+    constexpr int WM = BM / 2;
+    constexpr int FM = BM / 64, FN = BN / 64;
     if constexpr (!kFused) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -183,16 +127,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            float sxr[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = wrow0 + 32 * i + 8 * (r >> 2) + (r & 3);
-                sxr[r] = row < g.m ? g.row_absmax[row] * r127 : 0.0f;
-            }
             int64_t arow = m0 + wm * WM + i * 32 + (lane & 31);
             if (arow >= g.m) arow = g.m - 1;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
+                // row scales reloaded per block (L1 hits) to keep few registers live
+                float sxr[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = wrow0 + 32 * i + 8 * (r >> 2) + (r & 3);
+                    sxr[r] = row < g.m ? g.row_absmax[row] * r127 : 0.0f;
+                }
                 v16f p;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[r] = 0.0f;
@@ -223,20 +168,472 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
 }
 
-template <bool kFused>
-static hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
-    constexpr int BM = 256, BN = 256;
-    const bool aligned = ((g.lda & 15) == 0) && ((g.ldb & 15) == 0) &&
-                         ((reinterpret_cast<uintptr_t>(g.a) & 15) == 0) &&
-                         ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
+template <int BM, int BN, bool kFused, bool kAligned>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int A_CH = BM * BK / 16 / 256;
+    constexpr int B_CH = BN * BK / 16 / 256;
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int64_t tiles_m = (g.m + BM - 1) / BM;
+    const int64_t tiles_n = (g.n + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int64_t ktiles = (g.k + BK - 1) / BK;
+    const int ktail = (int)(g.k - (ktiles - 1) * BK);  // valid bytes in the last K tile
+
+    // per-thread chunk coordinates within a tile: row = id >> 3, chunk = id & 7
+    // The range ends 16-byte-rounded past the last valid row's k bytes: with
+    // 16-byte aligned rows that never leaves the row's final 16-byte granule.
+    const int64_t k16 = (g.k + 15) & ~(int64_t)15;
+    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + k16);
+    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + k16);
+    int a_off[A_CH], b_off[B_CH];
+#pragma unroll
+    for (int p = 0; p < A_CH; ++p) {
+        const int id = p * 256 + tid;
+        a_off[p] = (int)((id >> 3) * g.lda + (id & 7) * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < B_CH; ++p) {
+        const int id = p * 256 + tid;
+        b_off[p] = (int)((id >> 3) * g.ldb + (id & 7) * 16);
+    }
+
+    v4i ra[A_CH], rb[B_CH];
+    auto gload = [&](int64_t kt) {
+        const int kb = (int)(kt * BK);
+        if constexpr (kAligned) {
+#pragma unroll
+            for (int p = 0; p < A_CH; ++p)
+                ra[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_src, a_off[p], kb, 0));
+#pragma unroll
+            for (int p = 0; p < B_CH; ++p)
+                rb[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb_src, b_off[p], kb, 0));
+            if (kt == ktiles - 1 && ktail < BK) {
+                // bytes past k belong to the next row: zero them in A (B's are then harmless)
+#pragma unroll
+                for (int p = 0; p < A_CH; ++p) {
+                    const int id = p * 256 + tid;
+                    ra[p] = mask_tail(ra[p], ktail - (id & 7) * 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < A_CH; ++p) {
+                const int id = p * 256 + tid;
+                ra[p] = load16_bytes(g.a, g.lda, m0 + (id >> 3), g.m, kb + (id & 7) * 16, g.k);
+            }
+#pragma unroll
+            for (int p = 0; p < B_CH; ++p) {
+                const int id = p * 256 + tid;
+                rb[p] = load16_bytes(g.b, g.ldb, n0 + (id >> 3), g.n, kb + (id & 7) * 16, g.k);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < A_CH; ++p) {
+            const int id = p * 256 + tid;
+            *reinterpret_cast<v4i*>(&As[buf][swz(id >> 3, id & 7)]) = ra[p];
+        }
+#pragma unroll
+        for (int p = 0; p < B_CH; ++p) {
+            const int id = p * 256 + tid;
+            *reinterpret_cast<v4i*>(&Bs[buf][swz(id >> 3, id & 7)]) = rb[p];
+        }
+    };
+
+    // Fragments are double-buffered across the four 32-deep K steps of a tile:
+    // step s multiplies set s&1 while set (s+1)&1 is read from LDS.  The last
+    // step's MFMAs are split around the barrier so that reading the next
+    // tile's first fragments overlaps the second half of them.
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int s, int set) {
+        const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + i * 32 + (lane & 31);
+            fa[set][i] = *reinterpret_cast<const v4i*>(&As[buf][swz(row, ch)]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WN + j * 32 + (lane & 31);
+            fb[set][j] = *reinterpret_cast<const v4i*>(&Bs[buf][swz(row, ch)]);
+        }
+    };
+    auto mfmas = [&](int set, int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    };
+    constexpr int kFrags = FM + FN;   // LDS reads per step
+    constexpr int kMfma = FM * FN;    // MFMAs per step
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    read_frags(0, 0, 0);
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const int buf = (int)(kt & 1);
+        const bool more = kt + 1 < ktiles;
+        if (more) gload(kt + 1);
+#pragma unroll
+        for (int s = 0; s < BK / 32 - 1; ++s) {
+            read_frags(buf, s + 1, (s + 1) & 1);
+            mfmas(s & 1, 0, FM);
+            // interleave: one LDS read between consecutive MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+            for (int t = 0; t < kFrags; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kFrags - 1 > 0 ? kMfma - kFrags - 1 : 0, 0);
+        }
+        if (more) sstore(buf ^ 1);
+        mfmas(1, 0, FM / 2);
+        __syncthreads();
+        if (more) read_frags(buf ^ 1, 0, 0);
+        mfmas(1, FM / 2, FM);
+    }
+
+    // accumulator (i, j, r) of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
+    // column l%32 of the 32x32 block (i, j)
+    const int64_t wrow0 = m0 + wm * WM + 4 * (lane >> 5);
+    const int64_t wcol0 = n0 + wn * WN + (lane & 31);
+    epilogue<BM, BN, kFused>(g, acc, m0, wrow0, wcol0, lane, wm);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined variant for 16-byte aligned operands whose K extent is covered by
+// whole stages (k % BKS == 0, or A zero-padded past k as the forward's codes
+// are): operands go global -> LDS with buffer_load ... lds (no register
+// staging), STAGES stages of BKS bytes of K deep.  A wave's DMA instruction
+// writes 1 KB of LDS contiguously (1024 / BKS rows of BKS bytes; lane i ->
+// row i / (BKS/16), 16-byte slot i % (BKS/16)); the lane fetches the global
+// chunk that belongs in that slot under the swizzle of swz_k.
+
+// LDS rows of BKS bytes.  A wave's 16-byte LDS accesses are served 16 lanes
+// (256 bytes) at a time and lanes 0-15 of an MFMA fragment read rows r..r+15 at
+// one K chunk, so the chunk is XOR-ed with bits of the row that differ within
+// each group of rows sharing a 256-byte bank line.
+template <int BKS>
+__device__ inline int swz_k(int row, int chunk) {
+    if constexpr (BKS == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+    else return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// One wave-wide 16-byte-per-lane global -> LDS copy: lane i's bytes land at
+// lds + 16 * i (lds must be wave-uniform).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                             soffset, 0, 0);
+}
+
+__device__ inline void wait_vm(int n) {
+    // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt at their maxima);
+    // gfx9 encoding: vmcnt bits [3:0] and [15:14]
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0f73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0f76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0f77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0x0f79); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0f7a); break;
+        case 11: __builtin_amdgcn_s_waitcnt(0x0f7b); break;
+        case 12: __builtin_amdgcn_s_waitcnt(0x0f7c); break;
+        case 13: __builtin_amdgcn_s_waitcnt(0x0f7d); break;
+        case 14: __builtin_amdgcn_s_waitcnt(0x0f7e); break;
+        case 15: __builtin_amdgcn_s_waitcnt(0x0f7f); break;
+        case 16: __builtin_amdgcn_s_waitcnt(0x4f70); break;
+        case 17: __builtin_amdgcn_s_waitcnt(0x4f71); break;
+        case 18: __builtin_amdgcn_s_waitcnt(0x4f72); break;
+        case 19: __builtin_amdgcn_s_waitcnt(0x4f73); break;
+        case 20: __builtin_amdgcn_s_waitcnt(0x4f74); break;
+        case 21: __builtin_amdgcn_s_waitcnt(0x4f75); break;
+        case 22: __builtin_amdgcn_s_waitcnt(0x4f76); break;
+        case 23: __builtin_amdgcn_s_waitcnt(0x4f77); break;
+        case 24: __builtin_amdgcn_s_waitcnt(0x4f78); break;
+        case 25: __builtin_amdgcn_s_waitcnt(0x4f79); break;
+        case 26: __builtin_amdgcn_s_waitcnt(0x4f7a); break;
+        case 27: __builtin_amdgcn_s_waitcnt(0x4f7b); break;
+        case 28: __builtin_amdgcn_s_waitcnt(0x4f7c); break;
+        case 29: __builtin_amdgcn_s_waitcnt(0x4f7d); break;
+        case 30: __builtin_amdgcn_s_waitcnt(0x4f7e); break;
+        case 31: __builtin_amdgcn_s_waitcnt(0x4f7f); break;
+        case 32: __builtin_amdgcn_s_waitcnt(0x8f70); break;
+        case 33: __builtin_amdgcn_s_waitcnt(0x8f71); break;
+        case 34: __builtin_amdgcn_s_waitcnt(0x8f72); break;
+        case 35: __builtin_amdgcn_s_waitcnt(0x8f73); break;
+        case 36: __builtin_amdgcn_s_waitcnt(0x8f74); break;
+        case 37: __builtin_amdgcn_s_waitcnt(0x8f75); break;
+        case 38: __builtin_amdgcn_s_waitcnt(0x8f76); break;
+        case 39: __builtin_amdgcn_s_waitcnt(0x8f77); break;
+        case 40: __builtin_amdgcn_s_waitcnt(0x8f78); break;
+        case 41: __builtin_amdgcn_s_waitcnt(0x8f79); break;
+        case 42: __builtin_amdgcn_s_waitcnt(0x8f7a); break;
+        case 43: __builtin_amdgcn_s_waitcnt(0x8f7b); break;
+        case 44: __builtin_amdgcn_s_waitcnt(0x8f7c); break;
+        case 45: __builtin_amdgcn_s_waitcnt(0x8f7d); break;
+        case 46: __builtin_amdgcn_s_waitcnt(0x8f7e); break;
+        case 47: __builtin_amdgcn_s_waitcnt(0x8f7f); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    }
+}
+
+template <int BM, int BN, int BKS, int STAGES, bool kFused, int MINW = 1>
+__global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int NSTEP = BKS / 32;               // 32-deep MFMA steps per stage
+    constexpr int LPR = BKS / 16;                 // lanes per row in a DMA instruction
+    constexpr int RPI = 64 / LPR;                 // rows per DMA instruction
+    constexpr int STAGE_A = BM * BKS, STAGE_B = BN * BKS;
+    constexpr int STAGE = STAGE_A + STAGE_B;
+    constexpr int A_INS = STAGE_A / 1024 / 4;     // DMA instructions per wave per stage
+    constexpr int B_INS = STAGE_B / 1024 / 4;
+    constexpr int INS = A_INS + B_INS;
+    static_assert(A_INS >= 1 && B_INS >= 1, "tile too small for 4-wave DMA");
+    static_assert(STAGES >= 2, "need at least two stages");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int64_t tiles_m = (g.m + BM - 1) / BM;
+    const int64_t tiles_n = (g.n + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    const int64_t kr = (g.k + BKS - 1) / BKS * BKS;
+    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + kr);
+    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + kr);
+    int a_off[A_INS], b_off[B_INS];
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+        const int row = (wave * A_INS + j) * RPI + lane / LPR;
+        const int slot = lane % LPR;
+        a_off[j] = (int)(row * g.lda + ((swz_k<BKS>(row, slot) - row * BKS)));
+    }
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+        const int row = (wave * B_INS + j) * RPI + lane / LPR;
+        const int slot = lane % LPR;
+        b_off[j] = (int)(row * g.ldb + ((swz_k<BKS>(row, slot) - row * BKS)));
+    }
+    auto dma = [&](int64_t kt, int stage) {
+        const int kb = (int)(kt * BKS);
+        int8_t* base = smem + stage * STAGE;
+#pragma unroll
+        for (int j = 0; j < A_INS; ++j) dma16(ra_src, base + (wave * A_INS + j) * 1024, a_off[j], kb);
+#pragma unroll
+        for (int j = 0; j < B_INS; ++j) dma16(rb_src, base + STAGE_A + (wave * B_INS + j) * 1024, b_off[j], kb);
+    };
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int stage, int s, int set) {
+        const int8_t* base = smem + stage * STAGE;
+        const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + i * 32 + (lane & 31);
+            fa[set][i] = *reinterpret_cast<const v4i*>(base + swz_k<BKS>(row, ch));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WN + j * 32 + (lane & 31);
+            fb[set][j] = *reinterpret_cast<const v4i*>(base + STAGE_A + swz_k<BKS>(row, ch));
+        }
+    };
+    auto mfma_rows = [&](int set, int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    };
+    auto barrier = [&]() {
+        // LDS reads done, then s_barrier; the signal fences only stop the
+        // compiler from moving memory accesses across it.  A memory fence
+        // would also wait for the later tiles' DMA, which must stay in flight.
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    // Tile t lives in stage t % STAGES; STAGES - 1 tiles are requested ahead.
+    // The tile that refills stage (kt-1) % STAGES (free once every wave passed
+    // the barrier that ends iteration kt-1) is requested during iteration kt,
+    // its DMA instructions spread between the MFMAs so that the wave never
+    // stalls on a burst of them with the matrix core idle.  A wave waits for
+    // its own DMA of a tile with s_waitcnt vmcnt (the tiles requested after it
+    // stay in flight); the barrier then makes every wave's part visible.
+    // Requests past the last tile read through a zero-length buffer range:
+    // they fetch nothing, return zeros, and land in a stage that is not read
+    // again.  Issuing them keeps the instruction stream branch-free (so the DMA
+    // can be interleaved with the MFMAs) and every vmcnt wait a constant.
+    const __amdgpu_buffer_rsrc_t r_none = make_rsrc(g.a, 0);
+    auto dma_part = [&](int64_t kt, bool real, int stage, int first, int count) {
+        const int kb = (int)(kt * BKS);
+        int8_t* base = smem + stage * STAGE;
+        const __amdgpu_buffer_rsrc_t sa = real ? ra_src : r_none;
+        const __amdgpu_buffer_rsrc_t sb = real ? rb_src : r_none;
+#pragma unroll
+        for (int q = 0; q < INS; ++q) {
+            if (q < first || q >= first + count) continue;
+            if (q < A_INS)
+                dma16(sa, base + (wave * A_INS + q) * 1024, a_off[q], kb);
+            else
+                dma16(sb, base + STAGE_A + (wave * B_INS + (q - A_INS)) * 1024, b_off[q - A_INS], kb);
+        }
+    };
+    const int64_t ktiles = (g.k + BKS - 1) / BKS;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) dma_part(st, st < ktiles, st, 0, INS);
+    wait_vm((STAGES - 2) * INS);  // tile 0 landed (tiles 1 .. STAGES-2 may be in flight)
+    barrier();
+    read_frags(0, 0, 0);
+    // DMA instructions per MFMA step of this iteration
+    constexpr int DMA_PER_STEP = (INS + NSTEP - 1) / NSTEP;
+    constexpr int DMA_LAST = INS - (NSTEP - 1) * DMA_PER_STEP;
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const int stage = (int)(kt % STAGES);
+        const int64_t nt = kt + STAGES - 1;              // tile requested in this iteration
+        const bool req = nt < ktiles;
+        const int rstage = (int)(nt % STAGES);
+#pragma unroll
+        for (int s = 0; s < NSTEP - 1; ++s) {
+            read_frags(stage, s + 1, (s + 1) & 1);
+            dma_part(nt, req, rstage, s * DMA_PER_STEP, DMA_PER_STEP);
+            mfma_rows(s & 1, 0, FM);
+#pragma unroll
+            for (int t = 0; t < FM + FN; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < DMA_PER_STEP; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+        constexpr int LAST = (NSTEP - 1) & 1;
+        dma_part(nt, req, rstage, (NSTEP - 1) * DMA_PER_STEP, DMA_LAST);
+        mfma_rows(LAST, 0, FM - 1);
+#pragma unroll
+        for (int t = 0; t < DMA_LAST; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        if (kt + 1 < ktiles) {
+            // tiles requested after kt+1: kt+2 .. kt+STAGES-1 (real or not)
+            wait_vm((STAGES - 2) * INS);
+            barrier();  // tile kt+1 is in LDS everywhere; stage kt is no longer read
+            read_frags((int)((kt + 1) % STAGES), 0, 0);
+        }
+        // the last row of MFMAs covers the next fragments' LDS latency
+        mfma_rows(LAST, FM - 1, FM);
+    }
+
+    const int64_t wrow0 = m0 + wm * WM + 4 * (lane >> 5);
+    const int64_t wcol0 = n0 + wn * WN + (lane & 31);
+    epilogue<BM, BN, kFused>(g, acc, m0, wrow0, wcol0, lane, wm);
+}
+
+namespace {
+
+// Launch one tile shape: the pipelined direct-to-LDS kernel (128-byte K
+// stages, as many stages as fit 160 KB of LDS, at most 4) when both operands
+// are 16-byte aligned and A covers whole stages; the register-staged kernel
+// otherwise.
+template <int BM, int BN, bool kFused>
+hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t stream) {
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
     dim3 grid((unsigned)tiles);
-    if (aligned)
+    constexpr int kStages = (160 * 1024) / ((BM + BN) * 128) > 4 ? 4 : (160 * 1024) / ((BM + BN) * 128);
+    if (staged)
+        hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, 128, kStages, kFused>), grid, dim3(256), 0, stream, g);
+    else if (aligned)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, kFused, true>), grid, dim3(256), 0, stream, g);
     else
         hipLaunchKernelGGL((gemm_kernel<BM, BN, kFused, false>), grid, dim3(256), 0, stream, g);
     return hipGetLastError();
 }
+
+// Tile shape by a simple cost model: rounds of workgroups over the 256 CUs
+// times the tile's work, divided by the tile's measured relative efficiency
+// (operand reuse falls with the tile size).  Ties go to the larger tile.
+int pick_tile(int64_t m, int64_t n) {
+    constexpr int64_t kCUs = 256;
+    struct Cand { int bm, bn; double eff; };
+    const Cand cands[4] = {{256, 256, 1.0}, {256, 128, 1.0}, {128, 128, 0.85}, {64, 64, 0.35}};
+    int best = 0;
+    double best_cost = 1e300;
+    for (int c = 0; c < 4; ++c) {
+        const int64_t tiles = ((m + cands[c].bm - 1) / cands[c].bm) * ((n + cands[c].bn - 1) / cands[c].bn);
+        const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+        const double cost = (double)rounds * cands[c].bm * cands[c].bn / cands[c].eff;
+        if (cost < best_cost * 0.999) {
+            best_cost = cost;
+            best = c;
+        }
+    }
+    return best;
+}
+
+template <bool kFused>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+    const bool aligned = ((g.lda & 15) == 0) && ((g.ldb & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(g.a) & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
+    // the staged kernel reads whole 128-byte K stages: A must be zero past k
+    const bool staged = aligned && ((g.k & 127) == 0 || g.a_zero_padded);
+    switch (pick_tile(g.m, g.n)) {
+        case 0: return launch_tile<256, 256, kFused>(g, aligned, staged, stream);
+        case 1: return launch_tile<256, 128, kFused>(g, aligned, staged, stream);
+        case 2: return launch_tile<128, 128, kFused>(g, aligned, staged, stream);
+        default: return launch_tile<64, 64, kFused>(g, aligned, false, stream);
+    }
+}
+
+}  // namespace
 
 hipError_t launch_gemm_i32(const GemmArgs& g, hipStream_t stream) { return launch_gemm<false>(g, stream); }
 hipError_t launch_gemm_fused(const GemmArgs& g, hipStream_t stream) { return launch_gemm<true>(g, stream); }

@@ -13,11 +13,11 @@
 //   detect_kernel  one pass over X: per (row block, 256-column block) a word
 //                  of the partial outlier bitmap (no atomics, no zeroing: every
 //                  word of every partial is written);
-//   quant_kernel   ORs the partial bitmaps into LDS, then per row: coalesced
-//                  16-byte loads, wavefront-shuffle + LDS absmax over the
-//                  non-outlier columns, IEEE fp32 quantization, 8-byte code
-//                  stores, gather of the outlier values into the compact fp16
-//                  matrix.  Workgroup 0 also writes the bitmap, the ascending
+//   quant_kernel   ORs the partial bitmaps into LDS, then one row per
+//                  wavefront: coalesced 16-byte loads, wavefront-shuffle absmax
+//                  over the non-outlier columns, IEEE fp32 quantization, 8-byte
+//                  code stores, gather of the outlier values into the compact
+//                  fp16 matrix.  Workgroup 0 also writes the bitmap, the ascending
 //                  index list and the count.
 #include "common.h"
 
@@ -123,14 +123,17 @@ __global__ __launch_bounds__(256) void detect_kernel(const half_bits* __restrict
     }
 }
 
-// NCH > 0: each thread keeps NCH chunks of 8 columns of the row in registers
-// (k <= NCH * 2048); NCH == 0: the row is streamed twice (any k).
-template <int NCH, bool kVec>
+// Rows are processed one per wavefront (no workgroup barrier inside the row
+// loop), in batches of kBatch 16-byte loads per lane that are all in flight
+// together.  A row of at most one batch (k <= 4096) stays in registers; a
+// longer row is read twice, the second time from L2 / the infinity cache.
+constexpr int kBatch = 8;
+
+template <bool kVec>
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     extern __shared__ uint32_t smem[];
     uint32_t* bm = smem;                                       // [words]
     int32_t* pre = reinterpret_cast<int32_t*>(smem + a.words);  // [words]
-    __shared__ float red[4];
     __shared__ int32_t wave_tot[4];
 
     const int tid = threadIdx.x;
@@ -139,14 +142,28 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     const bool outl = a.partial != nullptr;
     const bool need_prefix = outl && (a.x_out || a.idx_out || a.count_out);
 
-    // 1. the final outlier bitmap: OR of the per-row-block partials
+    // 1. the final outlier bitmap: OR of the per-row-block partials.  The
+    // partial words are independent loads; 8 are kept in flight per thread and
+    // folded into LDS with ds_or.
     if (outl) {
-        for (int64_t w = tid; w < a.words; w += 256) {
-            uint32_t v = 0;
-            for (int64_t r = 0; r < a.row_blocks; ++r) v |= a.partial[r * a.words + w];
-            if (w == a.words - 1 && (a.k & 31)) v &= (1u << (a.k & 31)) - 1u;
-            bm[w] = v;
+        for (int64_t w = tid; w < a.words; w += 256) bm[w] = 0u;
+        __syncthreads();
+        const int64_t total_words = a.row_blocks * a.words;
+        for (int64_t f0 = tid; f0 < total_words; f0 += 256 * 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t f = f0 + 256 * u;
+                v[u] = f < total_words ? a.partial[f] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t f = f0 + 256 * u;
+                if (v[u]) atomicOr(&bm[f % a.words], v[u]);
+            }
         }
+        __syncthreads();
+        if (tid == 0 && (a.k & 31)) bm[a.words - 1] &= (1u << (a.k & 31)) - 1u;
     }
     __syncthreads();
 
@@ -204,55 +221,46 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
         }
     }
 
-    // 4. rows
+    // 4. rows, one per wavefront
     const int64_t nchunks = (a.k + 7) / 8;
+    const int64_t nbatch = (nchunks + 64 * kBatch - 1) / (64 * kBatch);
     const bool vec_q = a.q && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
-    for (int64_t rr = 0; rr < a.rows_per_block; ++rr) {
+    auto obyte = [&](int64_t col) -> uint32_t {
+        return outl ? (bm[col >> 5] >> (col & 31)) & 0xffu : 0u;
+    };
+    auto chunk_max = [&](const uint4& vv, uint32_t obits) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = fabsf(h2f(half_at(vv, e)));
+            t = ((obits >> e) & 1u) ? t : fmaxf(t, f);
+        }
+        return t;
+    };
+    for (int64_t rr = wave; rr < a.rows_per_block; rr += 4) {
         const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
         if (r >= a.m) break;
         const half_bits* __restrict__ xr = a.x + r * a.ldx;
-        constexpr int RC = NCH > 0 ? NCH : 1;
-        uint4 v[RC];
-        uint32_t ob[RC];
+        uint4 v[kBatch];
+        auto load_batch = [&](int64_t b) {
+#pragma unroll
+            for (int c = 0; c < kBatch; ++c) {
+                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
+                v[c] = col < a.k ? load8<kVec>(xr, col, a.k) : make_uint4(0, 0, 0, 0);
+            }
+        };
 
         // 4a. absmax over the non-outlier columns
         float mx = 0.0f;
-        auto chunk_max = [&](const uint4& vv, uint32_t obits) {
-            float t = 0.0f;
+        for (int64_t b = 0; b < nbatch; ++b) {
+            load_batch(b);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = fabsf(h2f(half_at(vv, e)));
-                t = ((obits >> e) & 1u) ? t : fmaxf(t, f);
-            }
-            return t;
-        };
-        auto obyte = [&](int64_t col) -> uint32_t {
-            return outl ? (bm[col >> 5] >> (col & 31)) & 0xffu : 0u;
-        };
-        if (NCH > 0) {
-#pragma unroll
-            for (int c = 0; c < RC; ++c) {
-                const int64_t col = ((int64_t)tid + 256 * c) * 8;
-                if (col < a.k) {
-                    v[c] = load8<kVec>(xr, col, a.k);
-                    ob[c] = obyte(col);
-                } else {
-                    v[c] = make_uint4(0, 0, 0, 0);
-                    ob[c] = 0;
-                }
-                mx = fmaxf(mx, chunk_max(v[c], ob[c]));
-            }
-        } else {
-            for (int64_t ch = tid; ch < nchunks; ch += 256) {
-                const int64_t col = ch * 8;
-                mx = fmaxf(mx, chunk_max(load8<kVec>(xr, col, a.k), obyte(col)));
+            for (int c = 0; c < kBatch; ++c) {
+                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
+                if (col < a.k) mx = fmaxf(mx, chunk_max(v[c], obyte(col)));
             }
         }
-        mx = wave_max(mx);
-        if (lane == 0) red[wave] = mx;
-        __syncthreads();
-        const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();
+        const float s = wave_max(mx);
 
         // 4b. codes, 4c. outlier gather
         const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
@@ -290,24 +298,20 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
                 }
             }
         };
-        if (NCH > 0) {
+        for (int64_t b = 0; b < nbatch; ++b) {
+            if (nbatch > 1) load_batch(b);  // one batch: still in registers
 #pragma unroll
-            for (int c = 0; c < RC; ++c) {
-                const int64_t col = ((int64_t)tid + 256 * c) * 8;
-                if (col < a.k) emit(v[c], ob[c], col);
-            }
-        } else {
-            for (int64_t ch = tid; ch < nchunks; ch += 256) {
-                const int64_t col = ch * 8;
-                emit(load8<kVec>(xr, col, a.k), obyte(col), col);
+            for (int c = 0; c < kBatch; ++c) {
+                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
+                if (col < a.k) emit(v[c], obyte(col), col);
             }
         }
         if (a.q) {
-            for (int64_t j = a.k + tid; j < a.kpad; j += 256) a.q[r * a.ldq + j] = 0;
-            if (tid == 0) a.absmax[r] = s;
+            for (int64_t j = a.k + lane; j < a.kpad; j += 64) a.q[r * a.ldq + j] = 0;
+            if (lane == 0) a.absmax[r] = s;
         }
         if (a.x_out)
-            for (int32_t t = kept + tid; t < a.xo_cols; t += 256) a.x_out[r * a.ldo + t] = 0;
+            for (int32_t t = kept + lane; t < a.xo_cols; t += 64) a.x_out[r * a.ldo + t] = 0;
     }
 }
 
@@ -324,26 +328,15 @@ hipError_t launch_detect(const half_bits* x, int64_t m, int64_t k, int64_t ldx, 
     return hipGetLastError();
 }
 
-template <int NCH>
-static void launch_quant_n(const QuantArgs& a, dim3 grid, size_t lds, bool vec, hipStream_t s) {
-    if (vec)
-        hipLaunchKernelGGL((quant_kernel<NCH, true>), grid, dim3(256), lds, s, a);
-    else
-        hipLaunchKernelGGL((quant_kernel<NCH, false>), grid, dim3(256), lds, s, a);
-}
-
 hipError_t launch_quant(const QuantArgs& a, hipStream_t stream) {
     const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-    int64_t blocks = a.m > 0 ? ceil_div(a.m, a.rows_per_block) : 1;
+    const int64_t blocks = a.m > 0 ? ceil_div(a.m, a.rows_per_block) : 1;
     dim3 grid((unsigned)blocks);
     const size_t lds = (size_t)a.words * 2 * sizeof(uint32_t);
-    const int64_t per = ceil_div(ceil_div(a.k, 8), 256);
-    if (per <= 1) launch_quant_n<1>(a, grid, lds, vec, stream);
-    else if (per <= 2) launch_quant_n<2>(a, grid, lds, vec, stream);
-    else if (per <= 4) launch_quant_n<4>(a, grid, lds, vec, stream);
-    else if (per <= 8) launch_quant_n<8>(a, grid, lds, vec, stream);
-    else if (per <= 12) launch_quant_n<12>(a, grid, lds, vec, stream);
-    else launch_quant_n<0>(a, grid, lds, vec, stream);
+    if (vec)
+        hipLaunchKernelGGL(quant_kernel<true>, grid, dim3(256), lds, stream, a);
+    else
+        hipLaunchKernelGGL(quant_kernel<false>, grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
