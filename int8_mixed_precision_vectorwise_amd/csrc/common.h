@@ -112,6 +112,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_i32(const GemmArgs& g, hipStream_t stream);
+// m <= 16, 16-byte aligned operands, A covering whole 128-byte K chunks
+hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream);
 hipError_t launch_gemm_fused(const GemmArgs& g, hipStream_t stream);
 
 struct DequantArgs {

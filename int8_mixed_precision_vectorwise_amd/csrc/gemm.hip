@@ -89,14 +89,13 @@ __device__ inline void tile_coords(int64_t bid, int64_t nblocks, int64_t tiles_m
 
 }  // namespace
 
-// Epilogue shared by both GEMM kernels.  Accumulator (i, j, r) of lane l
-// holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of 32x32 block (i, j);
-// wrow0 / wcol0 are this lane's first row and column.
-template <int BM, int BN, bool kFused>
-__device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[BM / 64][BN / 64], int64_t m0, int64_t wrow0,
-                                int64_t wcol0, int lane, int wm) {
-    constexpr int WM = BM / 2;
-    constexpr int FM = BM / 64, FN = BN / 64;
+// Epilogue shared by the GEMM kernels.  Accumulator (i, j, r) of lane l holds
+// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of 32x32 block (i, j).
+template <int FM, int FN, bool kFused>
+__device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t row0, int64_t col0, int lane) {
+    // row0 / col0: the first row and column of this wave's FM x FN blocks
+    const int64_t wrow0 = row0 + 4 * (lane >> 5);
+    const int64_t wcol0 = col0 + (lane & 31);
     if constexpr (!kFused) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -127,7 +126,7 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[BM / 64][BN / 64]
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            int64_t arow = m0 + wm * WM + i * 32 + (lane & 31);
+            int64_t arow = row0 + i * 32 + (lane & 31);
             if (arow >= g.m) arow = g.m - 1;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -317,11 +316,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         mfmas(1, FM / 2, FM);
     }
 
-    // accumulator (i, j, r) of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
-    // column l%32 of the 32x32 block (i, j)
-    const int64_t wrow0 = m0 + wm * WM + 4 * (lane >> 5);
-    const int64_t wcol0 = n0 + wn * WN + (lane & 31);
-    epilogue<BM, BN, kFused>(g, acc, m0, wrow0, wcol0, lane, wm);
+    epilogue<FM, FN, kFused>(g, acc, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -572,9 +567,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         mfma_rows(LAST, FM - 1, FM);
     }
 
-    const int64_t wrow0 = m0 + wm * WM + 4 * (lane >> 5);
-    const int64_t wcol0 = n0 + wn * WN + (lane & 31);
-    epilogue<BM, BN, kFused>(g, acc, m0, wrow0, wcol0, lane, wm);
+    epilogue<FM, FN, kFused>(g, acc, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 namespace {
@@ -623,8 +616,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     const bool aligned = ((g.lda & 15) == 0) && ((g.ldb & 15) == 0) &&
                          ((reinterpret_cast<uintptr_t>(g.a) & 15) == 0) &&
                          ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
-    // the staged kernel reads whole 128-byte K stages: A must be zero past k
+    // the staged kernels read whole 128-byte K stages: A must be zero past k
     const bool staged = aligned && ((g.k & 127) == 0 || g.a_zero_padded);
+    if (staged && g.m <= 16) return launch_decode(g, kFused, stream);
     switch (pick_tile(g.m, g.n)) {
         case 0: return launch_tile<256, 256, kFused>(g, aligned, staged, stream);
         case 1: return launch_tile<256, 128, kFused>(g, aligned, staged, stream);

@@ -129,7 +129,10 @@ __global__ __launch_bounds__(256) void detect_kernel(const half_bits* __restrict
 // longer row is read twice, the second time from L2 / the infinity cache.
 constexpr int kBatch = 8;
 
-template <bool kVec>
+// kBlockRow: the whole workgroup quantizes one row at a time (few rows: every
+// row's loads go out in one batch across 256 threads); otherwise one row per
+// wavefront.
+template <bool kVec, bool kBlockRow>
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     extern __shared__ uint32_t smem[];
     uint32_t* bm = smem;                                       // [words]
@@ -141,6 +144,23 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     const int wave = tid >> 6;
     const bool outl = a.partial != nullptr;
     const bool need_prefix = outl && (a.x_out || a.idx_out || a.count_out);
+
+    // The first row's first batch of loads goes out now, so that its latency
+    // overlaps the bitmap and prefix work below.
+    constexpr int P = kBlockRow ? 256 : 64;  // threads sharing a row
+    const int pid = kBlockRow ? tid : lane;
+    const int64_t rr0 = kBlockRow ? 0 : wave;
+    const int64_t r_first = (int64_t)blockIdx.x * a.rows_per_block + rr0;
+    const bool preload = rr0 < a.rows_per_block && r_first < a.m;
+    uint4 v[kBatch];
+    auto load_batch = [&](const half_bits* __restrict__ xr, int64_t b) {
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
+            v[c] = col < a.k ? load8<kVec>(xr, col, a.k) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (preload) load_batch(a.x + r_first * a.ldx, 0);
 
     // 1. the final outlier bitmap: OR of the per-row-block partials.  The
     // partial words are independent loads; 8 are kept in flight per thread and
@@ -223,7 +243,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 
     // 4. rows, one per wavefront
     const int64_t nchunks = (a.k + 7) / 8;
-    const int64_t nbatch = (nchunks + 64 * kBatch - 1) / (64 * kBatch);
+    const int64_t nbatch = (nchunks + (kBlockRow ? 256 : 64) * kBatch - 1) / ((kBlockRow ? 256 : 64) * kBatch);
     const bool vec_q = a.q && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
     auto obyte = [&](int64_t col) -> uint32_t {
         return outl ? (bm[col >> 5] >> (col & 31)) & 0xffu : 0u;
@@ -237,30 +257,29 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
         }
         return t;
     };
-    for (int64_t rr = wave; rr < a.rows_per_block; rr += 4) {
+    __shared__ float rmax[4];
+    for (int64_t rr = rr0; rr < a.rows_per_block; rr += kBlockRow ? 1 : 4) {
         const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
         if (r >= a.m) break;
         const half_bits* __restrict__ xr = a.x + r * a.ldx;
-        uint4 v[kBatch];
-        auto load_batch = [&](int64_t b) {
-#pragma unroll
-            for (int c = 0; c < kBatch; ++c) {
-                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
-                v[c] = col < a.k ? load8<kVec>(xr, col, a.k) : make_uint4(0, 0, 0, 0);
-            }
-        };
 
         // 4a. absmax over the non-outlier columns
         float mx = 0.0f;
         for (int64_t b = 0; b < nbatch; ++b) {
-            load_batch(b);
+            if (b > 0 || rr != rr0) load_batch(xr, b);  // batch 0 of the first row is in v
 #pragma unroll
             for (int c = 0; c < kBatch; ++c) {
-                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
+                const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
                 if (col < a.k) mx = fmaxf(mx, chunk_max(v[c], obyte(col)));
             }
         }
-        const float s = wave_max(mx);
+        float s = wave_max(mx);
+        if constexpr (kBlockRow) {
+            if (lane == 0) rmax[wave] = s;
+            __syncthreads();
+            s = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
+            __syncthreads();
+        }
 
         // 4b. codes, 4c. outlier gather
         const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
@@ -299,19 +318,19 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
             }
         };
         for (int64_t b = 0; b < nbatch; ++b) {
-            if (nbatch > 1) load_batch(b);  // one batch: still in registers
+            if (nbatch > 1) load_batch(xr, b);  // one batch: still in registers
 #pragma unroll
             for (int c = 0; c < kBatch; ++c) {
-                const int64_t col = (b * 64 * kBatch + (int64_t)lane + 64 * c) * 8;
+                const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
                 if (col < a.k) emit(v[c], obyte(col), col);
             }
         }
         if (a.q) {
-            for (int64_t j = a.k + lane; j < a.kpad; j += 64) a.q[r * a.ldq + j] = 0;
-            if (lane == 0) a.absmax[r] = s;
+            for (int64_t j = a.k + pid; j < a.kpad; j += P) a.q[r * a.ldq + j] = 0;
+            if (pid == 0) a.absmax[r] = s;
         }
         if (a.x_out)
-            for (int32_t t = kept + lane; t < a.xo_cols; t += 64) a.x_out[r * a.ldo + t] = 0;
+            for (int32_t t = kept + pid; t < a.xo_cols; t += P) a.x_out[r * a.ldo + t] = 0;
     }
 }
 
@@ -330,13 +349,24 @@ hipError_t launch_detect(const half_bits* x, int64_t m, int64_t k, int64_t ldx, 
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t stream) {
     const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-    const int64_t blocks = a.m > 0 ? ceil_div(a.m, a.rows_per_block) : 1;
-    dim3 grid((unsigned)blocks);
     const size_t lds = (size_t)a.words * 2 * sizeof(uint32_t);
+    // few rows: one workgroup per row, all of its threads on that row
+    if (a.m <= 64) {
+        QuantArgs b = a;
+        b.rows_per_block = 1;
+        dim3 grid((unsigned)(a.m > 0 ? a.m : 1));
+        if (vec)
+            hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(256), lds, stream, b);
+        else
+            hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(256), lds, stream, b);
+        return hipGetLastError();
+    }
+    const int64_t blocks = ceil_div(a.m, a.rows_per_block);
+    dim3 grid((unsigned)blocks);
     if (vec)
-        hipLaunchKernelGGL(quant_kernel<true>, grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((quant_kernel<true, false>), grid, dim3(256), lds, stream, a);
     else
-        hipLaunchKernelGGL(quant_kernel<false>, grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
