@@ -28,6 +28,8 @@
  *    may have been enqueued).
  *  - Sizes: m, n >= 0, k >= 1; k <= I8MP_MAX_K so that int32 accumulation of
  *    int8 products is exact.  m == 0 or n == 0 is a valid empty call.
+ *    Leading dimensions of the GEMM operands and outputs (lda, ldb, ldw, ldc,
+ *    ldout) and the outlier capacity are at most I8MP_MAX_LD elements.
  *  - Calls that share a workspace or outputs and overlap in time race; calls
  *    on one stream are ordered.
  *
@@ -65,6 +67,11 @@ typedef int32_t i8mp_status;
 
 /* floor((2^31 - 1) / 127^2): largest k whose worst-case int8 dot product fits int32. */
 #define I8MP_MAX_K 133144
+
+/* Largest leading dimension (elements) of the GEMM operands and outputs, and
+ * largest outlier capacity: the kernels address a tile of up to 256 rows with
+ * 32-bit byte offsets.  Larger values are I8MP_EINVAL. */
+#define I8MP_MAX_LD 1048576
 
 /* Host.  Static English text for a status code (never NULL). */
 const char* i8mp_status_string(i8mp_status s);

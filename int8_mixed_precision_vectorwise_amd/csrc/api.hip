@@ -32,6 +32,7 @@ i8mp_status check_device() {
 i8mp_status launched(hipError_t e) { return e == hipSuccess ? I8MP_OK : I8MP_ELAUNCH; }
 
 bool bad_k(int64_t k) { return k < 1; }
+bool bad_ld(int64_t ld) { return ld > I8MP_MAX_LD; }
 
 void forward_layout(int64_t m, int64_t k, int32_t cap, i8mp_linear_workspace* L) {
     const QuantPlan plan = make_quant_plan(m, k, true);
@@ -148,6 +149,7 @@ i8mp_status i8mp_int8_linear_matmul(const int8_t* a, int64_t lda, const int8_t* 
                                     int64_t m, int64_t n, int64_t k, int32_t* c, int64_t ldc,
                                     hipStream_t stream) {
     if (m < 0 || n < 0 || bad_k(k) || lda < k || ldb < k || ldc < n) return I8MP_EINVAL;
+    if (bad_ld(lda) || bad_ld(ldb) || bad_ld(ldc)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0 || n == 0) return I8MP_OK;
     if (!a || !b || !c) return I8MP_EINVAL;
@@ -200,7 +202,7 @@ i8mp_status i8mp_int8_mm_dequant(const int32_t* c, int64_t ldc, const float* row
 
 i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
                                         i8mp_linear_workspace* layout) {
-    if (!layout || m < 0 || n < 0 || bad_k(k) || cap < 0) return I8MP_EINVAL;
+    if (!layout || m < 0 || n < 0 || bad_k(k) || cap < 0 || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     forward_layout(m, k, cap, layout);
     return I8MP_OK;
@@ -278,7 +280,7 @@ i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* w
 i8mp_status i8mp_linear_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
                                  int32_t cap, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-    if (m < 0 || bad_k(k) || ldx < k || cap < 0) return I8MP_EINVAL;
+    if (m < 0 || bad_k(k) || ldx < k || cap < 0 || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0) return I8MP_OK;
     if (!x) return I8MP_EINVAL;
@@ -294,6 +296,7 @@ i8mp_status i8mp_linear_matmul_dequant(const void* workspace, size_t workspace_b
                                        const float* w_absmax, int64_t n, const void* bias, void* out,
                                        int64_t ldout, hipStream_t stream) {
     if (m < 0 || n < 0 || bad_k(k) || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
+    if (bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0 || n == 0) return I8MP_OK;
     if (!w_q || !w_absmax || !out) return I8MP_EINVAL;
@@ -311,6 +314,7 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
                                 int64_t ldout, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
     if (m < 0 || n < 0 || bad_k(k) || ldx < k || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
+    if (bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0 || n == 0) return I8MP_OK;
     if (!x || !w_q || !w_absmax || !out) return I8MP_EINVAL;

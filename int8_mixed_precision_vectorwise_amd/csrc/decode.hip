@@ -62,8 +62,10 @@ __device__ inline int swz(int row, int chunk) { return row * kChunk + ((chunk ^ 
 
 template <int G, bool kFused>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) int8_t ring[kWaves * kStages * kStageBytes];
-    __shared__ int32_t red[kWaves * 4 * 64];
+    // one LDS array (a second __shared__ object makes the compiler drain every
+    // DMA before each LDS read): the rings, then the partial-sum blocks
+    __shared__ __attribute__((aligned(1024))) int8_t ring[kWaves * kStages * kStageBytes + kWaves * 4 * 64 * 4];
+    int32_t* red = reinterpret_cast<int32_t*>(ring + kWaves * kStages * kStageBytes);
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

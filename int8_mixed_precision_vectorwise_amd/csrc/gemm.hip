@@ -89,80 +89,209 @@ __device__ inline void tile_coords(int64_t bid, int64_t nblocks, int64_t tiles_m
 
 }  // namespace
 
-// Epilogue shared by the GEMM kernels.  Accumulator (i, j, r) of lane l holds
-// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of 32x32 block (i, j).
-template <int FM, int FN, bool kFused>
-__device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t row0, int64_t col0, int lane) {
-    // row0 / col0: the first row and column of this wave's FM x FN blocks
-    const int64_t wrow0 = row0 + 4 * (lane >> 5);
-    const int64_t wcol0 = col0 + (lane & 31);
-    if constexpr (!kFused) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t col = wcol0 + 32 * j;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = wrow0 + 32 * i + 8 * (r >> 2) + (r & 3);
-                    if (row < g.m && col < g.n) g.c[row * g.ldc + col] = acc[i][j][r];
-                }
-            }
-    } else {
-        const float r127 = 1.0f / 127.0f;
-        int cnt = 0;
+// One wave-wide global -> LDS copy through a buffer resource: lane i's
+// `bytes` (4 or 16) land at lds + bytes * i (lds must be wave-uniform).
+// Out-of-range lanes write zeros.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                             soffset, 0, 0);
+}
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t src, void* lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, voffset, 0,
+                                             0, 0);
+}
+
+// Epilogue operands of a BM x BN tile, copied to LDS when the kernel starts
+// (their latency then hides behind the K loop): the tile's row and column
+// absmax, the first kEpiIdx outlier column indices and the outlier count.
+constexpr int kEpiIdx = 64;
+template <int BM, int BN>
+struct __attribute__((aligned(16))) EpiLds {
+    float sx[BM];
+    float sw[BN];
+    int32_t idx[kEpiIdx];
+    int32_t cnt[64];
+};
+
+template <int BM, int BN, bool kFused>
+__device__ inline void epi_prefetch(const GemmArgs& g, int64_t m0, int64_t n0, EpiLds<BM, BN>& e, int wave,
+                                    int lane) {
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies are 64 lanes wide");
+    if constexpr (kFused) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.row_absmax + m0, (g.m - m0) * 4);
+        const __amdgpu_buffer_rsrc_t cs = make_rsrc(g.col_absmax + n0, (g.n - n0) * 4);
+        for (int c = wave; c < BM / 64; c += 4) dma4(rs, e.sx + c * 64, (c * 64 + lane) * 4);
+        for (int c = wave; c < BN / 64; c += 4) dma4(cs, e.sw + c * 64, (c * 64 + lane) * 4);
         if (g.x_out) {
-            cnt = *g.count;
-            if (cnt > g.cap) cnt = g.cap;
+            if (wave == 0) dma4(make_rsrc(g.idx, (int64_t)g.cap * 4), e.idx, lane * 4);
+            if (wave == 1) dma4(make_rsrc(g.count, 4), e.cnt, 0);
         }
-        const int nsteps = (cnt + 15) / 16;
-        float swj[FN], bj[FN];
+    }
+}
+
+// Epilogue shared by the GEMM kernels.  Accumulator (i, j, r) of lane l holds
+// row wr0 + 32 i + 8 (r/4) + 4 (l/32) + r%4 and column wc0 + 32 j + l%32 of the
+// tile at (m0, n0); the same layout holds for the fp32 32x32 MFMA.  Every
+// load and store goes through a buffer resource, so rows past m and columns
+// past n need no branches (out-of-range loads return 0, stores are dropped),
+// and the loads of each phase are issued together.
+//
+// Fused: acc becomes float(C) * row_absmax / 127 in place, the outlier
+// sub-matmul accumulates into it on v_mfma_f32_32x32x16_f16 (16 outlier
+// columns per step: X_O from the workspace, weight bytes gathered through the
+// index list), then out = col_absmax / 127 * acc + bias in fp16.
+template <int BM, int BN, int FM, int FN, bool kFused, int kStageBytes>
+__device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t m0, int64_t n0, int wr0, int wc0,
+                                int lane, const EpiLds<BM, BN>& e, int8_t* stage) {
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int64_t rows_left = g.m - m0, cols_left = g.n - n0;
+    if constexpr (!kFused) {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.c + m0 * g.ldc + n0, ((rows_left - 1) * g.ldc + cols_left) * 4);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = wcol0 + 32 * j;
-            const bool ok = col < g.n;
-            swj[j] = ok ? g.col_absmax[col] * r127 : 0.0f;
-            bj[j] = (ok && g.bias) ? h2f(g.bias[col]) : 0.0f;
+            const int lcol = wc0 + 32 * j + l32;
+            const bool okc = lcol < cols_left;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lrow = wr0 + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const int off = okc ? (lrow * (int)g.ldc + lcol) * 4 : (int)0x80000000;
+                    __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][r], rc, off, 0, 0);
+                }
         }
+    } else {
+        const float r127 = 1.0f / 127.0f;
+        // bias first: its loads are in flight during the conversion and the outlier term
+        const __amdgpu_buffer_rsrc_t rbias = make_rsrc(g.bias ? g.bias + n0 : nullptr, g.bias ? cols_left * 2 : 0);
+        float bj[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            int64_t arow = row0 + i * 32 + (lane & 31);
-            if (arow >= g.m) arow = g.m - 1;
+        for (int j = 0; j < FN; ++j)
+            bj[j] = (float)__builtin_bit_cast(
+                _Float16, __builtin_amdgcn_raw_buffer_load_b16(rbias, (wc0 + 32 * j + l32) * 2, 0, 0));
+
+        int cnt = 0;
+        if (g.x_out) {
+            cnt = e.cnt[0];
+            cnt = cnt > g.cap ? g.cap : cnt;
+            cnt = cnt < 0 ? 0 : cnt;
+        }
+        cnt = __builtin_amdgcn_readfirstlane(cnt);
+        const __amdgpu_buffer_rsrc_t rxo = make_rsrc(g.x_out + m0 * g.ldo, g.x_out ? rows_left * g.ldo * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.b + n0 * g.ldb, (cols_left - 1) * g.ldb + g.k);
+        const __amdgpu_buffer_rsrc_t ridx = make_rsrc(g.idx, g.x_out ? (int64_t)g.cap * 4 : 0);
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(g.out + m0 * g.ldout + n0, ((rows_left - 1) * g.ldout + cols_left) * 2);
+
+        // rows of blocks in chunks of IC, so that at most 128 fp32 values are live
+        constexpr int IC = FM * FN * 16 <= 128 ? FM : (128 / (FN * 16) > 0 ? 128 / (FN * 16) : 1);
+        constexpr int WN = FN * 32;
+        constexpr int kPitch = WN * 2 + 16;   // LDS row pitch of the output staging area
+        static_assert(4 * IC * 32 * kPitch <= kStageBytes, "output staging does not fit the K stages");
+        const int wave = (wr0 / (FM * 32)) * 2 + wc0 / WN;
+        int8_t* area = stage + wave * (IC * 32 * kPitch);
+        const bool vec_ok = (g.ldout & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                // row scales reloaded per block (L1 hits) to keep few registers live
+        for (int ic = 0; ic < FM; ic += IC) {
+            v16f f[IC][FN];
+#pragma unroll
+            for (int ii = 0; ii < IC; ++ii) {
+                const int i = ic + ii;
                 float sxr[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = wrow0 + 32 * i + 8 * (r >> 2) + (r & 3);
-                    sxr[r] = row < g.m ? g.row_absmax[row] * r127 : 0.0f;
-                }
-                v16f p;
+                for (int q = 0; q < 4; ++q) {
+                    const v4f s4 = *reinterpret_cast<const v4f*>(&e.sx[wr0 + 32 * i + 8 * q + 4 * hi]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = 0.0f;
-                int64_t bcol = wcol0 + 32 * j;
-                if (bcol >= g.n) bcol = g.n - 1;
-                for (int st = 0; st < nsteps; ++st) {
-                    const int s0 = st * 16 + (lane >> 5) * 8;
-                    const v8h xa = *reinterpret_cast<const v8h*>(g.x_out + arow * g.ldo + s0);
+                    for (int t = 0; t < 4; ++t) sxr[4 * q + t] = s4[t] * r127;
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) f[ii][j][r] = (float)acc[i][j][r] * sxr[r];
+            }
+
+            for (int s0 = 0; s0 < cnt; s0 += 16) {
+                const int sb = s0 + 8 * hi;   // this lane's 8 outlier slots
+                int ix[8];
+                if (s0 + 16 <= kEpiIdx) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) ix[t] = e.idx[sb + t];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        ix[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(ridx, (sb + t) * 4, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ix[t] = sb + t < cnt ? ix[t] : -1;
+                v8h xa[IC];
+#pragma unroll
+                for (int ii = 0; ii < IC; ++ii) {
+                    const int lrow = wr0 + 32 * (ic + ii) + l32;
+                    xa[ii] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rxo, (lrow * (int)g.ldo + sb) * 2, 0, 0));
+                }
+                uint32_t wby[FN][8];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int lcol = wc0 + 32 * j + l32;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int off = ix[t] >= 0 ? lcol * (int)g.ldb + ix[t] : (int)0x80000000;
+                        wby[j][t] = __builtin_amdgcn_raw_buffer_load_b8(rw, off, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
                     v8h wb;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s = s0 + e;
-                        wb[e] = s < cnt ? (_Float16)(float)g.b[bcol * g.ldb + g.idx[s]] : (_Float16)0.0f;
-                    }
-                    p = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, p, 0, 0, 0);
-                }
-                const int64_t col = wcol0 + 32 * j;
+                    for (int t = 0; t < 8; ++t) wb[t] = (_Float16)(float)(int8_t)(uint8_t)wby[j][t];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = wrow0 + 32 * i + 8 * (r >> 2) + (r & 3);
-                    if (row < g.m && col < g.n) {
-                        const float y = swj[j] * ((float)acc[i][j][r] * sxr[r] + p[r]) + bj[j];
-                        g.out[row * g.ldout + col] = f2h(y);
+                    for (int ii = 0; ii < IC; ++ii)
+                        f[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[ii], wb, f[ii][j], 0, 0, 0);
+                }
+            }
+
+            // fp16 results go through this wave's LDS area (the idle K stages) so
+            // that each lane writes 16 contiguous bytes of a row: 8 columns per
+            // store instead of one
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int ccol = 32 * j + l32;
+                const float swj = e.sw[wc0 + ccol] * r127;
+#pragma unroll
+                for (int ii = 0; ii < IC; ++ii)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int crow = 32 * ii + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        *reinterpret_cast<_Float16*>(area + crow * kPitch + ccol * 2) =
+                            (_Float16)(swj * f[ii][j][r] + bj[j]);
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+            constexpr int CPR = WN / 8;          // 16-byte chunks per row
+            constexpr int RPI = 64 / CPR;        // rows per store instruction
+#pragma unroll
+            for (int q = 0; q < IC * 32 / RPI; ++q) {
+                const int crow = q * RPI + lane / CPR;
+                const int c = lane % CPR;
+                const v4i v = *reinterpret_cast<const v4i*>(area + crow * kPitch + c * 16);
+                const int trow = wr0 + 32 * ic + crow;   // tile row (rows past m are dropped by the range)
+                const int tcol = wc0 + 8 * c;
+                const int off = (trow * (int)g.ldout + tcol) * 2;
+                if (vec_ok && tcol + 8 <= cols_left) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ro, off, 0, 0);
+                } else if (tcol < cols_left) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t h = ((uint32_t)v[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h, ro,
+                                                              tcol + t < cols_left ? off + 2 * t : (int)0x80000000, 0, 0);
                     }
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the area is written again
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -173,8 +302,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int A_CH = BM * BK / 16 / 256;
     constexpr int B_CH = BN * BK / 16 / 256;
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
+    // one LDS array: A stages, B stages, the epilogue operands
+    __shared__ __attribute__((aligned(16))) int8_t smem[2 * (BM + BN) * BK + sizeof(EpiLds<BM, BN>)];
+    int8_t(*As)[BM * BK] = reinterpret_cast<int8_t(*)[BM * BK]>(smem);
+    int8_t(*Bs)[BN * BK] = reinterpret_cast<int8_t(*)[BN * BK]>(smem + 2 * BM * BK);
+    EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + 2 * (BM + BN) * BK);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -186,6 +318,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     int64_t tm, tn;
     tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
+    epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, __builtin_amdgcn_readfirstlane(wave), lane);
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -316,7 +449,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         mfmas(1, FM / 2, FM);
     }
 
-    epilogue<FM, FN, kFused>(g, acc, m0 + wm * WM, n0 + wn * WN, lane);
+    __syncthreads();  // K loop done everywhere; the epilogue operands copied at the start are visible
+    epilogue<BM, BN, FM, FN, kFused, 2 * (BM + BN) * BK>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,13 +470,6 @@ template <int BKS>
 __device__ inline int swz_k(int row, int chunk) {
     if constexpr (BKS == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
     else return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-
-// One wave-wide 16-byte-per-lane global -> LDS copy: lane i's bytes land at
-// lds + 16 * i (lds must be wave-uniform).
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                             soffset, 0, 0);
 }
 
 __device__ inline void wait_vm(int n) {
@@ -415,7 +542,10 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     constexpr int INS = A_INS + B_INS;
     static_assert(A_INS >= 1 && B_INS >= 1, "tile too small for 4-wave DMA");
     static_assert(STAGES >= 2, "need at least two stages");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE];
+    // one LDS array: the stages, then the epilogue operands (a second
+    // __shared__ object makes the compiler drain every DMA before each LDS read)
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE + sizeof(EpiLds<BM, BN>)];
+    EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + STAGES * STAGE);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -427,6 +557,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     int64_t tm, tn;
     tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
+    epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, wave, lane);
 
     const int64_t kr = (g.k + BKS - 1) / BKS * BKS;
     const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + kr);
@@ -567,7 +698,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         mfma_rows(LAST, FM - 1, FM);
     }
 
-    epilogue<FM, FN, kFused>(g, acc, m0 + wm * WM, n0 + wn * WN, lane);
+    __syncthreads();  // no DMA in flight, K loop done everywhere, epilogue operands visible
+    epilogue<BM, BN, FM, FN, kFused, STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem);
 }
 
 namespace {

@@ -19,6 +19,7 @@ HEADER = os.path.join(ROOT, "include", "i8mp.h")
 
 OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+MAX_LD = int(re.search(r"#define I8MP_MAX_LD (\d+)", open(HEADER).read()).group(1))
 
 
 def _header_functions():
@@ -99,6 +100,11 @@ def test_matmul_validation(L):
     k = 133145
     assert mm(FAKE, k, FAKE, k, 1, 1, k, FAKE, 1, None) == ERANGE
     assert mm(None, 64, None, 64, 0, 4, 64, None, 4, None) == OK      # empty m
+    big = MAX_LD + 1                                                   # 32-bit tile offsets
+    assert mm(FAKE, 64, FAKE, big, 4, 4, 64, FAKE, 4, None) == EINVAL
+    assert mm(FAKE, big, FAKE, 64, 4, 4, 64, FAKE, 4, None) == EINVAL
+    assert mm(FAKE, 64, FAKE, 64, 4, 4, 64, FAKE, big, None) == EINVAL
+    assert mm(None, 64, None, 64, 0, 4, 64, None, MAX_LD, None) == OK
     assert mm(None, 64, None, 64, 4, 0, 64, None, 0, None) == OK      # empty n
 
 
@@ -136,6 +142,10 @@ def test_forward_validation(L):
     assert call(wsb=lay.bytes - 1) == EWORKSPACE
     assert call(m=0) == OK
     assert call(n=0) == OK
+    assert call(ldw=MAX_LD + 1) == EINVAL
+    assert call(ldo=MAX_LD + 1) == EINVAL
+    assert call(cap=MAX_LD + 1) == EINVAL
+    assert L.i8mp_linear_workspace_query(16, 32, 64, MAX_LD + 1, ctypes.byref(lay)) == EINVAL
 
     qz = L.i8mp_linear_quantize
     assert qz(None, 16, 64, 64, 6.0, 8, FAKE, lay.bytes, None) == EINVAL
