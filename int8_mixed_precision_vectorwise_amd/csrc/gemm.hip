@@ -722,21 +722,26 @@ hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t
     return hipGetLastError();
 }
 
-// Tile shape by a simple cost model: rounds of workgroups over the 256 CUs
-// times the tile's work, divided by the tile's measured relative efficiency
-// (operand reuse falls with the tile size).  Ties go to the larger tile.
-int pick_tile(int64_t m, int64_t n) {
+// Tile shape by a cost model fitted to traced runs of the pipelined kernel on
+// MI355X: a workgroup costs a fixed ~3 us (first stage in flight, epilogue)
+// plus k-tiles x the per-128-byte-K-tile time of its shape; workgroups run in
+// rounds over the CUs (two 64 x 64 workgroups fit one CU's LDS).
+int pick_tile(int64_t m, int64_t n, int64_t k) {
     constexpr int64_t kCUs = 256;
-    struct Cand { int bm, bn; double eff; };
-    const Cand cands[4] = {{256, 256, 1.0}, {256, 128, 1.0}, {128, 128, 0.85}, {64, 64, 0.35}};
+    struct Cand { int bm, bn, per_cu; double tk, tk_shared; };
+    const Cand cands[6] = {{256, 256, 1, 1.71, 1.71}, {256, 128, 1, 0.97, 0.97}, {128, 128, 1, 0.50, 0.50},
+                           {128, 64, 1, 0.30, 0.30},   {64, 128, 1, 0.33, 0.33},  {64, 64, 2, 0.26, 0.38}};
+    const double ktiles = (double)((k + 127) / 128);
     int best = 0;
-    double best_cost = 1e300;
-    for (int c = 0; c < 4; ++c) {
+    double best_t = 1e300;
+    for (int c = 0; c < 6; ++c) {
         const int64_t tiles = ((m + cands[c].bm - 1) / cands[c].bm) * ((n + cands[c].bn - 1) / cands[c].bn);
-        const int64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double cost = (double)rounds * cands[c].bm * cands[c].bn / cands[c].eff;
-        if (cost < best_cost * 0.999) {
-            best_cost = cost;
+        const int64_t slots = kCUs * cands[c].per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double tk = tiles > kCUs ? cands[c].tk_shared : cands[c].tk;
+        const double t = (double)rounds * (3.0 + ktiles * tk);
+        if (t < best_t * 0.999) {
+            best_t = t;
             best = c;
         }
     }
@@ -751,11 +756,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     // the staged kernels read whole 128-byte K stages: A must be zero past k
     const bool staged = aligned && ((g.k & 127) == 0 || g.a_zero_padded);
     if (staged && g.m <= 16) return launch_decode(g, kFused, stream);
-    switch (pick_tile(g.m, g.n)) {
+    switch (pick_tile(g.m, g.n, g.k)) {
         case 0: return launch_tile<256, 256, kFused>(g, aligned, staged, stream);
         case 1: return launch_tile<256, 128, kFused>(g, aligned, staged, stream);
         case 2: return launch_tile<128, 128, kFused>(g, aligned, staged, stream);
-        default: return launch_tile<64, 64, kFused>(g, aligned, false, stream);
+        case 3: return launch_tile<128, 64, kFused>(g, aligned, staged, stream);
+        case 4: return launch_tile<64, 128, kFused>(g, aligned, staged, stream);
+        default: return launch_tile<64, 64, kFused>(g, aligned, staged, stream);
     }
 }
 
