@@ -34,6 +34,7 @@ PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
 DEFAULT_WORKLOAD = "opt350m_mlp_pair_m512"
 GEMM_SRC = os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+COPY_MB = 256              # calibration copy: 256 MiB read + 256 MiB written
 
 
 def log(msg: str) -> None:
@@ -128,6 +129,122 @@ def cpu_baseline(specs, kind: str, budget_s: float):
             "seconds": round(el, 2)}
 
 
+def capture_gemm_graphs(torch, i8, sets, specs, copies):
+    """One graph per layer: that layer's fused GEMM over every rotation copy."""
+    for c in range(copies):
+        for s, xc, wqc, wac, b, ws, out in sets[c]:
+            i8.linear_quantize(xc, ws, s.tau)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(st):
+        for li in range(len(specs)):
+            for c in range(copies):  # eager warm-up of this layer's launches
+                _, _, wqc, wac, b, ws, out = sets[c][li]
+                i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                for c in range(copies):
+                    _, _, wqc, wac, b, ws, out = sets[c][li]
+                    i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs, st
+
+
+def time_gemm_launches(torch, i8, sets, specs, copies, launches):
+    """Average duration of one fused-GEMM launch per layer: HIP events on the
+    replay stream around back-to-back graph replays of that layer's launches
+    (no host work between launches)."""
+    graphs, st = capture_gemm_graphs(torch, i8, sets, specs, copies)
+    out = {}
+    reps = max(1, launches // copies)
+    for li, s in enumerate(specs):
+        g = graphs[li]
+        with torch.cuda.stream(st):
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                g.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        out[s.name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    return out
+
+
+def traffic_summary(directory: str, workload: str, launches: int) -> int:
+    """Per-launch HBM bytes of the fused GEMM from rocprofv3 --pmc runs.
+
+    ``directory`` holds four rocprofv3 output folders: gemm_fetch, gemm_write
+    (``bench.py --mode gemm``) and copy_fetch, copy_write (``bench.py --mode
+    copy``).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what
+    the same counters read for the copy kernel, whose true bytes are known."""
+    import csv
+    import glob
+    specs, _ = workload_specs(workload)
+
+    def per_dispatch(folder: str, counter: str, name_part: str):
+        vals = {}
+        for f in glob.glob(os.path.join(directory, folder, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    d = int(r["Dispatch_Id"])
+                    vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"]) * 1024.0
+        return [vals[d] for d in sorted(vals)]
+
+    copy_f = per_dispatch("copy_fetch", "FETCH_SIZE", "elementwise")
+    copy_w = per_dispatch("copy_write", "WRITE_SIZE", "elementwise")
+    copy_bytes = COPY_MB * 2**20
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy-kernel counters found")
+    f_scale = copy_bytes / (sum(copy_f) / len(copy_f))
+    w_scale = copy_bytes / (sum(copy_w) / len(copy_w))
+    gf = per_dispatch("gemm_fetch", "FETCH_SIZE", "gemm")
+    gw = per_dispatch("gemm_write", "WRITE_SIZE", "gemm")
+    if len(gf) < len(specs) * launches or len(gw) < len(specs) * launches:
+        raise SystemExit(f"expected {len(specs) * launches} GEMM dispatches, got {len(gf)} / {len(gw)}")
+    layers = {}
+    tot = 0.0
+    for li, s in enumerate(specs):
+        f = gf[li * launches:(li + 1) * launches]
+        w = gw[li * launches:(li + 1) * launches]
+        fb = sum(f) / len(f) * f_scale
+        wb = sum(w) / len(w) * w_scale
+        layers[s.name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                          "algorithmic_bytes": gemm_alg_bytes(s)}
+        tot += fb + wb
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+        if d.get("gemm_source_sha") != src_sha():
+            d = {}
+    except (OSError, ValueError):
+        d = {}
+    d["gemm_source_sha"] = src_sha()
+    d.setdefault("per_launch_bytes", {})[workload] = round(tot)
+    d.setdefault("layers", {})[workload] = layers
+    d["calibration"] = {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(d, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps({"workload": workload, "traffic_bytes": round(tot), "layers": layers,
+                      "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}))
+    return 0
+
+
+def copy_run(launches: int) -> int:
+    """A plain copy of known size (COPY_MB MiB read, COPY_MB MiB written) for counter calibration."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_MB * 2**20 // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": COPY_MB, "launches": launches}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,7 +256,15 @@ def main() -> int:
     ap.add_argument("--graph", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", choices=("bench", "gemm", "copy"), default="bench",
+                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy")
+    ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        return traffic_summary(args.traffic_summary, args.workload, args.launches)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the multi-GPU path is not built (one GPU per box); "
@@ -153,6 +278,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.mode == "copy":
+        return copy_run(args.launches)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     specs, kind = workload_specs(args.workload)
@@ -191,6 +318,18 @@ def main() -> int:
     def step(c: int) -> None:
         for s, xc, wqc, wac, b, ws, out in sets[c]:
             i8.linear(xc, wqc, wac, b, s.tau, cap, ws, out)
+
+    if args.mode == "gemm":
+        # exactly args.launches GEMM dispatches per layer, layer after layer
+        for li, s in enumerate(specs):
+            for i in range(args.launches):
+                _, _, wqc, wac, b, ws, out = sets[i % copies][li]
+                if i < copies:
+                    i8.linear_quantize(sets[i % copies][li][1], ws, s.tau)
+                i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "gemm_launches_per_layer": args.launches}))
+        return 0
 
     # first call: check for outlier-capacity overflow once (outside timing)
     for c in range(copies):
@@ -238,25 +377,8 @@ def main() -> int:
             ms, launch = graph_ms, "hipGraph replay"
 
     # ---- dominant kernel: the fused GEMM, timed alone with events on its stream -----
-    stream = torch.cuda.current_stream()
-    for c in range(copies):
-        for s, xc, wqc, wac, b, ws, out in sets[c]:
-            i8.linear_quantize(xc, ws, s.tau)
-    torch.cuda.synchronize()
-    gemm_us = {}
-    for li, s in enumerate(specs):
-        reps = max(args.steps, 50)
-        for i in range(10):
-            _, _, wqc, wac, b, ws, out = sets[i % copies][li]
-            i8.linear_matmul_dequant(ws, wqc, wac, b, out)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            _, _, wqc, wac, b, ws, out = sets[i % copies][li]
-            i8.linear_matmul_dequant(ws, wqc, wac, b, out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        gemm_us[s.name] = e0.elapsed_time(e1) * 1e3 / reps
+    gemm_us = time_gemm_launches(torch, i8, sets, specs, copies, max(args.steps, 50))
+    for s in specs:
         log(f"gemm {s.name}: {gemm_us[s.name]:.2f} us/launch")
 
     ops = sum(2 * s.m * s.n * s.k for s in specs)
@@ -280,8 +402,9 @@ def main() -> int:
         achieved = g_bytes / g_time / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
-    roof["kernel"] = "i8mp::gemm_kernel (fused dequant epilogue)"
+    roof["kernel"] = "fused int8 GEMM + dequant epilogue (gemm_dtl_kernel / gemm_decode_kernel)"
     roof["per_launch_us"] = {k: round(v, 3) for k, v in gemm_us.items()}
+    roof["timing"] = "HIP events around graph replays of the layer's GEMM launches"
     roof["traffic"] = read_traffic(args.workload)
 
     cpu = None
