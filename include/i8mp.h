@@ -79,6 +79,7 @@ const char* i8mp_status_string(i8mp_status s);
 /* Host.  ABI version of this header: (major << 16) | minor. */
 int32_t i8mp_abi_version(void);
 
+
 /* ------------------------------------------------------------------------- */
 /* int8_vectorwise_quant: outlier-column detection + row-scale calibration +
  * int8 quantization in one op (bitsandbytes PR "LLM.int8() Refactoring:
@@ -92,8 +93,9 @@ int32_t i8mp_abi_version(void);
  *   outlier_bitmap  optional uint32 [ceil(k/32)] output, bit (j % 32) of word
  *                j / 32 set iff column j is an outlier; may be NULL
  *   workspace    device scratch of at least i8mp_quant_workspace_bytes(m, k)
- *                bytes (per-row-block partial outlier bitmaps); contents on
- *                entry are ignored; may be NULL iff that query returns 0
+ *                bytes (the per-row-block partial outlier bitmaps of the
+ *                detection); contents on entry are ignored; may be NULL iff
+ *                that query returns 0 or threshold <= 0
  *
  * Weight quantization is this op with threshold <= 0 on the fp16 weight
  * [n x k]: q is the int8 weight state and absmax its per-row statistics.
@@ -188,8 +190,8 @@ typedef struct i8mp_linear_workspace {
     size_t count_offset;   /* int32 [1] outlier count                             */
     size_t xo_offset;      /* fp16 [m x cap_pad] gathered outlier columns         */
     int32_t cap_pad;       /* cap rounded up to the fp16 MFMA depth               */
-    size_t partial_offset; /* private: per-row-block partial bitmaps              */
-    size_t partial_bytes;
+    size_t scratch_offset; /* private: partial outlier bitmaps of the detection   */
+    size_t scratch_bytes;
 } i8mp_linear_workspace;
 
 i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,

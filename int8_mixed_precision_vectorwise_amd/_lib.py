@@ -44,8 +44,8 @@ class LinearWorkspaceLayout(Structure):
         ("count_offset", c_size_t),
         ("xo_offset", c_size_t),
         ("cap_pad", c_int32),
-        ("partial_offset", c_size_t),
-        ("partial_bytes", c_size_t),
+        ("scratch_offset", c_size_t),
+        ("scratch_bytes", c_size_t),
     ]
 
 

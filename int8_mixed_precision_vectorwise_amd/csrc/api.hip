@@ -35,16 +35,15 @@ bool bad_k(int64_t k) { return k < 1; }
 bool bad_ld(int64_t ld) { return ld > I8MP_MAX_LD; }
 
 void forward_layout(int64_t m, int64_t k, int32_t cap, i8mp_linear_workspace* L) {
-    const QuantPlan plan = make_quant_plan(m, k, true);
     std::memset(L, 0, sizeof(*L));
     L->ldq = round_up(k, 128);
     L->cap_pad = (int32_t)round_up(cap, 32);
     size_t off = 0;
-    L->partial_offset = off;
-    L->partial_bytes = plan.partial_bytes;
-    off = align_up(off + plan.partial_bytes);
+    L->scratch_offset = off;
+    L->scratch_bytes = quant_scratch_bytes(k);
+    off = align_up(off + L->scratch_bytes);
     L->bitmap_offset = off;
-    off = align_up(off + (size_t)plan.words * 4);
+    off = align_up(off + (size_t)ceil_div(k, 32) * 4);
     L->idx_offset = off;
     off = align_up(off + (size_t)(L->cap_pad > 0 ? L->cap_pad : 1) * 4);
     L->count_offset = off;
@@ -74,11 +73,11 @@ const char* i8mp_status_string(i8mp_status s) {
     }
 }
 
-int32_t i8mp_abi_version(void) { return (1 << 16) | 0; }
+int32_t i8mp_abi_version(void) { return (2 << 16) | 0; }
 
 size_t i8mp_quant_workspace_bytes(int64_t m, int64_t k) {
-    if (m < 0 || k < 1 || k > I8MP_MAX_K) return 0;
-    return make_quant_plan(m, k, true).partial_bytes;
+    if (m <= 0 || k < 1 || k > I8MP_MAX_K) return 0;
+    return quant_scratch_bytes(k);
 }
 
 i8mp_status i8mp_int8_vectorwise_quant(const void* x, int64_t m, int64_t k, int64_t ldx,
@@ -89,32 +88,23 @@ i8mp_status i8mp_int8_vectorwise_quant(const void* x, int64_t m, int64_t k, int6
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m > 0 && (!x || !q || !absmax)) return I8MP_EINVAL;
     const bool detect = threshold > 0.0f;
-    const QuantPlan plan = make_quant_plan(m, k, detect);
-    if (detect && m > 0 && (!workspace || workspace_bytes < plan.partial_bytes)) return I8MP_EWORKSPACE;
+    if (detect && m > 0 && (!workspace || workspace_bytes < quant_scratch_bytes(k))) return I8MP_EWORKSPACE;
     if (m == 0 && !outlier_bitmap) return I8MP_OK;
     if (i8mp_status s = check_device(); s != I8MP_OK) return s;
-    uint32_t* partial = static_cast<uint32_t*>(workspace);
-    if (detect && m > 0) {
-        if (launch_detect(static_cast<const half_bits*>(x), m, k, ldx, threshold, plan, partial,
-                          stream) != hipSuccess)
-            return I8MP_ELAUNCH;
-    }
     QuantArgs a{};
     a.x = static_cast<const half_bits*>(x);
     a.m = m;
     a.k = k;
     a.ldx = ldx;
     a.threshold = threshold;
-    a.partial = (detect && m > 0) ? partial : nullptr;
-    a.row_blocks = plan.row_blocks;
-    a.words = plan.words;
+    a.partial = static_cast<uint32_t*>(workspace);
+    a.words = ceil_div(k, 32);
     a.q = q;
     a.ldq = ldq;
     a.kpad = k;
     a.absmax = absmax;
     a.bitmap_out = outlier_bitmap;
-    a.rows_per_block = plan.rows_per_quant_block;
-    return launched(launch_quant(a, stream));
+    return launched(launch_quantize(a, stream));
 }
 
 i8mp_status i8mp_outlier_extract(const void* x, int64_t m, int64_t k, int64_t ldx,
@@ -131,7 +121,7 @@ i8mp_status i8mp_outlier_extract(const void* x, int64_t m, int64_t k, int64_t ld
     a.m = x_out ? m : 0;
     a.k = k;
     a.ldx = ldx;
-    a.partial = outlier_bitmap;
+    a.bitmap_in = outlier_bitmap;
     a.row_blocks = 1;
     a.words = ceil_div(k, 32);
     a.idx_out = cap > 0 ? idx : nullptr;
@@ -141,8 +131,7 @@ i8mp_status i8mp_outlier_extract(const void* x, int64_t m, int64_t k, int64_t ld
     a.x_out = static_cast<half_bits*>(x_out);
     a.ldo = ldo;
     a.xo_cols = cap;
-    a.rows_per_block = 8;
-    return launched(launch_quant(a, stream));
+    return launched(launch_quant_rows(a, stream));
 }
 
 i8mp_status i8mp_int8_linear_matmul(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
@@ -215,23 +204,14 @@ namespace {
 i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
                              int32_t cap, const i8mp_linear_workspace& L, char* ws,
                              hipStream_t stream) {
-    const bool detect = threshold > 0.0f;
-    const QuantPlan plan = make_quant_plan(m, k, detect);
-    uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial_offset);
-    if (detect) {
-        if (launch_detect(static_cast<const half_bits*>(x), m, k, ldx, threshold, plan, partial,
-                          stream) != hipSuccess)
-            return I8MP_ELAUNCH;
-    }
     QuantArgs a{};
     a.x = static_cast<const half_bits*>(x);
     a.m = m;
     a.k = k;
     a.ldx = ldx;
     a.threshold = threshold;
-    a.partial = detect ? partial : nullptr;
-    a.row_blocks = plan.row_blocks;
-    a.words = plan.words;
+    a.partial = reinterpret_cast<uint32_t*>(ws + L.scratch_offset);
+    a.words = ceil_div(k, 32);
     a.q = reinterpret_cast<int8_t*>(ws + L.q_offset);
     a.ldq = L.ldq;
     a.kpad = L.ldq;
@@ -244,8 +224,7 @@ i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, f
     a.x_out = L.cap_pad > 0 ? reinterpret_cast<half_bits*>(ws + L.xo_offset) : nullptr;
     a.ldo = L.cap_pad;
     a.xo_cols = L.cap_pad;
-    a.rows_per_block = plan.rows_per_quant_block;
-    return launched(launch_quant(a, stream));
+    return launched(launch_quantize(a, stream));
 }
 
 // The fused GEMM + dequant epilogue reading the forward workspace.

@@ -45,7 +45,7 @@ def test_exports_match_header(L):
 def test_status_strings(L):
     for s in (OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE, -5):
         assert len(L.i8mp_status_string(s)) > 0
-    assert L.i8mp_abi_version() >> 16 == 1
+    assert L.i8mp_abi_version() >> 16 == 2
 
 
 def test_workspace_queries(L):
@@ -56,11 +56,12 @@ def test_workspace_queries(L):
     assert L.i8mp_linear_workspace_query(2048, 4096, 4096, 20, ctypes.byref(lay)) == OK
     assert lay.ldq % 128 == 0 and lay.ldq >= 4096
     assert lay.cap_pad == 32
-    offs = [lay.partial_offset, lay.bitmap_offset, lay.idx_offset, lay.count_offset,
+    offs = [lay.scratch_offset, lay.bitmap_offset, lay.idx_offset, lay.count_offset,
             lay.absmax_offset, lay.q_offset, lay.xo_offset]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.bytes >= lay.xo_offset + 2048 * 32 * 2
     assert lay.q_offset + 2048 * lay.ldq <= lay.xo_offset
+    assert 0 < lay.scratch_bytes <= lay.bitmap_offset - lay.scratch_offset
     assert L.i8mp_linear_workspace_query(16, 16, 133145, 8, ctypes.byref(lay)) == ERANGE
     assert L.i8mp_linear_workspace_query(16, 16, 0, 8, ctypes.byref(lay)) == EINVAL
     assert L.i8mp_linear_workspace_query(16, 16, 64, -1, ctypes.byref(lay)) == EINVAL

@@ -31,6 +31,8 @@ QUANT_CASES = [
     (130, 4096, 7, 1.0, TAU),
     (9, 20000, 20, 0.3, TAU),      # register-resident chunks, largest bucket
     (4, 40000, 5, 1.0, TAU),       # streamed rows
+    (2100, 4000, 6, 0.4, TAU),     # two kernels, a wavefront per row
+    (300, 20000, 9, 0.5, TAU),     # two kernels, a workgroup per row, 16-load batches
     (33, 300, 0, 1.0, 0.0),        # threshold off
     (8, 96, 96, 1.0, TAU),         # every column an outlier
 ]
@@ -96,6 +98,27 @@ def test_outlier_extract_bit_exact(m, k, o, cap):
     assert int(host(count)[0]) == rcount
     assert_equal(idx, ridx, "idx")
     assert_equal(xo.view(torch.int16), rxo.view(np.int16), "x_out")
+
+
+@pytest.mark.parametrize("m,k", [(512, 1024), (300, 20000)], ids=["wave_rows", "block_rows"])
+def test_quant_workspace_reuse(m, k):
+    """Three calls on one workspace, each with other outlier columns: every
+    result is the oracle's (nothing carries over from the previous call)."""
+    ws = i8.LinearWorkspace.create(m, 8, k, 64, torch.device("cuda"))
+    for call in range(3):
+        L = make_inputs(m, k, 1, n_outlier=3 + call, lo=6.0, hi=60.0, seed=(72, call, m), outlier_row_frac=0.5,
+                        with_weight=False)
+        say(f"linear_quantize reuse m={m} k={k} call={call}")
+        i8.linear_quantize(dev(L.x), ws, TAU)
+        torch.cuda.synchronize()
+        ref = oracle.vectorwise_quant(L.x, TAU)
+        assert_equal(ws.codes(), ref.q, "codes")
+        assert_equal(ws.absmax(), ref.absmax, "absmax")
+        assert_equal(ws.bitmap().view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+        ridx, rcount, rxo = oracle.outlier_extract(L.x, ref.cols, 64)
+        assert int(host(ws.count())[0]) == rcount
+        assert_equal(ws.idx()[:64], ridx, "idx")
+        assert_equal(ws.x_out().view(torch.int16), rxo.view(np.int16), "x_out")
 
 
 MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128), (300, 600, 300),
