@@ -185,7 +185,221 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// m <= 4 (and m x K fits 32 KB): a dot-product GEMV on the vector ALUs.
+// With one to four activation rows the matrix cores would idle over zero
+// padding, and the MFMA kernel above spends as many load instructions on the
+// activations as on the weights.  Here the int8 activations are copied to LDS
+// once per workgroup, and the weight streams straight into registers: each
+// wave owns 8 weight rows and a share of the 128-byte K chunks (chunks p,
+// p + G, ...), one 1 KB load per chunk (lane i: row i / 8, bytes 16 (i % 8)
+// of the chunk), kGvBatch loads in flight.  v_dot4_i32_i8 against the LDS
+// activation bytes (lanes with equal i % 8 read the same 16 bytes: a
+// broadcast) accumulates exactly in int32.  The outlier sub-matmul is taken
+// from the streamed weight bytes as they pass: a chunk that contains an
+// outlier column adds W[n, j] * x[r, j] (fp16 x, fp32 sum) for the lanes that
+// hold that byte, so no weight byte is read twice.  Sums meet across the 8
+// lanes of a row (shuffles) and the G waves of a row group (LDS).
+namespace {
+
+constexpr int kGvRows = 8;     // weight rows per wave
+constexpr int kGvBatch = 8;    // weight loads in flight per wave
+constexpr int kGvOutl = 64;    // outlier columns handled in the stream (more: gathered at the end)
+
+__device__ inline int8_t byte_of(const v4i_t& v, int b) {
+    return (int8_t)(((uint32_t)v[b >> 2] >> (8 * (b & 3))) & 0xffu);
+}
+
+}  // namespace
+
+template <int G, int M, bool kFused>
+__global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) int8_t gsm[];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wid % G;
+    const int64_t n0 = ((int64_t)blockIdx.x * (4 / G) + wid / G) * kGvRows;
+    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
+    const int64_t nchunks = kr / kChunk;
+    const int64_t mine = nchunks > part ? (nchunks - part + G - 1) / G : 0;
+
+    // LDS: activations [M][kr] | int32 partials [4][M][8] | fp32 partials [4][M][8] |
+    //      outlier columns [kGvOutl] | outlier values [M][kGvOutl]
+    int8_t* xs = gsm;
+    int32_t* red = reinterpret_cast<int32_t*>(gsm + M * kr);
+    float* pred = reinterpret_cast<float*>(red + 4 * M * kGvRows);
+    int32_t* oidx = reinterpret_cast<int32_t*>(pred + 4 * M * kGvRows);
+    float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
+
+    // 1. the first batch of weight loads goes out first
+    const __amdgpu_buffer_rsrc_t rw = rsrc(g.b + n0 * g.ldb, n0 < g.n ? (g.n - n0 - 1) * g.ldb + kr : 0);
+    const int w_off = (int)((lane >> 3) * g.ldb + (lane & 7) * 16);
+    v4i_t w[kGvBatch];
+    auto load_batch = [&](int64_t j0) {
+#pragma unroll
+        for (int u = 0; u < kGvBatch; ++u) {
+            const int64_t j = j0 + u;
+            const int kb = (int)((part + j * G) * kChunk);
+            // the K offset goes in the range-checked VGPR offset: bytes past
+            // the end of the weight read as 0
+            w[u] = j < mine ? __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + kb, 0, 0))
+                            : v4i_t{0, 0, 0, 0};
+        }
+    };
+    load_batch(0);
+
+    // 2. activations (rows >= m as zeros), and the outlier columns / values
+    {
+        const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
+        const int64_t per_row = kr / 16;
+        for (int64_t f = threadIdx.x; f < M * per_row; f += 256) {
+            const int64_t r = f / per_row, c = f - r * per_row;
+            v4i_t v = {0, 0, 0, 0};
+            if (r < g.m)
+                v = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(r * g.lda + c * 16), 0, 0));
+            *reinterpret_cast<v4i_t*>(xs + r * kr + c * 16) = v;
+        }
+    }
+    int cnt = 0;
+    if (kFused && g.x_out) {
+        cnt = *g.count;
+        cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+        const int lc = cnt < kGvOutl ? cnt : kGvOutl;
+        for (int t = threadIdx.x; t < kGvOutl; t += 256) oidx[t] = t < lc ? g.idx[t] : 0x7fffffff;
+        for (int t = threadIdx.x; t < M * kGvOutl; t += 256) {
+            const int r = t / kGvOutl, s2 = t % kGvOutl;
+            oval[t] = (s2 < lc && r < g.m) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
+        }
+    }
+    __syncthreads();
+    const int lc = cnt < kGvOutl ? cnt : kGvOutl;
+
+    // 3. stream: dot4 per 4 weight bytes, outliers from the bytes in flight
+    int32_t acc[M];
+    float pacc[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        acc[r] = 0;
+        pacc[r] = 0.0f;
+    }
+    const int slice = (lane & 7) * 16;  // this lane's 16 bytes of each chunk
+    int next = 0;                        // first outlier column not yet behind the stream
+    for (int64_t j0 = 0; j0 < mine; j0 += kGvBatch) {
+        if (j0 > 0) load_batch(j0);
+#pragma unroll
+        for (int u = 0; u < kGvBatch; ++u) {
+            const int64_t j = j0 + u;
+            if (j >= mine) break;
+            const int64_t kb = (part + j * G) * kChunk;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                const v4i_t xv = *reinterpret_cast<const v4i_t*>(xs + r * kr + kb + slice);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) acc[r] = __builtin_amdgcn_sdot4(w[u][d], xv[d], acc[r], false);
+            }
+            if (kFused) {
+                while (next < lc && oidx[next] < kb) ++next;  // columns in other waves' chunks
+                for (int s2 = next; s2 < lc && oidx[s2] < kb + kChunk; ++s2) {
+                    const int off = oidx[s2] - (int)kb - slice;  // byte of this lane's slice, if any
+                    if (off >= 0 && off < 16) {
+                        const float wv = (float)byte_of(w[u], off);
+#pragma unroll
+                        for (int r = 0; r < M; ++r) pacc[r] += wv * oval[r * kGvOutl + s2];
+                    }
+                }
+            }
+        }
+    }
+
+    // 4. sums over the 8 lanes of a row, then over the G waves of the group
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+            acc[r] += __shfl_xor(acc[r], off, 64);
+            if (kFused) pacc[r] += __shfl_xor(pacc[r], off, 64);
+        }
+    }
+    const int row = lane >> 3;
+    if (part > 0 && (lane & 7) == 0) {
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            red[(wid * M + r) * kGvRows + row] = acc[r];
+            if (kFused) pred[(wid * M + r) * kGvRows + row] = pacc[r];
+        }
+    }
+    __syncthreads();
+    if (part > 0 || (lane & 7) != 0) return;  // no barrier below
+#pragma unroll
+    for (int w2 = 1; w2 < G; ++w2)
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            acc[r] += red[((wid + w2) * M + r) * kGvRows + row];
+            if (kFused) pacc[r] += pred[((wid + w2) * M + r) * kGvRows + row];
+        }
+
+    // 5. epilogue: lane 8 q owns weight row n0 + q
+    const int64_t n = n0 + row;
+    if (n >= g.n) return;
+    if constexpr (!kFused) {
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+            if (r < g.m) g.c[r * g.ldc + n] = acc[r];
+    } else {
+        // outlier columns past the streamed ones: gathered
+        for (int s2 = lc; s2 < cnt; ++s2) {
+            const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
+#pragma unroll
+            for (int r = 0; r < M; ++r)
+                if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
+        }
+        const float r127 = 1.0f / 127.0f;
+        const float sw = g.col_absmax[n] * r127;
+        const float bj = g.bias ? h2f(g.bias[n]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+            if (r < g.m) {
+                const float sx = g.row_absmax[r] * r127;
+                g.out[r * g.ldout + n] = f2h(sw * ((float)acc[r] * sx + pacc[r]) + bj);
+            }
+    }
+}
+
+// m <= 4 with the activations in at most 32 KB of LDS
+bool gemv_fits(const GemmArgs& g) {
+    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
+    // at most 32 KB: four workgroups per CU by LDS (a larger block measured slower
+    // than the MFMA kernel: too few workgroups resident)
+    return g.m >= 1 && g.m <= 4 && (g.m > 2 ? 4 : g.m) * kr <= 32 * 1024;
+}
+
+template <int M, bool kFused>
+hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t stream) {
+    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
+    const int64_t nchunks = kr / kChunk;
+    const int64_t groups = (g.n + kGvRows - 1) / kGvRows;
+    // K splits: about 2500 waves or more, each with at least 8 chunks
+    int gs = 1;
+    while (gs < 4 && groups * gs < 2560 && nchunks / (2 * gs) >= kGvBatch) gs *= 2;
+    const size_t lds = (size_t)M * kr + (size_t)4 * M * kGvRows * 8 + (size_t)kGvOutl * 4 + (size_t)M * kGvOutl * 4;
+    const dim3 grid((unsigned)((groups * gs + 3) / 4));
+    switch (gs) {
+        case 1: hipLaunchKernelGGL((gemv_kernel<1, M, kFused>), grid, dim3(256), lds, stream, g); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<2, M, kFused>), grid, dim3(256), lds, stream, g); break;
+        default: hipLaunchKernelGGL((gemv_kernel<4, M, kFused>), grid, dim3(256), lds, stream, g); break;
+    }
+    return hipGetLastError();
+}
+
+template <bool kFused>
+hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
+    if (g.m == 1) return launch_gemv_m<1, kFused>(g, stream);
+    if (g.m == 2) return launch_gemv_m<2, kFused>(g, stream);
+    return launch_gemv_m<4, kFused>(g, stream);
+}
+
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
+    if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
     // waves per 16-row group: enough K splits that each wave has a long run of
     // 128-byte chunks, with all groups resident at once (two workgroups per CU)
     const int64_t groups = (g.n + kRows - 1) / kRows;

@@ -21,6 +21,10 @@
 //                  values into the compact fp16 matrix.  Workgroup 0 also
 //                  writes the bitmap, the ascending index list and the count.
 //
+// One or two rows of at most 65536 columns (decode) take quant_small_kernel:
+// one workgroup of 1024 threads holds all of x in registers and does every
+// step in one launch.
+//
 // (A single kernel with a grid-wide meeting point instead of the second
 // launch measured slower on MI355X: the device-scope release / acquire round
 // trips it needs cost more than the launch they replace.)
@@ -94,7 +98,8 @@ __device__ inline float chunk_max(const uint4& v, uint32_t obits) {
 // outlier column in the index list); returns the total (all threads call).
 __device__ inline int32_t bitmap_prefix(const uint32_t* bm, int32_t* pre, int64_t words, int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t per = (words + 255) / 256;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t per = (words + blockDim.x - 1) / blockDim.x;
     const int64_t w0 = (int64_t)tid * per;
     int64_t w1 = w0 + per;
     if (w1 > words) w1 = words;
@@ -109,7 +114,7 @@ __device__ inline int32_t bitmap_prefix(const uint32_t* bm, int32_t* pre, int64_
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int32_t off = 0, total = 0;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < nwaves; ++i) {
         if (i < wave) off += wave_tot[i];
         total += wave_tot[i];
     }
@@ -126,15 +131,16 @@ __device__ inline int32_t bitmap_prefix(const uint32_t* bm, int32_t* pre, int64_
 __device__ inline void publish(const QuantArgs& a, const uint32_t* bm, const int32_t* pre, int32_t total,
                                bool outl) {
     const int tid = threadIdx.x;
+    const int nt = blockDim.x;
     const int32_t kept = total < a.cap ? total : a.cap;
     if (a.bitmap_out)
-        for (int64_t w = tid; w < a.words; w += 256) a.bitmap_out[w] = outl ? bm[w] : 0u;
+        for (int64_t w = tid; w < a.words; w += nt) a.bitmap_out[w] = outl ? bm[w] : 0u;
     if (a.count_out && tid == 0) *a.count_out = total;
     if (a.idx_out) {
-        for (int32_t s = tid; s < a.idx_len; s += 256)
+        for (int32_t s = tid; s < a.idx_len; s += nt)
             if (s >= kept) a.idx_out[s] = -1;
         if (outl) {
-            for (int64_t w = tid; w < a.words; w += 256) {
+            for (int64_t w = tid; w < a.words; w += nt) {
                 uint32_t v = bm[w];
                 int32_t slot = pre[w];
                 while (v) {
@@ -334,8 +340,111 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// One or two rows (decode): one workgroup of 1024 threads holds all of x in
+// registers and so sees the whole outlier set itself: detection, calibration,
+// quantization and extraction in one launch, x read once.  Chunk f = tid +
+// 1024 i of the flattened (row, 8-column chunk) range, L per thread.  (For
+// more rows one workgroup's memory pipeline measured slower than the two
+// kernels, which spread the rows over the CUs.)
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallMaxL = 8;
+constexpr int kSmallMaxRows = 2;
+
+template <bool kVec, int L>
+__global__ __launch_bounds__(1024) void quant_small_kernel(QuantArgs a) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* bm = smem;                                       // [words]
+    int32_t* pre = reinterpret_cast<int32_t*>(smem + a.words);  // [words]
+    uint32_t* rmax = smem + 2 * a.words;                        // [m] float bits
+    float* rinv = reinterpret_cast<float*>(rmax + a.m);         // [m]
+    __shared__ int32_t wave_tot[kSmallThreads / 64];
+
+    const int tid = threadIdx.x;
+    const bool outl = a.threshold > 0.0f;
+    const int32_t cpr = (int32_t)((a.k + 7) / 8);
+    const int32_t total_chunks = (int32_t)a.m * cpr;
+
+    uint4 v[L];
+    uint32_t rc[L];  // row << 16 | chunk (rows < kSmallMaxRows, chunks < 65536)
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int32_t f = tid + kSmallThreads * i;
+        const int32_t r = f / cpr, ch = f - r * cpr;
+        rc[i] = ((uint32_t)r << 16) | (uint32_t)ch;
+        v[i] = f < total_chunks ? load8<kVec>(a.x + r * a.ldx, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
+    }
+    for (int64_t w = tid; w < a.words; w += kSmallThreads) bm[w] = 0u;
+    for (int64_t r = tid; r < a.m; r += kSmallThreads) rmax[r] = 0u;
+    __syncthreads();
+    if (outl) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if (tid + kSmallThreads * i < total_chunks) {
+                const uint32_t bits = outlier_bits8(v[i], a.threshold);
+                const int32_t ch = (int32_t)(rc[i] & 0xffffu);
+                if (bits) atomicOr(&bm[ch >> 2], bits << ((ch & 3) * 8));
+            }
+        }
+        __syncthreads();
+    }
+    const bool need_prefix = outl && (a.x_out || a.idx_out || a.count_out);
+    const int32_t total = need_prefix ? bitmap_prefix(bm, pre, a.words, wave_tot) : 0;
+    const int32_t kept = total < a.cap ? total : a.cap;
+    publish(a, bm, pre, total, outl);
+
+    // row absmax over the non-outlier columns (float bits order as uints for x >= 0)
+    auto obyte = [&](int32_t ch) -> uint32_t { return outl ? (bm[ch >> 2] >> ((ch & 3) * 8)) & 0xffu : 0u; };
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        if (tid + kSmallThreads * i < total_chunks) {
+            const float mx = chunk_max(v[i], obyte((int32_t)(rc[i] & 0xffffu)));
+            if (mx > 0.0f) atomicMax(&rmax[rc[i] >> 16], __float_as_uint(mx));
+        }
+    }
+    __syncthreads();
+    for (int64_t r = tid; r < a.m; r += kSmallThreads) {
+        const float s = __uint_as_float(rmax[r]);
+        rinv[r] = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
+        if (a.q) a.absmax[r] = s;
+    }
+    __syncthreads();
+
+    const bool vec_q = a.q && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        if (tid + kSmallThreads * i < total_chunks) {
+            const int32_t r = (int32_t)(rc[i] >> 16), ch = (int32_t)(rc[i] & 0xffffu);
+            const float s = __uint_as_float(rmax[r]);
+            emit8(a, v[i], obyte(ch), r, (int64_t)ch * 8, rinv[r], !(s > 0.0f), vec_q, bm, pre);
+        }
+    }
+    if (a.q && a.kpad > a.k) {
+        const int64_t pad = a.kpad - a.k;
+        for (int64_t f = tid; f < a.m * pad; f += kSmallThreads) a.q[(f / pad) * a.ldq + a.k + f % pad] = 0;
+    }
+    if (a.x_out && a.xo_cols > kept) {
+        const int64_t pad = a.xo_cols - kept;
+        for (int64_t f = tid; f < a.m * pad; f += kSmallThreads) a.x_out[(f / pad) * a.ldo + kept + f % pad] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
 
 namespace {
+
+template <bool kVec, int L>
+hipError_t launch_small_l(const QuantArgs& a, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL((quant_small_kernel<kVec, L>), dim3(1), dim3(kSmallThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <bool kVec>
+hipError_t launch_small(const QuantArgs& a, int64_t per_thread, size_t lds, hipStream_t stream) {
+    if (per_thread <= 1) return launch_small_l<kVec, 1>(a, lds, stream);
+    if (per_thread <= 2) return launch_small_l<kVec, 2>(a, lds, stream);
+    if (per_thread <= 4) return launch_small_l<kVec, 4>(a, lds, stream);
+    return launch_small_l<kVec, 8>(a, lds, stream);
+}
 
 template <bool kVec, bool kBlockRow>
 hipError_t launch_rows(const QuantArgs& a, int64_t blocks, bool big, size_t lds, hipStream_t stream) {
@@ -376,6 +485,11 @@ hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
     QuantArgs a = in;
     const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
     a.bitmap_in = nullptr;
+    const int64_t per_thread = ceil_div(a.m * ceil_div(a.k, 8), kSmallThreads);
+    if (a.m > 0 && a.m <= kSmallMaxRows && per_thread <= kSmallMaxL) {
+        const size_t lds = ((size_t)a.words * 2 + (size_t)a.m * 2) * sizeof(uint32_t);
+        return vec ? launch_small<true>(a, per_thread, lds, stream) : launch_small<false>(a, per_thread, lds, stream);
+    }
     if (a.threshold > 0.0f && a.m > 0) {
         // detect: 256 columns x RB rows per workgroup, at most kMaxRowBlocks
         // row blocks (RB >= 8), about 1024 workgroups when the shape allows

@@ -122,7 +122,8 @@ def test_quant_workspace_reuse(m, k):
 
 
 MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128), (300, 600, 300),
-             (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100)]
+             (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100),
+             (3, 777, 1280), (2, 513, 640), (4, 100, 13824)]
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -193,6 +194,13 @@ FWD_CASES = [
     (12, 96, 70, 96, 1.0, True, TAU, 96),         # every column an outlier
     (4, 5120, 1000, 8, 1.0, False, TAU, 256),     # decode-shaped
     (16, 2048, 512, 40, 0.5, False, TAU, 64),     # more outliers than one fp16 MFMA step
+    # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
+    (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
+    (2, 4096, 264, 5, 0.5, False, TAU, 32),
+    (3, 2000, 130, 9, 1.0, True, TAU, 32),
+    (4, 8192, 600, 8, 1.0, False, TAU, 256),      # the largest K the GEMV takes at m = 4
+    (1, 13824, 1024, 70, 0.5, True, TAU, 128),    # more outlier columns than the stream handles
+    (2, 640, 2048, 0, 1.0, False, TAU, 8),        # no outliers
 ]
 
 
