@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const bool active = n0 < g.n;
 
     const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-    const __amdgpu_buffer_rsrc_t rw = rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + kr);
+    // the weight's range ends at the last row's k rounded up to a dword (the
+    // range check is per dword); the activations are zero-padded to kr
+    const __amdgpu_buffer_rsrc_t rw = rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3));
     const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
     const __amdgpu_buffer_rsrc_t r_none = rsrc(g.a, 0);
 
@@ -102,10 +104,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         int8_t* st = my_ring + slot * kStageBytes;
         const __amdgpu_buffer_rsrc_t sw = real ? rw : r_none;
         const __amdgpu_buffer_rsrc_t sx = real ? rx : r_none;
-        dma16(sw, st, w_off[0], kb);
-        dma16(sw, st + 1024, w_off[1], kb);
-        xr[slot][0] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off, kb, 0));
-        xr[slot][1] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off + 16, kb, 0));
+        dma16(sw, st, w_off[0] + kb, 0);
+        dma16(sw, st + 1024, w_off[1] + kb, 0);
+        xr[slot][0] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off + kb, 0, 0));
+        xr[slot][1] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off + 16 + kb, 0, 0));
     };
 
     v4i_t acc = {0, 0, 0, 0};
@@ -232,7 +234,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
     float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
 
     // 1. the first batch of weight loads goes out first
-    const __amdgpu_buffer_rsrc_t rw = rsrc(g.b + n0 * g.ldb, n0 < g.n ? (g.n - n0 - 1) * g.ldb + kr : 0);
+    const __amdgpu_buffer_rsrc_t rw =
+        rsrc(g.b + n0 * g.ldb, n0 < g.n ? (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3) : 0);
     const int w_off = (int)((lane >> 3) * g.ldb + (lane & 7) * 16);
     v4i_t w[kGvBatch];
     auto load_batch = [&](int64_t j0) {

@@ -91,7 +91,9 @@ __device__ inline void tile_coords(int64_t bid, int64_t nblocks, int64_t tiles_m
 
 // One wave-wide global -> LDS copy through a buffer resource: lane i's
 // `bytes` (4 or 16) land at lds + bytes * i (lds must be wave-uniform).
-// Out-of-range lanes write zeros.
+// Lanes whose VGPR offset is out of range write zeros; the range check does
+// not cover the SGPR offset, so every kernel here passes its K offset in the
+// VGPR offset and 0 as the SGPR offset.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
                                              soffset, 0, 0);
@@ -334,9 +336,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // per-thread chunk coordinates within a tile: row = id >> 3, chunk = id & 7
     // The range ends 16-byte-rounded past the last valid row's k bytes: with
     // 16-byte aligned rows that never leaves the row's final 16-byte granule.
-    const int64_t k16 = (g.k + 15) & ~(int64_t)15;
-    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + k16);
-    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + k16);
+    // ranges end at the last row's k rounded up to a dword: the range check is
+    // per dword, so no load reaches more than 3 bytes past the operands
+    const int64_t k4 = (g.k + 3) & ~(int64_t)3;
+    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + k4);
+    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + k4);
     int a_off[A_CH], b_off[B_CH];
 #pragma unroll
     for (int p = 0; p < A_CH; ++p) {
@@ -355,10 +359,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         if constexpr (kAligned) {
 #pragma unroll
             for (int p = 0; p < A_CH; ++p)
-                ra[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_src, a_off[p], kb, 0));
+                ra[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_src, a_off[p] + kb, 0, 0));
 #pragma unroll
             for (int p = 0; p < B_CH; ++p)
-                rb[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb_src, b_off[p], kb, 0));
+                rb[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb_src, b_off[p] + kb, 0, 0));
             if (kt == ktiles - 1 && ktail < BK) {
                 // bytes past k belong to the next row: zero them in A (B's are then harmless)
 #pragma unroll
@@ -561,7 +565,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
 
     const int64_t kr = (g.k + BKS - 1) / BKS * BKS;
     const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + kr);
-    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + kr);
+    // the weight's range ends at the last row's k rounded up to a dword (the
+    // range check is per dword); A's codes are zero-padded to whole stages
+    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3));
     int a_off[A_INS], b_off[B_INS];
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
@@ -579,9 +585,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         const int kb = (int)(kt * BKS);
         int8_t* base = smem + stage * STAGE;
 #pragma unroll
-        for (int j = 0; j < A_INS; ++j) dma16(ra_src, base + (wave * A_INS + j) * 1024, a_off[j], kb);
+        for (int j = 0; j < A_INS; ++j) dma16(ra_src, base + (wave * A_INS + j) * 1024, a_off[j] + kb, 0);
 #pragma unroll
-        for (int j = 0; j < B_INS; ++j) dma16(rb_src, base + STAGE_A + (wave * B_INS + j) * 1024, b_off[j], kb);
+        for (int j = 0; j < B_INS; ++j) dma16(rb_src, base + STAGE_A + (wave * B_INS + j) * 1024, b_off[j] + kb, 0);
     };
 
     v16i acc[FM][FN];
@@ -645,9 +651,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         for (int q = 0; q < INS; ++q) {
             if (q < first || q >= first + count) continue;
             if (q < A_INS)
-                dma16(sa, base + (wave * A_INS + q) * 1024, a_off[q], kb);
+                dma16(sa, base + (wave * A_INS + q) * 1024, a_off[q] + kb, 0);
             else
-                dma16(sb, base + STAGE_A + (wave * B_INS + (q - A_INS)) * 1024, b_off[q - A_INS], kb);
+                dma16(sb, base + STAGE_A + (wave * B_INS + (q - A_INS)) * 1024, b_off[q - A_INS] + kb, 0);
         }
     };
     const int64_t ktiles = (g.k + BKS - 1) / BKS;
