@@ -462,8 +462,11 @@ hipError_t launch_quant_rows(const QuantArgs& in, hipStream_t stream) {
     const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
     const size_t lds = (size_t)a.words * 2 * sizeof(uint32_t);
     const int64_t cpr = (a.k + 7) / 8;
-    // long rows (or few of them): a workgroup per row; short rows: a wavefront per row
-    const bool block_row = cpr > 64 * 8 || a.m <= 64;
+    // a workgroup per row for long rows (over 4096 columns), for few rows, and
+    // for rows of 2048+ columns when there are at most 512 of them (one row per
+    // workgroup spreads the per-element work over the CUs); else a wavefront
+    // per row
+    const bool block_row = cpr > 512 || a.m <= 64 || (cpr >= 256 && a.m <= 512);
     const bool big = cpr > (block_row ? 256 : 64) * 8;
     int64_t blocks;
     // enough rows per workgroup to amortize the OR of the partial bitmaps
