@@ -32,8 +32,11 @@ METRIC = "int8 linear TOPS & % int8-MFMA peak (prefill); GB/s & % HBM peak (deco
 PEAK_INT8_OPS = 5.0e15     # MI355X dense int8 MFMA
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
 DEFAULT_WORKLOAD = "opt350m_mlp_pair_m512"
-GEMM_SRC = os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", "gemm.hip")
+# sources of the GEMM-side kernels (prefill tiles, decode kernels, shared helpers)
+GEMM_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
+             for f in ("gemm.hip", "decode.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_KERNELS = ("i8mp::gemm", "i8mp::gemv")  # kernel-name parts of the fused GEMM launches
 COPY_MB = 256              # calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -73,7 +76,8 @@ def gemm_alg_bytes(s) -> int:
 
 def src_sha() -> str:
     h = hashlib.sha256()
-    h.update(open(GEMM_SRC, "rb").read())
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -185,24 +189,24 @@ def traffic_summary(directory: str, workload: str, launches: int) -> int:
     import glob
     specs, _ = workload_specs(workload)
 
-    def per_dispatch(folder: str, counter: str, name_part: str):
+    def per_dispatch(folder: str, counter: str, name_part: tuple):
         vals = {}
         for f in glob.glob(os.path.join(directory, folder, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in name_part):
                     d = int(r["Dispatch_Id"])
                     vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"]) * 1024.0
         return [vals[d] for d in sorted(vals)]
 
-    copy_f = per_dispatch("copy_fetch", "FETCH_SIZE", "elementwise")
-    copy_w = per_dispatch("copy_write", "WRITE_SIZE", "elementwise")
+    copy_f = per_dispatch("copy_fetch", "FETCH_SIZE", ("elementwise",))
+    copy_w = per_dispatch("copy_write", "WRITE_SIZE", ("elementwise",))
     copy_bytes = COPY_MB * 2**20
     if not copy_f or not copy_w:
         raise SystemExit("no copy-kernel counters found")
     f_scale = copy_bytes / (sum(copy_f) / len(copy_f))
     w_scale = copy_bytes / (sum(copy_w) / len(copy_w))
-    gf = per_dispatch("gemm_fetch", "FETCH_SIZE", "gemm")
-    gw = per_dispatch("gemm_write", "WRITE_SIZE", "gemm")
+    gf = per_dispatch("gemm_fetch", "FETCH_SIZE", GEMM_KERNELS)
+    gw = per_dispatch("gemm_write", "WRITE_SIZE", GEMM_KERNELS)
     if len(gf) < len(specs) * launches or len(gw) < len(specs) * launches:
         raise SystemExit(f"expected {len(specs) * launches} GEMM dispatches, got {len(gf)} / {len(gw)}")
     layers = {}

@@ -199,11 +199,10 @@ i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t
 
 namespace {
 
-// Codes, absmax, bitmap, index list, count and gathered outlier values of x
-// into the forward workspace (detect + quant kernels).
-i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
-                             int32_t cap, const i8mp_linear_workspace& L, char* ws,
-                             hipStream_t stream) {
+// Quantizer arguments writing codes, absmax, bitmap, index list, count and
+// gathered outlier values of x into the forward workspace.
+QuantArgs forward_quant_args(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold, int32_t cap,
+                             const i8mp_linear_workspace& L, char* ws) {
     QuantArgs a{};
     a.x = static_cast<const half_bits*>(x);
     a.m = m;
@@ -224,14 +223,19 @@ i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, f
     a.x_out = L.cap_pad > 0 ? reinterpret_cast<half_bits*>(ws + L.xo_offset) : nullptr;
     a.ldo = L.cap_pad;
     a.xo_cols = L.cap_pad;
-    return launched(launch_quantize(a, stream));
+    return a;
 }
 
-// The fused GEMM + dequant epilogue reading the forward workspace.
-i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* ws, int64_t m,
-                                   int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
-                                   const float* w_absmax, int64_t n, const void* bias, void* out,
-                                   int64_t ldout, hipStream_t stream) {
+i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
+                             int32_t cap, const i8mp_linear_workspace& L, char* ws,
+                             hipStream_t stream) {
+    return launched(launch_quantize(forward_quant_args(x, m, k, ldx, threshold, cap, L, ws), stream));
+}
+
+// Arguments of the fused GEMM + dequant epilogue reading the forward workspace.
+GemmArgs forward_gemm_args(const i8mp_linear_workspace& L, const char* ws, int64_t m, int64_t k, int32_t cap,
+                           const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+                           const void* bias, void* out, int64_t ldout) {
     GemmArgs g{};
     g.a = reinterpret_cast<const int8_t*>(ws + L.q_offset);
     g.lda = L.ldq;
@@ -251,7 +255,15 @@ i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* w
     g.cap = cap;
     g.out = static_cast<half_bits*>(out);
     g.ldout = ldout;
-    return launched(launch_gemm_fused(g, stream));
+    return g;
+}
+
+i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* ws, int64_t m,
+                                   int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
+                                   const float* w_absmax, int64_t n, const void* bias, void* out,
+                                   int64_t ldout, hipStream_t stream) {
+    return launched(launch_gemm_fused(
+        forward_gemm_args(L, ws, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout), stream));
 }
 
 }  // namespace
@@ -302,9 +314,12 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
     if (!workspace || workspace_bytes < L.bytes) return I8MP_EWORKSPACE;
     if (i8mp_status s = check_device(); s != I8MP_OK) return s;
     char* ws = static_cast<char*>(workspace);
-    if (i8mp_status s = enqueue_quantize(x, m, k, ldx, threshold, cap, L, ws, stream); s != I8MP_OK)
-        return s;
-    return enqueue_matmul_dequant(L, ws, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout, stream);
+    // one to four rows: quantization inside the GEMV's workgroups, one launch
+    const QuantArgs qa = forward_quant_args(x, m, k, ldx, threshold, cap, L, ws);
+    const GemmArgs g = forward_gemm_args(L, ws, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout);
+    if (decode_forward_fits(qa, g)) return launched(launch_decode_forward(qa, g, stream));
+    if (i8mp_status s = launched(launch_quantize(qa, stream)); s != I8MP_OK) return s;
+    return launched(launch_gemm_fused(g, stream));
 }
 
 }  // extern "C"

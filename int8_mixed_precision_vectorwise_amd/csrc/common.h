@@ -17,6 +17,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint16_t half_bits;
 
+// IEEE binary16 bits <-> fp32 (exact widening; round to nearest even when narrowing)
+__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, (_Float16)f); }
+
 // ---- outlier detection and quantization -------------------------------------
 constexpr int kQuantThreads = 256;
 constexpr int kDetectCols = 256;      // columns per detect workgroup (32 lanes x 8 fp16)
@@ -80,6 +84,11 @@ hipError_t launch_gemm_i32(const GemmArgs& g, hipStream_t stream);
 // m <= 16, 16-byte aligned operands, A covering whole 128-byte K chunks
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream);
 hipError_t launch_gemm_fused(const GemmArgs& g, hipStream_t stream);
+// The whole forward of one to four rows in one launch (quantization inside the
+// GEMV's workgroups); qa / g as for launch_quantize / launch_gemm_fused with the
+// same workspace.  Only where decode_forward_fits.
+bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g);
+hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream);
 
 struct DequantArgs {
     const int32_t* c; int64_t ldc;

@@ -24,6 +24,7 @@
 // Requests past the last chunk go through a zero-length buffer range (they
 // fetch nothing), which keeps every vmcnt wait a constant.
 #include "common.h"
+#include "quant_util.h"
 
 namespace i8mp {
 
@@ -39,8 +40,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
-__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
-__device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, (_Float16)f); }
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
@@ -202,6 +201,17 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 // outlier column adds W[n, j] * x[r, j] (fp16 x, fp32 sum) for the lanes that
 // hold that byte, so no weight byte is read twice.  Sums meet across the 8
 // lanes of a row (shuffles) and the G waves of a row group (LDS).
+//
+// The whole forward in one launch (kQuantL > 0): every workgroup holds all
+// of the one to four rows of x, so it runs the quantizer's steps itself and
+// no grid-wide step separates them.  x sits in registers (kQuantL 8-column
+// chunks per thread); outlier bits are OR-ed into an LDS bitmap; the row
+// absmax over the non-outlier columns comes from wave maxima and an LDS
+// atomicMax; the codes go straight into the LDS activation rows and the
+// outlier values into the stream's list.  The quantization kernels' own
+// helpers compute each step, so the codes are theirs bit for bit.
+// Workgroup 0 also writes the intermediates (codes, absmax, bitmap, index
+// list, count, gathered outlier values) to the workspace.
 namespace {
 
 constexpr int kGvRows = 8;     // weight rows per wave
@@ -212,30 +222,266 @@ __device__ inline int8_t byte_of(const v4i_t& v, int b) {
     return (int8_t)(((uint32_t)v[b >> 2] >> (8 * (b & 3))) & 0xffu);
 }
 
+// LDS of the fused forward's quantizer state, after the stream's arrays
+struct GvQuantLds {
+    uint32_t* bm;        // [words] outlier bitmap
+    int32_t* pre;        // [words] exclusive prefix of the word popcounts
+    uint32_t* rmax;      // [M] row absmax (fp32 bits)
+    int32_t* wave_tot;   // [waves]
+    int32_t* any;        // [1] an outlier bit was set
+};
+
+// The a.m <= M rows of x as 8-column chunks f = tid + T i (row-major over the
+// rows, T threads) into registers: v[i] and rc[i] = row << 16 | chunk.  With k
+// a multiple of 8 and 16-byte aligned rows every chunk is one 16-byte load;
+// all L loads are issued before any is used (a chunk past the end re-reads
+// chunk 0 and is zeroed after), so they are in flight together.
+template <int L, int T>
+__device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L], uint32_t (&rc)[L]) {
+    const int tid = threadIdx.x;
+    const int32_t cpr = (int32_t)(a.k / 8);
+    const int32_t total_chunks = (int32_t)a.m * cpr;
+    int64_t off[L];
+    {
+        int32_t r = tid / cpr, c = tid - r * cpr;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            rc[i] = ((uint32_t)r << 16) | (uint32_t)c;  // chunks < 4096 here
+            off[i] = tid + T * i < total_chunks ? (int64_t)r * a.ldx + (int64_t)c * 8 : 0;
+            c += T;
+            while (c >= cpr) {
+                c -= cpr;
+                ++r;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) v[i] = *reinterpret_cast<const uint4*>(a.x + off[i]);
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+        if (tid + T * i >= total_chunks) v[i] = make_uint4(0, 0, 0, 0);
+}
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// largest |x| of the 8 fp16 values (packed fp16 maxima of the magnitudes: exact)
+__device__ inline float chunk_absmax(const uint4& v) {
+    const uint32_t mag = 0x7fff7fffu;
+    const h2_t a = __builtin_bit_cast(h2_t, v.x & mag), b = __builtin_bit_cast(h2_t, v.y & mag);
+    const h2_t c = __builtin_bit_cast(h2_t, v.z & mag), d = __builtin_bit_cast(h2_t, v.w & mag);
+    const h2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return fmaxf((float)m.x, (float)m.y);
+}
+
+// Codes of a chunk with no outlier column: rne(x * inv) in fp32.  Every |x|
+// of the chunk is at most the row absmax s and inv = fl32(127 / s), so the
+// product rounds into [-127, 127] and the clamp of the code definition never
+// acts; inv = 0 (a zero row) gives 0.
+__device__ inline uint2 codes8_plain(const uint4& v, float inv) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = (int)__builtin_rintf(h2f(half_at(v, e)) * inv);
+        w[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// Quantize the chunks of load_x_chunks into the LDS activation rows xs
+// [M][kr]; the first kGvOutl kept outlier columns and their values go to
+// oidx / oval.  Returns the outlier count (columns kept: the count capped at
+// a.cap).  Every thread calls.
+template <int M, int L, int T>
+__device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)[L], const uint32_t (&rc)[L],
+                                            int64_t kr, int8_t* xs, int32_t* oidx, float* oval,
+                                            const GvQuantLds& q) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool outl = a.threshold > 0.0f;
+    const int32_t cpr = (int32_t)(a.k / 8);  // k % 8 == 0
+    const int32_t total_chunks = (int32_t)a.m * cpr;
+    auto valid = [&](int i) { return tid + T * i < total_chunks; };
+
+    // zero: bitmap, row maxima, flag, the stream's outlier list, activation
+    // rows past a.m and each row's bytes past k
+    for (int64_t w = tid; w < a.words; w += T) q.bm[w] = 0u;
+    if (tid < M) q.rmax[tid] = 0u;
+    if (tid == 0) *q.any = 0;
+    for (int t = tid; t < kGvOutl; t += T) oidx[t] = 0x7fffffff;
+    for (int t = tid; t < M * kGvOutl; t += T) oval[t] = 0.0f;
+    for (int64_t r = 0; r < a.m; ++r)
+        for (int64_t col = a.k + tid; col < kr; col += T) xs[r * kr + col] = 0;
+    for (int64_t u = tid; u < (M - a.m) * kr / 16; u += T)
+        *reinterpret_cast<v4i_t*>(xs + a.m * kr + u * 16) = v4i_t{0, 0, 0, 0};
+
+    // chunk maxima; a chunk reaching the threshold sets its columns' bits
+    float cmax[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) cmax[i] = chunk_absmax(v[i]);
+    __syncthreads();
+    if (outl) {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            if (valid(i) && cmax[i] >= a.threshold) {
+                const uint32_t bits = outlier_bits8(v[i], a.threshold);
+                const int32_t c = (int32_t)(rc[i] & 0xffffu);
+                atomicOr(&q.bm[c >> 2], bits << ((c & 3) * 8));
+                *q.any = 1;
+            }
+    }
+    __syncthreads();
+    const bool any = outl && *q.any != 0;
+    const int32_t total = any ? bitmap_prefix(q.bm, q.pre, a.words, q.wave_tot) : 0;
+    const int32_t kept = total < a.cap ? total : a.cap;
+    auto obyte = [&](int32_t c) -> uint32_t { return any ? (q.bm[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u; };
+
+    // row absmax over the non-outlier columns (float bits order as uints for x >= 0)
+    float tmax[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) tmax[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+        if (valid(i)) {
+            const uint32_t ob = obyte((int32_t)(rc[i] & 0xffffu));
+            const float mx = ob ? chunk_max(v[i], ob) : cmax[i];
+            const int r = (int)(rc[i] >> 16);
+#pragma unroll
+            for (int rr = 0; rr < M; ++rr)
+                if (rr == r) tmax[rr] = fmaxf(tmax[rr], mx);
+        }
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const float t = wave_max(tmax[r]);
+        if (lane == 0 && t > 0.0f) atomicMax(&q.rmax[r], __float_as_uint(t));
+    }
+    __syncthreads();
+    float inv[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const float s = __uint_as_float(q.rmax[r]);
+        inv[r] = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
+    }
+
+    // codes into LDS; chunks with outlier columns take the general path
+    const int32_t lc = kept < kGvOutl ? kept : kGvOutl;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        if (!valid(i)) continue;
+        const int r = (int)(rc[i] >> 16);
+        const int32_t c = (int32_t)(rc[i] & 0xffffu);
+        float ir = inv[0];
+#pragma unroll
+        for (int rr = 1; rr < M; ++rr)
+            if (rr == r) ir = inv[rr];
+        const uint32_t ob = obyte(c);
+        uint2 code;
+        if (ob == 0u) {
+            code = codes8_plain(v[i], ir);
+        } else {
+            const bool zero_row = !(ir > 0.0f);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t b = code_byte(h2f(half_at(v[i], e)), ir, zero_row || ((ob >> e) & 1u));
+                if (e < 4) lo |= b << (8 * e);
+                else hi |= b << (8 * (e - 4));
+            }
+            code = make_uint2(lo, hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((ob >> e) & 1u) {
+                    const int64_t j = (int64_t)c * 8 + e;
+                    const int64_t w = j >> 5;
+                    const int32_t slot = q.pre[w] + __popc(q.bm[w] & ((1u << (j & 31)) - 1u));
+                    if (slot < lc) {
+                        oval[r * kGvOutl + slot] = h2f(half_at(v[i], e));
+                        if (r == 0) oidx[slot] = (int32_t)j;
+                    }
+                }
+        }
+        *reinterpret_cast<uint2*>(xs + r * kr + (int64_t)c * 8) = code;
+    }
+    return total;
+}
+
+// The forward's intermediates into the workspace, spread over the grid (each
+// thread writes at most a few entries): codes (the LDS rows, kpad == kr),
+// absmax, bitmap, count, index list (-1 past the kept columns) and gathered
+// outlier values (read from x, zero past the kept columns).  After the
+// barrier that follows quantize_rows_lds.
+template <int M, int T>
+__device__ inline void publish_spread(const QuantArgs& a, int64_t kr, const int8_t* xs, const GvQuantLds& q,
+                                      bool any, int32_t total, int32_t kept) {
+    const int64_t gt = (int64_t)blockIdx.x * T + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * T;
+    for (int64_t u = gt; u < a.m * kr / 16; u += stride)
+        *reinterpret_cast<v4i_t*>(a.q + u * 16) = *reinterpret_cast<const v4i_t*>(xs + u * 16);
+    if (gt < a.m) a.absmax[gt] = __uint_as_float(q.rmax[gt]);
+    if (gt == 0 && a.count_out) *a.count_out = total;
+    for (int64_t w = gt; w < a.words; w += stride) {
+        const uint32_t bits0 = any ? q.bm[w] : 0u;
+        if (a.bitmap_out) a.bitmap_out[w] = bits0;
+        uint32_t bits = bits0;
+        int32_t slot = bits ? q.pre[w] : 0;
+        while (bits) {
+            const int64_t j = w * 32 + (__ffs(bits) - 1);
+            bits &= bits - 1u;
+            if (slot < a.cap) {
+                if (a.idx_out) a.idx_out[slot] = (int32_t)j;
+                if (a.x_out)
+                    for (int64_t r = 0; r < a.m; ++r) a.x_out[r * a.ldo + slot] = a.x[r * a.ldx + j];
+            }
+            ++slot;
+        }
+    }
+    if (a.idx_out)
+        for (int64_t s = kept + gt; s < a.idx_len; s += stride) a.idx_out[s] = -1;
+    if (a.x_out && a.xo_cols > kept) {
+        const int64_t pad = a.xo_cols - kept;
+        for (int64_t f = gt; f < a.m * pad; f += stride) a.x_out[(f / pad) * a.ldo + kept + f % pad] = 0;
+    }
+}
+
 }  // namespace
 
-template <int G, int M, bool kFused>
-__global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
+template <int G, int M, bool kFused, int kQuantL = 0, int W = 4>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa) {
+    constexpr bool kQuant = kQuantL > 0;
+    static_assert(!kQuant || kFused, "the one-launch forward has the fused epilogue");
     extern __shared__ __attribute__((aligned(16))) int8_t gsm[];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wid % G;
-    const int64_t n0 = ((int64_t)blockIdx.x * (4 / G) + wid / G) * kGvRows;
+    const int64_t n0 = ((int64_t)blockIdx.x * (W / G) + wid / G) * kGvRows;
     const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
     const int64_t nchunks = kr / kChunk;
     const int64_t mine = nchunks > part ? (nchunks - part + G - 1) / G : 0;
 
-    // LDS: activations [M][kr] | int32 partials [4][M][8] | fp32 partials [4][M][8] |
-    //      outlier columns [kGvOutl] | outlier values [M][kGvOutl]
+    // LDS: activations [M][kr] | int32 partials [W][M][8] | fp32 partials [W][M][8] |
+    //      outlier columns [kGvOutl] | outlier values [M][kGvOutl] |
+    //      (one-launch forward) bitmap [words] | prefix [words] | row absmax [M] | wave totals [W] |
+    //      outlier flag [1]
     int8_t* xs = gsm;
     int32_t* red = reinterpret_cast<int32_t*>(gsm + M * kr);
-    float* pred = reinterpret_cast<float*>(red + 4 * M * kGvRows);
-    int32_t* oidx = reinterpret_cast<int32_t*>(pred + 4 * M * kGvRows);
+    float* pred = reinterpret_cast<float*>(red + W * M * kGvRows);
+    int32_t* oidx = reinterpret_cast<int32_t*>(pred + W * M * kGvRows);
     float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
+    GvQuantLds ql;
+    ql.bm = reinterpret_cast<uint32_t*>(oval + M * kGvOutl);
+    ql.pre = reinterpret_cast<int32_t*>(ql.bm + qa.words);
+    ql.rmax = reinterpret_cast<uint32_t*>(ql.pre + qa.words);
+    ql.wave_tot = reinterpret_cast<int32_t*>(ql.rmax + M);
+    ql.any = ql.wave_tot + W;
 
-    // 1. the first batch of weight loads goes out first
+    // 1. the first batch of weight loads goes out first (after x in the
+    // one-launch forward, so that x's wait does not include them: loads
+    // complete in order)
+    constexpr int kXL = kQuant ? kQuantL : 1;
+    uint4 xv[kXL];
+    uint32_t xrc[kXL];
+    if constexpr (kQuant) load_x_chunks<kXL, 64 * W>(qa, xv, xrc);
     const __amdgpu_buffer_rsrc_t rw =
         rsrc(g.b + n0 * g.ldb, n0 < g.n ? (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3) : 0);
+    const __amdgpu_buffer_rsrc_t r_none = rsrc(g.b, 0);
     const int w_off = (int)((lane >> 3) * g.ldb + (lane & 7) * 16);
     v4i_t w[kGvBatch];
     auto load_batch = [&](int64_t j0) {
@@ -244,34 +490,41 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
             const int64_t j = j0 + u;
             const int kb = (int)((part + j * G) * kChunk);
             // the K offset goes in the range-checked VGPR offset: bytes past
-            // the end of the weight read as 0
-            w[u] = j < mine ? __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + kb, 0, 0))
-                            : v4i_t{0, 0, 0, 0};
+            // the end of the weight read as 0.  Chunks past this wave's read
+            // through a zero-length range (nothing fetched, zeros returned):
+            // no branch, so every later wait counts all of the batch's loads
+            w[u] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(j < mine ? rw : r_none,
+                                                                                  w_off + kb, 0, 0));
         }
     };
     load_batch(0);
 
     // 2. activations (rows >= m as zeros), and the outlier columns / values
-    {
+    int cnt = 0;
+    if constexpr (kQuant) {
+        const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kr, xs, oidx, oval, ql);
+        cnt = total < qa.cap ? total : qa.cap;
+        __syncthreads();
+        publish_spread<M, 64 * W>(qa, kr, xs, ql, total > 0, total, cnt);
+    } else {
         const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
         const int64_t per_row = kr / 16;
-        for (int64_t f = threadIdx.x; f < M * per_row; f += 256) {
+        for (int64_t f = threadIdx.x; f < M * per_row; f += 64 * W) {
             const int64_t r = f / per_row, c = f - r * per_row;
             v4i_t v = {0, 0, 0, 0};
             if (r < g.m)
                 v = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(r * g.lda + c * 16), 0, 0));
             *reinterpret_cast<v4i_t*>(xs + r * kr + c * 16) = v;
         }
-    }
-    int cnt = 0;
-    if (kFused && g.x_out) {
-        cnt = *g.count;
-        cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
-        const int lc = cnt < kGvOutl ? cnt : kGvOutl;
-        for (int t = threadIdx.x; t < kGvOutl; t += 256) oidx[t] = t < lc ? g.idx[t] : 0x7fffffff;
-        for (int t = threadIdx.x; t < M * kGvOutl; t += 256) {
-            const int r = t / kGvOutl, s2 = t % kGvOutl;
-            oval[t] = (s2 < lc && r < g.m) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
+        if (kFused && g.x_out) {
+            cnt = *g.count;
+            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+            const int lc = cnt < kGvOutl ? cnt : kGvOutl;
+            for (int t = threadIdx.x; t < kGvOutl; t += 64 * W) oidx[t] = t < lc ? g.idx[t] : 0x7fffffff;
+            for (int t = threadIdx.x; t < M * kGvOutl; t += 64 * W) {
+                const int r = t / kGvOutl, s2 = t % kGvOutl;
+                oval[t] = (s2 < lc && r < g.m) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
+            }
         }
     }
     __syncthreads();
@@ -349,12 +602,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
         for (int r = 0; r < M; ++r)
             if (r < g.m) g.c[r * g.ldc + n] = acc[r];
     } else {
-        // outlier columns past the streamed ones: gathered
-        for (int s2 = lc; s2 < cnt; ++s2) {
-            const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
+        // outlier columns past the streamed ones: gathered, in slot order
+        if constexpr (kQuant) {
+            // slots from the LDS bitmap and its prefix, values from x
+            for (int64_t wd = 0; wd < qa.words && cnt > lc; ++wd) {
+                uint32_t bits = ql.bm[wd];
+                int32_t slot = ql.pre[wd];
+                if (slot >= cnt) break;
+                while (bits) {
+                    const int64_t j = wd * 32 + (__ffs(bits) - 1);
+                    bits &= bits - 1u;
+                    if (slot >= lc && slot < cnt) {
+                        const float wv = (float)g.b[n * g.ldb + j];
 #pragma unroll
-            for (int r = 0; r < M; ++r)
-                if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
+                        for (int r = 0; r < M; ++r)
+                            if (r < g.m) pacc[r] += wv * h2f(qa.x[r * qa.ldx + j]);
+                    }
+                    ++slot;
+                }
+            }
+        } else {
+            for (int s2 = lc; s2 < cnt; ++s2) {
+                const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
+#pragma unroll
+                for (int r = 0; r < M; ++r)
+                    if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
+            }
         }
         const float r127 = 1.0f / 127.0f;
         const float sw = g.col_absmax[n] * r127;
@@ -362,11 +635,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < M; ++r)
             if (r < g.m) {
-                const float sx = g.row_absmax[r] * r127;
+                const float sx = (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127;
                 g.out[r * g.ldout + n] = f2h(sw * ((float)acc[r] * sx + pacc[r]) + bj);
             }
     }
 }
+
+namespace {
 
 // m <= 4 with the activations in at most 32 KB of LDS
 bool gemv_fits(const GemmArgs& g) {
@@ -376,29 +651,59 @@ bool gemv_fits(const GemmArgs& g) {
     return g.m >= 1 && g.m <= 4 && (g.m > 2 ? 4 : g.m) * kr <= 32 * 1024;
 }
 
-template <int M, bool kFused>
-hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t stream) {
+template <int M, bool kFused, int kQuantL, int W>
+hipError_t launch_gemv_m(const GemmArgs& g, const QuantArgs& qa, hipStream_t stream) {
     const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
     const int64_t nchunks = kr / kChunk;
     const int64_t groups = (g.n + kGvRows - 1) / kGvRows;
     // K splits: about 2500 waves or more, each with at least 8 chunks
     int gs = 1;
     while (gs < 4 && groups * gs < 2560 && nchunks / (2 * gs) >= kGvBatch) gs *= 2;
-    const size_t lds = (size_t)M * kr + (size_t)4 * M * kGvRows * 8 + (size_t)kGvOutl * 4 + (size_t)M * kGvOutl * 4;
-    const dim3 grid((unsigned)((groups * gs + 3) / 4));
+    size_t lds = (size_t)M * kr + (size_t)W * M * kGvRows * 8 + (size_t)kGvOutl * 4 + (size_t)M * kGvOutl * 4;
+    if (kQuantL > 0) lds += ((size_t)2 * qa.words + M + W + 1) * 4;
+    const dim3 grid((unsigned)((groups * gs + W - 1) / W)), block(64 * W);
     switch (gs) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<1, M, kFused>), grid, dim3(256), lds, stream, g); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<2, M, kFused>), grid, dim3(256), lds, stream, g); break;
-        default: hipLaunchKernelGGL((gemv_kernel<4, M, kFused>), grid, dim3(256), lds, stream, g); break;
+        case 1: hipLaunchKernelGGL((gemv_kernel<1, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<2, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
+        default: hipLaunchKernelGGL((gemv_kernel<4, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
     }
     return hipGetLastError();
 }
 
 template <bool kFused>
 hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
-    if (g.m == 1) return launch_gemv_m<1, kFused>(g, stream);
-    if (g.m == 2) return launch_gemv_m<2, kFused>(g, stream);
-    return launch_gemv_m<4, kFused>(g, stream);
+    const QuantArgs none{};
+    if (g.m == 1) return launch_gemv_m<1, kFused, 0, 4>(g, none, stream);
+    if (g.m == 2) return launch_gemv_m<2, kFused, 0, 4>(g, none, stream);
+    return launch_gemv_m<4, kFused, 0, 4>(g, none, stream);
+}
+
+// 8-wave workgroups: x is quantized by 512 threads (at most 8 chunks each) in
+// half as many workgroups as 4-wave ones would need
+template <int M>
+hipError_t launch_forward_m(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
+    const int64_t per_thread = (qa.m * ((qa.k + 7) / 8) + 511) / 512;
+    if (per_thread <= 4) return launch_gemv_m<M, true, 4, 8>(g, qa, stream);
+    return launch_gemv_m<M, true, 8, 8>(g, qa, stream);
+}
+
+}  // namespace
+
+bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g) {
+    const bool w_aligned = ((g.ldb & 15) == 0) && ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
+    // whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
+    const bool x_vec = ((qa.k & 7) == 0) && ((qa.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(qa.x) & 15) == 0);
+    // gemv_fits bounds the chunks: m * k / 8 <= 4096, 8 per thread of 512
+    // the codes are copied from the LDS rows: same pitch, 16-byte aligned
+    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
+    const bool q_rows = qa.q && qa.ldq == kr && qa.kpad == kr && ((reinterpret_cast<uintptr_t>(qa.q) & 15) == 0);
+    return qa.m == g.m && qa.k == g.k && gemv_fits(g) && w_aligned && x_vec && q_rows && qa.absmax;
+}
+
+hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
+    if (g.m == 1) return launch_forward_m<1>(qa, g, stream);
+    if (g.m == 2) return launch_forward_m<2>(qa, g, stream);
+    return launch_forward_m<4>(qa, g, stream);
 }
 
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {

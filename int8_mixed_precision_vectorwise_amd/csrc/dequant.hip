@@ -14,8 +14,6 @@
 namespace i8mp {
 
 namespace {
-__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
-__device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, (_Float16)f); }
 constexpr int kRegSlots = 32;
 }  // namespace
 

@@ -34,8 +34,6 @@ constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
-__device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, (_Float16)f); }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;

@@ -33,163 +33,10 @@
 // even, clamp to [-127, 127]; 0 in outlier columns and in rows whose absmax
 // is 0.
 #include "common.h"
+#include "quant_util.h"
 
 namespace i8mp {
 
-namespace {
-
-__device__ inline float h2f(half_bits h) { return (float)__builtin_bit_cast(_Float16, h); }
-
-// bit e of the result: |x_e| >= tau for the 8 fp16 values of v
-__device__ inline uint32_t outlier_bits8(const uint4& v, float tau) {
-    uint32_t m = 0;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = h2f((half_bits)(w[i] & 0x7fffu));
-        const float hi = h2f((half_bits)((w[i] >> 16) & 0x7fffu));
-        m |= (lo >= tau ? 1u : 0u) << (2 * i);
-        m |= (hi >= tau ? 1u : 0u) << (2 * i + 1);
-    }
-    return m;
-}
-
-// 8 fp16 values starting at column col of a row; columns >= k read as 0.
-template <bool kVec>
-__device__ inline uint4 load8(const half_bits* __restrict__ row, int64_t col, int64_t k) {
-    if (kVec && col + 8 <= k) return *reinterpret_cast<const uint4*>(row + col);
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        if (col + e < k) w[e >> 1] |= (uint32_t)row[col + e] << (16 * (e & 1));
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-__device__ inline half_bits half_at(const uint4& v, int e) {
-    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-    return (half_bits)((w >> (16 * (e & 1))) & 0xffffu);
-}
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ inline uint32_t code_byte(float x, float inv, bool zero) {
-    float q = __builtin_rintf(x * inv);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    const int iq = zero ? 0 : (int)q;
-    return (uint32_t)iq & 0xffu;
-}
-
-// largest |x| of the chunk over the columns whose outlier bit is clear
-__device__ inline float chunk_max(const uint4& v, uint32_t obits) {
-    float t = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float f = fabsf(h2f(half_at(v, e)));
-        t = ((obits >> e) & 1u) ? t : fmaxf(t, f);
-    }
-    return t;
-}
-
-// Exclusive prefix of the per-word popcounts of bm into pre (slot of each
-// outlier column in the index list); returns the total (all threads call).
-__device__ inline int32_t bitmap_prefix(const uint32_t* bm, int32_t* pre, int64_t words, int32_t* wave_tot) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int64_t per = (words + blockDim.x - 1) / blockDim.x;
-    const int64_t w0 = (int64_t)tid * per;
-    int64_t w1 = w0 + per;
-    if (w1 > words) w1 = words;
-    int32_t s = 0;
-    for (int64_t w = w0; w < w1; ++w) s += __popc(bm[w]);
-    int32_t incl = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int32_t off = 0, total = 0;
-    for (int i = 0; i < nwaves; ++i) {
-        if (i < wave) off += wave_tot[i];
-        total += wave_tot[i];
-    }
-    int32_t run = off + incl - s;
-    for (int64_t w = w0; w < w1; ++w) {
-        pre[w] = run;
-        run += __popc(bm[w]);
-    }
-    __syncthreads();
-    return total;
-}
-
-// Workgroup 0 publishes the bitmap, the count and the ascending index list.
-__device__ inline void publish(const QuantArgs& a, const uint32_t* bm, const int32_t* pre, int32_t total,
-                               bool outl) {
-    const int tid = threadIdx.x;
-    const int nt = blockDim.x;
-    const int32_t kept = total < a.cap ? total : a.cap;
-    if (a.bitmap_out)
-        for (int64_t w = tid; w < a.words; w += nt) a.bitmap_out[w] = outl ? bm[w] : 0u;
-    if (a.count_out && tid == 0) *a.count_out = total;
-    if (a.idx_out) {
-        for (int32_t s = tid; s < a.idx_len; s += nt)
-            if (s >= kept) a.idx_out[s] = -1;
-        if (outl) {
-            for (int64_t w = tid; w < a.words; w += nt) {
-                uint32_t v = bm[w];
-                int32_t slot = pre[w];
-                while (v) {
-                    const int b = __ffs(v) - 1;
-                    if (slot < a.cap) a.idx_out[slot] = (int32_t)(w * 32 + b);
-                    ++slot;
-                    v &= v - 1u;
-                }
-            }
-        }
-    }
-}
-
-// Codes of the 8 columns starting at col of row r, and the row's outlier
-// values among them gathered into x_out at their slots.
-__device__ inline void emit8(const QuantArgs& a, const uint4& v, uint32_t obits, int64_t r, int64_t col,
-                             float inv, bool zero_row, bool vec_q, const uint32_t* bm, const int32_t* pre) {
-    if (a.q) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t b = code_byte(h2f(half_at(v, e)), inv, zero_row || ((obits >> e) & 1u));
-            if (e < 4) lo |= b << (8 * e);
-            else hi |= b << (8 * (e - 4));
-        }
-        int8_t* qr = a.q + r * a.ldq + col;
-        if (vec_q && col + 8 <= a.k) {
-            *reinterpret_cast<uint2*>(qr) = make_uint2(lo, hi);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (col + e < a.k) qr[e] = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
-        }
-    }
-    if (a.x_out && obits) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if ((obits >> e) & 1u) {
-                const int64_t j = col + e;
-                const int64_t w = j >> 5;
-                const uint32_t below = bm[w] & ((1u << (j & 31)) - 1u);
-                const int32_t slot = pre[w] + __popc(below);
-                if (slot < a.cap) a.x_out[r * a.ldo + slot] = half_at(v, e);
-            }
-        }
-    }
-}
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // detect: per (RB rows, 256 columns) workgroup, the OR of the rows' outlier

@@ -201,6 +201,8 @@ FWD_CASES = [
     (4, 8192, 600, 8, 1.0, False, TAU, 256),      # the largest K the GEMV takes at m = 4
     (1, 13824, 1024, 70, 0.5, True, TAU, 128),    # more outlier columns than the stream handles
     (2, 640, 2048, 0, 1.0, False, TAU, 8),        # no outliers
+    (2, 512, 96, 0, 1.0, True, 0.0, 8),           # threshold off
+    (1, 96, 70, 96, 1.0, True, TAU, 96),          # every column an outlier, past the stream's 64
 ]
 
 
@@ -269,6 +271,58 @@ def test_linear_forward_capacity_overflow_reports_count():
     assert_equal(wsp.idx(), ref.cols[:4].astype(np.int32), "first cap indices")
 
 
+def _workspace_state(wsp):
+    return [wsp.codes().clone(), wsp.absmax().clone(), wsp.bitmap().clone(), wsp.idx().clone(),
+            wsp.count().clone(), wsp.x_out().clone()]
+
+
+@pytest.mark.parametrize("m,k,n,o,cap", [(1, 5120, 384, 8, 256), (2, 4096, 264, 5, 32), (3, 2000, 130, 9, 4),
+                                         (4, 8192, 200, 70, 128), (4, 5120, 256, 0, 8), (1, 64, 16, 40, 16)])
+def test_decode_forward_matches_two_launches(m, k, n, o, cap):
+    """One to four rows: the one-launch forward (quantization inside the GEMV)
+    leaves the workspace and the output of quantize + matmul_dequant, bit for bit."""
+    L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01, seed=(82, m, k), outlier_row_frac=0.5)
+    wq, ws = oracle.quantize_weight(L.w)
+    x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
+    wa = i8.LinearWorkspace.create(m, n, k, cap, "cuda")
+    wb = i8.LinearWorkspace.create(m, n, k, cap, "cuda")
+    say(f"one-launch forward m={m} k={k} n={n} o={o} cap={cap}")
+    one = i8.linear(x, w, s, b, TAU, cap, wa)
+    torch.cuda.synchronize()
+    say(f"two-launch forward m={m} k={k} n={n} o={o} cap={cap}")
+    i8.linear_quantize(x, wb, TAU)
+    two = i8.linear_matmul_dequant(wb, w, s, b)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    for name, a, c in zip(("codes", "absmax", "bitmap", "idx", "count", "x_out"),
+                          _workspace_state(wa), _workspace_state(wb)):
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8)), name
+    assert int(host(wa.count())[0]) == o
+    assert wa.outlier_overflow() == (o > cap)
+    if o <= cap:
+        ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+        assert_fp16_close(one, ref.out)
+
+
+@pytest.mark.parametrize("pad", [8, 1], ids=["ldx_aligned", "ldx_odd"])
+def test_decode_forward_strided_x(pad):
+    """x with a row stride: an aligned one takes the one-launch forward, an odd
+    one the two-launch path; both give the oracle's result."""
+    m, k, n = 3, 1536, 256
+    L = make_inputs(m, k, n, n_outlier=4, bias_std=0.01, seed=(83, pad, 0))
+    wq, ws = oracle.quantize_weight(L.w)
+    big = torch.zeros((m, k + pad), dtype=torch.float16, device="cuda")
+    big[:, :k] = dev(L.x)
+    x = big[:, :k]
+    say(f"strided x m={m} k={k} ldx={k + pad}")
+    wsp = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
+    out = i8.linear(x, dev(wq), dev(ws), dev(L.bias), TAU, 32, wsp)
+    torch.cuda.synchronize()
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_equal(wsp.codes(), ref.quant.q, "codes")
+    assert_fp16_close(out, ref.out)
+
+
 def test_empty_calls_are_noops():
     say("empty calls")
     x = torch.empty((0, 64), dtype=torch.float16, device="cuda")
@@ -309,13 +363,14 @@ def test_non_default_stream():
     assert_fp16_close(out, ref.out)
 
 
-def test_graph_capture_replays_match_eager():
-    L = make_inputs(128, 1024, 512, n_outlier=5, bias_std=0.01, seed=(81, 0, 0))
+@pytest.mark.parametrize("m", [128, 2])
+def test_graph_capture_replays_match_eager(m):
+    L = make_inputs(m, 1024, 512, n_outlier=5, bias_std=0.01, seed=(81, m, 0))
     wq, ws = oracle.quantize_weight(L.w)
     x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
-    wsp = i8.LinearWorkspace.create(128, 512, 1024, 32, "cuda")
-    out = torch.empty((128, 512), dtype=torch.float16, device="cuda")
-    say("graph capture")
+    wsp = i8.LinearWorkspace.create(m, 512, 1024, 32, "cuda")
+    out = torch.empty((m, 512), dtype=torch.float16, device="cuda")
+    say(f"graph capture m={m}")
     eager = i8.linear(x, w, s, b, TAU, 32, wsp).clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
