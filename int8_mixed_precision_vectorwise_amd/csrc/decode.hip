@@ -47,9 +47,12 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// 16 bytes per lane global -> LDS; the weight is streamed once per call, so
+// its loads carry the nt (non-temporal) cache policy
+constexpr int kWeightPolicy = 2;
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                             soffset, 0, 0);
+                                             soffset, 0, kWeightPolicy);
 }
 
 // 128-byte LDS rows; lanes 0-15 of a fragment read rows 0-15 at one 16-byte
@@ -187,39 +190,78 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// m <= 4 (and m x K fits 32 KB): a dot-product GEMV on the vector ALUs.
-// With one to four activation rows the matrix cores would idle over zero
-// padding, and the MFMA kernel above spends as many load instructions on the
-// activations as on the weights.  Here the int8 activations are copied to LDS
-// once per workgroup, and the weight streams straight into registers: each
-// wave owns 8 weight rows and a share of the 128-byte K chunks (chunks p,
-// p + G, ...), one 1 KB load per chunk (lane i: row i / 8, bytes 16 (i % 8)
-// of the chunk), kGvBatch loads in flight.  v_dot4_i32_i8 against the LDS
-// activation bytes (lanes with equal i % 8 read the same 16 bytes: a
-// broadcast) accumulates exactly in int32.  The outlier sub-matmul is taken
-// from the streamed weight bytes as they pass: a chunk that contains an
-// outlier column adds W[n, j] * x[r, j] (fp16 x, fp32 sum) for the lanes that
-// hold that byte, so no weight byte is read twice.  Sums meet across the 8
-// lanes of a row (shuffles) and the G waves of a row group (LDS).
+// m <= 4: a dot-product GEMV on the vector ALUs.  With one to four activation
+// rows the matrix cores would idle over zero padding.  The int8 activations
+// sit in LDS (rows of kx = K rounded up to 1 KB, zeros past K), and each wave
+// reads R weight rows front to back, one row after the other: a load is one
+// row's next 1 KB of K (lane i: bytes 16 i .. 16 i + 15).  Wave v of the nw
+// waves takes rows v, v + nw, ..., so the grid reads one band of neighbouring
+// rows at a time (plain reads of 70 MB measured fastest as one such sweep on
+// MI355X, with about 2048 waves).  Batches of kGvBatch loads are
+// double-buffered: the next batch is in flight while this one is used (the
+// first goes out before the activations are staged).  The weight loads
+// carry the nt cache policy (each byte is read once).  A row's bytes past K
+// read through the row's own buffer range and come back as zeros, with no
+// memory traffic.  v_dot4_i32_i8 against the LDS
+// activation bytes accumulates exactly in int32; the outlier sub-matmul is
+// taken from the streamed weight bytes as they pass (a lane holding byte j of
+// an outlier column adds W[n, j] * x[r, j] in fp32), so no weight byte is read
+// twice.  At the end of a row the 64 lanes' sums are added up (DPP) and lane
+// 0 runs the fused epilogue.
 //
 // The whole forward in one launch (kQuantL > 0): every workgroup holds all
 // of the one to four rows of x, so it runs the quantizer's steps itself and
 // no grid-wide step separates them.  x sits in registers (kQuantL 8-column
-// chunks per thread); outlier bits are OR-ed into an LDS bitmap; the row
+// chunks per thread); chunk maxima come from packed fp16 maxima; a chunk
+// reaching the threshold sets its outlier bits in an LDS bitmap; the row
 // absmax over the non-outlier columns comes from wave maxima and an LDS
 // atomicMax; the codes go straight into the LDS activation rows and the
-// outlier values into the stream's list.  The quantization kernels' own
-// helpers compute each step, so the codes are theirs bit for bit.
-// Workgroup 0 also writes the intermediates (codes, absmax, bitmap, index
-// list, count, gathered outlier values) to the workspace.
+// outlier values into the stream's list.  The codes are the quantization
+// kernels' own, bit for bit (same helpers, same IEEE operations).  The
+// intermediates (codes, absmax, bitmap, index list, count, gathered outlier
+// values) are written to the workspace spread over the grid.
 namespace {
 
-constexpr int kGvRows = 8;     // weight rows per wave
-constexpr int kGvBatch = 8;    // weight loads in flight per wave
-constexpr int kGvOutl = 64;    // outlier columns handled in the stream (more: gathered at the end)
+constexpr int kGvChunk = 1024;   // K bytes per wave load
+constexpr int kGvBatch = 8;      // loads per batch (two batches in flight)
+constexpr int kGvOutl = 64;      // outlier columns handled in the stream (more: gathered per row)
+constexpr int kGvWaves = 2048;   // waves the grid aims at
 
 __device__ inline int8_t byte_of(const v4i_t& v, int b) {
     return (int8_t)(((uint32_t)v[b >> 2] >> (8 * (b & 3))) & 0xffu);
+}
+
+// Sums over the 64 lanes, returned wave-uniform: DPP adds within each row of
+// 16 lanes (quad swaps, half-row and row mirrors), then the four row totals
+// read out with v_readlane.  No LDS traffic, unlike a shuffle ladder.
+template <int kCtrl>
+__device__ inline int32_t dpp_i32(int32_t v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ inline int32_t wave_sum_i32(int32_t v) {
+    v += dpp_i32<kDppQuadSwap1>(v);
+    v += dpp_i32<kDppQuadSwap2>(v);
+    v += dpp_i32<kDppHalfMirror>(v);
+    v += dpp_i32<kDppRowMirror>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ inline float wave_sum_f32(float v) {
+    v += __int_as_float(dpp_i32<kDppQuadSwap1>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppQuadSwap2>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppRowMirror>(__float_as_int(v)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // LDS of the fused forward's quantizer state, after the stream's arrays
@@ -288,7 +330,7 @@ __device__ inline uint2 codes8_plain(const uint4& v, float inv) {
 }
 
 // Quantize the chunks of load_x_chunks into the LDS activation rows xs
-// [M][kr]; the first kGvOutl kept outlier columns and their values go to
+// [M][kr] (kr >= k, zeros past k); the first kGvOutl kept outlier columns and their values go to
 // oidx / oval.  Returns the outlier count (columns kept: the count capped at
 // a.cap).  Every thread calls.
 template <int M, int L, int T>
@@ -404,17 +446,20 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
 }
 
 // The forward's intermediates into the workspace, spread over the grid (each
-// thread writes at most a few entries): codes (the LDS rows, kpad == kr),
+// thread writes at most a few entries): codes (the LDS rows, kpad == ldq),
 // absmax, bitmap, count, index list (-1 past the kept columns) and gathered
 // outlier values (read from x, zero past the kept columns).  After the
 // barrier that follows quantize_rows_lds.
 template <int M, int T>
-__device__ inline void publish_spread(const QuantArgs& a, int64_t kr, const int8_t* xs, const GvQuantLds& q,
+__device__ inline void publish_spread(const QuantArgs& a, int64_t kx, const int8_t* xs, const GvQuantLds& q,
                                       bool any, int32_t total, int32_t kept) {
     const int64_t gt = (int64_t)blockIdx.x * T + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * T;
-    for (int64_t u = gt; u < a.m * kr / 16; u += stride)
-        *reinterpret_cast<v4i_t*>(a.q + u * 16) = *reinterpret_cast<const v4i_t*>(xs + u * 16);
+    const int64_t units = a.ldq / 16;  // 16-byte units per code row (ldq <= kx, zeros past k)
+    for (int64_t u = gt; u < a.m * units; u += stride) {
+        const int64_t r = u / units, c = u - r * units;
+        *reinterpret_cast<v4i_t*>(a.q + r * a.ldq + c * 16) = *reinterpret_cast<const v4i_t*>(xs + r * kx + c * 16);
+    }
     if (gt < a.m) a.absmax[gt] = __uint_as_float(q.rmax[gt]);
     if (gt == 0 && a.count_out) *a.count_out = total;
     for (int64_t w = gt; w < a.words; w += stride) {
@@ -443,27 +488,30 @@ __device__ inline void publish_spread(const QuantArgs& a, int64_t kr, const int8
 
 }  // namespace
 
-template <int G, int M, bool kFused, int kQuantL = 0, int W = 4>
-__global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa) {
+// rows_per_wave weight rows per wave, W waves per workgroup.
+template <int M, bool kFused, int kQuantL, int W>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, int rows_per_wave) {
     constexpr bool kQuant = kQuantL > 0;
     static_assert(!kQuant || kFused, "the one-launch forward has the fused epilogue");
     extern __shared__ __attribute__((aligned(16))) int8_t gsm[];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = wid % G;
-    const int64_t n0 = ((int64_t)blockIdx.x * (W / G) + wid / G) * kGvRows;
-    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-    const int64_t nchunks = kr / kChunk;
-    const int64_t mine = nchunks > part ? (nchunks - part + G - 1) / G : 0;
+    const int64_t kx = (g.k + kGvChunk - 1) / kGvChunk * kGvChunk;
+    const int nck = (int)(kx / kGvChunk);                         // 1 KB chunks per row
+    const int bpr = (nck + kGvBatch - 1) / kGvBatch;              // batches per row
+    const int R = rows_per_wave;
+    // wave v of nw takes rows v, v + nw, v + 2 nw, ...: at any time the grid
+    // reads one band of neighbouring rows
+    const int64_t nw = (g.n + R - 1) / R;
+    const int64_t wv = (int64_t)blockIdx.x * W + wid;
+    auto row_of = [&](int rr) -> int64_t { return wv + (int64_t)rr * nw; };
+    const int nb = R * bpr;                                       // batches of this wave
 
-    // LDS: activations [M][kr] | int32 partials [W][M][8] | fp32 partials [W][M][8] |
-    //      outlier columns [kGvOutl] | outlier values [M][kGvOutl] |
-    //      (one-launch forward) bitmap [words] | prefix [words] | row absmax [M] | wave totals [W] |
-    //      outlier flag [1]
+    // LDS: activations [M][kx] | outlier columns [kGvOutl] | outlier values [M][kGvOutl] |
+    //      (one-launch forward) bitmap [words] | prefix [words] | row absmax [M] |
+    //      wave totals [W] | outlier flag [1]
     int8_t* xs = gsm;
-    int32_t* red = reinterpret_cast<int32_t*>(gsm + M * kr);
-    float* pred = reinterpret_cast<float*>(red + W * M * kGvRows);
-    int32_t* oidx = reinterpret_cast<int32_t*>(pred + W * M * kGvRows);
+    int32_t* oidx = reinterpret_cast<int32_t*>(gsm + M * kx);
     float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
     GvQuantLds ql;
     ql.bm = reinterpret_cast<uint32_t*>(oval + M * kGvOutl);
@@ -472,49 +520,49 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa) 
     ql.wave_tot = reinterpret_cast<int32_t*>(ql.rmax + M);
     ql.any = ql.wave_tot + W;
 
-    // 1. the first batch of weight loads goes out first (after x in the
-    // one-launch forward, so that x's wait does not include them: loads
-    // complete in order)
+    // weight loads: batch b covers row b / bpr, chunks from (b % bpr) * kGvBatch.
+    // Past a row's K, past the wave's rows or past n: zero-length / range-checked
+    // reads (nothing fetched, zeros returned); no branches, so every wait
+    // counts all loads in flight.
+    const int64_t row_bytes = (g.k + 3) & ~(int64_t)3;  // the range check is per dword
+    const __amdgpu_buffer_rsrc_t r_none = rsrc(g.b, 0);
+    auto issue = [&](int b, v4i_t (&wb)[kGvBatch]) {
+        const int rr = b / bpr;
+        const int c0 = (b - rr * bpr) * kGvBatch;
+        const int64_t n = row_of(rr);
+        const __amdgpu_buffer_rsrc_t rw = (b < nb && n < g.n) ? rsrc(g.b + n * g.ldb, row_bytes) : r_none;
+#pragma unroll
+        for (int u = 0; u < kGvBatch; ++u)
+            wb[u] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rw, (c0 + u) * kGvChunk + lane * 16, 0, kWeightPolicy));
+    };
+    v4i_t w[2][kGvBatch];
+    // x first in the one-launch forward, so that its wait does not include
+    // the weight loads (loads complete in order)
     constexpr int kXL = kQuant ? kQuantL : 1;
     uint4 xv[kXL];
     uint32_t xrc[kXL];
     if constexpr (kQuant) load_x_chunks<kXL, 64 * W>(qa, xv, xrc);
-    const __amdgpu_buffer_rsrc_t rw =
-        rsrc(g.b + n0 * g.ldb, n0 < g.n ? (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3) : 0);
-    const __amdgpu_buffer_rsrc_t r_none = rsrc(g.b, 0);
-    const int w_off = (int)((lane >> 3) * g.ldb + (lane & 7) * 16);
-    v4i_t w[kGvBatch];
-    auto load_batch = [&](int64_t j0) {
-#pragma unroll
-        for (int u = 0; u < kGvBatch; ++u) {
-            const int64_t j = j0 + u;
-            const int kb = (int)((part + j * G) * kChunk);
-            // the K offset goes in the range-checked VGPR offset: bytes past
-            // the end of the weight read as 0.  Chunks past this wave's read
-            // through a zero-length range (nothing fetched, zeros returned):
-            // no branch, so every later wait counts all of the batch's loads
-            w[u] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(j < mine ? rw : r_none,
-                                                                                  w_off + kb, 0, 0));
-        }
-    };
-    load_batch(0);
+    issue(0, w[0]);
 
-    // 2. activations (rows >= m as zeros), and the outlier columns / values
+    // activations (rows >= m and bytes past K as zeros), outlier columns / values
     int cnt = 0;
     if constexpr (kQuant) {
-        const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kr, xs, oidx, oval, ql);
+        const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kx, xs, oidx, oval, ql);
         cnt = total < qa.cap ? total : qa.cap;
         __syncthreads();
-        publish_spread<M, 64 * W>(qa, kr, xs, ql, total > 0, total, cnt);
+        publish_spread<M, 64 * W>(qa, kx, xs, ql, total > 0, total, cnt);
     } else {
+        // the codes' rows hold zeros from k to a multiple of 128 (lda >= that)
+        const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
         const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
-        const int64_t per_row = kr / 16;
+        const int64_t per_row = kx / 16;
         for (int64_t f = threadIdx.x; f < M * per_row; f += 64 * W) {
             const int64_t r = f / per_row, c = f - r * per_row;
             v4i_t v = {0, 0, 0, 0};
-            if (r < g.m)
+            if (r < g.m && c * 16 < kr)
                 v = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(r * g.lda + c * 16), 0, 0));
-            *reinterpret_cast<v4i_t*>(xs + r * kr + c * 16) = v;
+            *reinterpret_cast<v4i_t*>(xs + r * kx + c * 16) = v;
         }
         if (kFused && g.x_out) {
             cnt = *g.count;
@@ -529,8 +577,23 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa) 
     }
     __syncthreads();
     const int lc = cnt < kGvOutl ? cnt : kGvOutl;
+    // epilogue operands of the wave's rows (lane i: the wave's row i) and the
+    // activation scales, loaded before the stream: a load at the end of a row
+    // would wait for every weight load in flight (loads complete in order)
+    const float r127 = 1.0f / 127.0f;
+    float sw_lane = 0.0f, bias_lane = 0.0f;
+    float sx[M];
+    if constexpr (kFused) {
+        const int64_t nl = row_of(lane);
+        if (lane < R && nl < g.n) {
+            sw_lane = g.col_absmax[nl] * r127;
+            bias_lane = g.bias ? h2f(g.bias[nl]) : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+            sx[r] = r < g.m ? (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127 : 0.0f;
+    }
 
-    // 3. stream: dot4 per 4 weight bytes, outliers from the bytes in flight
     int32_t acc[M];
     float pacc[M];
 #pragma unroll
@@ -538,135 +601,135 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa) 
         acc[r] = 0;
         pacc[r] = 0.0f;
     }
-    const int slice = (lane & 7) * 16;  // this lane's 16 bytes of each chunk
-    int next = 0;                        // first outlier column not yet behind the stream
-    for (int64_t j0 = 0; j0 < mine; j0 += kGvBatch) {
-        if (j0 > 0) load_batch(j0);
+
+    // end of row rr: sums over the 64 lanes, epilogue in lane 0
+    auto finish_row = [&](int rr) {
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            acc[r] = wave_sum_i32(acc[r]);
+            if (kFused) pacc[r] = wave_sum_f32(pacc[r]);
+        }
+        const int64_t n = row_of(rr);
+        float sw = 0.0f, bj = 0.0f;
+        if constexpr (kFused) {
+            sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sw_lane), rr));
+            bj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bias_lane), rr));
+        }
+        if (lane == 0 && n < g.n) {
+            if constexpr (!kFused) {
+#pragma unroll
+                for (int r = 0; r < M; ++r)
+                    if (r < g.m) g.c[r * g.ldc + n] = acc[r];
+            } else {
+                // outlier columns past the streamed ones: gathered, in slot order
+                if constexpr (kQuant) {
+                    // slots from the LDS bitmap and its prefix, values from x
+                    for (int64_t wd = 0; wd < qa.words && cnt > lc; ++wd) {
+                        uint32_t bits = ql.bm[wd];
+                        int32_t slot = ql.pre[wd];
+                        if (slot >= cnt) break;
+                        while (bits) {
+                            const int64_t j = wd * 32 + (__ffs(bits) - 1);
+                            bits &= bits - 1u;
+                            if (slot >= lc && slot < cnt) {
+                                const float wv = (float)g.b[n * g.ldb + j];
+#pragma unroll
+                                for (int r = 0; r < M; ++r)
+                                    if (r < g.m) pacc[r] += wv * h2f(qa.x[r * qa.ldx + j]);
+                            }
+                            ++slot;
+                        }
+                    }
+                } else {
+                    for (int s2 = lc; s2 < cnt; ++s2) {
+                        const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
+#pragma unroll
+                        for (int r = 0; r < M; ++r)
+                            if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < M; ++r)
+                    if (r < g.m) g.out[r * g.ldout + n] = f2h(sw * ((float)acc[r] * sx[r] + pacc[r]) + bj);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            acc[r] = 0;
+            pacc[r] = 0.0f;
+        }
+    };
+
+    // dot4 per 4 weight bytes against the LDS activations; outliers from the bytes in flight
+    const int slice = lane * 16;  // this lane's 16 bytes of each chunk
+    auto consume = [&](int b, const v4i_t (&wb)[kGvBatch]) {
+        const int rr = b / bpr;
+        const int c0 = (b - rr * bpr) * kGvBatch;
+        int next = 0;  // first outlier column not yet behind the stream
 #pragma unroll
         for (int u = 0; u < kGvBatch; ++u) {
-            const int64_t j = j0 + u;
-            if (j >= mine) break;
-            const int64_t kb = (part + j * G) * kChunk;
+            const int c = c0 + u;
+            if (c >= nck) break;
+            const int kb = c * kGvChunk;
 #pragma unroll
             for (int r = 0; r < M; ++r) {
-                const v4i_t xv = *reinterpret_cast<const v4i_t*>(xs + r * kr + kb + slice);
+                const v4i_t xw = *reinterpret_cast<const v4i_t*>(xs + r * kx + kb + slice);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) acc[r] = __builtin_amdgcn_sdot4(w[u][d], xv[d], acc[r], false);
+                for (int d = 0; d < 4; ++d) acc[r] = __builtin_amdgcn_sdot4(wb[u][d], xw[d], acc[r], false);
             }
             if (kFused) {
-                while (next < lc && oidx[next] < kb) ++next;  // columns in other waves' chunks
-                for (int s2 = next; s2 < lc && oidx[s2] < kb + kChunk; ++s2) {
-                    const int off = oidx[s2] - (int)kb - slice;  // byte of this lane's slice, if any
+                while (next < lc && oidx[next] < kb) ++next;
+                for (int s2 = next; s2 < lc && oidx[s2] < kb + kGvChunk; ++s2) {
+                    const int off = oidx[s2] - kb - slice;  // byte of this lane's slice, if any
                     if (off >= 0 && off < 16) {
-                        const float wv = (float)byte_of(w[u], off);
+                        const float wv = (float)byte_of(wb[u], off);
 #pragma unroll
                         for (int r = 0; r < M; ++r) pacc[r] += wv * oval[r * kGvOutl + s2];
                     }
                 }
             }
         }
-    }
+        if (c0 + kGvBatch >= nck) finish_row(rr);
+    };
 
-    // 4. sums over the 8 lanes of a row, then over the G waves of the group
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) {
-            acc[r] += __shfl_xor(acc[r], off, 64);
-            if (kFused) pacc[r] += __shfl_xor(pacc[r], off, 64);
-        }
-    }
-    const int row = lane >> 3;
-    if (part > 0 && (lane & 7) == 0) {
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-            red[(wid * M + r) * kGvRows + row] = acc[r];
-            if (kFused) pred[(wid * M + r) * kGvRows + row] = pacc[r];
-        }
-    }
-    __syncthreads();
-    if (part > 0 || (lane & 7) != 0) return;  // no barrier below
-#pragma unroll
-    for (int w2 = 1; w2 < G; ++w2)
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-            acc[r] += red[((wid + w2) * M + r) * kGvRows + row];
-            if (kFused) pacc[r] += pred[((wid + w2) * M + r) * kGvRows + row];
-        }
-
-    // 5. epilogue: lane 8 q owns weight row n0 + q
-    const int64_t n = n0 + row;
-    if (n >= g.n) return;
-    if constexpr (!kFused) {
-#pragma unroll
-        for (int r = 0; r < M; ++r)
-            if (r < g.m) g.c[r * g.ldc + n] = acc[r];
-    } else {
-        // outlier columns past the streamed ones: gathered, in slot order
-        if constexpr (kQuant) {
-            // slots from the LDS bitmap and its prefix, values from x
-            for (int64_t wd = 0; wd < qa.words && cnt > lc; ++wd) {
-                uint32_t bits = ql.bm[wd];
-                int32_t slot = ql.pre[wd];
-                if (slot >= cnt) break;
-                while (bits) {
-                    const int64_t j = wd * 32 + (__ffs(bits) - 1);
-                    bits &= bits - 1u;
-                    if (slot >= lc && slot < cnt) {
-                        const float wv = (float)g.b[n * g.ldb + j];
-#pragma unroll
-                        for (int r = 0; r < M; ++r)
-                            if (r < g.m) pacc[r] += wv * h2f(qa.x[r * qa.ldx + j]);
-                    }
-                    ++slot;
-                }
-            }
-        } else {
-            for (int s2 = lc; s2 < cnt; ++s2) {
-                const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
-#pragma unroll
-                for (int r = 0; r < M; ++r)
-                    if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
-            }
-        }
-        const float r127 = 1.0f / 127.0f;
-        const float sw = g.col_absmax[n] * r127;
-        const float bj = g.bias ? h2f(g.bias[n]) : 0.0f;
-#pragma unroll
-        for (int r = 0; r < M; ++r)
-            if (r < g.m) {
-                const float sx = (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127;
-                g.out[r * g.ldout + n] = f2h(sw * ((float)acc[r] * sx + pacc[r]) + bj);
-            }
+    for (int b = 0; b < nb; b += 2) {
+        issue(b + 1, w[1]);
+        consume(b, w[0]);
+        issue(b + 2, w[0]);
+        if (b + 1 < nb) consume(b + 1, w[1]);
     }
 }
 
 namespace {
 
-// m <= 4 with the activations in at most 32 KB of LDS
+// Rows per wave: about kGvWaves waves over the n weight rows, at most 64
+// (a row's epilogue operands sit in one lane each).
+int gemv_rows_per_wave(int64_t n) {
+    const int64_t r = (n + kGvWaves - 1) / kGvWaves;
+    return (int)(r < 64 ? r : 64);
+}
+
+size_t gemv_lds(int64_t m_pad, int64_t k, int64_t words, int W, bool quant) {
+    const int64_t kx = (k + kGvChunk - 1) / kGvChunk * kGvChunk;
+    size_t lds = (size_t)m_pad * kx + (size_t)kGvOutl * 4 + (size_t)m_pad * kGvOutl * 4;
+    if (quant) lds += ((size_t)2 * words + m_pad + W + 1) * 4;
+    return lds;
+}
+
+// m <= 4 with the activations in at most 32 KB of LDS (above that, at m = 4
+// and K = 13824, the MFMA kernel measured faster)
 bool gemv_fits(const GemmArgs& g) {
-    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-    // at most 32 KB: four workgroups per CU by LDS (a larger block measured slower
-    // than the MFMA kernel: too few workgroups resident)
-    return g.m >= 1 && g.m <= 4 && (g.m > 2 ? 4 : g.m) * kr <= 32 * 1024;
+    const int64_t kx = (g.k + kGvChunk - 1) / kGvChunk * kGvChunk;
+    return g.m >= 1 && g.m <= 4 && (g.m > 2 ? 4 : g.m) * kx <= 32 * 1024;
 }
 
 template <int M, bool kFused, int kQuantL, int W>
 hipError_t launch_gemv_m(const GemmArgs& g, const QuantArgs& qa, hipStream_t stream) {
-    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-    const int64_t nchunks = kr / kChunk;
-    const int64_t groups = (g.n + kGvRows - 1) / kGvRows;
-    // K splits: about 2500 waves or more, each with at least 8 chunks
-    int gs = 1;
-    while (gs < 4 && groups * gs < 2560 && nchunks / (2 * gs) >= kGvBatch) gs *= 2;
-    size_t lds = (size_t)M * kr + (size_t)W * M * kGvRows * 8 + (size_t)kGvOutl * 4 + (size_t)M * kGvOutl * 4;
-    if (kQuantL > 0) lds += ((size_t)2 * qa.words + M + W + 1) * 4;
-    const dim3 grid((unsigned)((groups * gs + W - 1) / W)), block(64 * W);
-    switch (gs) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<1, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<2, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
-        default: hipLaunchKernelGGL((gemv_kernel<4, M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa); break;
-    }
+    const int R = gemv_rows_per_wave(g.n);
+    const int64_t waves = (g.n + R - 1) / R;
+    const size_t lds = gemv_lds(M, g.k, qa.words, W, kQuantL > 0);
+    const dim3 grid((unsigned)((waves + W - 1) / W)), block(64 * W);
+    hipLaunchKernelGGL((gemv_kernel<M, kFused, kQuantL, W>), grid, block, lds, stream, g, qa, R);
     return hipGetLastError();
 }
 
@@ -678,11 +741,10 @@ hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
     return launch_gemv_m<4, kFused, 0, 4>(g, none, stream);
 }
 
-// 8-wave workgroups: x is quantized by 512 threads (at most 8 chunks each) in
-// half as many workgroups as 4-wave ones would need
+// 8-wave workgroups: x is quantized by 512 threads, at most 8 chunks each
 template <int M>
 hipError_t launch_forward_m(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
-    const int64_t per_thread = (qa.m * ((qa.k + 7) / 8) + 511) / 512;
+    const int64_t per_thread = (qa.m * (qa.k / 8) + 511) / 512;
     if (per_thread <= 4) return launch_gemv_m<M, true, 4, 8>(g, qa, stream);
     return launch_gemv_m<M, true, 8, 8>(g, qa, stream);
 }
@@ -693,11 +755,12 @@ bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g) {
     const bool w_aligned = ((g.ldb & 15) == 0) && ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
     // whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
     const bool x_vec = ((qa.k & 7) == 0) && ((qa.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(qa.x) & 15) == 0);
-    // gemv_fits bounds the chunks: m * k / 8 <= 4096, 8 per thread of 512
-    // the codes are copied from the LDS rows: same pitch, 16-byte aligned
-    const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-    const bool q_rows = qa.q && qa.ldq == kr && qa.kpad == kr && ((reinterpret_cast<uintptr_t>(qa.q) & 15) == 0);
-    return qa.m == g.m && qa.k == g.k && gemv_fits(g) && w_aligned && x_vec && q_rows && qa.absmax;
+    // at most 8 chunks of x per thread of 512
+    const bool x_regs = qa.m * (qa.k / 8) <= 8 * 512;
+    // the codes are copied from the LDS rows in 16-byte units
+    const bool q_rows = qa.q && qa.kpad == qa.ldq && (qa.ldq & 15) == 0 &&
+                        ((reinterpret_cast<uintptr_t>(qa.q) & 15) == 0);
+    return qa.m == g.m && qa.k == g.k && gemv_fits(g) && w_aligned && x_vec && x_regs && q_rows && qa.absmax;
 }
 
 hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
