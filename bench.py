@@ -406,7 +406,8 @@ def main() -> int:
         achieved = g_bytes / g_time / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
-    roof["kernel"] = "fused int8 GEMM + dequant epilogue (gemm_dtl_kernel / gemm_decode_kernel)"
+    roof["kernel"] = ("fused int8 GEMM + dequant epilogue, the GEMM half of the linear run alone "
+                      "(gemm_dtl_kernel for prefill; gemv_kernel for m <= 4, gemm_decode_kernel for m <= 16)")
     roof["per_launch_us"] = {k: round(v, 3) for k, v in gemm_us.items()}
     roof["timing"] = "HIP events around graph replays of the layer's GEMM launches"
     roof["traffic"] = read_traffic(args.workload)

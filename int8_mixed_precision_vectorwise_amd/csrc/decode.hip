@@ -226,6 +226,7 @@ constexpr int kGvChunk = 1024;   // K bytes per wave load
 constexpr int kGvBatch = 8;      // loads per batch (two batches in flight)
 constexpr int kGvOutl = 64;      // outlier columns handled in the stream (more: gathered per row)
 constexpr int kGvWaves = 2048;   // waves the grid aims at
+constexpr int kGvOwn = 2;        // outlier columns a lane keeps in registers
 
 __device__ inline int8_t byte_of(const v4i_t& v, int b) {
     return (int8_t)(((uint32_t)v[b >> 2] >> (8 * (b & 3))) & 0xffu);
@@ -448,11 +449,14 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
 // The forward's intermediates into the workspace, spread over the grid (each
 // thread writes at most a few entries): codes (the LDS rows, kpad == ldq),
 // absmax, bitmap, count, index list (-1 past the kept columns) and gathered
-// outlier values (read from x, zero past the kept columns).  After the
+// outlier values (zero past the kept columns).  The first kGvOutl slots come
+// from the stream's LDS list (columns, and values as fp32 that convert back
+// to the same fp16); later slots, if any, from the bitmap and x.  After the
 // barrier that follows quantize_rows_lds.
 template <int M, int T>
 __device__ inline void publish_spread(const QuantArgs& a, int64_t kx, const int8_t* xs, const GvQuantLds& q,
-                                      bool any, int32_t total, int32_t kept) {
+                                      const int32_t* oidx, const float* oval, bool any, int32_t total,
+                                      int32_t kept) {
     const int64_t gt = (int64_t)blockIdx.x * T + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * T;
     const int64_t units = a.ldq / 16;  // 16-byte units per code row (ldq <= kx, zeros past k)
@@ -462,28 +466,34 @@ __device__ inline void publish_spread(const QuantArgs& a, int64_t kx, const int8
     }
     if (gt < a.m) a.absmax[gt] = __uint_as_float(q.rmax[gt]);
     if (gt == 0 && a.count_out) *a.count_out = total;
-    for (int64_t w = gt; w < a.words; w += stride) {
-        const uint32_t bits0 = any ? q.bm[w] : 0u;
-        if (a.bitmap_out) a.bitmap_out[w] = bits0;
-        uint32_t bits = bits0;
-        int32_t slot = bits ? q.pre[w] : 0;
-        while (bits) {
-            const int64_t j = w * 32 + (__ffs(bits) - 1);
-            bits &= bits - 1u;
-            if (slot < a.cap) {
-                if (a.idx_out) a.idx_out[slot] = (int32_t)j;
-                if (a.x_out)
-                    for (int64_t r = 0; r < a.m; ++r) a.x_out[r * a.ldo + slot] = a.x[r * a.ldx + j];
-            }
-            ++slot;
-        }
-    }
+    if (a.bitmap_out)
+        for (int64_t w = gt; w < a.words; w += stride) a.bitmap_out[w] = any ? q.bm[w] : 0u;
+    const int32_t lc = kept < kGvOutl ? kept : kGvOutl;
     if (a.idx_out)
-        for (int64_t s = kept + gt; s < a.idx_len; s += stride) a.idx_out[s] = -1;
-    if (a.x_out && a.xo_cols > kept) {
-        const int64_t pad = a.xo_cols - kept;
-        for (int64_t f = gt; f < a.m * pad; f += stride) a.x_out[(f / pad) * a.ldo + kept + f % pad] = 0;
-    }
+        for (int64_t s = gt; s < a.idx_len; s += stride)
+            if (s < lc) a.idx_out[s] = oidx[s];
+            else if (s >= kept) a.idx_out[s] = -1;
+    if (a.x_out)
+        for (int64_t f = gt; f < a.m * a.xo_cols; f += stride) {
+            const int64_t r = f / a.xo_cols, s = f - r * a.xo_cols;
+            if (s < lc) a.x_out[r * a.ldo + s] = f2h(oval[r * kGvOutl + s]);
+            else if (s >= kept) a.x_out[r * a.ldo + s] = 0;
+        }
+    if (kept > kGvOutl)  // slots from kGvOutl on: walk the bitmap words
+        for (int64_t w = gt; w < a.words; w += stride) {
+            uint32_t bits = q.bm[w];
+            int32_t slot = bits ? q.pre[w] : 0;
+            while (bits) {
+                const int64_t j = w * 32 + (__ffs(bits) - 1);
+                bits &= bits - 1u;
+                if (slot >= kGvOutl && slot < kept) {
+                    if (a.idx_out) a.idx_out[slot] = (int32_t)j;
+                    if (a.x_out)
+                        for (int64_t r = 0; r < a.m; ++r) a.x_out[r * a.ldo + slot] = a.x[r * a.ldx + j];
+                }
+                ++slot;
+            }
+        }
 }
 
 }  // namespace
@@ -513,8 +523,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     int8_t* xs = gsm;
     int32_t* oidx = reinterpret_cast<int32_t*>(gsm + M * kx);
     float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
+    int32_t* own_lds = reinterpret_cast<int32_t*>(oval + M * kGvOutl);  // [W][64 * (1 + kOwn)]
     GvQuantLds ql;
-    ql.bm = reinterpret_cast<uint32_t*>(oval + M * kGvOutl);
+    ql.bm = reinterpret_cast<uint32_t*>(own_lds + W * 64 * (1 + kGvOwn));
     ql.pre = reinterpret_cast<int32_t*>(ql.bm + qa.words);
     ql.rmax = reinterpret_cast<uint32_t*>(ql.pre + qa.words);
     ql.wave_tot = reinterpret_cast<int32_t*>(ql.rmax + M);
@@ -551,7 +562,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
         const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kx, xs, oidx, oval, ql);
         cnt = total < qa.cap ? total : qa.cap;
         __syncthreads();
-        publish_spread<M, 64 * W>(qa, kx, xs, ql, total > 0, total, cnt);
+        publish_spread<M, 64 * W>(qa, kx, xs, ql, oidx, oval, total > 0, total, cnt);
     } else {
         // the codes' rows hold zeros from k to a multiple of 128 (lda >= that)
         const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
@@ -593,6 +604,54 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
         for (int r = 0; r < M; ++r)
             sx[r] = r < g.m ? (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127 : 0.0f;
     }
+    // The streamed outlier columns: column j of a chunk sits in lane
+    // (j % 1024) / 16, byte j % 16, of every row's load of chunk j / 1024.
+    // Each lane takes up to kOwn of the columns it will hold (chunk, byte, x
+    // values in registers), so that per chunk the owning lanes add their
+    // terms together; a column past its lane's kOwn is walked one by one
+    // (spill: a wave-uniform slot mask, empty unless three or more columns
+    // share a lane).  Slot lane s finds its rank at its owner with an LDS
+    // atomic on the wave's counters; the owner reads its entries back.
+    // chunks_hit (uniform): bit c set if chunk c holds an outlier column.
+    constexpr int kOwn = kGvOwn;
+    int own_chunk[kOwn], own_byte[kOwn];
+    float own_x[kOwn][M];
+    uint64_t spill = 0;
+    uint32_t chunks_hit = 0;
+    const int ocol = lane < lc ? oidx[lane] : 0x7fffffff;  // lane s: column of slot s
+    if constexpr (kFused) {
+        int32_t* cnt_w = own_lds + wid * 64 * (1 + kOwn);   // [64] counters | [64][kOwn] slots
+        int32_t* tab_w = cnt_w + 64;
+        cnt_w[lane] = 0;
+#pragma unroll
+        for (int e = 0; e < kOwn; ++e) tab_w[lane * kOwn + e] = -1;
+        __syncthreads();
+        bool spilled = false;
+        if (lane < lc) {
+            const int owner = (ocol & (kGvChunk - 1)) >> 4;
+            const int rank = atomicAdd(&cnt_w[owner], 1);
+            if (rank < kOwn) tab_w[owner * kOwn + rank] = lane;
+            else spilled = true;
+        }
+        spill = __ballot(spilled);
+        uint32_t hit = lane < lc ? 1u << (ocol / kGvChunk) : 0u;  // chunks < 32 (k <= 32 KB)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) hit |= (uint32_t)__shfl_xor((int)hit, off, 64);
+        chunks_hit = __builtin_amdgcn_readfirstlane(hit);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kOwn; ++e) {
+            const int sl = tab_w[lane * kOwn + e];
+            const int col = sl >= 0 ? oidx[sl] : 0;
+            own_chunk[e] = sl >= 0 ? col / kGvChunk : -1;
+            own_byte[e] = col & 15;
+#pragma unroll
+            for (int r = 0; r < M; ++r) own_x[e][r] = sl >= 0 ? oval[r * kGvOutl + sl] : 0.0f;
+        }
+    }
+    float oxv[M];  // lane s: x values of slot s (for spilled columns)
+#pragma unroll
+    for (int r = 0; r < M; ++r) oxv[r] = oval[r * kGvOutl + lane];
 
     int32_t acc[M];
     float pacc[M];
@@ -665,7 +724,6 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     auto consume = [&](int b, const v4i_t (&wb)[kGvBatch]) {
         const int rr = b / bpr;
         const int c0 = (b - rr * bpr) * kGvBatch;
-        int next = 0;  // first outlier column not yet behind the stream
 #pragma unroll
         for (int u = 0; u < kGvBatch; ++u) {
             const int c = c0 + u;
@@ -677,14 +735,27 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
 #pragma unroll
                 for (int d = 0; d < 4; ++d) acc[r] = __builtin_amdgcn_sdot4(wb[u][d], xw[d], acc[r], false);
             }
-            if (kFused) {
-                while (next < lc && oidx[next] < kb) ++next;
-                for (int s2 = next; s2 < lc && oidx[s2] < kb + kGvChunk; ++s2) {
-                    const int off = oidx[s2] - kb - slice;  // byte of this lane's slice, if any
+            if (kFused && ((chunks_hit >> c) & 1u)) {
+#pragma unroll
+                for (int e = 0; e < kOwn; ++e)
+                    if (own_chunk[e] == c) {
+                        const float wv = (float)byte_of(wb[u], own_byte[e]);
+#pragma unroll
+                        for (int r = 0; r < M; ++r) pacc[r] += wv * own_x[e][r];
+                    }
+                // spilled columns inside this chunk, one by one
+                uint64_t hits = spill ? (__ballot(ocol >= kb && ocol < kb + kGvChunk) & spill) : 0;
+                while (hits) {
+                    const int s2 = __builtin_ctzll(hits);
+                    hits &= hits - 1;
+                    const int off = __builtin_amdgcn_readlane(ocol, s2) - kb - slice;  // byte of this lane's slice?
+                    float xo[M];
+#pragma unroll
+                    for (int r = 0; r < M; ++r) xo[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(oxv[r]), s2));
                     if (off >= 0 && off < 16) {
                         const float wv = (float)byte_of(wb[u], off);
 #pragma unroll
-                        for (int r = 0; r < M; ++r) pacc[r] += wv * oval[r * kGvOutl + s2];
+                        for (int r = 0; r < M; ++r) pacc[r] += wv * xo[r];
                     }
                 }
             }
@@ -711,7 +782,8 @@ int gemv_rows_per_wave(int64_t n) {
 
 size_t gemv_lds(int64_t m_pad, int64_t k, int64_t words, int W, bool quant) {
     const int64_t kx = (k + kGvChunk - 1) / kGvChunk * kGvChunk;
-    size_t lds = (size_t)m_pad * kx + (size_t)kGvOutl * 4 + (size_t)m_pad * kGvOutl * 4;
+    size_t lds = (size_t)m_pad * kx + (size_t)kGvOutl * 4 + (size_t)m_pad * kGvOutl * 4 +
+                 (size_t)W * 64 * (1 + kGvOwn) * 4;
     if (quant) lds += ((size_t)2 * words + m_pad + W + 1) * 4;
     return lds;
 }

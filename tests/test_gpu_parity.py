@@ -306,6 +306,30 @@ def test_decode_forward_matches_two_launches(m, k, n, o, cap):
         assert_fp16_close(one, ref.out)
 
 
+@pytest.mark.parametrize("m", [1, 4])
+def test_gemv_outlier_columns_sharing_a_lane(m):
+    """Outlier columns 5, 6, 7, 1029 and 2053 all sit in lane 0's bytes of
+    their 1 KB chunks (more than a lane keeps in registers), 100 in lane 6."""
+    k, n = 4096, 300
+    L = make_inputs(m, k, n, bias_std=0.01, seed=(84, m, 0))
+    cols = [5, 6, 7, 100, 1029, 2053]
+    L.x[:, cols] = np.float16(25.0)
+    L.x[0, 6] = np.float16(-40.0)
+    wq, ws = oracle.quantize_weight(L.w)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert list(ref.quant.cols) == cols
+    x, w, s_, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
+    say(f"gemv outliers sharing a lane m={m}")
+    wa = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
+    one = i8.linear(x, w, s_, b, TAU, 32, wa)
+    wb = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
+    i8.linear_quantize(x, wb, TAU)
+    two = i8.linear_matmul_dequant(wb, w, s_, b)
+    torch.cuda.synchronize()
+    assert_fp16_close(one, ref.out)
+    assert_fp16_close(two, ref.out)
+
+
 @pytest.mark.parametrize("pad", [8, 1], ids=["ldx_aligned", "ldx_odd"])
 def test_decode_forward_strided_x(pad):
     """x with a row stride: an aligned one takes the one-launch forward, an odd
