@@ -232,39 +232,6 @@ __device__ inline int8_t byte_of(const v4i_t& v, int b) {
     return (int8_t)(((uint32_t)v[b >> 2] >> (8 * (b & 3))) & 0xffu);
 }
 
-// Sums over the 64 lanes, returned wave-uniform: DPP adds within each row of
-// 16 lanes (quad swaps, half-row and row mirrors), then the four row totals
-// read out with v_readlane.  No LDS traffic, unlike a shuffle ladder.
-template <int kCtrl>
-__device__ inline int32_t dpp_i32(int32_t v) {
-    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
-}
-constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-
-__device__ inline int32_t wave_sum_i32(int32_t v) {
-    v += dpp_i32<kDppQuadSwap1>(v);
-    v += dpp_i32<kDppQuadSwap2>(v);
-    v += dpp_i32<kDppHalfMirror>(v);
-    v += dpp_i32<kDppRowMirror>(v);
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
-           __builtin_amdgcn_readlane(v, 48);
-}
-
-__device__ inline float wave_sum_f32(float v) {
-    v += __int_as_float(dpp_i32<kDppQuadSwap1>(__float_as_int(v)));
-    v += __int_as_float(dpp_i32<kDppQuadSwap2>(__float_as_int(v)));
-    v += __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v)));
-    v += __int_as_float(dpp_i32<kDppRowMirror>(__float_as_int(v)));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
 // LDS of the fused forward's quantizer state, after the stream's arrays
 struct GvQuantLds {
     uint32_t* bm;        // [words] outlier bitmap
@@ -303,31 +270,6 @@ __device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L], uint32_t
 #pragma unroll
     for (int i = 0; i < L; ++i)
         if (tid + T * i >= total_chunks) v[i] = make_uint4(0, 0, 0, 0);
-}
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-
-// largest |x| of the 8 fp16 values (packed fp16 maxima of the magnitudes: exact)
-__device__ inline float chunk_absmax(const uint4& v) {
-    const uint32_t mag = 0x7fff7fffu;
-    const h2_t a = __builtin_bit_cast(h2_t, v.x & mag), b = __builtin_bit_cast(h2_t, v.y & mag);
-    const h2_t c = __builtin_bit_cast(h2_t, v.z & mag), d = __builtin_bit_cast(h2_t, v.w & mag);
-    const h2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-    return fmaxf((float)m.x, (float)m.y);
-}
-
-// Codes of a chunk with no outlier column: rne(x * inv) in fp32.  Every |x|
-// of the chunk is at most the row absmax s and inv = fl32(127 / s), so the
-// product rounds into [-127, 127] and the clamp of the code definition never
-// acts; inv = 0 (a zero row) gives 0.
-__device__ inline uint2 codes8_plain(const uint4& v, float inv) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int q = (int)__builtin_rintf(h2f(half_at(v, e)) * inv);
-        w[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
-    }
-    return make_uint2(w[0], w[1]);
 }
 
 // Quantize the chunks of load_x_chunks into the LDS activation rows xs
@@ -375,7 +317,13 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
     const bool any = outl && *q.any != 0;
     const int32_t total = any ? bitmap_prefix(q.bm, q.pre, a.words, q.wave_tot) : 0;
     const int32_t kept = total < a.cap ? total : a.cap;
-    auto obyte = [&](int32_t c) -> uint32_t { return any ? (q.bm[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u; };
+    // each chunk's outlier bits, read once (the reads issue back to back)
+    uint32_t obits[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int32_t c = (int32_t)(rc[i] & 0xffffu);
+        obits[i] = any && valid(i) ? (q.bm[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
+    }
 
     // row absmax over the non-outlier columns (float bits order as uints for x >= 0)
     float tmax[M];
@@ -384,8 +332,7 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
 #pragma unroll
     for (int i = 0; i < L; ++i)
         if (valid(i)) {
-            const uint32_t ob = obyte((int32_t)(rc[i] & 0xffffu));
-            const float mx = ob ? chunk_max(v[i], ob) : cmax[i];
+            const float mx = obits[i] ? chunk_max(v[i], obits[i]) : cmax[i];
             const int r = (int)(rc[i] >> 16);
 #pragma unroll
             for (int rr = 0; rr < M; ++rr)
@@ -393,7 +340,7 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
         }
 #pragma unroll
     for (int r = 0; r < M; ++r) {
-        const float t = wave_max(tmax[r]);
+        const float t = wave_max_uniform(tmax[r]);
         if (lane == 0 && t > 0.0f) atomicMax(&q.rmax[r], __float_as_uint(t));
     }
     __syncthreads();
@@ -415,7 +362,7 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
 #pragma unroll
         for (int rr = 1; rr < M; ++rr)
             if (rr == r) ir = inv[rr];
-        const uint32_t ob = obyte(c);
+        const uint32_t ob = obits[i];
         uint2 code;
         if (ob == 0u) {
             code = codes8_plain(v[i], ir);

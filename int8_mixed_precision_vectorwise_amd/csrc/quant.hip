@@ -37,6 +37,12 @@
 
 namespace i8mp {
 
+namespace {
+// whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
+bool vector_rows(const QuantArgs& a) {
+    return ((a.k & 7) == 0) && ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // detect: per (RB rows, 256 columns) workgroup, the OR of the rows' outlier
@@ -108,12 +114,14 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     const int64_t rr0 = kBlockRow ? 0 : wave;
     const int64_t r_first = (int64_t)blockIdx.x * a.rows_per_block + rr0;
     const bool preload = rr0 < a.rows_per_block && r_first < a.m;
+    // chunk indices (8 columns each) fit 32 bits: k <= 133144
+    const int32_t nchunks = (int32_t)((a.k + 7) / 8);
     uint4 v[kBatch];
-    auto load_batch = [&](const half_bits* __restrict__ xr, int64_t b) {
+    auto load_batch = [&](const half_bits* __restrict__ xr, int32_t b) {
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
-            const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
-            v[c] = col < a.k ? load8<kVec>(xr, col, a.k) : make_uint4(0, 0, 0, 0);
+            const int32_t ch = b * P * kBatch + pid + P * c;
+            v[c] = ch < nchunks ? load8<kVec>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
         }
     };
     if (preload) load_batch(a.x + r_first * a.ldx, 0);
@@ -142,47 +150,81 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     const int32_t kept = total < a.cap ? total : a.cap;
     if (blockIdx.x == 0) publish(a, bm, pre, total, outl);
 
-    const int64_t nchunks = (a.k + 7) / 8;
-    const int64_t nbatch = (nchunks + P * kBatch - 1) / (P * kBatch);
-    const bool vec_q = a.q && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
-    auto obyte = [&](int64_t col) -> uint32_t { return outl ? (bm[col >> 5] >> (col & 31)) & 0xffu : 0u; };
+    const int32_t nbatch = (nchunks + P * kBatch - 1) / (P * kBatch);
+    // byte c of the bitmap: the outlier bits of chunk c (8 columns)
+    const uint8_t* bmb = reinterpret_cast<const uint8_t*>(bm);
+    // a batch's chunks with their outlier columns set to 0: the packed fp16
+    // maximum of the rest is the row absmax over the non-outlier columns, and
+    // the clamp-free codes of the rest are the codes, 0 in outlier columns
+    auto mask_batch = [&](int32_t b) {
+        if (!outl) return;
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int32_t ch = b * P * kBatch + pid + P * c;
+            v[c] = mask_outliers(v[c], ch < nchunks ? (uint32_t)bmb[ch] : 0u);
+        }
+    };
     for (int64_t rr = rr0; rr < a.rows_per_block; rr += kBlockRow ? 1 : 4) {
         const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
         if (r >= a.m) break;
         const half_bits* __restrict__ xr = a.x + r * a.ldx;
 
         float mx = 0.0f;
-        for (int64_t b = 0; b < nbatch; ++b) {
+        for (int32_t b = 0; b < nbatch; ++b) {
             if (b > 0 || rr != rr0) load_batch(xr, b);  // batch 0 of the first row is in v
+            mask_batch(b);
 #pragma unroll
-            for (int c = 0; c < kBatch; ++c) {
-                const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
-                if (col < a.k) mx = fmaxf(mx, chunk_max(v[c], obyte(col)));
-            }
+            for (int c = 0; c < kBatch; ++c) mx = fmaxf(mx, chunk_absmax(v[c]));  // chunks past k are 0
         }
-        float s = wave_max(mx);
+        float s = wave_max_uniform(mx);
         if constexpr (kBlockRow) {
             if (lane == 0) rmax[wave] = s;
             __syncthreads();
             s = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
             __syncthreads();
         }
-        const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
-        const bool zero_row = !(s > 0.0f);
-        for (int64_t b = 0; b < nbatch; ++b) {
-            if (nbatch > 1) load_batch(xr, b);  // one batch: still in registers
-#pragma unroll
-            for (int c = 0; c < kBatch; ++c) {
-                const int64_t col = (b * P * kBatch + (int64_t)pid + P * c) * 8;
-                if (col < a.k) emit8(a, v[c], obyte(col), r, col, inv, zero_row, vec_q, bm, pre);
-            }
-        }
+        const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division; 0 for a zero row
         if (a.q) {
-            for (int64_t j = a.k + pid; j < a.kpad; j += P) a.q[r * a.ldq + j] = 0;
+            int8_t* qr = a.q + r * a.ldq;
+            for (int32_t b = 0; b < nbatch; ++b) {
+                if (nbatch > 1) {  // one batch: still in registers, masked
+                    load_batch(xr, b);
+                    mask_batch(b);
+                }
+#pragma unroll
+                for (int c = 0; c < kBatch; ++c) {
+                    const int32_t ch = b * P * kBatch + pid + P * c;
+                    if (ch >= nchunks) continue;
+                    const int64_t col = (int64_t)ch * 8;
+                    const uint2 code = codes8_plain(v[c], inv);
+                    if (kVec) {  // whole chunks, 8-byte aligned code rows (checked by the launcher)
+                        *reinterpret_cast<uint2*>(qr + col) = code;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (col + e < a.k) qr[col + e] = (int8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+                    }
+                }
+            }
+            for (int64_t j = a.k + pid; j < a.kpad; j += P) qr[j] = 0;
             if (pid == 0) a.absmax[r] = s;
         }
-        if (a.x_out)
+        // the row's outlier values into their slots of the compact matrix
+        // (bitmap words walked in order, slot from the prefix), zeros after
+        if (a.x_out) {
+            if (total > 0)
+                for (int64_t w = pid; w < a.words; w += P) {
+                    uint32_t bits = bm[w];
+                    int32_t slot = bits ? pre[w] : 0;
+                    while (bits) {
+                        const int64_t j = w * 32 + (__ffs(bits) - 1);
+                        bits &= bits - 1u;
+                        if (slot < a.cap) a.x_out[r * a.ldo + slot] = xr[j];
+                        ++slot;
+                    }
+                }
             for (int32_t t = kept + pid; t < a.xo_cols; t += P) a.x_out[r * a.ldo + t] = 0;
+        }
     }
 }
 
@@ -293,12 +335,21 @@ hipError_t launch_small(const QuantArgs& a, int64_t per_thread, size_t lds, hipS
     return launch_small_l<kVec, 8>(a, lds, stream);
 }
 
+// kBatch: the 16-byte loads per lane in flight, as many as the row needs up
+// to 16 (longer rows take several batches)
 template <bool kVec, bool kBlockRow>
-hipError_t launch_rows(const QuantArgs& a, int64_t blocks, bool big, size_t lds, hipStream_t stream) {
-    if (big)
-        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 16>), dim3((unsigned)blocks), dim3(256), lds, stream, a);
+hipError_t launch_rows(const QuantArgs& a, int64_t blocks, size_t lds, hipStream_t stream) {
+    constexpr int P = kBlockRow ? 256 : 64;
+    const int64_t per_lane = ceil_div(ceil_div(a.k, 8), P);
+    const dim3 grid((unsigned)blocks), block(256);
+    if (per_lane <= 2)
+        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 2>), grid, block, lds, stream, a);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 4>), grid, block, lds, stream, a);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 8>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 8>), dim3((unsigned)blocks), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((quant_kernel<kVec, kBlockRow, 16>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
@@ -306,7 +357,7 @@ hipError_t launch_rows(const QuantArgs& a, int64_t blocks, bool big, size_t lds,
 
 hipError_t launch_quant_rows(const QuantArgs& in, hipStream_t stream) {
     QuantArgs a = in;
-    const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+    const bool vec = vector_rows(a);
     const size_t lds = (size_t)a.words * 2 * sizeof(uint32_t);
     const int64_t cpr = (a.k + 7) / 8;
     // a workgroup per row for long rows (over 4096 columns), for few rows, and
@@ -314,7 +365,6 @@ hipError_t launch_quant_rows(const QuantArgs& in, hipStream_t stream) {
     // workgroup spreads the per-element work over the CUs); else a wavefront
     // per row
     const bool block_row = cpr > 512 || a.m <= 64 || (cpr >= 256 && a.m <= 512);
-    const bool big = cpr > (block_row ? 256 : 64) * 8;
     int64_t blocks;
     // enough rows per workgroup to amortize the OR of the partial bitmaps
     if (block_row) {
@@ -324,16 +374,18 @@ hipError_t launch_quant_rows(const QuantArgs& in, hipStream_t stream) {
         a.rows_per_block = 4 * ceil_div(a.m, 4 * 512);
         blocks = ceil_div(a.m, a.rows_per_block);
     }
-    if (vec)
-        return block_row ? launch_rows<true, true>(a, blocks, big, lds, stream)
-                         : launch_rows<true, false>(a, blocks, big, lds, stream);
-    return block_row ? launch_rows<false, true>(a, blocks, big, lds, stream)
-                     : launch_rows<false, false>(a, blocks, big, lds, stream);
+    // the vector path also stores whole 8-byte code chunks
+    const bool vec_codes = vec && (!a.q || (((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0)));
+    if (vec_codes)
+        return block_row ? launch_rows<true, true>(a, blocks, lds, stream)
+                         : launch_rows<true, false>(a, blocks, lds, stream);
+    return block_row ? launch_rows<false, true>(a, blocks, lds, stream)
+                     : launch_rows<false, false>(a, blocks, lds, stream);
 }
 
 hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
     QuantArgs a = in;
-    const bool vec = ((a.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+    const bool vec = vector_rows(a);
     a.bitmap_in = nullptr;
     const int64_t per_thread = ceil_div(a.m * ceil_div(a.k, 8), kSmallThreads);
     if (a.m > 0 && a.m <= kSmallMaxRows && per_thread <= kSmallMaxL) {

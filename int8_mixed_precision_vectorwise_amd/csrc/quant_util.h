@@ -21,10 +21,13 @@ __device__ inline uint32_t outlier_bits8(const uint4& v, float tau) {
     return m;
 }
 
-// 8 fp16 values starting at column col of a row; columns >= k read as 0.
+// 8 fp16 values starting at column col of a row.  kVec: one 16-byte load
+// (the caller guarantees col + 8 <= k and 16-byte aligned rows: k and ldx
+// multiples of 8; no per-element path, so the compiler keeps several such
+// loads in flight).  Otherwise element by element, columns >= k as 0.
 template <bool kVec>
 __device__ inline uint4 load8(const half_bits* __restrict__ row, int64_t col, int64_t k) {
-    if (kVec && col + 8 <= k) return *reinterpret_cast<const uint4*>(row + col);
+    if (kVec) return *reinterpret_cast<const uint4*>(row + col);
     uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -155,6 +158,87 @@ __device__ inline void emit8(const QuantArgs& a, const uint4& v, uint32_t obits,
             }
         }
     }
+}
+
+// Sums over the 64 lanes, returned wave-uniform: DPP adds within each row of
+// 16 lanes (quad swaps, half-row and row mirrors), then the four row totals
+// read out with v_readlane.  No LDS traffic, unlike a shuffle ladder.
+template <int kCtrl>
+__device__ inline int32_t dpp_i32(int32_t v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ inline int32_t wave_sum_i32(int32_t v) {
+    v += dpp_i32<kDppQuadSwap1>(v);
+    v += dpp_i32<kDppQuadSwap2>(v);
+    v += dpp_i32<kDppHalfMirror>(v);
+    v += dpp_i32<kDppRowMirror>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ inline float wave_sum_f32(float v) {
+    v += __int_as_float(dpp_i32<kDppQuadSwap1>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppQuadSwap2>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v)));
+    v += __int_as_float(dpp_i32<kDppRowMirror>(__float_as_int(v)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Largest value over the 64 lanes (values >= 0), wave-uniform, as wave_sum_f32.
+__device__ inline float wave_max_uniform(float v) {
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppQuadSwap1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppQuadSwap2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppRowMirror>(__float_as_int(v))));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// largest |x| of the 8 fp16 values (packed fp16 maxima of the magnitudes: exact)
+__device__ inline float chunk_absmax(const uint4& v) {
+    const uint32_t mag = 0x7fff7fffu;
+    const h2_t a = __builtin_bit_cast(h2_t, v.x & mag), b = __builtin_bit_cast(h2_t, v.y & mag);
+    const h2_t c = __builtin_bit_cast(h2_t, v.z & mag), d = __builtin_bit_cast(h2_t, v.w & mag);
+    const h2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return fmaxf((float)m.x, (float)m.y);
+}
+
+// The 8 fp16 values with those whose bit is set in ob replaced by +0.
+__device__ inline uint4 mask_outliers(const uint4& v, uint32_t ob) {
+    auto keep = [&](uint32_t w, int d) {
+        const uint32_t lo = (uint32_t)((int32_t)(ob << (31 - 2 * d)) >> 31);      // all ones if bit 2d
+        const uint32_t hi = (uint32_t)((int32_t)(ob << (30 - 2 * d)) >> 31);      // all ones if bit 2d + 1
+        return w & ~((lo & 0x0000ffffu) | (hi & 0xffff0000u));
+    };
+    return make_uint4(keep(v.x, 0), keep(v.y, 1), keep(v.z, 2), keep(v.w, 3));
+}
+
+// Codes of a chunk with no outlier column: rne(x * inv) in fp32.  Every |x|
+// of the chunk is at most the row absmax s and inv = fl32(127 / s), so the
+// product rounds into [-127, 127] and the clamp of the code definition never
+// acts; inv = 0 (a zero row) gives 0.
+__device__ inline uint2 codes8_plain(const uint4& v, float inv) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = (int)__builtin_rintf(h2f(half_at(v, e)) * inv);
+        w[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+    }
+    return make_uint2(w[0], w[1]);
 }
 
 }  // namespace i8mp
