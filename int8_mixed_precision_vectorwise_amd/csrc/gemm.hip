@@ -23,6 +23,8 @@
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that each XCD works on a contiguous run of tiles (sharing
 // operand rows in its own L2), walked in groups of kGroupM tile rows.
+#include <stdint.h>
+
 #include "common.h"
 
 namespace i8mp {
@@ -105,6 +107,16 @@ __device__ inline void dma4(__amdgpu_buffer_rsrc_t src, void* lds, int voffset) 
 // (their latency then hides behind the K loop): the tile's row and column
 // absmax, the first kEpiIdx outlier column indices and the outlier count.
 constexpr int kEpiIdx = 64;
+// Outlier slots whose weight bytes the pipelined kernel stashes in LDS as the
+// K tiles pass: int32 [kStash][BN], slot s of tile row r = W[n0 + r, idx[s]]
+// zero-extended (a 1-byte buffer_load ... lds writes one dword per lane).
+// Later slots are gathered from memory in the epilogue.  Only the 256 x 256
+// tile stashes: the large GEMMs that use it stream weights far larger than L2,
+// so the epilogue's gather would miss; with smaller weights the gather hits
+// L2 and the stash measured slower.
+constexpr int kStash = 24;
+template <int BM, int BN, bool kFused>
+constexpr bool stash_on() { return kFused && BM == 256 && BN == 256; }
 template <int BM, int BN>
 struct __attribute__((aligned(16))) EpiLds {
     float sx[BM];
@@ -142,7 +154,8 @@ __device__ inline void epi_prefetch(const GemmArgs& g, int64_t m0, int64_t n0, E
 // index list), then out = col_absmax / 127 * acc + bias in fp16.
 template <int BM, int BN, int FM, int FN, bool kFused, int kStageBytes>
 __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t m0, int64_t n0, int wr0, int wc0,
-                                int lane, const EpiLds<BM, BN>& e, int8_t* stage) {
+                                int lane, const EpiLds<BM, BN>& e, int8_t* stage, const int32_t* stash = nullptr,
+                                int n_stash = 0) {
     const int hi = lane >> 5, l32 = lane & 31;
     const int64_t rows_left = g.m - m0, cols_left = g.n - n0;
     if constexpr (!kFused) {
@@ -231,13 +244,25 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
                                                          rxo, (lrow * (int)g.ldo + sb) * 2, 0, 0));
                 }
                 uint32_t wby[FN][8];
+                if (sb + 8 <= n_stash) {
+                    // weight bytes stashed from the K tiles: 8 slots of the lane's column
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int lcol = wc0 + 32 * j + l32;
+                    for (int j = 0; j < FN; ++j) {
+                        const int lcol = wc0 + 32 * j + l32;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const int off = ix[t] >= 0 ? lcol * (int)g.ldb + ix[t] : (int)0x80000000;
-                        wby[j][t] = __builtin_amdgcn_raw_buffer_load_b8(rw, off, 0, 0);
+                        for (int t = 0; t < 8; ++t) wby[j][t] = (uint32_t)stash[(sb + t) * BN + lcol];
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int lcol = wc0 + 32 * j + l32;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            const int slot = sb + t;
+                            const int off = ix[t] >= 0 ? lcol * (int)g.ldb + ix[t] : (int)0x80000000;
+                            wby[j][t] = slot < n_stash ? (uint32_t)stash[slot * BN + lcol]
+                                                       : __builtin_amdgcn_raw_buffer_load_b8(rw, off, 0, 0);
+                        }
                     }
                 }
 #pragma unroll
@@ -546,8 +571,10 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     static_assert(STAGES >= 2, "need at least two stages");
     // one LDS array: the stages, then the epilogue operands (a second
     // __shared__ object makes the compiler drain every DMA before each LDS read)
-    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE + sizeof(EpiLds<BM, BN>)];
+    __shared__ __attribute__((aligned(1024))) int8_t
+        smem[STAGES * STAGE + sizeof(EpiLds<BM, BN>) + (stash_on<BM, BN, kFused>() ? kStash * BN * 4 : 0)];
     EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + STAGES * STAGE);
+    int32_t* stash = reinterpret_cast<int32_t*>(smem + STAGES * STAGE + sizeof(EpiLds<BM, BN>));  // fused only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -658,8 +685,36 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) dma_part(st, st < ktiles, st, 0, INS);
     wait_vm((STAGES - 2) * INS);  // tile 0 landed (tiles 1 .. STAGES-2 may be in flight)
-    barrier();
+    barrier();                    // ... and the epilogue operands copied at the start
     read_frags(0, 0, 0);
+
+    // The weight bytes of the first n_st outlier columns (ascending) are
+    // stashed in LDS by 1-byte DMA issued next to the DMA of the K tile that
+    // holds them (the line is then on its way through L2 anyway): waves 0 ..
+    // BN/64 - 1 take 64 weight rows each.  st_col is the next column to stash
+    // (wave-uniform).  These loads only make the vmcnt waits of the wave that
+    // issued them stricter (loads complete in order).
+    int n_st = 0, st_next = 0;
+    int64_t st_col = INT64_MAX;
+    if constexpr (stash_on<BM, BN, kFused>()) {
+        if (g.x_out) {
+            int cnt = epi.cnt[0];
+            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+            n_st = __builtin_amdgcn_readfirstlane(cnt < kStash ? cnt : kStash);
+            if (n_st > 0) st_col = __builtin_amdgcn_readfirstlane(epi.idx[0]);
+        }
+    }
+    auto stash_upto = [&](int64_t col_end) {  // the slots whose column is below col_end
+        while (st_col < col_end) {
+            if (wave < BN / 64)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb_src, (__attribute__((address_space(3))) void*)(stash + st_next * BN + wave * 64), 1,
+                    (int)((wave * 64 + lane) * g.ldb + st_col), 0, 0, 0);
+            ++st_next;
+            st_col = st_next < n_st ? (int64_t)__builtin_amdgcn_readfirstlane(epi.idx[st_next]) : INT64_MAX;
+        }
+    };
+    if constexpr (stash_on<BM, BN, kFused>()) stash_upto((int64_t)(STAGES - 1) * BKS);  // the tiles requested so far
     // DMA instructions per MFMA step of this iteration
     constexpr int DMA_PER_STEP = (INS + NSTEP - 1) / NSTEP;
     constexpr int DMA_LAST = INS - (NSTEP - 1) * DMA_PER_STEP;
@@ -700,10 +755,13 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         }
         // the last row of MFMAs covers the next fragments' LDS latency
         mfma_rows(LAST, FM - 1, FM);
+        if constexpr (stash_on<BM, BN, kFused>()) stash_upto((nt + 1) * BKS);  // with tile nt, requested in this iteration
     }
 
-    __syncthreads();  // no DMA in flight, K loop done everywhere, epilogue operands visible
-    epilogue<BM, BN, FM, FN, kFused, STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem);
+    if constexpr (stash_on<BM, BN, kFused>()) wait_vm(0);  // the stash DMA
+    __syncthreads();  // no DMA in flight, K loop done everywhere, epilogue operands and stash visible
+    epilogue<BM, BN, FM, FN, kFused, STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem, stash,
+                                                      st_next);
 }
 
 namespace {
@@ -716,7 +774,10 @@ template <int BM, int BN, bool kFused>
 hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t stream) {
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
     dim3 grid((unsigned)tiles);
-    constexpr int kStages = (160 * 1024) / ((BM + BN) * 128) > 4 ? 4 : (160 * 1024) / ((BM + BN) * 128);
+    // stages that fit 160 KB of LDS beside the epilogue operands and the stash, at most 4
+    constexpr int kFit =
+        (160 * 1024 - (int)sizeof(EpiLds<BM, BN>) - (stash_on<BM, BN, kFused>() ? kStash * BN * 4 : 0)) / ((BM + BN) * 128);
+    constexpr int kStages = kFit > 4 ? 4 : kFit;
     if (staged)
         hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, 128, kStages, kFused>), grid, dim3(256), 0, stream, g);
     else if (aligned)
