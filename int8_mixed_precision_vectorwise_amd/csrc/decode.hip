@@ -36,6 +36,7 @@ constexpr int kStages = 8;    // per-wave ring depth
 constexpr int kChunk = 128;   // K bytes per stage
 constexpr int kStageBytes = kRows * kChunk;  // weight rows only
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kDecOutl = 32;  // outlier columns the MFMA decode kernel takes from its ring
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
@@ -66,8 +67,11 @@ template <int G, bool kFused>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     // one LDS array (a second __shared__ object makes the compiler drain every
     // DMA before each LDS read): the rings, then the partial-sum blocks
-    __shared__ __attribute__((aligned(1024))) int8_t ring[kWaves * kStages * kStageBytes + kWaves * 4 * 64 * 4];
+    __shared__ __attribute__((aligned(1024))) int8_t
+        ring[kWaves * kStages * kStageBytes + 2 * kWaves * 4 * 64 * 4 + (kFused ? kRows * kDecOutl * 4 : 0)];
     int32_t* red = reinterpret_cast<int32_t*>(ring + kWaves * kStages * kStageBytes);
+    float* pred = reinterpret_cast<float*>(red + kWaves * 4 * 64);
+    float* xo = pred + kWaves * 4 * 64;  // [16 activation rows][kDecOutl] outlier values (fused)
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -116,6 +120,46 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < kStages - 1; ++j) issue(j, j);
     const int row = lane & 15;
+
+    // The first kDecOutl outlier columns (ascending) are taken from the ring
+    // as their chunk passes: lane l reads its weight row's byte (row l % 16)
+    // and adds byte * x into p, laid out like acc (activation rows
+    // 4 (l / 16) + r).  ocol is the next such column (wave-uniform); columns
+    // in other waves' chunks are passed over.  Later columns are gathered in
+    // the epilogue.
+    int cnt = 0, n_ring = 0, optr = 0;
+    int64_t ocol = INT64_MAX;
+    int ocol_lane = 0x7fffffff;  // lane s: column of slot s
+    v4f_t p = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (kFused) {
+        if (g.x_out) {
+            cnt = *g.count;
+            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+        }
+        n_ring = cnt < kDecOutl ? cnt : kDecOutl;
+        for (int t = threadIdx.x; t < kRows * kDecOutl; t += 256) {
+            const int r = t / kDecOutl, s2 = t % kDecOutl;
+            xo[t] = (r < g.m && s2 < n_ring) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
+        }
+        if (lane < n_ring) ocol_lane = g.idx[lane];
+        if (n_ring > 0) ocol = __builtin_amdgcn_readfirstlane(ocol_lane);
+        __syncthreads();
+    }
+    const int arow0 = 4 * (lane >> 4);
+    auto take_outliers = [&](int64_t chunk, const int8_t* st) {
+        const int64_t c0 = chunk * kChunk;
+        while (ocol < c0 + kChunk) {
+            if (ocol >= c0) {
+                const int cb = (int)(ocol - c0);
+                const float wv = (float)st[swz(row, cb >> 4) + (cb & 15)];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r] += wv * xo[(arow0 + r) * kDecOutl + optr];
+            }
+            ++optr;
+            ocol = optr < n_ring ? (int64_t)__builtin_amdgcn_readlane(ocol_lane, optr) : INT64_MAX;
+        }
+    };
+
     for (int64_t j0 = 0; j0 < mine; j0 += kStages) {
 #pragma unroll
         for (int u = 0; u < kStages; ++u) {
@@ -126,6 +170,8 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             v4i_t wf[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) wf[t] = *reinterpret_cast<const v4i_t*>(st + swz(row, (lane >> 4) * 2 + t));
+            if constexpr (kFused)
+                if (j0 + u < mine) take_outliers(part + (j0 + u) * G, st);
             const v4i_t x0 = xr[u][0], x1 = xr[u][1];
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             issue(j0 + u + kStages - 1, (u + kStages - 1) % kStages);
@@ -138,14 +184,20 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     // sum each group's partial blocks
     if (part > 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wid * 4 + r) * 64 + lane] = acc[r];
+        for (int r = 0; r < 4; ++r) {
+            red[(wid * 4 + r) * 64 + lane] = acc[r];
+            if (kFused) pred[(wid * 4 + r) * 64 + lane] = p[r];
+        }
     }
     __syncthreads();
     if (part > 0 || !active) return;  // no barrier below
 #pragma unroll
     for (int w = 1; w < G; ++w)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += red[((wid + w) * 4 + r) * 64 + lane];
+        for (int r = 0; r < 4; ++r) {
+            acc[r] += red[((wid + w) * 4 + r) * 64 + lane];
+            if (kFused) p[r] += pred[((wid + w) * 4 + r) * 64 + lane];
+        }
 
     // acc[r] of lane l: activation row 4*(l/16) + r, weight row n0 + l%16
     const int64_t col = n0 + (lane & 15);
@@ -156,16 +208,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             if (row0 + r < g.m && col < g.n) g.c[(row0 + r) * g.ldc + col] = acc[r];
     } else {
         const float r127 = 1.0f / 127.0f;
-        int cnt = 0;
-        if (g.x_out) {
-            cnt = *g.count;
-            if (cnt > g.cap) cnt = g.cap;
-        }
-        v4f_t p = {0.0f, 0.0f, 0.0f, 0.0f};
         int64_t arow = lane & 15;
         if (arow >= g.m) arow = g.m - 1;
         const int64_t bcol = col < g.n ? col : g.n - 1;
-        for (int s0 = 0; s0 < cnt; s0 += 32) {
+        // columns past the ring's kDecOutl: gathered (kDecOutl is a multiple of 32)
+        for (int s0 = n_ring; s0 < cnt; s0 += 32) {
             const int s1 = s0 + (lane >> 4) * 8;
             const v8h xa = *reinterpret_cast<const v8h*>(g.x_out + arow * g.ldo + s1);
             v8h wb;

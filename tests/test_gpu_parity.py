@@ -203,6 +203,9 @@ FWD_CASES = [
     (2, 640, 2048, 0, 1.0, False, TAU, 8),        # no outliers
     (2, 512, 96, 0, 1.0, True, 0.0, 8),           # threshold off
     (1, 2048, 5000, 3, 1.0, True, TAU, 16),       # three weight rows per wave, the last wave short
+    # 5 <= m <= 16, or m <= 4 past the GEMV's LDS: the MFMA decode kernel (outliers from its ring)
+    (4, 13824, 300, 12, 0.5, True, TAU, 64),
+    (9, 3000, 200, 33, 1.0, False, TAU, 64),      # past the ring's 32 columns: the rest gathered
     (3, 1024, 4500, 70, 0.5, False, TAU, 128),    # several rows per wave and the gathered outliers
     (1, 96, 70, 96, 1.0, True, TAU, 96),          # every column an outlier, past the stream's 64
 ]
