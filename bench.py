@@ -236,6 +236,48 @@ def traffic_summary(directory: str, workload: str, launches: int) -> int:
     return 0
 
 
+def dequant_run(steps: int, warmup: int) -> int:
+    """The int8 vectorwise dequantize op on the 65B up-projection's weight
+    (22016 x 8192 codes -> fp16), rotated over copies past the 256 MB MALL;
+    one JSON line with its HBM roofline (bytes: codes + absmax + fp16 out)."""
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+    from synth import layer_specs
+    dev = torch.device("cuda:0")
+    spec = [s for s in layer_specs("llama65b_prefill_m4096") if s.name == "up"][0]
+    n, k = spec.n, spec.k
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.config_id * 1000 + spec.layer_id)
+    copies = 4  # 4 x 180 MB codes + 4 x 360 MB out
+    qs = [torch.randint(-127, 128, (n, k), device=dev, dtype=torch.int8, generator=gen) for _ in range(copies)]
+    ss = [torch.rand(n, device=dev, generator=gen) + 0.01 for _ in range(copies)]
+    outs = [torch.empty((n, k), device=dev, dtype=torch.float16) for _ in range(copies)]
+    for i in range(max(warmup, copies)):
+        i8.vectorwise_dequant(qs[i % copies], ss[i % copies], torch.float16, outs[i % copies])
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        i8.vectorwise_dequant(qs[i % copies], ss[i % copies], torch.float16, outs[i % copies])
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = n * k + 4 * n + 2 * n * k
+    gbs = byts / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "int8 vectorwise dequant GB/s & % HBM peak", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8->f16",
+        "data": "synthetic (seeded codes and scales)",
+        "config": {"workload": "dequant_65b_up_weight", "rows": n, "cols": k, "rotation_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(gbs / (PEAK_HBM / 1e9), 4), "traffic": None,
+                     "kernel": "vectorwise_dequant_kernel", "per_launch_us": round(us, 3)},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def copy_run(launches: int) -> int:
     """A plain copy of known size (COPY_MB MiB read, COPY_MB MiB written) for counter calibration."""
     import torch
@@ -260,8 +302,9 @@ def main() -> int:
     ap.add_argument("--graph", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "gemm", "copy"), default="bench",
-                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy")
+    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant"), default="bench",
+                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
+                         "dequant: the int8 dequantize op on a 65B weight")
     ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
@@ -284,6 +327,8 @@ def main() -> int:
         return 2
     if args.mode == "copy":
         return copy_run(args.launches)
+    if args.mode == "dequant":
+        return dequant_run(args.steps, args.warmup)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     specs, kind = workload_specs(args.workload)

@@ -163,6 +163,28 @@ i8mp_status i8mp_int8_mm_dequant(const int32_t* c, int64_t ldc, const float* row
                                  int64_t k, void* out, int64_t ldout, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
+/* int8 vectorwise dequantize (bitsandbytes PR "LLM.int8() Refactoring: Part 1",
+ * "Next steps": an int8 dequantize op), the inverse of the row-wise
+ * quantization up to the codes' rounding:
+ *
+ *   out[i,j] = q[i,j] * fl32(absmax[i] / 127)   (fp32 arithmetic: IEEE quotient,
+ *              one fp32 product), stored as fp16 (round to nearest even) or fp32
+ *
+ *   q          int8 [m x ldq], ldq >= k (e.g. codes and absmax from
+ *              i8mp_int8_vectorwise_quant, or int8 weights and their w_absmax)
+ *   absmax     fp32 [m], the rows' absmax
+ *   out_dtype  I8MP_DTYPE_F16 or I8MP_DTYPE_F32
+ *   out        fp16 or fp32 [m x ldout], ldout >= k
+ *   m == 0 or k == 0 is a no-op; leading dimensions above I8MP_MAX_LD, or an
+ *   unknown out_dtype, return I8MP_EINVAL.
+ */
+#define I8MP_DTYPE_F16 0
+#define I8MP_DTYPE_F32 1
+i8mp_status i8mp_int8_vectorwise_dequant(const int8_t* q, int64_t ldq, int64_t m, int64_t k,
+                                         const float* absmax, int32_t out_dtype, void* out, int64_t ldout,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
 /* The whole mixed-precision linear, fused: quantize + detect, extract, int8
  * MFMA GEMM with the dequant, outlier sub-matmul and bias in its epilogue.
  *

@@ -32,6 +32,7 @@ __all__ = [
     "outlier_extract",
     "linear_matmul",
     "mm_dequant",
+    "vectorwise_dequant",
     "linear",
     "linear_quantize",
     "linear_matmul_dequant",
@@ -220,6 +221,28 @@ class LinearWorkspace:
     def outlier_overflow(self) -> bool:
         """True if the last call found more outlier columns than cap (synchronizes)."""
         return int(self.count().item()) > self.cap
+
+
+def vectorwise_dequant(q: torch.Tensor, absmax: torch.Tensor, dtype: torch.dtype = torch.float16,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 vectorwise dequantize: q[i, j] * (absmax[i] / 127) in fp32, as fp16 or fp32."""
+    if dtype not in (torch.float16, torch.float32):
+        raise ValueError("dtype must be torch.float16 or torch.float32")
+    dev = _device_of(q, absmax, out)
+    ldq = _rowmajor(q, "q", torch.int8)
+    m, k = q.shape
+    _vec(absmax, "absmax", torch.float32, m)
+    if out is None:
+        out = torch.empty((m, k), dtype=dtype, device=dev)
+    ldout = _rowmajor(out, "out", dtype)
+    if tuple(out.shape) != (m, k):
+        raise ValueError("out has the wrong shape")
+    code = 0 if dtype == torch.float16 else 1
+    with torch.cuda.device(dev):
+        check(lib().i8mp_int8_vectorwise_dequant(_ptr(q), ldq, m, k, _ptr(absmax), code, _ptr(out), ldout,
+                                                 _stream(dev)),
+              "i8mp_int8_vectorwise_dequant")
+    return out
 
 
 def linear(x: torch.Tensor, w_q: torch.Tensor, w_absmax: torch.Tensor,

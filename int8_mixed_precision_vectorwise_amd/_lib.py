@@ -26,6 +26,7 @@ EXPORTS = (
     "i8mp_outlier_extract",
     "i8mp_int8_linear_matmul",
     "i8mp_int8_mm_dequant",
+    "i8mp_int8_vectorwise_dequant",
     "i8mp_linear_workspace_query",
     "i8mp_linear_quantize",
     "i8mp_linear_matmul_dequant",
@@ -78,6 +79,9 @@ def _declare(lib):
                                          c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p, c_int64,
                                          c_int64, c_void_p, c_int64, c_void_p]
     lib.i8mp_int8_mm_dequant.restype = c_int32
+    lib.i8mp_int8_vectorwise_dequant.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p,
+                                                 c_int64, c_void_p]
+    lib.i8mp_int8_vectorwise_dequant.restype = c_int32
     lib.i8mp_linear_workspace_query.argtypes = [c_int64, c_int64, c_int64, c_int32,
                                                 POINTER(LinearWorkspaceLayout)]
     lib.i8mp_linear_workspace_query.restype = c_int32

@@ -189,6 +189,26 @@ i8mp_status i8mp_int8_mm_dequant(const int32_t* c, int64_t ldc, const float* row
     return launched(launch_dequant(d, stream));
 }
 
+i8mp_status i8mp_int8_vectorwise_dequant(const int8_t* q, int64_t ldq, int64_t m, int64_t k,
+                                         const float* absmax, int32_t out_dtype, void* out, int64_t ldout,
+                                         hipStream_t stream) {
+    if (m < 0 || k < 0 || ldq < k || ldout < k || bad_ld(ldq) || bad_ld(ldout)) return I8MP_EINVAL;
+    if (out_dtype != I8MP_DTYPE_F16 && out_dtype != I8MP_DTYPE_F32) return I8MP_EINVAL;
+    if (m == 0 || k == 0) return I8MP_OK;
+    if (!q || !absmax || !out) return I8MP_EINVAL;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    VecDequantArgs d{};
+    d.q = q;
+    d.ldq = ldq;
+    d.m = m;
+    d.k = k;
+    d.absmax = absmax;
+    d.out = out;
+    d.ldout = ldout;
+    d.half_out = out_dtype == I8MP_DTYPE_F16;
+    return launched(launch_vectorwise_dequant(d, stream));
+}
+
 i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
                                         i8mp_linear_workspace* layout) {
     if (!layout || m < 0 || n < 0 || bad_k(k) || cap < 0 || bad_ld(cap)) return I8MP_EINVAL;

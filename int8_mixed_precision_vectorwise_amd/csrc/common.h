@@ -106,4 +106,14 @@ struct DequantArgs {
 
 hipError_t launch_dequant(const DequantArgs& d, hipStream_t stream);
 
+struct VecDequantArgs {
+    const int8_t* q; int64_t ldq;
+    int64_t m, k;
+    const float* absmax;
+    void* out; int64_t ldout;
+    bool half_out;                       // fp16 output, else fp32
+};
+
+hipError_t launch_vectorwise_dequant(const VecDequantArgs& d, hipStream_t stream);
+
 }  // namespace i8mp

@@ -118,6 +118,20 @@ def test_dequant_validation(L):
     assert d(FAKE, 4, FAKE, FAKE, None, 4, 4, FAKE, 7, FAKE, FAKE, 8, FAKE, 64, 64, FAKE, 4, None) == EINVAL
 
 
+def test_vectorwise_dequant_validation(L):
+    d = L.i8mp_int8_vectorwise_dequant
+    F16, F32 = 0, 1
+    assert d(FAKE, 3, 4, 4, FAKE, F16, FAKE, 4, None) == EINVAL        # ldq < k
+    assert d(FAKE, 4, 4, 4, FAKE, F16, FAKE, 3, None) == EINVAL        # ldout < k
+    assert d(FAKE, 4, 4, 4, FAKE, 2, FAKE, 4, None) == EINVAL          # unknown output type
+    assert d(FAKE, 4, -1, 4, FAKE, F16, FAKE, 4, None) == EINVAL
+    assert d(None, 4, 4, 4, FAKE, F32, FAKE, 4, None) == EINVAL        # NULL codes
+    assert d(FAKE, 4, 4, 4, FAKE, F32, None, 4, None) == EINVAL        # NULL out
+    assert d(FAKE, MAX_LD + 1, 4, 4, FAKE, F16, FAKE, 4, None) == EINVAL
+    assert d(None, 4, 0, 4, None, F16, None, 4, None) == OK           # empty
+    assert d(None, 4, 4, 0, None, F32, None, 0, None) == OK
+
+
 def test_forward_validation(L):
     f = L.i8mp_linear_forward
     lay = _lib.LinearWorkspaceLayout()

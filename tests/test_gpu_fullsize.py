@@ -89,3 +89,24 @@ def test_llama13b_decode(spec):
 @pytest.mark.parametrize("spec", P65, ids=_ids(P65))
 def test_llama65b_prefill(spec):
     _run_layer(spec)
+
+
+def test_vectorwise_dequant_65b_weight():
+    """The int8 dequantize op on the 65B up-projection's weight (22016 x 8192
+    codes, quantized on the GPU from a seeded fp16 weight): sampled rows
+    against the oracle, fp16 output (one more rounding than fp32: half an fp16
+    ulp)."""
+    spec = [s for s in layer_specs("llama65b_prefill_m4096") if s.name == "up"][0]
+    say(f"full-size dequant {spec.n}x{spec.k}")
+    L = make_layer(spec, m=1)
+    wq, ws = i8.quantize_weight(dev(L.w))
+    out = i8.vectorwise_dequant(wq, ws, torch.float16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(spec.n, seed=7)
+    ridx = torch.from_numpy(rows).cuda()
+    got = out[ridx].cpu().numpy().astype(np.float64)
+    ref = oracle.vectorwise_dequant(wq[ridx].cpu().numpy(), ws[ridx].cpu().numpy())
+    assert np.all(np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) * (1 + 2.0 ** -10) + 2.0 ** -24)
+    # the weight codes themselves are the oracle's
+    wq_ref, ws_ref = oracle.quantize_weight(L.w[rows])
+    assert_equal(wq[ridx], wq_ref, "weight codes")

@@ -352,6 +352,61 @@ def test_decode_forward_strided_x(pad):
     assert_fp16_close(out, ref.out)
 
 
+DEQ_CASES = [
+    # m, k, ldq pad, dtype
+    (1, 1, 0, "f16"),
+    (3, 17, 0, "f32"),        # ragged: a partial 16-code chunk
+    (64, 4096, 0, "f16"),
+    (64, 4096, 0, "f32"),
+    (300, 1000, 24, "f16"),   # strided codes: the element-wise path
+    (5, 7000, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DEQ_CASES, ids=lambda c: "m%d_k%d_pad%d_%s" % c)
+def test_vectorwise_dequant(case):
+    """out = q * fl32(absmax / 127) against the oracle (fp32: two fp32
+    roundings, |err| <= 2^-22 |ref|; fp16: one more, half an fp16 ulp or the
+    subnormal step), and bit for bit against the same two IEEE fp32 operations."""
+    m, k, pad, dt = case
+    rng = np.random.default_rng(m * 131 + k)
+    qfull = rng.integers(-127, 128, size=(m, k + pad), dtype=np.int8)
+    absmax = (rng.random(m) * 8 + 1e-3).astype(np.float32)
+    q = torch.from_numpy(qfull).cuda()[:, :k]
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    say(f"vectorwise_dequant m={m} k={k} pad={pad} {dt}")
+    out = i8.vectorwise_dequant(q, dev(absmax), dtype)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    ref = oracle.vectorwise_dequant(qfull[:, :k], absmax)
+    if dt == "f32":
+        assert np.all(np.abs(got - ref) <= 2.0 ** -22 * np.abs(ref))
+    else:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) * (1 + 2.0 ** -10) + 2.0 ** -24)
+    f32 = qfull[:, :k].astype(np.float32) * (absmax / np.float32(127))[:, None]
+    want = f32 if dt == "f32" else f32.astype(np.float16)
+    assert np.array_equal(host(out).view(np.uint32 if dt == "f32" else np.uint16),
+                          want.view(np.uint32 if dt == "f32" else np.uint16))
+
+
+def test_vectorwise_dequant_round_trip():
+    """Quantize then dequantize: within half a code of x (s / 254 plus the fp32
+    roundings) in every non-outlier column, 0 in outlier columns."""
+    L = make_inputs(40, 3000, 1, n_outlier=5, seed=(85, 0, 0), with_weight=False)
+    say("quant -> dequant round trip")
+    q, s_, bm = i8.vectorwise_quant(dev(L.x), TAU)
+    back = i8.vectorwise_dequant(q, s_, torch.float32)
+    torch.cuda.synchronize()
+    x = L.x.astype(np.float64)
+    sx = host(s_).astype(np.float64)
+    ref = oracle.vectorwise_quant(L.x, TAU)
+    keep = np.ones(x.shape[1], bool)
+    keep[ref.cols] = False
+    err = np.abs(host(back).astype(np.float64) - x)[:, keep]
+    assert np.all(err <= (sx / 254.0)[:, None] * (1 + 2.0 ** -12) + 1e-30)
+    assert np.all(host(back)[:, ~keep] == 0)
+
+
 def test_empty_calls_are_noops():
     say("empty calls")
     x = torch.empty((0, 64), dtype=torch.float16, device="cuda")
