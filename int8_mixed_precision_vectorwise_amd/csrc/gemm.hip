@@ -555,8 +555,14 @@ __device__ inline void wait_vm(int n) {
     }
 }
 
-template <int BM, int BN, int BKS, int STAGES, bool kFused, int MINW = 1>
-__global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
+// KS > 1: KS pipelines of 4 waves in one workgroup split the K tiles (pipe p
+// takes global tiles t KS + p), each with its own stages, in lockstep at the
+// same barriers; the accumulators meet through LDS at the end.  For grids
+// with at most one workgroup per CU, where a single pipeline leaves the CU's
+// memory pipe half idle.
+template <int BM, int BN, int BKS, int STAGES, bool kFused, int MINW = 1, int KS = 1>
+__global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
+    static_assert(KS == 1 || !stash_on<BM, BN, kFused>(), "the split pipelines do not stash");
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int NSTEP = BKS / 32;               // 32-deep MFMA steps per stage
@@ -572,21 +578,24 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     // one LDS array: the stages, then the epilogue operands (a second
     // __shared__ object makes the compiler drain every DMA before each LDS read)
     __shared__ __attribute__((aligned(1024))) int8_t
-        smem[STAGES * STAGE + sizeof(EpiLds<BM, BN>) + (stash_on<BM, BN, kFused>() ? kStash * BN * 4 : 0)];
-    EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + STAGES * STAGE);
-    int32_t* stash = reinterpret_cast<int32_t*>(smem + STAGES * STAGE + sizeof(EpiLds<BM, BN>));  // fused only
+        smem[KS * STAGES * STAGE + sizeof(EpiLds<BM, BN>) + (stash_on<BM, BN, kFused>() ? kStash * BN * 4 : 0)];
+    EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + KS * STAGES * STAGE);
+    int32_t* stash = reinterpret_cast<int32_t*>(smem + KS * STAGES * STAGE + sizeof(EpiLds<BM, BN>));  // fused only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pipe = wave_all >> 2;    // K pipeline
+    const int wave = wave_all & 3;     // wave within the pipeline
     const int wm = wave >> 1, wn = wave & 1;
+    int8_t* const pstage = smem + pipe * STAGES * STAGE;  // this pipeline's stages
 
     const int64_t tiles_m = (g.m + BM - 1) / BM;
     const int64_t tiles_n = (g.n + BN - 1) / BN;
     int64_t tm, tn;
     tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
-    epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, wave, lane);
+    if (pipe == 0) epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, wave, lane);
 
     const int64_t kr = (g.k + BKS - 1) / BKS * BKS;
     const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + kr);
@@ -606,15 +615,6 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
         const int slot = lane % LPR;
         b_off[j] = (int)(row * g.ldb + ((swz_k<BKS>(row, slot) - row * BKS)));
     }
-    auto dma = [&](int64_t kt, int stage) {
-        const int kb = (int)(kt * BKS);
-        int8_t* base = smem + stage * STAGE;
-#pragma unroll
-        for (int j = 0; j < A_INS; ++j) dma16(ra_src, base + (wave * A_INS + j) * 1024, a_off[j] + kb, 0);
-#pragma unroll
-        for (int j = 0; j < B_INS; ++j) dma16(rb_src, base + STAGE_A + (wave * B_INS + j) * 1024, b_off[j] + kb, 0);
-    };
-
     v16i acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
 
     v4i fa[2][FM], fb[2][FN];
     auto read_frags = [&](int stage, int s, int set) {
-        const int8_t* base = smem + stage * STAGE;
+        const int8_t* base = pstage + stage * STAGE;
         const int ch = 2 * s + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -667,9 +667,15 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     // again.  Issuing them keeps the instruction stream branch-free (so the DMA
     // can be interleaved with the MFMAs) and every vmcnt wait a constant.
     const __amdgpu_buffer_rsrc_t r_none = make_rsrc(g.a, 0);
-    auto dma_part = [&](int64_t kt, bool real, int stage, int first, int count) {
-        const int kb = (int)(kt * BKS);
-        int8_t* base = smem + stage * STAGE;
+    const int64_t ktiles = (g.k + BKS - 1) / BKS;
+    // pipeline step t holds global K tile t KS + pipe; every pipeline takes
+    // the same number of steps (a step past the last tile reads zeros)
+    const int64_t nsteps = (ktiles + KS - 1) / KS;
+    auto dma_part = [&](int64_t t, int stage, int first, int count) {
+        const int64_t gt = t * KS + pipe;
+        const bool real = gt < ktiles;
+        const int kb = real ? (int)(gt * BKS) : 0;
+        int8_t* base = pstage + stage * STAGE;
         const __amdgpu_buffer_rsrc_t sa = real ? ra_src : r_none;
         const __amdgpu_buffer_rsrc_t sb = real ? rb_src : r_none;
 #pragma unroll
@@ -681,9 +687,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
                 dma16(sb, base + STAGE_A + (wave * B_INS + (q - A_INS)) * 1024, b_off[q - A_INS] + kb, 0);
         }
     };
-    const int64_t ktiles = (g.k + BKS - 1) / BKS;
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) dma_part(st, st < ktiles, st, 0, INS);
+    for (int st = 0; st < STAGES - 1; ++st) dma_part(st, st, 0, INS);
     wait_vm((STAGES - 2) * INS);  // tile 0 landed (tiles 1 .. STAGES-2 may be in flight)
     barrier();                    // ... and the epilogue operands copied at the start
     read_frags(0, 0, 0);
@@ -718,15 +723,14 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
     // DMA instructions per MFMA step of this iteration
     constexpr int DMA_PER_STEP = (INS + NSTEP - 1) / NSTEP;
     constexpr int DMA_LAST = INS - (NSTEP - 1) * DMA_PER_STEP;
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
+    for (int64_t kt = 0; kt < nsteps; ++kt) {
         const int stage = (int)(kt % STAGES);
-        const int64_t nt = kt + STAGES - 1;              // tile requested in this iteration
-        const bool req = nt < ktiles;
+        const int64_t nt = kt + STAGES - 1;              // step requested in this iteration
         const int rstage = (int)(nt % STAGES);
 #pragma unroll
         for (int s = 0; s < NSTEP - 1; ++s) {
             read_frags(stage, s + 1, (s + 1) & 1);
-            dma_part(nt, req, rstage, s * DMA_PER_STEP, DMA_PER_STEP);
+            dma_part(nt, rstage, s * DMA_PER_STEP, DMA_PER_STEP);
             mfma_rows(s & 1, 0, FM);
 #pragma unroll
             for (int t = 0; t < FM + FN; ++t) {
@@ -740,15 +744,15 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
             }
         }
         constexpr int LAST = (NSTEP - 1) & 1;
-        dma_part(nt, req, rstage, (NSTEP - 1) * DMA_PER_STEP, DMA_LAST);
+        dma_part(nt, rstage, (NSTEP - 1) * DMA_PER_STEP, DMA_LAST);
         mfma_rows(LAST, 0, FM - 1);
 #pragma unroll
         for (int t = 0; t < DMA_LAST; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        if (kt + 1 < ktiles) {
-            // tiles requested after kt+1: kt+2 .. kt+STAGES-1 (real or not)
+        if (kt + 1 < nsteps) {
+            // steps requested after kt+1: kt+2 .. kt+STAGES-1 (real or not)
             wait_vm((STAGES - 2) * INS);
             barrier();  // tile kt+1 is in LDS everywhere; stage kt is no longer read
             read_frags((int)((kt + 1) % STAGES), 0, 0);
@@ -760,6 +764,35 @@ __global__ __launch_bounds__(256, MINW) void gemm_dtl_kernel(GemmArgs g) {
 
     if constexpr (stash_on<BM, BN, kFused>()) wait_vm(0);  // the stash DMA
     __syncthreads();  // no DMA in flight, K loop done everywhere, epilogue operands and stash visible
+    if constexpr (KS > 1) {
+        // pipelines 1 .. KS-1 hand their accumulators to pipeline 0 through
+        // the idle stages: [pipe - 1][wave][i][j][r][lane] int32
+        int32_t* red = reinterpret_cast<int32_t*>(smem);
+        static_assert((KS - 1) * 4 * FM * FN * 16 * 64 * 4 <= KS * STAGES * STAGE, "reduction area");
+        if (pipe > 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        red[((((pipe - 1) * 4 + wave) * FM + i) * FN + j) * 16 * 64 + r * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (pipe == 0) {
+#pragma unroll
+            for (int p = 1; p < KS; ++p)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] += red[((((p - 1) * 4 + wave) * FM + i) * FN + j) * 16 * 64 + r * 64 + lane];
+        }
+        __syncthreads();  // the area is free for the epilogue's staging
+        if (pipe > 0) return;
+    }
     epilogue<BM, BN, FM, FN, kFused, STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem, stash,
                                                       st_next);
 }
@@ -778,7 +811,16 @@ hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t
     constexpr int kFit =
         (160 * 1024 - (int)sizeof(EpiLds<BM, BN>) - (stash_on<BM, BN, kFused>() ? kStash * BN * 4 : 0)) / ((BM + BN) * 128);
     constexpr int kStages = kFit > 4 ? 4 : kFit;
-    if (staged)
+    // two K pipelines per workgroup when the grid leaves a CU per workgroup
+    // and K is long enough; their stages share the same 160 KB
+    constexpr int kFit2 = (160 * 1024 - (int)sizeof(EpiLds<BM, BN>)) / (2 * (BM + BN) * 128);
+    constexpr int kStages2 = kFit2 > 4 ? 4 : kFit2;
+    constexpr bool kCanSplit = !stash_on<BM, BN, kFused>() && kStages2 >= 2;
+    const bool split = kCanSplit && tiles <= 256 && (g.k + 127) / 128 >= 16;
+    if (staged && split) {
+        if constexpr (kCanSplit)
+            hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, 128, kStages2, kFused, 1, 2>), grid, dim3(512), 0, stream, g);
+    } else if (staged)
         hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, 128, kStages, kFused>), grid, dim3(256), 0, stream, g);
     else if (aligned)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, kFused, true>), grid, dim3(256), 0, stream, g);

@@ -123,7 +123,8 @@ def test_quant_workspace_reuse(m, k):
 
 MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128), (300, 600, 300),
              (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100),
-             (3, 777, 1280), (2, 513, 640), (4, 100, 13824)]
+             (3, 777, 1280), (2, 513, 640), (4, 100, 13824),
+             (200, 300, 2560), (130, 190, 2176)]  # two K pipelines per workgroup (17 K tiles: one pipeline's last is empty)
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -189,6 +190,7 @@ FWD_CASES = [
     (3, 33, 5, 2, 1.0, True, TAU, 8),
     (300, 520, 600, 11, 0.3, True, TAU, 64),
     (257, 1000, 259, 5, 1.0, False, TAU, 32),
+    (40, 2100, 300, 5, 1.0, True, TAU, 32),       # two K pipelines, 17 K tiles
     (64, 256, 512, 0, 1.0, True, TAU, 32),        # no outliers present
     (40, 300, 100, 3, 1.0, True, 0.0, 32),        # threshold off
     (12, 96, 70, 96, 1.0, True, TAU, 96),         # every column an outlier
