@@ -117,6 +117,13 @@ constexpr int kEpiIdx = 64;
 constexpr int kStash = 24;
 template <int BM, int BN, bool kFused>
 constexpr bool stash_on() { return kFused && BM == 256 && BN == 256; }
+
+// MFMA steps of a pipelined iteration over which the DMA of the tile it
+// requests is spread.  With two stages that tile is waited for at the end of
+// the same iteration, so its DMA goes out in the first two steps (more bytes
+// in flight on average); deeper pipelines spread it over every step.
+template <int STAGES, int NSTEP>
+constexpr int dma_steps() { return STAGES == 2 && NSTEP > 2 ? 2 : NSTEP; }
 template <int BM, int BN>
 struct __attribute__((aligned(16))) EpiLds {
     float sx[BM];
@@ -204,6 +211,51 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
         const int wave = (wr0 / (FM * 32)) * 2 + wc0 / WN;
         int8_t* area = stage + wave * (IC * 32 * kPitch);
         const bool vec_ok = (g.ldout & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+
+        // The operands of the first 16 outlier slots are copied to LDS before
+        // the conversion, so that their latency hides behind it: the wave's
+        // X_O rows (fp16 [FM*32][16]; X_O is zero past the count) and, for
+        // slots the stash does not hold, the weight bytes of its columns (one
+        // zero-extended dword each, [16][WN]).  Each wave has a private area:
+        // in the idle K stages past the output staging, or where that does not
+        // fit, at the start of its own staging area (one row chunk only: the
+        // wave reads the copies before it writes its results there).
+        constexpr int kXoOff = (4 * IC * 32 * kPitch + 1023) / 1024 * 1024;
+        constexpr int kXoBytes = FM * 32 * 16 * 2;
+        constexpr int kPreBytes = kXoBytes + 16 * WN * 4;
+        constexpr bool kSep = kXoOff + 4 * kPreBytes <= kStageBytes;
+        static_assert(kSep || (IC == FM && kPreBytes <= IC * 32 * kPitch), "outlier operands do not fit the K stages");
+        int8_t* const pre = kSep ? stage + kXoOff + wave * kPreBytes : area;
+        const int32_t* const pre_w = reinterpret_cast<const int32_t*>(pre + kXoBytes);
+        // the 256 x 256 tile's weight bytes come from its stash instead
+        constexpr bool kPreW = !(BM == 256 && BN == 256);
+        constexpr int kWIns = 16 * WN / 64;   // weight-byte copies: entry q*64 + lane -> slot, column
+        const int npre = cnt < 16 ? cnt : 16;
+        const bool pre_ok = kPreW || npre <= n_stash;   // every slot below npre has LDS operands
+        if (npre > 0) {
+            int ixv[kPreW ? kWIns : 1];
+            if constexpr (kPreW) {
+                // index reads first: an LDS read issued after a copy to LDS waits for it
+#pragma unroll
+                for (int q = 0; q < kWIns; ++q) ixv[q] = e.idx[(q * 64 + lane) / WN];
+            }
+#pragma unroll
+            for (int q = 0; q < FM; ++q)   // 32 rows per instruction: lane -> row lane / 2, half lane % 2
+                dma16(rxo, pre + q * 1024, ((wr0 + q * 32 + (lane >> 1)) * (int)g.ldo + 8 * (lane & 1)) * 2, 0);
+            if constexpr (kPreW) {
+                if (npre > n_stash) {
+#pragma unroll
+                    for (int q = 0; q < kWIns; ++q) {
+                        const int ent = q * 64 + lane, slot = ent / WN;
+                        const int off = slot < npre && slot >= n_stash ? (wc0 + ent % WN) * (int)g.ldb + ixv[q]
+                                                                      : (int)0x80000000;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rw, (__attribute__((address_space(3))) void*)(pre + kXoBytes + q * 256), 1, off, 0, 0,
+                            0);
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int ic = 0; ic < FM; ic += IC) {
             v16f f[IC][FN];
@@ -223,8 +275,38 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
                     for (int r = 0; r < 16; ++r) f[ii][j][r] = (float)acc[i][j][r] * sxr[r];
             }
 
+            if (ic == 0 && npre > 0) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the LDS copies landed
             for (int s0 = 0; s0 < cnt; s0 += 16) {
                 const int sb = s0 + 8 * hi;   // this lane's 8 outlier slots
+                if (s0 == 0 && pre_ok) {
+                    // the slots copied to LDS above (and the stash)
+                    v8h xa[IC];
+#pragma unroll
+                    for (int ii = 0; ii < IC; ++ii)
+                        xa[ii] = *reinterpret_cast<const v8h*>(pre + (32 * (ic + ii) + l32) * 32 + hi * 16);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int lc = 32 * j + l32;
+                        v8h wb;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            // the copies hold zeros past npre; the stash holds npre <= n_stash slots
+                            const int slot = sb + t;
+                            int32_t w;
+                            if constexpr (kPreW) {
+                                w = pre_w[slot * WN + lc];
+                            } else {
+                                const int32_t v = stash[slot * BN + wc0 + lc];
+                                w = slot < npre ? v : 0;
+                            }
+                            wb[t] = (_Float16)(float)(int8_t)(uint8_t)(uint32_t)w;
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < IC; ++ii)
+                            f[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[ii], wb, f[ii][j], 0, 0, 0);
+                    }
+                    continue;
+                }
                 int ix[8];
                 if (s0 + 16 <= kEpiIdx) {
 #pragma unroll
@@ -720,9 +802,35 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
         }
     };
     if constexpr (stash_on<BM, BN, kFused>()) stash_upto((int64_t)(STAGES - 1) * BKS);  // the tiles requested so far
-    // DMA instructions per MFMA step of this iteration
-    constexpr int DMA_PER_STEP = (INS + NSTEP - 1) / NSTEP;
-    constexpr int DMA_LAST = INS - (NSTEP - 1) * DMA_PER_STEP;
+    // The DMA instructions of the tile requested in an iteration go out over
+    // its first DSTEPS MFMA steps, DPS per step, each next to an MFMA.
+    constexpr int DSTEPS = dma_steps<STAGES, NSTEP>();
+    constexpr int DPS = (INS + DSTEPS - 1) / DSTEPS;
+    auto dma_count = [](int s) { const int c = INS - s * DPS; return c < 0 ? 0 : (c > DPS ? DPS : c); };
+    // one step's order: MFMAs paired with its fragment reads, then with its
+    // DMA; MFMA, fragment read and DMA triples where front-loaded DMA makes
+    // more of them than MFMAs
+    auto schedule_step = [](int nvm) {
+        if (DSTEPS == NSTEP || FM + FN + nvm <= FM * FN) {
+#pragma unroll
+            for (int t = 0; t < FM + FN; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < nvm; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < FM * FN; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (t < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (t < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+    };
     for (int64_t kt = 0; kt < nsteps; ++kt) {
         const int stage = (int)(kt % STAGES);
         const int64_t nt = kt + STAGES - 1;              // step requested in this iteration
@@ -730,24 +838,15 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
 #pragma unroll
         for (int s = 0; s < NSTEP - 1; ++s) {
             read_frags(stage, s + 1, (s + 1) & 1);
-            dma_part(nt, rstage, s * DMA_PER_STEP, DMA_PER_STEP);
+            dma_part(nt, rstage, s * DPS, dma_count(s));
             mfma_rows(s & 1, 0, FM);
-#pragma unroll
-            for (int t = 0; t < FM + FN; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int t = 0; t < DMA_PER_STEP; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
+            schedule_step(dma_count(s));
         }
         constexpr int LAST = (NSTEP - 1) & 1;
-        dma_part(nt, rstage, (NSTEP - 1) * DMA_PER_STEP, DMA_LAST);
+        dma_part(nt, rstage, (NSTEP - 1) * DPS, dma_count(NSTEP - 1));
         mfma_rows(LAST, 0, FM - 1);
 #pragma unroll
-        for (int t = 0; t < DMA_LAST; ++t) {
+        for (int t = 0; t < dma_count(NSTEP - 1); ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
