@@ -22,7 +22,7 @@
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that each XCD works on a contiguous run of tiles (sharing
-// operand rows in its own L2), walked in groups of kGroupM tile rows.
+// operand rows in its own L2), walked in groups of group_m tile rows.
 #include <stdint.h>
 
 #include "common.h"
@@ -32,8 +32,13 @@ namespace i8mp {
 namespace {
 
 constexpr int BK = 128;
-constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
+
+// Tile rows per group of the launch order.  An XCD runs 32 of its tiles at a
+// time: a group of r rows walks them r x 32/r, and the K stage of those tiles
+// touches r A blocks of BM rows and 32/r B blocks of BN rows.
+template <int BM, int BN>
+constexpr int group_m() { return BM > BN ? 4 : 8; }
 constexpr int kRsrcWord3 = 0x00020000;
 
 
@@ -73,6 +78,7 @@ __device__ inline v4i load16_bytes(const int8_t* __restrict__ base, int64_t ld, 
     return r;
 }
 
+template <int kGroupM>
 __device__ inline void tile_coords(int64_t bid, int64_t nblocks, int64_t tiles_m, int64_t tiles_n,
                                    int64_t& tm, int64_t& tn) {
     const int64_t full = (nblocks / kXcds) * kXcds;
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     const int64_t tiles_m = (g.m + BM - 1) / BM;
     const int64_t tiles_n = (g.n + BN - 1) / BN;
     int64_t tm, tn;
-    tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_coords<group_m<BM, BN>()>(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
     epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, __builtin_amdgcn_readfirstlane(wave), lane);
 
@@ -675,7 +681,7 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
     const int64_t tiles_m = (g.m + BM - 1) / BM;
     const int64_t tiles_n = (g.n + BN - 1) / BN;
     int64_t tm, tn;
-    tile_coords(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_coords<group_m<BM, BN>()>(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
     if (pipe == 0) epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, wave, lane);
 
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
         __syncthreads();  // the area is free for the epilogue's staging
         if (pipe > 0) return;
     }
-    epilogue<BM, BN, FM, FN, kFused, STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem, stash,
+    epilogue<BM, BN, FM, FN, kFused, KS * STAGES * STAGE>(g, acc, m0, n0, wm * WM, wn * WN, lane, epi, smem, stash,
                                                       st_next);
 }
 
