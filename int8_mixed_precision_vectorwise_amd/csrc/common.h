@@ -23,7 +23,6 @@ __device__ inline half_bits f2h(float f) { return __builtin_bit_cast(half_bits, 
 
 // ---- outlier detection and quantization -------------------------------------
 constexpr int kQuantThreads = 256;
-constexpr int kDetectCols = 256;      // columns per detect workgroup (32 lanes x 8 fp16)
 constexpr int kMaxRowBlocks = 8;      // partial bitmaps written by the detect pass
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -10,7 +10,7 @@
 // A row's scale excludes every outlier column and the outlier set is a
 // property of all rows, so every row waits for one global view of the outlier
 // columns; the work is split at that point:
-//   detect_kernel  one pass over x: per (row block, 256 columns) workgroup, a
+//   detect_kernel  one pass over x: per (row block, 256 or 64 columns) workgroup, a
 //                  word per 32 columns of the row block's partial bitmap
 //                  (every word written, no atomics, at most 8 row blocks);
 //   quant_kernel   ORs the partial bitmaps into LDS, then quantizes one row per
@@ -45,18 +45,21 @@ bool vector_rows(const QuantArgs& a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// detect: per (RB rows, 256 columns) workgroup, the OR of the rows' outlier
+// detect: per (RB rows, 8 CG columns) workgroup, the OR of the rows' outlier
 // bits, written to the row block's partial bitmap (every word, no atomics).
-template <bool kVec>
+// CG lanes read one row's 16 CG-byte segment, 256 / CG rows at a time: 256
+// columns (512-byte segments) where that fills the GPU, else 64 columns
+// (128-byte segments, four times the workgroups).
+template <bool kVec, int CG>
 __global__ __launch_bounds__(256) void detect_kernel(const half_bits* __restrict__ x, int64_t m, int64_t k,
                                                      int64_t ldx, float tau, int64_t rows_per_block,
                                                      int64_t words, uint32_t* __restrict__ partial) {
+    constexpr int RL = 256 / CG;         // rows read together (CG groups of 8 columns per row)
+    static_assert(CG % 4 == 0 && 256 % CG == 0, "whole bitmap words per workgroup");
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int cg = tid & 31;  // group of 8 columns
-    const int rsub = tid >> 5;
-    const int64_t col0 = (int64_t)blockIdx.x * kDetectCols + cg * 8;
+    const int cg = tid % CG;
+    const int rsub = tid / CG;
+    const int64_t col0 = (int64_t)blockIdx.x * (8 * CG) + cg * 8;
     const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
     int64_t r_end = r_begin + rows_per_block;
     if (r_end > m) r_end = m;
@@ -65,26 +68,26 @@ __global__ __launch_bounds__(256) void detect_kernel(const half_bits* __restrict
     if (col0 < k) {
         if (kVec && col0 + 8 <= k) {
 #pragma unroll 8
-            for (int64_t r = r_begin + rsub; r < r_end; r += 8)
+            for (int64_t r = r_begin + rsub; r < r_end; r += RL)
                 mask |= outlier_bits8(*reinterpret_cast<const uint4*>(x + r * ldx + col0), tau);
         } else {
-            for (int64_t r = r_begin + rsub; r < r_end; r += 8)
+            for (int64_t r = r_begin + rsub; r < r_end; r += RL)
                 mask |= outlier_bits8(load8<false>(x + r * ldx, col0, k), tau);
         }
     }
-    mask |= __shfl_xor(mask, 32, 64);  // lanes l and l^32 hold the same columns
-    __shared__ uint32_t red[4][32];
-    if (lane < 32) red[wave][lane] = mask;
+    __shared__ uint32_t red[256];
+    red[tid] = mask;
     __syncthreads();
-    if (tid < 8) {
+    if (tid < CG / 4) {
         uint32_t word = 0;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int g = tid * 4 + q4;
-            const uint32_t mm = red[0][g] | red[1][g] | red[2][g] | red[3][g];
+            uint32_t mm = 0;
+            for (int q = 0; q < RL; ++q) mm |= red[q * CG + g];
             word |= (mm & 0xffu) << (8 * q4);
         }
-        const int64_t w = (int64_t)blockIdx.x * 8 + tid;
+        const int64_t w = (int64_t)blockIdx.x * (CG / 4) + tid;
         if (w < words) partial[(int64_t)blockIdx.y * words + w] = word;
     }
 }
@@ -124,13 +127,24 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
             v[c] = ch < nchunks ? load8<kVec>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
         }
     };
+    // the first 2048 partial bitmap words are requested before the row's
+    // batch, so that the bitmap work waits for them only, not for x
+    const int64_t total_words = outl ? a.row_blocks * a.words : 0;
+    uint32_t pw0[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t f = tid + 256 * u;
+        pw0[u] = f < total_words ? a.bitmap_in[f] : 0u;
+    }
     if (preload) load_batch(a.x + r_first * a.ldx, 0);
 
     if (outl) {
         for (int64_t w = tid; w < a.words; w += 256) bm[w] = 0u;
         __syncthreads();
-        const int64_t total_words = a.row_blocks * a.words;
-        for (int64_t f0 = tid; f0 < total_words; f0 += 256 * 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (pw0[u]) atomicOr(&bm[(tid + 256 * u) % a.words], pw0[u]);
+        for (int64_t f0 = tid + 256 * 8; f0 < total_words; f0 += 256 * 8) {
             uint32_t pw[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -393,21 +407,32 @@ hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
         return vec ? launch_small<true>(a, per_thread, lds, stream) : launch_small<false>(a, per_thread, lds, stream);
     }
     if (a.threshold > 0.0f && a.m > 0) {
-        // detect: 256 columns x RB rows per workgroup, at most kMaxRowBlocks
-        // row blocks (RB >= 8), about 1024 workgroups when the shape allows
-        const int64_t gx = ceil_div(a.k, kDetectCols);
-        int64_t gy = ceil_div(1024, gx);
-        if (gy > kMaxRowBlocks) gy = kMaxRowBlocks;
-        if (gy > ceil_div(a.m, 8)) gy = ceil_div(a.m, 8);
-        if (gy < 1) gy = 1;
+        // detect: 256 or 64 columns x RB rows per workgroup, at most
+        // kMaxRowBlocks row blocks (RB >= 8), about 1024 workgroups when the
+        // shape allows
+        auto row_blocks = [&](int64_t gx) {
+            int64_t gy = ceil_div(1024, gx);
+            if (gy > kMaxRowBlocks) gy = kMaxRowBlocks;
+            if (gy > ceil_div(a.m, 8)) gy = ceil_div(a.m, 8);
+            return gy < 1 ? (int64_t)1 : gy;
+        };
+        const bool narrow = ceil_div(a.k, 256) * row_blocks(ceil_div(a.k, 256)) < 256;
+        const int64_t gx = ceil_div(a.k, narrow ? 64 : 256);
+        int64_t gy = row_blocks(gx);
         const int64_t rb = round_up(ceil_div(a.m, gy), 8);
         gy = ceil_div(a.m, rb);
         const dim3 grid((unsigned)gx, (unsigned)gy);
-        if (vec)
-            hipLaunchKernelGGL(detect_kernel<true>, grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx, a.threshold, rb,
-                               a.words, a.partial);
+        if (vec && narrow)
+            hipLaunchKernelGGL((detect_kernel<true, 8>), grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx, a.threshold,
+                               rb, a.words, a.partial);
+        else if (vec)
+            hipLaunchKernelGGL((detect_kernel<true, 32>), grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx,
+                               a.threshold, rb, a.words, a.partial);
+        else if (narrow)
+            hipLaunchKernelGGL((detect_kernel<false, 8>), grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx,
+                               a.threshold, rb, a.words, a.partial);
         else
-            hipLaunchKernelGGL(detect_kernel<false>, grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx,
+            hipLaunchKernelGGL((detect_kernel<false, 32>), grid, dim3(256), 0, stream, a.x, a.m, a.k, a.ldx,
                                a.threshold, rb, a.words, a.partial);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -232,13 +232,23 @@ __device__ inline uint4 mask_outliers(const uint4& v, uint32_t ob) {
 // product rounds into [-127, 127] and the clamp of the code definition never
 // acts; inv = 0 (a zero row) gives 0.
 __device__ inline uint2 codes8_plain(const uint4& v, float inv) {
-    uint32_t w[2] = {0u, 0u};
+    // p = fl32(x * inv) has |p| <= 127, so fl32(p + 1.5 * 2^23) is p rounded
+    // to the nearest integer, ties to even (the ulp there is 1), held in the
+    // low mantissa bits: the low byte is the code.  The multiply and the add
+    // must stay two roundings (no fused multiply-add).
+#pragma clang fp contract(off)
+    uint32_t b[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int q = (int)__builtin_rintf(h2f(half_at(v, e)) * inv);
-        w[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+        const float p = h2f(half_at(v, e)) * inv;
+        b[e] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
     }
-    return make_uint2(w[0], w[1]);
+    // byte selects: low bytes of (b1, b0) to bytes 1, 0; then two such halves
+    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+    return make_uint2(lo, hi);
 }
 
 }  // namespace i8mp
