@@ -196,6 +196,12 @@ FWD_CASES = [
     (12, 96, 70, 96, 1.0, True, TAU, 96),         # every column an outlier
     (4, 5120, 1000, 8, 1.0, False, TAU, 256),     # decode-shaped
     (16, 2048, 512, 40, 0.5, False, TAU, 64),     # more outliers than one fp16 MFMA step
+    # prefill tiles past the 16 outlier slots copied to LDS before the epilogue
+    (1536, 384, 6144, 20, 0.5, True, TAU, 64),    # 256 x 256: slots 16..19 from the stash
+    (1536, 256, 6144, 40, 0.5, False, TAU, 64),   # 256 x 256: slots 24..39 gathered
+    (768, 256, 6144, 30, 0.5, True, TAU, 64),     # 256 x 128: slots 16..29 gathered
+    (768, 256, 3072, 17, 1.0, False, TAU, 32),    # 128 x 128: one slot past 16
+    (256, 256, 6144, 16, 0.5, True, TAU, 16),     # 128 x 64: exactly 16 slots, cap 16
     # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
     (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
     (2, 4096, 264, 5, 0.5, False, TAU, 32),
