@@ -291,20 +291,24 @@ struct GvQuantLds {
 // The a.m <= M rows of x as 8-column chunks f = tid + T i (row-major over the
 // rows, T threads) into registers: v[i] and rc[i] = row << 16 | chunk.  With k
 // a multiple of 8 and 16-byte aligned rows every chunk is one 16-byte load;
-// all L loads are issued before any is used (a chunk past the end re-reads
-// chunk 0 and is zeroed after), so they are in flight together.
+// all L loads are issued before any is used (a chunk past the end reads
+// zeros through the range check), so they are in flight together.
 template <int L, int T>
 __device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L], uint32_t (&rc)[L]) {
     const int tid = threadIdx.x;
     const int32_t cpr = (int32_t)(a.k / 8);
     const int32_t total_chunks = (int32_t)a.m * cpr;
-    int64_t off[L];
+    // chunks past the rows read through the range check as zeros: zeroing the
+    // registers after the loads would wait for them before anything else is issued
+    const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, ((int64_t)(a.m - 1) * a.ldx + a.k) * 2);
+    int off[L];
     {
         int32_t r = tid / cpr, c = tid - r * cpr;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             rc[i] = ((uint32_t)r << 16) | (uint32_t)c;  // chunks < 4096 here
-            off[i] = tid + T * i < total_chunks ? (int64_t)r * a.ldx + (int64_t)c * 8 : 0;
+            // byte offsets < 2^31: m <= 4 rows of at most I8MP_MAX_LD elements
+            off[i] = tid + T * i < total_chunks ? (int)(((int64_t)r * a.ldx + (int64_t)c * 8) * 2) : (int)0x80000000;
             c += T;
             while (c >= cpr) {
                 c -= cpr;
@@ -313,10 +317,7 @@ __device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L], uint32_t
         }
     }
 #pragma unroll
-    for (int i = 0; i < L; ++i) v[i] = *reinterpret_cast<const uint4*>(a.x + off[i]);
-#pragma unroll
-    for (int i = 0; i < L; ++i)
-        if (tid + T * i >= total_chunks) v[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < L; ++i) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off[i], 0, 0));
 }
 
 // Quantize the chunks of load_x_chunks into the LDS activation rows xs
@@ -542,58 +543,100 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
                                                   rw, (c0 + u) * kGvChunk + lane * 16, 0, kWeightPolicy));
     };
     v4i_t w[2][kGvBatch];
-    // x first in the one-launch forward, so that its wait does not include
-    // the weight loads (loads complete in order)
+    // Every small load goes out before the weight stream, so that the waits
+    // of the prologue count only them (loads complete in order): x (one-launch
+    // forward) or the codes and the outlier list (unfused), and the epilogue
+    // operands of the wave's rows (lane i: the wave's row i).  Then the first
+    // weight batch streams while the prologue runs (a second one in flight
+    // there measured slower).
     constexpr int kXL = kQuant ? kQuantL : 1;
     uint4 xv[kXL];
     uint32_t xrc[kXL];
     if constexpr (kQuant) load_x_chunks<kXL, 64 * W>(qa, xv, xrc);
+    // unfused: the codes (M rows of kx bytes, at most 32 KB: 16-byte chunks f =
+    // tid + 64 W i), the first kGvOutl outlier columns and their x values
+    constexpr int kCL = kQuant ? 1 : (32 * 1024 / 16 + 64 * W - 1) / (64 * W);
+    v4i_t cv[kCL];
+    // (raw load results only: converting them here would wait for the load
+    // before the weight batches go out)
+    int32_t idx_t = 0x7fffffff;
+    uint32_t oval_bits = 0;
+    int cnt = 0;
+    const int64_t per_row = kx / 16;
+    if constexpr (!kQuant) {
+        // the codes' rows hold zeros from k to a multiple of 128 (lda >= that)
+        const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
+        const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
+        const int pr = (int)per_row;   // <= 2048
+        int r = (int)threadIdx.x / pr, c = (int)threadIdx.x - r * pr;
+#pragma unroll
+        for (int i = 0; i < kCL; ++i) {
+            const int f = (int)threadIdx.x + 64 * W * i;
+            const int off = (f < M * pr && r < g.m && (int64_t)c * 16 < kr) ? (int)(r * g.lda + c * 16) : (int)0x80000000;
+            cv[i] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            c += 64 * W;   // the next chunk of this thread: row and chunk without a division
+            while (c >= pr) {
+                c -= pr;
+                ++r;
+            }
+        }
+        if (kFused && g.x_out) {
+            cnt = *g.count;
+            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+            // thread t < kGvOutl: idx[t]; thread t < M kGvOutl: x_out[t / kGvOutl, t % kGvOutl]
+            // (past cap or m: zeros through the range checks; masked by the count below)
+            const int t = threadIdx.x;
+            const __amdgpu_buffer_rsrc_t ri = rsrc(g.idx, (int64_t)g.cap * 4);
+            const __amdgpu_buffer_rsrc_t ro = rsrc(g.x_out, (int64_t)g.m * g.ldo * 2);
+            const int r = t / kGvOutl, s2 = t % kGvOutl;
+            idx_t = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, t < kGvOutl ? t * 4 : (int)0x80000000, 0, 0);
+            oval_bits = __builtin_amdgcn_raw_buffer_load_b16(
+                ro, t < M * kGvOutl && r < g.m ? (int)((r * g.ldo + s2) * 2) : (int)0x80000000, 0, 0);
+        }
+    }
+    const float r127 = 1.0f / 127.0f;
+    uint32_t sw_bits = 0, bias_bits = 0;
+    if constexpr (kFused) {
+        const int64_t nl = row_of(lane);
+        const bool own = lane < R && nl < g.n;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(g.col_absmax, g.n * 4);
+        const __amdgpu_buffer_rsrc_t rb = rsrc(g.bias, g.bias ? g.n * 2 : 0);
+        sw_bits = __builtin_amdgcn_raw_buffer_load_b32(rs, own ? (int)(nl * 4) : (int)0x80000000, 0, 0);
+        bias_bits = __builtin_amdgcn_raw_buffer_load_b16(rb, own ? (int)(nl * 2) : (int)0x80000000, 0, 0);
+    }
     issue(0, w[0]);
+    // keeps the compiler from converting the x value right after its load
+    // (a wait ahead of the weight batches)
+    asm volatile("" : "+v"(oval_bits));
+    const float sw_lane = __uint_as_float(sw_bits) * r127;
+    const float bias_lane = h2f((half_bits)bias_bits);
 
     // activations (rows >= m and bytes past K as zeros), outlier columns / values
-    int cnt = 0;
     if constexpr (kQuant) {
         const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kx, xs, oidx, oval, ql);
         cnt = total < qa.cap ? total : qa.cap;
         __syncthreads();
         publish_spread<M, 64 * W>(qa, kx, xs, ql, oidx, oval, total > 0, total, cnt);
     } else {
-        // the codes' rows hold zeros from k to a multiple of 128 (lda >= that)
-        const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
-        const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
-        const int64_t per_row = kx / 16;
-        for (int64_t f = threadIdx.x; f < M * per_row; f += 64 * W) {
-            const int64_t r = f / per_row, c = f - r * per_row;
-            v4i_t v = {0, 0, 0, 0};
-            if (r < g.m && c * 16 < kr)
-                v = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(r * g.lda + c * 16), 0, 0));
-            *reinterpret_cast<v4i_t*>(xs + r * kx + c * 16) = v;
+#pragma unroll
+        for (int i = 0; i < kCL; ++i) {
+            const int f = (int)threadIdx.x + 64 * W * i;
+            if (f < M * (int)per_row) *reinterpret_cast<v4i_t*>(xs + f * 16) = cv[i];  // row f / per_row, chunk f % per_row
         }
         if (kFused && g.x_out) {
-            cnt = *g.count;
-            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
-            const int lc = cnt < kGvOutl ? cnt : kGvOutl;
-            for (int t = threadIdx.x; t < kGvOutl; t += 64 * W) oidx[t] = t < lc ? g.idx[t] : 0x7fffffff;
-            for (int t = threadIdx.x; t < M * kGvOutl; t += 64 * W) {
-                const int r = t / kGvOutl, s2 = t % kGvOutl;
-                oval[t] = (s2 < lc && r < g.m) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
-            }
+            const int lc0 = cnt < kGvOutl ? cnt : kGvOutl;
+            const int t = threadIdx.x;
+            if (t < kGvOutl) oidx[t] = t < lc0 ? idx_t : 0x7fffffff;
+            if (t < M * kGvOutl) oval[t] = t % kGvOutl < lc0 ? h2f((half_bits)oval_bits) : 0.0f;
+        } else {
+            for (int t = threadIdx.x; t < kGvOutl; t += 64 * W) oidx[t] = 0x7fffffff;
+            for (int t = threadIdx.x; t < M * kGvOutl; t += 64 * W) oval[t] = 0.0f;
         }
     }
     __syncthreads();
     const int lc = cnt < kGvOutl ? cnt : kGvOutl;
-    // epilogue operands of the wave's rows (lane i: the wave's row i) and the
-    // activation scales, loaded before the stream: a load at the end of a row
-    // would wait for every weight load in flight (loads complete in order)
-    const float r127 = 1.0f / 127.0f;
-    float sw_lane = 0.0f, bias_lane = 0.0f;
     float sx[M];
     if constexpr (kFused) {
-        const int64_t nl = row_of(lane);
-        if (lane < R && nl < g.n) {
-            sw_lane = g.col_absmax[nl] * r127;
-            bias_lane = g.bias ? h2f(g.bias[nl]) : 0.0f;
-        }
 #pragma unroll
         for (int r = 0; r < M; ++r)
             sx[r] = r < g.m ? (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127 : 0.0f;
@@ -757,6 +800,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
         if (c0 + kGvBatch >= nck) finish_row(rr);
     };
 
+    // batches b and b + 1 in flight while b is consumed
     for (int b = 0; b < nb; b += 2) {
         issue(b + 1, w[1]);
         consume(b, w[0]);
