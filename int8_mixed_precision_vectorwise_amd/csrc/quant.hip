@@ -127,24 +127,13 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
             v[c] = ch < nchunks ? load8<kVec>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
         }
     };
-    // the first 2048 partial bitmap words are requested before the row's
-    // batch, so that the bitmap work waits for them only, not for x
-    const int64_t total_words = outl ? a.row_blocks * a.words : 0;
-    uint32_t pw0[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int64_t f = tid + 256 * u;
-        pw0[u] = f < total_words ? a.bitmap_in[f] : 0u;
-    }
     if (preload) load_batch(a.x + r_first * a.ldx, 0);
 
     if (outl) {
         for (int64_t w = tid; w < a.words; w += 256) bm[w] = 0u;
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (pw0[u]) atomicOr(&bm[(tid + 256 * u) % a.words], pw0[u]);
-        for (int64_t f0 = tid + 256 * 8; f0 < total_words; f0 += 256 * 8) {
+        const int64_t total_words = a.row_blocks * a.words;
+        for (int64_t f0 = tid; f0 < total_words; f0 += 256 * 8) {
             uint32_t pw[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
