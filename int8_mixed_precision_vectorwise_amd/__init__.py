@@ -25,9 +25,12 @@ from ._lib import (  # noqa: F401
     lib,
     status_string,
 )
+from .serialize import load_int8_weights, save_int8_weights  # noqa: F401
 
 __all__ = [
     "quantize_weight",
+    "save_int8_weights",
+    "load_int8_weights",
     "vectorwise_quant",
     "outlier_extract",
     "linear_matmul",

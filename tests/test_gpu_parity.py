@@ -261,6 +261,25 @@ def test_linear_forward_gpu_quantized_weights():
     assert_fp16_close(out, ref.out)
 
 
+def test_saved_int8_weights_reload_bit_exact(tmp_path):
+    """Weight state quantized on the GPU, saved with its row absmax, read back
+    onto the GPU: the same tensors, and the forward from them is the same."""
+    L = make_inputs(40, 520, 300, n_outlier=4, bias_std=0.01, seed=(76, 1, 0))
+    say("save / load int8 weights")
+    wq_g, ws_g = i8.quantize_weight(dev(L.w))
+    path = str(tmp_path / "w.safetensors")
+    i8.save_int8_weights(path, {"layer": (wq_g, ws_g)})
+    wq_l, ws_l = i8.load_int8_weights(path, device="cuda")["layer"]
+    assert wq_l.device.type == "cuda" and torch.equal(wq_l, wq_g) and torch.equal(ws_l, ws_g)
+    out_a = i8.linear(dev(L.x), wq_g, ws_g, dev(L.bias), TAU, 32)
+    out_b = i8.linear(dev(L.x), wq_l, ws_l, dev(L.bias), TAU, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    wq, ws = oracle.quantize_weight(L.w)
+    assert_equal(wq_l, wq, "weight codes")
+    assert_equal(ws_l, ws, "weight row absmax")
+
+
 def test_linear_forward_zero_rows_and_zero_input():
     L = make_inputs(20, 256, 130, n_outlier=2, bias_std=0.01, seed=(77, 0, 0))
     L.x[[0, 7, 19]] = 0
