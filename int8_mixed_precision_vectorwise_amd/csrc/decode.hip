@@ -596,6 +596,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     }
     const float r127 = 1.0f / 127.0f;
     uint32_t sw_bits = 0, bias_bits = 0;
+    float sx_raw[M];   // unfused: the row absmax of x, read before the stream too
+#pragma unroll
+    for (int r = 0; r < M; ++r) sx_raw[r] = (kFused && !kQuant && r < g.m) ? g.row_absmax[r] : 0.0f;
     if constexpr (kFused) {
         const int64_t nl = row_of(lane);
         const bool own = lane < R && nl < g.n;
@@ -639,7 +642,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     if constexpr (kFused) {
 #pragma unroll
         for (int r = 0; r < M; ++r)
-            sx[r] = r < g.m ? (kQuant ? __uint_as_float(ql.rmax[r]) : g.row_absmax[r]) * r127 : 0.0f;
+            sx[r] = r < g.m ? (kQuant ? __uint_as_float(ql.rmax[r]) : sx_raw[r]) * r127 : 0.0f;
     }
     // The streamed outlier columns: column j of a chunk sits in lane
     // (j % 1024) / 16, byte j % 16, of every row's load of chunk j / 1024.
@@ -656,13 +659,21 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     uint64_t spill = 0;
     uint32_t chunks_hit = 0;
     const int ocol = lane < lc ? oidx[lane] : 0x7fffffff;  // lane s: column of slot s
+    // the counters and slot tables are the wave's own: ordering its LDS
+    // accesses is enough, no workgroup barrier
+    auto wave_lds_sync = [] {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS accesses are done
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
     if constexpr (kFused) {
         int32_t* cnt_w = own_lds + wid * 64 * (1 + kOwn);   // [64] counters | [64][kOwn] slots
         int32_t* tab_w = cnt_w + 64;
         cnt_w[lane] = 0;
 #pragma unroll
         for (int e = 0; e < kOwn; ++e) tab_w[lane * kOwn + e] = -1;
-        __syncthreads();
+        wave_lds_sync();
         bool spilled = false;
         if (lane < lc) {
             const int owner = (ocol & (kGvChunk - 1)) >> 4;
@@ -675,7 +686,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) hit |= (uint32_t)__shfl_xor((int)hit, off, 64);
         chunks_hit = __builtin_amdgcn_readfirstlane(hit);
-        __syncthreads();
+        wave_lds_sync();
 #pragma unroll
         for (int e = 0; e < kOwn; ++e) {
             const int sl = tab_w[lane * kOwn + e];
