@@ -285,60 +285,48 @@ struct GvQuantLds {
     int32_t* pre;        // [words] exclusive prefix of the word popcounts
     uint32_t* rmax;      // [M] row absmax (fp32 bits)
     int32_t* wave_tot;   // [waves]
-    int32_t* any;        // [1] an outlier bit was set
+    float* wmax;         // [waves][M] each wave's row maxima
 };
 
-// The a.m <= M rows of x as 8-column chunks f = tid + T i (row-major over the
-// rows, T threads) into registers: v[i] and rc[i] = row << 16 | chunk.  With k
-// a multiple of 8 and 16-byte aligned rows every chunk is one 16-byte load;
-// all L loads are issued before any is used (a chunk past the end reads
-// zeros through the range check), so they are in flight together.
-template <int L, int T>
-__device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L], uint32_t (&rc)[L]) {
+// x as 8-column chunks, chunk-major: thread tid holds chunks c = tid + T q
+// (q < L / M) with all M rows of each, v[q M + r] = x[r, c].  A chunk's
+// outlier bits are then the OR over the thread's own rows, with no global
+// view needed.  With k a multiple of 8 and 16-byte aligned rows every chunk
+// is one 16-byte load; chunks past k and rows past m read zeros through the
+// range check, so all L loads are in flight together.
+template <int M, int L, int T>
+__device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L]) {
+    static_assert(L % M == 0, "whole chunks of M rows");
     const int tid = threadIdx.x;
     const int32_t cpr = (int32_t)(a.k / 8);
-    const int32_t total_chunks = (int32_t)a.m * cpr;
-    // chunks past the rows read through the range check as zeros: zeroing the
-    // registers after the loads would wait for them before anything else is issued
     const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, ((int64_t)(a.m - 1) * a.ldx + a.k) * 2);
-    int off[L];
-    {
-        int32_t r = tid / cpr, c = tid - r * cpr;
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
-            rc[i] = ((uint32_t)r << 16) | (uint32_t)c;  // chunks < 4096 here
+    for (int q = 0; q < L / M; ++q)
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            const int32_t c = tid + T * q;
             // byte offsets < 2^31: m <= 4 rows of at most I8MP_MAX_LD elements
-            off[i] = tid + T * i < total_chunks ? (int)(((int64_t)r * a.ldx + (int64_t)c * 8) * 2) : (int)0x80000000;
-            c += T;
-            while (c >= cpr) {
-                c -= cpr;
-                ++r;
-            }
+            const int off = (c < cpr && r < a.m) ? (int)(((int64_t)r * a.ldx + (int64_t)c * 8) * 2) : (int)0x80000000;
+            v[q * M + r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
-    }
-#pragma unroll
-    for (int i = 0; i < L; ++i) v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off[i], 0, 0));
 }
 
 // Quantize the chunks of load_x_chunks into the LDS activation rows xs
-// [M][kr] (kr >= k, zeros past k); the first kGvOutl kept outlier columns and their values go to
-// oidx / oval.  Returns the outlier count (columns kept: the count capped at
-// a.cap).  Every thread calls.
+// [M][kr] (kr >= k, zeros past k and in rows past m); the first kGvOutl kept
+// outlier columns and their values go to oidx / oval; the bitmap, its prefix
+// and the row absmax to q.  Returns the outlier count (the kept columns are
+// that count capped at a.cap).  Every thread calls; one workgroup barrier
+// between the local pass and the codes, two inside the prefix.
 template <int M, int L, int T>
-__device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)[L], const uint32_t (&rc)[L],
-                                            int64_t kr, int8_t* xs, int32_t* oidx, float* oval,
-                                            const GvQuantLds& q) {
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)[L], int64_t kr, int8_t* xs,
+                                            int32_t* oidx, float* oval, const GvQuantLds& q) {
+    constexpr int NQ = L / M;
+    constexpr int NW = T / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool outl = a.threshold > 0.0f;
     const int32_t cpr = (int32_t)(a.k / 8);  // k % 8 == 0
-    const int32_t total_chunks = (int32_t)a.m * cpr;
-    auto valid = [&](int i) { return tid + T * i < total_chunks; };
 
-    // zero: bitmap, row maxima, flag, the stream's outlier list, activation
-    // rows past a.m and each row's bytes past k
-    for (int64_t w = tid; w < a.words; w += T) q.bm[w] = 0u;
-    if (tid < M) q.rmax[tid] = 0u;
-    if (tid == 0) *q.any = 0;
+    // zero: the stream's outlier list, activation bytes past k and rows past m
     for (int t = tid; t < kGvOutl; t += T) oidx[t] = 0x7fffffff;
     for (int t = tid; t < M * kGvOutl; t += T) oval[t] = 0.0f;
     for (int64_t r = 0; r < a.m; ++r)
@@ -346,97 +334,94 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
     for (int64_t u = tid; u < (M - a.m) * kr / 16; u += T)
         *reinterpret_cast<v4i_t*>(xs + a.m * kr + u * 16) = v4i_t{0, 0, 0, 0};
 
-    // chunk maxima; a chunk reaching the threshold sets its columns' bits
-    float cmax[L];
-#pragma unroll
-    for (int i = 0; i < L; ++i) cmax[i] = chunk_absmax(v[i]);
-    __syncthreads();
-    if (outl) {
-#pragma unroll
-        for (int i = 0; i < L; ++i)
-            if (valid(i) && cmax[i] >= a.threshold) {
-                const uint32_t bits = outlier_bits8(v[i], a.threshold);
-                const int32_t c = (int32_t)(rc[i] & 0xffffu);
-                atomicOr(&q.bm[c >> 2], bits << ((c & 3) * 8));
-                *q.any = 1;
-            }
-    }
-    __syncthreads();
-    const bool any = outl && *q.any != 0;
-    const int32_t total = any ? bitmap_prefix(q.bm, q.pre, a.words, q.wave_tot) : 0;
-    const int32_t kept = total < a.cap ? total : a.cap;
-    // each chunk's outlier bits, read once (the reads issue back to back)
-    uint32_t obits[L];
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int32_t c = (int32_t)(rc[i] & 0xffffu);
-        obits[i] = any && valid(i) ? (q.bm[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
-    }
-
-    // row absmax over the non-outlier columns (float bits order as uints for x >= 0)
+    // local pass: each chunk's outlier bits (OR over its rows), the rows'
+    // maxima over the chunk's other columns, and the bitmap words: the four
+    // chunks of a word sit in the four lanes of a quad (c % 4 == lane % 4)
+    uint32_t obits[NQ];
     float tmax[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) tmax[r] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < L; ++i)
-        if (valid(i)) {
-            const float mx = obits[i] ? chunk_max(v[i], obits[i]) : cmax[i];
-            const int r = (int)(rc[i] >> 16);
+    for (int qq = 0; qq < NQ; ++qq) {
+        float cm[M];
+        uint32_t ob = 0;
 #pragma unroll
-            for (int rr = 0; rr < M; ++rr)
-                if (rr == r) tmax[rr] = fmaxf(tmax[rr], mx);
+        for (int r = 0; r < M; ++r) {
+            cm[r] = chunk_absmax(v[qq * M + r]);
+            if (outl && cm[r] >= a.threshold) ob |= outlier_bits8(v[qq * M + r], a.threshold);
         }
+        obits[qq] = ob;
+#pragma unroll
+        for (int r = 0; r < M; ++r) tmax[r] = fmaxf(tmax[r], ob ? chunk_max(v[qq * M + r], ob) : cm[r]);
+        const int32_t c = tid + T * qq;
+        int32_t wv = (int32_t)(ob << (8 * (lane & 3)));
+        wv |= dpp_i32<kDppQuadSwap1>(wv);
+        wv |= dpp_i32<kDppQuadSwap2>(wv);
+        if ((lane & 3) == 0 && (c >> 2) < a.words) q.bm[c >> 2] = (uint32_t)wv;
+    }
 #pragma unroll
     for (int r = 0; r < M; ++r) {
         const float t = wave_max_uniform(tmax[r]);
-        if (lane == 0 && t > 0.0f) atomicMax(&q.rmax[r], __float_as_uint(t));
+        if (lane == 0) q.wmax[wave * M + r] = t;
     }
     __syncthreads();
+
+    // row absmax from the waves' maxima; codes of the chunks into LDS
     float inv[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) {
-        const float s = __uint_as_float(q.rmax[r]);
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s = fmaxf(s, q.wmax[w * M + r]);
         inv[r] = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division
+        if (tid == 0) q.rmax[r] = __float_as_uint(s);
     }
-
-    // codes into LDS; chunks with outlier columns take the general path
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+        const int32_t c = tid + T * qq;
+        if (c >= cpr) continue;
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            const uint4& x8 = v[qq * M + r];
+            uint2 code;
+            if (obits[qq] == 0u) {
+                code = codes8_plain(x8, inv[r]);
+            } else {
+                const bool zero_row = !(inv[r] > 0.0f);
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t b = code_byte(h2f(half_at(x8, e)), inv[r], zero_row || ((obits[qq] >> e) & 1u));
+                    if (e < 4) lo |= b << (8 * e);
+                    else hi |= b << (8 * (e - 4));
+                }
+                code = make_uint2(lo, hi);
+            }
+            *reinterpret_cast<uint2*>(xs + r * kr + (int64_t)c * 8) = code;
+        }
+    }
+    const int32_t total = outl ? bitmap_prefix(q.bm, q.pre, a.words, q.wave_tot) : 0;
+    // the first kGvOutl kept outlier columns and their values, in slot order
+    const int32_t kept = total < a.cap ? total : a.cap;
     const int32_t lc = kept < kGvOutl ? kept : kGvOutl;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        if (!valid(i)) continue;
-        const int r = (int)(rc[i] >> 16);
-        const int32_t c = (int32_t)(rc[i] & 0xffffu);
-        float ir = inv[0];
+    for (int qq = 0; qq < NQ; ++qq) {
+        const uint32_t ob = obits[qq];
+        if (ob == 0u) continue;
+        const int32_t c = tid + T * qq;
+        const int32_t w = c >> 2;
+        const uint32_t below = q.bm[w] & ((1u << (8 * (c & 3))) - 1u);   // bits of the word's earlier chunks
+        int32_t slot = q.pre[w] + __popc(below);
 #pragma unroll
-        for (int rr = 1; rr < M; ++rr)
-            if (rr == r) ir = inv[rr];
-        const uint32_t ob = obits[i];
-        uint2 code;
-        if (ob == 0u) {
-            code = codes8_plain(v[i], ir);
-        } else {
-            const bool zero_row = !(ir > 0.0f);
-            uint32_t lo = 0, hi = 0;
+        for (int e = 0; e < 8; ++e)
+            if ((ob >> e) & 1u) {
+                if (slot < lc) {
+                    oidx[slot] = c * 8 + e;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t b = code_byte(h2f(half_at(v[i], e)), ir, zero_row || ((ob >> e) & 1u));
-                if (e < 4) lo |= b << (8 * e);
-                else hi |= b << (8 * (e - 4));
-            }
-            code = make_uint2(lo, hi);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if ((ob >> e) & 1u) {
-                    const int64_t j = (int64_t)c * 8 + e;
-                    const int64_t w = j >> 5;
-                    const int32_t slot = q.pre[w] + __popc(q.bm[w] & ((1u << (j & 31)) - 1u));
-                    if (slot < lc) {
-                        oval[r * kGvOutl + slot] = h2f(half_at(v[i], e));
-                        if (r == 0) oidx[slot] = (int32_t)j;
-                    }
+                    for (int r = 0; r < M; ++r) oval[r * kGvOutl + slot] = h2f(half_at(v[qq * M + r], e));
                 }
-        }
-        *reinterpret_cast<uint2*>(xs + r * kr + (int64_t)c * 8) = code;
+                ++slot;
+            }
     }
     return total;
 }
@@ -524,7 +509,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     ql.pre = reinterpret_cast<int32_t*>(ql.bm + qa.words);
     ql.rmax = reinterpret_cast<uint32_t*>(ql.pre + qa.words);
     ql.wave_tot = reinterpret_cast<int32_t*>(ql.rmax + M);
-    ql.any = ql.wave_tot + W;
+    ql.wmax = reinterpret_cast<float*>(ql.wave_tot + W);
 
     // weight loads: batch b covers row b / bpr, chunks from (b % bpr) * kGvBatch.
     // Past a row's K, past the wave's rows or past n: zero-length / range-checked
@@ -551,8 +536,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     // there measured slower).
     constexpr int kXL = kQuant ? kQuantL : 1;
     uint4 xv[kXL];
-    uint32_t xrc[kXL];
-    if constexpr (kQuant) load_x_chunks<kXL, 64 * W>(qa, xv, xrc);
+    if constexpr (kQuant) load_x_chunks<M, kXL, 64 * W>(qa, xv);
     // unfused: the codes (M rows of kx bytes, at most 32 KB: 16-byte chunks f =
     // tid + 64 W i), the first kGvOutl outlier columns and their x values
     constexpr int kCL = kQuant ? 1 : (32 * 1024 / 16 + 64 * W - 1) / (64 * W);
@@ -616,7 +600,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
 
     // activations (rows >= m and bytes past K as zeros), outlier columns / values
     if constexpr (kQuant) {
-        const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, xrc, kx, xs, oidx, oval, ql);
+        const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, kx, xs, oidx, oval, ql);
         cnt = total < qa.cap ? total : qa.cap;
         __syncthreads();
         publish_spread<M, 64 * W>(qa, kx, xs, ql, oidx, oval, total > 0, total, cnt);
@@ -833,7 +817,7 @@ size_t gemv_lds(int64_t m_pad, int64_t k, int64_t words, int W, bool quant) {
     const int64_t kx = (k + kGvChunk - 1) / kGvChunk * kGvChunk;
     size_t lds = (size_t)m_pad * kx + (size_t)kGvOutl * 4 + (size_t)m_pad * kGvOutl * 4 +
                  (size_t)W * 64 * (1 + kGvOwn) * 4;
-    if (quant) lds += ((size_t)2 * words + m_pad + W + 1) * 4;
+    if (quant) lds += ((size_t)2 * words + m_pad + W + (size_t)W * m_pad) * 4;
     return lds;
 }
 
@@ -865,7 +849,8 @@ hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
 // 8-wave workgroups: x is quantized by 512 threads, at most 8 chunks each
 template <int M>
 hipError_t launch_forward_m(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
-    const int64_t per_thread = (qa.m * (qa.k / 8) + 511) / 512;
+    // chunk-major x: each of the 512 threads holds ceil(k/8 / 512) chunks of all M rows
+    const int64_t per_thread = M * ((qa.k / 8 + 511) / 512);
     if (per_thread <= 4) return launch_gemv_m<M, true, 4, 8>(g, qa, stream);
     return launch_gemv_m<M, true, 8, 8>(g, qa, stream);
 }
@@ -876,8 +861,9 @@ bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g) {
     const bool w_aligned = ((g.ldb & 15) == 0) && ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
     // whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
     const bool x_vec = ((qa.k & 7) == 0) && ((qa.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(qa.x) & 15) == 0);
-    // at most 8 chunks of x per thread of 512
-    const bool x_regs = qa.m * (qa.k / 8) <= 8 * 512;
+    // at most 8 chunks of x per thread of 512 (chunk-major over the padded rows)
+    const int64_t m_pad = qa.m > 2 ? 4 : qa.m;
+    const bool x_regs = m_pad * ((qa.k / 8 + 511) / 512) <= 8;
     // the codes are copied from the LDS rows in 16-byte units
     const bool q_rows = qa.q && qa.kpad == qa.ldq && (qa.ldq & 15) == 0 &&
                         ((reinterpret_cast<uintptr_t>(qa.q) & 15) == 0);
