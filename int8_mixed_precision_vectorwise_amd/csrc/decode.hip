@@ -498,8 +498,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     const int nb = R * bpr;                                       // batches of this wave
 
     // LDS: activations [M][kx] | outlier columns [kGvOutl] | outlier values [M][kGvOutl] |
+    //      per-wave outlier slot tables [W][64 (1 + kGvOwn)] |
     //      (one-launch forward) bitmap [words] | prefix [words] | row absmax [M] |
-    //      wave totals [W] | outlier flag [1]
+    //      wave totals [W] | wave row maxima [W][M]
     int8_t* xs = gsm;
     int32_t* oidx = reinterpret_cast<int32_t*>(gsm + M * kx);
     float* oval = reinterpret_cast<float*>(oidx + kGvOutl);
