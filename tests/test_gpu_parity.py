@@ -211,6 +211,8 @@ FWD_CASES = [
     (2, 640, 2048, 0, 1.0, False, TAU, 8),        # no outliers
     (2, 512, 96, 0, 1.0, True, 0.0, 8),           # threshold off
     (1, 2048, 5000, 3, 1.0, True, TAU, 16),       # three weight rows per wave, the last wave short
+    (2, 16384, 256, 10, 1.0, True, TAU, 64),      # the one-launch forward's most chunks per thread at m = 2
+    (1, 32768, 128, 12, 0.5, False, TAU, 64),     # ... and at m = 1 (32 KB of activations)
     # 5 <= m <= 16, or m <= 4 past the GEMV's LDS: the MFMA decode kernel (outliers from its ring)
     (4, 13824, 300, 12, 0.5, True, TAU, 64),
     (9, 3000, 200, 33, 1.0, False, TAU, 64),      # past the ring's 32 columns: the rest gathered
