@@ -202,6 +202,9 @@ FWD_CASES = [
     (768, 256, 6144, 30, 0.5, True, TAU, 64),     # 256 x 128: slots 16..29 gathered
     (768, 256, 3072, 17, 1.0, False, TAU, 32),    # 128 x 128: one slot past 16
     (256, 256, 6144, 16, 0.5, True, TAU, 16),     # 128 x 64: exactly 16 slots, cap 16
+    # weights with rows of 250 bytes (not 16-byte aligned): the register-staged kernel
+    (768, 250, 6144, 20, 0.5, True, TAU, 64),     # 256 x 128: copies in the wave's staging area
+    (1536, 250, 6144, 30, 0.5, False, TAU, 64),   # 256 x 256 without a stash: every slot gathered
     # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
     (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
     (2, 4096, 264, 5, 0.5, False, TAU, 32),
