@@ -10,15 +10,16 @@
 //
 // Design (CDNA4): 256 threads = 4 wave64 in a 2 x 2 grid; each wave owns a
 // (BM/2) x (BN/2) block of 32x32 accumulators fed by v_mfma_i32_32x32x32_i8.
-// K advances in 128-byte tiles staged through LDS, double-buffered; the next
-// tile is fetched into registers with 16-byte buffer loads while the current
-// one is multiplied.  Buffer loads return 0 past the end of the matrix, so
-// rows beyond m or n need no branches; only the last K tile of an operand
-// whose rows are not zero-padded is masked.  LDS rows are 128 bytes with the
-// 16-byte chunk index XOR-swizzled (swz) so that fragment reads are free of
-// bank conflicts.  The contraction order inside an
-// MFMA does not matter: A and B fragments use the same lane -> k mapping, and
-// integer sums are exact in any order.
+// K advances in 128-byte tiles staged through LDS.  gemm_dtl_kernel, used
+// whenever both operands are 16-byte aligned, copies them global -> LDS with
+// buffer_load ... lds and keeps 2-4 tiles in flight (optionally two K
+// pipelines per workgroup); gemm_kernel, for unaligned operands, double-buffers
+// one tile through registers.  Buffer loads return 0 past the end of the
+// matrix, so rows beyond m or n need no branches.  LDS rows are 128 bytes with
+// the 16-byte chunk index XOR-swizzled so that fragment reads are free of bank
+// conflicts.  The contraction order inside an MFMA does not matter: A and B
+// fragments use the same lane -> k mapping, and integer sums are exact in any
+// order.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so that each XCD works on a contiguous run of tiles (sharing
