@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -74,10 +75,19 @@ def gemm_alg_bytes(s) -> int:
     return b
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and blank lines: what a compiler sees."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def src_sha() -> str:
+    """Hash of the GEMM-side kernel sources' code (comments and blank lines
+    ignored), which the stored traffic counters must match."""
     h = hashlib.sha256()
     for f in GEMM_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f).read()).encode())
     return h.hexdigest()[:16]
 
 
