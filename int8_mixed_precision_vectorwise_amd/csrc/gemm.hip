@@ -394,7 +394,9 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
                 const int tcol = wc0 + 8 * c;
                 const int off = (trow * (int)g.ldout + tcol) * 2;
                 if (vec_ok && tcol + 8 <= cols_left) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ro, off, 0, 0);
+                    // streaming (nt) stores: every tile writes its whole output
+                    // at once at the end, and nothing here reads it back
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ro, off, 0, 2);
                 } else if (tcol < cols_left) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
