@@ -23,3 +23,11 @@ from .llm_int8 import (  # noqa: F401
     QuantResult,
     ForwardResult,
 )
+from .backward import (  # noqa: F401
+    colwise_absmax,
+    colwise_quant,
+    grad_input,
+    grad_weight,
+    linear_backward,
+    BackwardResult,
+)

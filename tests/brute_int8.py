@@ -134,3 +134,41 @@ def brute_weight_quant(w: Sequence[Sequence[float]]):
         s.append(a)
         q.append([0 if a == 0 else quant_code(v, a) for v in R])
     return q, s
+
+
+def brute_colwise_quant(a: Sequence[Sequence[float]], zero_cols: Sequence[int] = ()):
+    """Column-wise codes, transposed ([c][r]), and column absmax, by nested loops."""
+    r = len(a)
+    c = len(a[0]) if r else 0
+    A = [[Fraction(float(v)) for v in row] for row in a]
+    zc = set(zero_cols)
+    qt, s = [], []
+    for j in range(c):
+        col = [A[i][j] for i in range(r)]
+        sj = max((abs(v) for v in col), default=Fraction(0))
+        s.append(sj)
+        qt.append([0 if (sj == 0 or j in zc) else quant_code(v, sj) for v in col])
+    return qt, s
+
+
+class BruteBackward:
+    """Nested-loop evaluation of both gradients on exact rationals (tiny inputs)."""
+
+    def __init__(self, g, x, w, cols):
+        m, n, k = len(g), len(w), len(w[0])
+        G = [[Fraction(float(v)) for v in row] for row in g]
+        X = [[Fraction(float(v)) for v in row] for row in x]
+        # grad_x: g row-wise (threshold off), W column-wise
+        gq, gs = brute_weight_quant(g)
+        wtq, wts = brute_colwise_quant(w)
+        self.c_x = [[sum(gq[i][nn] * wtq[j][nn] for nn in range(n)) for j in range(k)] for i in range(m)]
+        self.gx = [[(wts[j] / 127) * (self.c_x[i][j] * gs[i] / 127) for j in range(k)] for i in range(m)]
+        # grad_W: g column-wise, x column-wise with the outlier columns zeroed
+        gtq, gts = brute_colwise_quant(g)
+        xtq, xts = brute_colwise_quant(x, cols)
+        self.c_w = [[sum(gtq[nn][i] * xtq[j][i] for i in range(m)) for j in range(k)] for nn in range(n)]
+        oc = set(cols)
+        self.gw = [[(sum((G[i][nn] * X[i][j] for i in range(m)), Fraction(0)) if j in oc else
+                     (xts[j] / 127) * (self.c_w[nn][j] * gts[nn] / 127)) for j in range(k)] for nn in range(n)]
+        self.g_q, self.g_s, self.wt_q, self.wt_s = gq, gs, wtq, wts
+        self.gt_q, self.gt_s, self.xt_q, self.xt_s = gtq, gts, xtq, xts
