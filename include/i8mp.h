@@ -246,6 +246,94 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
                                 int64_t ldout, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Backward pass through the int8 linear (training with the fp16 weight kept).
+ * The bitsandbytes PR "LLM.int8() Refactoring: Part 1", in its review of
+ * bitsandbytes/autograd/_functions.py, keeps a transposed int8 copy of the
+ * layer input (CAt) whose outlier columns, listed by the forward's saved index,
+ * are zeroed; the transformers PR page ("`bitsandbytes` - `Linear8bitLt`
+ * integration into `transformers` models") notes that fine-tuning through the
+ * layers works while the fp16 weights are kept.  No formula is printed; the
+ * readings, in the forward's int8/fp16 split:
+ *
+ *  - column-wise quantization of A [r x c]: column scale s[j] = max_i |A[i,j]|
+ *    (fp32, exact), code = clamp(rne(fl32(A[i,j] * fl32(127 / s[j]))), -127, 127)
+ *    (0 if s[j] == 0), handed over transposed: qt[j, i] (K-contiguous);
+ *  - grad_x[i,j] = fp16( (s_wt[j]/127) * (C[i,j] * s_g[i]/127) ),
+ *    C = g_q . wt_q^T exact (contraction over n): g = dL/dy quantized row-wise,
+ *    the weight W quantized column-wise; no outlier term;
+ *  - grad_w[n,j] = fp16( (s_xt[j]/127) * (C[n,j] * s_gt[n]/127) ) for j not an
+ *    outlier column, C = gt_q . xt_q^T exact (contraction over the m rows), g
+ *    and x quantized column-wise with x's outlier columns zeroed;
+ *    grad_w[n,j] = fp16( sum_i g[i,n] * x[i,j] ) (fp32) for the outlier columns.
+ */
+
+/* Column-wise ("transposed") int8 quantization:
+ *
+ *   a            fp16 [rows x lda], lda >= cols
+ *   zero_idx     optional int32 [cap] columns whose codes are all 0 (their scale
+ *                is still reported); only the first min(*zero_count, cap) are
+ *                used (device values, e.g. the idx / count of a forward)
+ *   zero_count   int32 [1], required with zero_idx
+ *   qt           int8 [cols x ldqt] output, ldqt >= rows: qt[j, i] = code of
+ *                a[i, j]; qt[j, i] = 0 for rows <= i < ldqt
+ *   col_absmax   fp32 [cols] output
+ *   workspace    at least i8mp_colwise_quant_workspace_bytes(rows, cols) bytes
+ * rows >= 0, cols >= 1; ldqt at most I8MP_MAX_LD.  cols == 0 is a no-op.
+ */
+size_t i8mp_colwise_quant_workspace_bytes(int64_t rows, int64_t cols);
+i8mp_status i8mp_int8_colwise_quant(const void* a, int64_t rows, int64_t cols, int64_t lda,
+                                    const int32_t* zero_idx, const int32_t* zero_count, int32_t cap,
+                                    int8_t* qt, int64_t ldqt, float* col_absmax, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace of i8mp_linear_backward; after a call it holds the operands of both
+ * gradient GEMMs at these offsets. */
+typedef struct i8mp_backward_workspace {
+    size_t bytes;          /* total size needed                                   */
+    int64_t ld_n;          /* round_up(n, 128): row length of g_q and wt_q        */
+    int64_t ld_m;          /* round_up(m, 128): row length of gt_q and xt_q       */
+    size_t gq_offset;      /* int8 [m x ld_n] row-wise codes of g, zero-padded    */
+    size_t gs_offset;      /* fp32 [m] row absmax of g                            */
+    size_t wtq_offset;     /* int8 [k x ld_n] column-wise codes of W (CBt)        */
+    size_t wts_offset;     /* fp32 [k] column absmax of W                         */
+    size_t gtq_offset;     /* int8 [n x ld_m] column-wise codes of g              */
+    size_t gts_offset;     /* fp32 [n] column absmax of g                         */
+    size_t xtq_offset;     /* int8 [k x ld_m] column-wise codes of x, outlier
+                              columns zeroed (CAt)                                */
+    size_t xts_offset;     /* fp32 [k] column absmax of x                         */
+    size_t scratch_offset; /* private: column maxima, outlier-gradient sums       */
+    size_t scratch_bytes;
+} i8mp_backward_workspace;
+
+i8mp_status i8mp_linear_backward_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
+                                                 i8mp_backward_workspace* layout /* host */);
+
+/* Both gradients of out = x . W^T (+ bias) for grad_out = dL/dout:
+ *
+ *   grad_out   fp16 [m x ldg], ldg >= n
+ *   x          fp16 [m x ldx], ldx >= k   (the forward's input)
+ *   w          fp16 [n x ldw], ldw >= k   (the weight kept in fp16 for training;
+ *              required when grad_x is requested)
+ *   cap, fwd_workspace   the forward's outlier capacity and its workspace (from
+ *              i8mp_linear_forward or i8mp_linear_quantize on this x with this
+ *              m, k and cap), read for its outlier index, count and gathered
+ *              outlier columns; NULL = no outlier columns.  As in the forward,
+ *              with more than cap outlier columns only the first cap take the
+ *              fp16 path.
+ *   grad_x     optional fp16 [m x ldgx] output, ldgx >= k (NULL: not computed)
+ *   grad_w     optional fp16 [n x ldgw] output, ldgw >= k (NULL: not computed)
+ *   workspace  at least the query's bytes
+ * m, n >= 0, k >= 1; m and n at most I8MP_MAX_K (they are contraction lengths),
+ * leading dimensions at most I8MP_MAX_LD.  The bias gradient is the column sum
+ * of grad_out and is not part of this call.
+ */
+i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* x, int64_t ldx,
+                                 const void* w, int64_t ldw, int64_t m, int64_t n, int64_t k,
+                                 int32_t cap, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                 void* grad_x, int64_t ldgx, void* grad_w, int64_t ldgw,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     EXPORTS,
+    BackwardWorkspaceLayout,
     I8MP_MAX_K,
     I8mpError,
     LinearWorkspaceLayout,
@@ -40,6 +41,9 @@ __all__ = [
     "linear_quantize",
     "linear_matmul_dequant",
     "LinearWorkspace",
+    "colwise_quant",
+    "linear_backward",
+    "BackwardWorkspace",
     "I8mpError",
 ]
 
@@ -71,7 +75,7 @@ def _rowmajor(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    if t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
     return max(t.stride(0), t.shape[1], 1)
 
@@ -316,3 +320,131 @@ def linear_matmul_dequant(workspace: LinearWorkspace, w_q: torch.Tensor, w_absma
                                                ldout, _stream(dev)),
               "i8mp_linear_matmul_dequant")
     return out
+
+
+def colwise_quant(a: torch.Tensor, zero_idx: Optional[torch.Tensor] = None,
+                  zero_count: Optional[torch.Tensor] = None, ldqt: Optional[int] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Column-wise (transposed) int8 quantization: (qt int8 [cols, ldqt], col absmax fp32 [cols]).
+
+    qt[j, i] is the code of a[i, j] under column j's absmax; columns listed in
+    zero_idx[:min(zero_count, len)] get zero codes; rows >= a.shape[0] of qt are 0.
+    """
+    dev = _device_of(a, zero_idx, zero_count)
+    lda = _rowmajor(a, "a", torch.float16)
+    rows, cols = a.shape
+    if (zero_idx is None) != (zero_count is None):
+        raise ValueError("zero_idx and zero_count go together")
+    cap = 0
+    if zero_idx is not None:
+        if zero_idx.dtype != torch.int32 or zero_idx.dim() != 1 or not zero_idx.is_contiguous():
+            raise ValueError("zero_idx must be a contiguous int32 vector")
+        _vec(zero_count, "zero_count", torch.int32, 1)
+        cap = zero_idx.shape[0]
+    ldqt = rows if ldqt is None else ldqt
+    qt = torch.empty((cols, max(ldqt, 1)), dtype=torch.int8, device=dev)
+    absmax = torch.empty(cols, dtype=torch.float32, device=dev)
+    L = lib()
+    wsb = L.i8mp_colwise_quant_workspace_bytes(rows, max(cols, 1))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        check(L.i8mp_int8_colwise_quant(_ptr(a), rows, cols, lda, _ptr(zero_idx), _ptr(zero_count), cap, _ptr(qt),
+                                        ldqt, _ptr(absmax), _ptr(ws), wsb, _stream(dev)),
+              "i8mp_int8_colwise_quant")
+    return qt[:, :ldqt], absmax
+
+
+@dataclass
+class BackwardWorkspace:
+    """Device workspace of i8mp_linear_backward plus views of the GEMM operands it holds."""
+
+    m: int
+    n: int
+    k: int
+    cap: int
+    layout: BackwardWorkspaceLayout
+    buf: torch.Tensor
+
+    @classmethod
+    def create(cls, m: int, n: int, k: int, cap: int, device) -> "BackwardWorkspace":
+        L = BackwardWorkspaceLayout()
+        check(lib().i8mp_linear_backward_workspace_query(m, n, k, cap, ctypes.byref(L)),
+              "i8mp_linear_backward_workspace_query")
+        return cls(m, n, k, cap, L, torch.empty(max(L.bytes, 1), dtype=torch.uint8, device=device))
+
+    def _mat(self, off: int, rows: int, ld: int, cols: int) -> torch.Tensor:
+        return self.buf[off:off + rows * ld].view(rows, ld)[:, :cols]
+
+    def _f32(self, off: int, count: int) -> torch.Tensor:
+        return self.buf[off:off + 4 * count].view(torch.float32)
+
+    # operands left by the last call (for tests and inspection)
+    def g_q(self):
+        return self._mat(self.layout.gq_offset, self.m, self.layout.ld_n, self.n).view(torch.int8)
+
+    def g_s(self):
+        return self._f32(self.layout.gs_offset, self.m)
+
+    def wt_q(self):
+        return self._mat(self.layout.wtq_offset, self.k, self.layout.ld_n, self.n).view(torch.int8)
+
+    def wt_s(self):
+        return self._f32(self.layout.wts_offset, self.k)
+
+    def gt_q(self):
+        return self._mat(self.layout.gtq_offset, self.n, self.layout.ld_m, self.m).view(torch.int8)
+
+    def gt_s(self):
+        return self._f32(self.layout.gts_offset, self.n)
+
+    def xt_q(self):
+        return self._mat(self.layout.xtq_offset, self.k, self.layout.ld_m, self.m).view(torch.int8)
+
+    def xt_s(self):
+        return self._f32(self.layout.xts_offset, self.k)
+
+
+def linear_backward(grad_out: torch.Tensor, x: torch.Tensor, w: Optional[torch.Tensor],
+                    forward_workspace: Optional[LinearWorkspace] = None,
+                    need_grad_x: bool = True, need_grad_w: bool = True,
+                    workspace: Optional[BackwardWorkspace] = None,
+                    ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Both gradients of ``linear`` for dL/dout = grad_out: (grad_x fp16 [m, k], grad_w fp16 [n, k]).
+
+    w is the fp16 weight kept for training (needed for grad_x).  The outlier
+    columns are those the forward left in ``forward_workspace`` (None: none).
+    """
+    dev = _device_of(grad_out, x, w, None if forward_workspace is None else forward_workspace.buf)
+    ldg = _rowmajor(grad_out, "grad_out", torch.float16)
+    ldx = _rowmajor(x, "x", torch.float16)
+    m, n = grad_out.shape
+    mx, k = x.shape
+    if mx != m:
+        raise ValueError("grad_out and x differ in rows")
+    ldw = k
+    if need_grad_x:
+        if w is None:
+            raise ValueError("grad_x needs the fp16 weight")
+        ldw = _rowmajor(w, "w", torch.float16)
+        if tuple(w.shape) != (n, k):
+            raise ValueError("w must be [n, k]")
+    cap = 0
+    if forward_workspace is not None:
+        if (forward_workspace.m, forward_workspace.k) != (m, k):
+            raise ValueError("forward workspace was made for another shape")
+        cap = forward_workspace.cap
+    if workspace is None:
+        workspace = BackwardWorkspace.create(m, n, k, cap, dev)
+    elif (workspace.m, workspace.n, workspace.k, workspace.cap) != (m, n, k, cap):
+        raise ValueError("backward workspace was created for another shape or capacity")
+    gx = torch.empty((m, k), dtype=torch.float16, device=dev) if need_grad_x else None
+    gw = torch.empty((n, k), dtype=torch.float16, device=dev) if need_grad_w else None
+    fws = None if forward_workspace is None else forward_workspace.buf
+    with torch.cuda.device(dev):
+        check(lib().i8mp_linear_backward(_ptr(grad_out), ldg, _ptr(x), ldx, _ptr(w if need_grad_x else None), ldw,
+                                         m, n, k, cap, _ptr(fws), 0 if fws is None else fws.numel(),
+                                         _ptr(gx), k, _ptr(gw), k, _ptr(workspace.buf), workspace.buf.numel(),
+                                         _stream(dev)),
+              "i8mp_linear_backward")
+    return gx, gw
+

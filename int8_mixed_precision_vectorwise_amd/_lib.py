@@ -31,6 +31,10 @@ EXPORTS = (
     "i8mp_linear_quantize",
     "i8mp_linear_matmul_dequant",
     "i8mp_linear_forward",
+    "i8mp_colwise_quant_workspace_bytes",
+    "i8mp_int8_colwise_quant",
+    "i8mp_linear_backward_workspace_query",
+    "i8mp_linear_backward",
 )
 
 
@@ -45,6 +49,24 @@ class LinearWorkspaceLayout(Structure):
         ("count_offset", c_size_t),
         ("xo_offset", c_size_t),
         ("cap_pad", c_int32),
+        ("scratch_offset", c_size_t),
+        ("scratch_bytes", c_size_t),
+    ]
+
+
+class BackwardWorkspaceLayout(Structure):
+    _fields_ = [
+        ("bytes", c_size_t),
+        ("ld_n", c_int64),
+        ("ld_m", c_int64),
+        ("gq_offset", c_size_t),
+        ("gs_offset", c_size_t),
+        ("wtq_offset", c_size_t),
+        ("wts_offset", c_size_t),
+        ("gtq_offset", c_size_t),
+        ("gts_offset", c_size_t),
+        ("xtq_offset", c_size_t),
+        ("xts_offset", c_size_t),
         ("scratch_offset", c_size_t),
         ("scratch_bytes", c_size_t),
     ]
@@ -96,6 +118,18 @@ def _declare(lib):
                                                c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                                c_void_p]
     lib.i8mp_linear_matmul_dequant.restype = c_int32
+    lib.i8mp_colwise_quant_workspace_bytes.argtypes = [c_int64, c_int64]
+    lib.i8mp_colwise_quant_workspace_bytes.restype = c_size_t
+    lib.i8mp_int8_colwise_quant.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_int32,
+                                            c_void_p, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.i8mp_int8_colwise_quant.restype = c_int32
+    lib.i8mp_linear_backward_workspace_query.argtypes = [c_int64, c_int64, c_int64, c_int32,
+                                                         POINTER(BackwardWorkspaceLayout)]
+    lib.i8mp_linear_backward_workspace_query.restype = c_int32
+    lib.i8mp_linear_backward.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                         c_int64, c_int64, c_int32, c_void_p, c_size_t, c_void_p, c_int64,
+                                         c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
+    lib.i8mp_linear_backward.restype = c_int32
 
 
 def lib():

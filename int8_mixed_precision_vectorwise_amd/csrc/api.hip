@@ -57,6 +57,37 @@ void forward_layout(int64_t m, int64_t k, int32_t cap, i8mp_linear_workspace* L)
     L->bytes = off;
 }
 
+void backward_layout(int64_t m, int64_t n, int64_t k, int32_t cap, i8mp_backward_workspace* L) {
+    std::memset(L, 0, sizeof(*L));
+    L->ld_n = round_up(n > 0 ? n : 1, 128);
+    L->ld_m = round_up(m > 0 ? m : 1, 128);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + (bytes > 0 ? bytes : 1));
+        return at;
+    };
+    L->gq_offset = take((size_t)m * (size_t)L->ld_n);
+    L->gs_offset = take((size_t)m * 4);
+    L->wtq_offset = take((size_t)k * (size_t)L->ld_n);
+    L->wts_offset = take((size_t)k * 4);
+    L->gtq_offset = take((size_t)n * (size_t)L->ld_m);
+    L->gts_offset = take((size_t)n * 4);
+    L->xtq_offset = take((size_t)k * (size_t)L->ld_m);
+    L->xts_offset = take((size_t)k * 4);
+    // column maxima of the three column-wise quantizations (run one after the
+    // other on the stream, so they share one buffer), then the fp32 sums of
+    // the outlier columns of grad_w
+    size_t colmax = colquant_scratch_bytes(n, k);
+    if (colquant_scratch_bytes(m, n) > colmax) colmax = colquant_scratch_bytes(m, n);
+    if (colquant_scratch_bytes(m, k) > colmax) colmax = colquant_scratch_bytes(m, k);
+    L->scratch_offset = off;
+    const size_t acc_at = align_up(colmax);
+    L->scratch_bytes = acc_at + fix_acc_bytes(n, cap);
+    off = align_up(off + L->scratch_bytes);
+    L->bytes = off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -340,6 +371,175 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
     if (decode_forward_fits(qa, g)) return launched(launch_decode_forward(qa, g, stream));
     if (i8mp_status s = launched(launch_quantize(qa, stream)); s != I8MP_OK) return s;
     return launched(launch_gemm_fused(g, stream));
+}
+
+size_t i8mp_colwise_quant_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 1) return 0;
+    return colquant_scratch_bytes(rows, cols);
+}
+
+i8mp_status i8mp_int8_colwise_quant(const void* a, int64_t rows, int64_t cols, int64_t lda,
+                                    const int32_t* zero_idx, const int32_t* zero_count, int32_t cap,
+                                    int8_t* qt, int64_t ldqt, float* col_absmax, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ldqt < rows || bad_ld(ldqt) || cap < 0) return I8MP_EINVAL;
+    if (cols == 0) return I8MP_OK;
+    if (lda < cols || !qt || !col_absmax || (rows > 0 && !a)) return I8MP_EINVAL;
+    if (zero_idx && !zero_count) return I8MP_EINVAL;
+    if (!workspace || workspace_bytes < colquant_scratch_bytes(rows, cols)) return I8MP_EWORKSPACE;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    ColQuantArgs c{};
+    c.x = static_cast<const half_bits*>(a);
+    c.rows = rows;
+    c.cols = cols;
+    c.lda = lda;
+    c.zero_idx = zero_idx;
+    c.zero_count = zero_count;
+    c.cap = cap;
+    c.qt = qt;
+    c.ldqt = ldqt;
+    c.col_absmax = col_absmax;
+    c.partial = static_cast<float*>(workspace);
+    return launched(launch_colwise_quant(c, stream));
+}
+
+i8mp_status i8mp_linear_backward_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
+                                                 i8mp_backward_workspace* layout) {
+    if (!layout || m < 0 || n < 0 || bad_k(k) || cap < 0 || bad_ld(cap)) return I8MP_EINVAL;
+    if (m > I8MP_MAX_K || n > I8MP_MAX_K) return I8MP_ERANGE;
+    backward_layout(m, n, k, cap, layout);
+    return I8MP_OK;
+}
+
+i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* x, int64_t ldx,
+                                 const void* w, int64_t ldw, int64_t m, int64_t n, int64_t k,
+                                 int32_t cap, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                 void* grad_x, int64_t ldgx, void* grad_w, int64_t ldgw,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (m < 0 || n < 0 || bad_k(k) || cap < 0 || bad_ld(cap) || ldg < n) return I8MP_EINVAL;
+    if (grad_x && (ldw < k || ldgx < k || bad_ld(ldgx))) return I8MP_EINVAL;
+    if (grad_w && (ldx < k || ldgw < k || bad_ld(ldgw))) return I8MP_EINVAL;
+    if (m > I8MP_MAX_K || n > I8MP_MAX_K) return I8MP_ERANGE;
+    const bool want_x = grad_x && m > 0;
+    const bool want_w = grad_w && n > 0;
+    if (!want_x && !want_w) return I8MP_OK;
+    if (want_x && n > 0 && (!grad_out || !w)) return I8MP_EINVAL;
+    if (want_w && m > 0 && (!grad_out || !x)) return I8MP_EINVAL;
+    i8mp_backward_workspace L;
+    backward_layout(m, n, k, cap, &L);
+    if (!workspace || workspace_bytes < L.bytes) return I8MP_EWORKSPACE;
+    i8mp_linear_workspace F;
+    forward_layout(m, k, cap, &F);
+    if (fwd_workspace && fwd_workspace_bytes < F.bytes) return I8MP_EWORKSPACE;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    char* ws = static_cast<char*>(workspace);
+    float* colmax = reinterpret_cast<float*>(ws + L.scratch_offset);
+    const half_bits* g = static_cast<const half_bits*>(grad_out);
+
+    if (want_x) {
+        if (n == 0) {  // empty contraction
+            if (i8mp_status s = launched(launch_fill_f16(static_cast<half_bits*>(grad_x), m, k, ldgx, stream));
+                s != I8MP_OK)
+                return s;
+        } else {
+            // g row-wise (threshold off), W column-wise (CBt), then the GEMM
+            QuantArgs q{};
+            q.x = g;
+            q.m = m;
+            q.k = n;
+            q.ldx = ldg;
+            q.threshold = 0.0f;
+            q.words = ceil_div(n, 32);
+            q.q = reinterpret_cast<int8_t*>(ws + L.gq_offset);
+            q.ldq = L.ld_n;
+            q.kpad = L.ld_n;
+            q.absmax = reinterpret_cast<float*>(ws + L.gs_offset);
+            if (i8mp_status s = launched(launch_quantize(q, stream)); s != I8MP_OK) return s;
+            ColQuantArgs c{};
+            c.x = static_cast<const half_bits*>(w);
+            c.rows = n;
+            c.cols = k;
+            c.lda = ldw;
+            c.qt = reinterpret_cast<int8_t*>(ws + L.wtq_offset);
+            c.ldqt = L.ld_n;
+            c.col_absmax = reinterpret_cast<float*>(ws + L.wts_offset);
+            c.partial = colmax;
+            if (i8mp_status s = launched(launch_colwise_quant(c, stream)); s != I8MP_OK) return s;
+            GemmArgs G{};
+            G.a = reinterpret_cast<const int8_t*>(ws + L.gq_offset);
+            G.lda = L.ld_n;
+            G.a_zero_padded = true;
+            G.b = reinterpret_cast<const int8_t*>(ws + L.wtq_offset);
+            G.ldb = L.ld_n;
+            G.m = m;
+            G.n = k;
+            G.k = n;
+            G.row_absmax = reinterpret_cast<const float*>(ws + L.gs_offset);
+            G.col_absmax = reinterpret_cast<const float*>(ws + L.wts_offset);
+            G.out = static_cast<half_bits*>(grad_x);
+            G.ldout = ldgx;
+            if (i8mp_status s = launched(launch_gemm_fused(G, stream)); s != I8MP_OK) return s;
+        }
+    }
+    if (want_w) {
+        if (m == 0) {  // empty contraction
+            return launched(launch_fill_f16(static_cast<half_bits*>(grad_w), n, k, ldgw, stream));
+        }
+        const char* fws = static_cast<const char*>(fwd_workspace);
+        const int32_t* idx = fws ? reinterpret_cast<const int32_t*>(fws + F.idx_offset) : nullptr;
+        const int32_t* count = fws ? reinterpret_cast<const int32_t*>(fws + F.count_offset) : nullptr;
+        // g and x column-wise, x's outlier columns zeroed (CAt), then the GEMM
+        ColQuantArgs c{};
+        c.x = g;
+        c.rows = m;
+        c.cols = n;
+        c.lda = ldg;
+        c.qt = reinterpret_cast<int8_t*>(ws + L.gtq_offset);
+        c.ldqt = L.ld_m;
+        c.col_absmax = reinterpret_cast<float*>(ws + L.gts_offset);
+        c.partial = colmax;
+        if (i8mp_status s = launched(launch_colwise_quant(c, stream)); s != I8MP_OK) return s;
+        c.x = static_cast<const half_bits*>(x);
+        c.cols = k;
+        c.lda = ldx;
+        c.zero_idx = cap > 0 ? idx : nullptr;
+        c.zero_count = count;
+        c.cap = cap;
+        c.qt = reinterpret_cast<int8_t*>(ws + L.xtq_offset);
+        c.col_absmax = reinterpret_cast<float*>(ws + L.xts_offset);
+        if (i8mp_status s = launched(launch_colwise_quant(c, stream)); s != I8MP_OK) return s;
+        GemmArgs G{};
+        G.a = reinterpret_cast<const int8_t*>(ws + L.gtq_offset);
+        G.lda = L.ld_m;
+        G.a_zero_padded = true;
+        G.b = reinterpret_cast<const int8_t*>(ws + L.xtq_offset);
+        G.ldb = L.ld_m;
+        G.m = n;
+        G.n = k;
+        G.k = m;
+        G.row_absmax = reinterpret_cast<const float*>(ws + L.gts_offset);
+        G.col_absmax = reinterpret_cast<const float*>(ws + L.xts_offset);
+        G.out = static_cast<half_bits*>(grad_w);
+        G.ldout = ldgw;
+        if (i8mp_status s = launched(launch_gemm_fused(G, stream)); s != I8MP_OK) return s;
+        if (fws && cap > 0) {
+            FixArgs f{};
+            f.g = g;
+            f.ldg = ldg;
+            f.m = m;
+            f.n = n;
+            f.x_out = reinterpret_cast<const half_bits*>(fws + F.xo_offset);
+            f.ldo = F.cap_pad;
+            f.idx = idx;
+            f.count = count;
+            f.cap = cap;
+            f.acc = reinterpret_cast<float*>(ws + L.scratch_offset + (L.scratch_bytes - fix_acc_bytes(n, cap)));
+            f.grad_w = static_cast<half_bits*>(grad_w);
+            f.ldgw = ldgw;
+            if (i8mp_status s = launched(launch_outlier_grad(f, stream)); s != I8MP_OK) return s;
+        }
+    }
+    return I8MP_OK;
 }
 
 }  // extern "C"

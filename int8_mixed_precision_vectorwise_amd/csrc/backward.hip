@@ -1,0 +1,298 @@
+// Kernels of the backward pass through the int8 linear:
+//  - column-wise ("transposed") int8 quantization: a column-maximum pass and a
+//    code pass that writes the codes transposed (the K-contiguous operand
+//    layout of the int8 GEMM), with listed columns zeroed (the CAt of the
+//    bitsandbytes PR "LLM.int8() Refactoring: Part 1", its review of
+//    bitsandbytes/autograd/_functions.py);
+//  - the fp16 outlier columns of the weight gradient, sum_i g[i, n] * x[i, j]
+//    for j in the forward's outlier list.
+// The two gradient GEMMs themselves are the forward's int8 GEMM with its
+// dequant epilogue (gemm.hip), called from api.hip.
+#include "common.h"
+#include "quant_util.h"
+
+namespace i8mp {
+
+namespace {
+
+// A workgroup of 4 waves covers 64 columns x 512 rows; lane l of a wave takes
+// the 8 columns (l & 7) * 8 .. + 8 of 16 consecutive rows, so one lane's codes
+// of one column are 16 consecutive bytes of a transposed row.
+constexpr int kStripCols = 64;
+constexpr int kLaneRows = 16;
+constexpr int kWaveRows = 8 * kLaneRows;        // 128
+constexpr int kBlockRows = 4 * kWaveRows;       // 512
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// per-half maximum of two words of fp16 magnitudes (non-negative fp16 bit
+// patterns order like unsigned integers)
+__device__ inline uint32_t umax16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ inline uint4 umax16x8(const uint4& a, const uint4& b) {
+    return make_uint4(umax16x2(a.x, b.x), umax16x2(a.y, b.y), umax16x2(a.z, b.z), umax16x2(a.w, b.w));
+}
+
+__device__ inline uint4 shfl_xor4(const uint4& v, int off) {
+    return make_uint4(__shfl_xor(v.x, off, 64), __shfl_xor(v.y, off, 64), __shfl_xor(v.z, off, 64),
+                      __shfl_xor(v.w, off, 64));
+}
+
+// The 16 row chunks of one lane: rows r0 .. r0 + 15, columns c .. c + 7 of x
+// (rows >= rows and columns >= cols read as 0).  kVec: 16-byte loads (cols and
+// lda multiples of 8, 16-byte aligned base), so a chunk is all in or all out.
+template <bool kVec>
+__device__ inline void load_lane_rows(const ColQuantArgs& a, int64_t r0, int64_t c, uint4 (&v)[kLaneRows]) {
+#pragma unroll
+    for (int j = 0; j < kLaneRows; ++j) {
+        const int64_t r = r0 + j;
+        v[j] = (r < a.rows && c < a.cols) ? load8<kVec>(a.x + r * a.lda, c, a.cols) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Pass 1: maxima of |x| per column over each 512-row block,
+// partial[blockIdx.y][col] (fp32, exact).
+template <bool kVec>
+__global__ __launch_bounds__(256) void colmax_kernel(ColQuantArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cc = lane & 7, rl = lane >> 3;
+    const int64_t c = (int64_t)blockIdx.x * kStripCols + cc * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * kBlockRows + wave * kWaveRows + rl * kLaneRows;
+    uint4 v[kLaneRows];
+    load_lane_rows<kVec>(a, r0, c, v);
+    const uint4 mag = make_uint4(0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu);
+    uint4 mx = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kLaneRows; ++j)
+        mx = umax16x8(mx, make_uint4(v[j].x & mag.x, v[j].y & mag.y, v[j].z & mag.z, v[j].w & mag.w));
+    // the 8 row lanes of a column chunk differ in lane bits 3..5
+    mx = umax16x8(mx, shfl_xor4(mx, 8));
+    mx = umax16x8(mx, shfl_xor4(mx, 16));
+    mx = umax16x8(mx, shfl_xor4(mx, 32));
+    __shared__ uint4 red[4][8];
+    if (rl == 0) red[wave][cc] = mx;
+    __syncthreads();
+    if (tid < kStripCols) {
+        const int q = tid >> 3, e = tid & 7;
+        uint4 m = umax16x8(umax16x8(red[0][q], red[1][q]), umax16x8(red[2][q], red[3][q]));
+        const int64_t col = (int64_t)blockIdx.x * kStripCols + tid;
+        if (col < a.cols) a.partial[(int64_t)blockIdx.y * a.cols_pad + col] = h2f(half_at(m, e));
+    }
+}
+
+// Pass 2: codes of x^T.  Column scale s = max over the partial maxima, inv =
+// fl32(127 / s) (0 for a zero column or a listed one), code = rne(fl32(x * inv))
+// as in the row quantizer (|x| <= s keeps the product in [-127, 127]).  Rows
+// rows .. ldqt - 1 of the transposed codes are written as 0.
+template <bool kVecIn, bool kVecOut>
+__global__ __launch_bounds__(256) void colquant_kernel(ColQuantArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cc = lane & 7, rl = lane >> 3;
+    const int64_t c = (int64_t)blockIdx.x * kStripCols + cc * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * kBlockRows + wave * kWaveRows + rl * kLaneRows;
+    if (c >= a.cols) return;  // no barrier below
+    // the rows first (their latency hides behind the scale computation); a
+    // lane past ldqt loads nothing but may still write the column scales
+    const bool live = r0 < a.ldqt;
+    uint4 v[kLaneRows];
+    if (live) load_lane_rows<kVecIn>(a, r0, c, v);
+
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    for (int64_t rb = 0; rb < a.row_blocks; ++rb) {
+        const float4* p = reinterpret_cast<const float4*>(a.partial + rb * a.cols_pad + c);
+        const float4 p0 = p[0], p1 = p[1];
+        s[0] = fmaxf(s[0], p0.x); s[1] = fmaxf(s[1], p0.y); s[2] = fmaxf(s[2], p0.z); s[3] = fmaxf(s[3], p0.w);
+        s[4] = fmaxf(s[4], p1.x); s[5] = fmaxf(s[5], p1.y); s[6] = fmaxf(s[6], p1.z); s[7] = fmaxf(s[7], p1.w);
+    }
+    uint32_t zmask = 0;
+    if (a.zero_idx) {
+        int32_t nz = *a.zero_count;
+        if (nz > a.cap) nz = a.cap;
+        for (int32_t t = 0; t < nz; ++t) {
+            const int64_t d = (int64_t)a.zero_idx[t] - c;
+            if (d >= 0 && d < 8) zmask |= 1u << d;
+        }
+    }
+    float inv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        inv[e] = (s[e] > 0.0f && !((zmask >> e) & 1u)) ? 127.0f / s[e] : 0.0f;  // IEEE division
+    if (blockIdx.y == 0 && wave == 0 && rl == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (c + e < a.cols) a.col_absmax[c + e] = s[e];
+    }
+    if (!live) return;
+
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (c + e >= a.cols) break;
+        // fl32(fl32(x * inv) + 1.5 * 2^23): the low byte is the code (two
+        // roundings, no fused multiply-add)
+        uint32_t b[kLaneRows];
+        {
+#pragma clang fp contract(off)
+#pragma unroll
+            for (int j = 0; j < kLaneRows; ++j) {
+                const float p = h2f(half_at(v[j], e)) * inv[e];
+                b[j] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
+            }
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            w[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u),
+                                         __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u), 0x05040100u);
+        int8_t* dst = a.qt + (c + e) * a.ldqt + r0;
+        if (kVecOut) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kLaneRows; ++j)
+                if (r0 + j < a.ldqt) dst[j] = (int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xffu);
+        }
+    }
+}
+
+// ---- fp16 outlier columns of the weight gradient ---------------------------
+
+constexpr int kFixCols = 2;      // columns of g per thread
+constexpr int kFixGroup = 8;     // outlier slots per pass over the rows
+
+// acc[s][n] = 0 for the slots s < min(count, cap)
+__global__ __launch_bounds__(256) void fix_zero_kernel(FixArgs f) {
+    int32_t cnt = *f.count;
+    if (cnt > f.cap) cnt = f.cap;
+    const int64_t total = (int64_t)cnt * f.n_pad;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256)
+        f.acc[t] = 0.0f;
+}
+
+// acc[s][n] += sum over this workgroup's rows i of g[i, n] * x_out[i, s]
+// (fp32, one atomic add per slot and column per workgroup)
+__global__ __launch_bounds__(256) void fix_partial_kernel(FixArgs f) {
+    int32_t cnt = *f.count;
+    if (cnt > f.cap) cnt = f.cap;
+    const int64_t n0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kFixCols;
+    if (n0 >= f.n) return;
+    const int64_t i0 = (int64_t)blockIdx.y * f.rows_per_block;
+    const int64_t i1 = i0 + f.rows_per_block < f.m ? i0 + f.rows_per_block : f.m;
+    const bool pair = n0 + 1 < f.n;
+    for (int s0 = 0; s0 < cnt; s0 += kFixGroup) {
+        float acc[kFixGroup][kFixCols];
+#pragma unroll
+        for (int s = 0; s < kFixGroup; ++s) acc[s][0] = acc[s][1] = 0.0f;
+#pragma unroll 4
+        for (int64_t i = i0; i < i1; ++i) {
+            const half_bits* gr = f.g + i * f.ldg + n0;
+            const float g0 = h2f(gr[0]);
+            const float g1 = pair ? h2f(gr[1]) : 0.0f;
+            const half_bits* xr = f.x_out + i * f.ldo + s0;   // slots past cnt hold zeros
+#pragma unroll
+            for (int s = 0; s < kFixGroup; ++s) {
+                const float xv = h2f(xr[s]);
+                acc[s][0] = fmaf(g0, xv, acc[s][0]);
+                acc[s][1] = fmaf(g1, xv, acc[s][1]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kFixGroup; ++s) {
+            if (s0 + s < cnt) {
+                float* dst = f.acc + (int64_t)(s0 + s) * f.n_pad + n0;
+                unsafeAtomicAdd(dst, acc[s][0]);
+                if (pair) unsafeAtomicAdd(dst + 1, acc[s][1]);
+            }
+        }
+    }
+}
+
+// grad_w[n, idx[s]] = fp16(acc[s][n]) for s < min(count, cap)
+__global__ __launch_bounds__(256) void fix_store_kernel(FixArgs f) {
+    int32_t cnt = *f.count;
+    if (cnt > f.cap) cnt = f.cap;
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= f.n) return;
+    for (int32_t s = 0; s < cnt; ++s)
+        f.grad_w[n * f.ldgw + f.idx[s]] = f2h(f.acc[(int64_t)s * f.n_pad + n]);
+}
+
+__global__ __launch_bounds__(256) void fill_f16_kernel(half_bits* out, int64_t rows, int64_t cols, int64_t ld) {
+    const int64_t total = rows * cols;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256)
+        out[(t / cols) * ld + t % cols] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_fill_f16(half_bits* out, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    int64_t blocks = ceil_div(rows * cols, 256);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(fill_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols, ld);
+    return hipGetLastError();
+}
+
+int64_t colquant_row_blocks(int64_t rows) { return ceil_div(rows > 0 ? rows : 1, kBlockRows); }
+
+hipError_t launch_colwise_quant(const ColQuantArgs& in, hipStream_t stream) {
+    ColQuantArgs a = in;
+    a.cols_pad = round_up(a.cols, kStripCols);
+    a.row_blocks = colquant_row_blocks(a.rows);
+    const bool vec_in = a.cols % 8 == 0 && a.lda % 8 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+    const bool vec_out = a.ldqt % 16 == 0 && (reinterpret_cast<uintptr_t>(a.qt) & 15) == 0;
+    const unsigned gx = (unsigned)ceil_div(a.cols, kStripCols);
+    if (a.rows > 0) {
+        const dim3 grid(gx, (unsigned)a.row_blocks);
+        if (vec_in)
+            hipLaunchKernelGGL(colmax_kernel<true>, grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(colmax_kernel<false>, grid, dim3(256), 0, stream, a);
+    } else {
+        // no rows: every column scale is 0 (one zero partial row)
+        a.row_blocks = 0;
+    }
+    // at least one row block: it writes the column scales even when ldqt == 0
+    const dim3 grid(gx, (unsigned)(a.ldqt > 0 ? ceil_div(a.ldqt, kBlockRows) : 1));
+    if (vec_in && vec_out)
+        hipLaunchKernelGGL((colquant_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    else if (vec_in)
+        hipLaunchKernelGGL((colquant_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    else if (vec_out)
+        hipLaunchKernelGGL((colquant_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((colquant_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+FixArgs fix_geometry(FixArgs f) {
+    f.n_pad = round_up(f.n, 2);
+    const int64_t gx = ceil_div(f.n, 256 * kFixCols);
+    int64_t rb = ceil_div(2048, gx);                 // about 2048 workgroups
+    const int64_t max_rb = ceil_div(f.m, 32);        // at least 32 rows each
+    if (rb > max_rb) rb = max_rb;
+    if (rb < 1) rb = 1;
+    f.rows_per_block = ceil_div(f.m, rb);
+    f.row_blocks = ceil_div(f.m, f.rows_per_block);
+    return f;
+}
+
+size_t fix_acc_bytes(int64_t n, int32_t cap) { return (size_t)(cap > 0 ? cap : 1) * (size_t)round_up(n, 2) * 4; }
+
+hipError_t launch_outlier_grad(const FixArgs& in, hipStream_t stream) {
+    const FixArgs f = fix_geometry(in);
+    if (f.cap <= 0 || f.m <= 0 || f.n <= 0) return hipSuccess;
+    int64_t zero_blocks = ceil_div((int64_t)f.cap * f.n_pad, 256);
+    if (zero_blocks > 2048) zero_blocks = 2048;     // grid-stride beyond
+    hipLaunchKernelGGL(fix_zero_kernel, dim3((unsigned)zero_blocks), dim3(256), 0, stream, f);
+    hipLaunchKernelGGL(fix_partial_kernel, dim3((unsigned)ceil_div(f.n, 256 * kFixCols), (unsigned)f.row_blocks),
+                       dim3(256), 0, stream, f);
+    hipLaunchKernelGGL(fix_store_kernel, dim3((unsigned)ceil_div(f.n, 256)), dim3(256), 0, stream, f);
+    return hipGetLastError();
+}
+
+}  // namespace i8mp

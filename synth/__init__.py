@@ -1,7 +1,7 @@
 """Seeded synthetic layers for the int8 mixed-precision linear.
 
 This package only draws random inputs (fp16 activations with planted outlier
-columns, fp16 weights, optional fp16 bias) with numpy's PCG64 generator.  It
+columns, fp16 weights, optional fp16 bias, fp16 upstream gradients) with numpy's PCG64 generator.  It
 holds none of the method's arithmetic: no thresholds are applied to decide
 anything, nothing is quantized, nothing is multiplied.  Both the CPU oracle's
 tests and the GPU path's tests and benchmark draw their inputs from here.
@@ -16,4 +16,5 @@ from .layers import (  # noqa: F401
     draw_activations,
     draw_weight,
     draw_bias,
+    draw_grad,
 )

@@ -163,6 +163,13 @@ def draw_bias(n: int, *, seed: Tuple[int, int, int] = (0, 0, 0), std: float = 0.
     return (r3.standard_normal(n, dtype=np.float32) * np.float32(std)).astype(np.float16)
 
 
+def draw_grad(m: int, n: int, *, seed: Tuple[int, int, int] = (0, 0, 0), std: float = 1.0) -> np.ndarray:
+    """fp16 upstream gradient dL/dy [m, n]: seeded normal draws times ``std``."""
+    cfg, lay, var = seed
+    r4 = _rng(cfg, lay, 4, var)
+    return (r4.standard_normal(m * n, dtype=np.float32) * np.float32(std)).astype(np.float16).reshape(m, n)
+
+
 @dataclass
 class Layer:
     spec: LayerSpec

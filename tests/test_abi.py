@@ -178,6 +178,72 @@ def test_forward_validation(L):
     assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 0, None, FAKE, 32, None) == OK
 
 
+def test_backward_validation(L):
+    lay = _lib.BackwardWorkspaceLayout()
+    assert L.i8mp_linear_backward_workspace_query(2048, 4096, 11008, 20, ctypes.byref(lay)) == OK
+    assert lay.ld_n == 4096 and lay.ld_m == 2048
+    offs = [lay.gq_offset, lay.gs_offset, lay.wtq_offset, lay.wts_offset, lay.gtq_offset, lay.gts_offset,
+            lay.xtq_offset, lay.xts_offset, lay.scratch_offset]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.wtq_offset - lay.gq_offset >= 2048 * 4096
+    assert lay.bytes >= lay.scratch_offset + lay.scratch_bytes
+    assert L.i8mp_linear_backward_workspace_query(133145, 16, 64, 0, ctypes.byref(lay)) == ERANGE
+    assert L.i8mp_linear_backward_workspace_query(16, 133145, 64, 0, ctypes.byref(lay)) == ERANGE
+    assert L.i8mp_linear_backward_workspace_query(16, 16, 0, 0, ctypes.byref(lay)) == EINVAL
+    assert L.i8mp_linear_backward_workspace_query(16, 16, 64, -1, ctypes.byref(lay)) == EINVAL
+    assert L.i8mp_linear_backward_workspace_query(16, 16, 64, 0, None) == EINVAL
+
+    assert L.i8mp_linear_backward_workspace_query(16, 32, 64, 8, ctypes.byref(lay)) == OK
+    fl = _lib.LinearWorkspaceLayout()
+    assert L.i8mp_linear_workspace_query(16, 32, 64, 8, ctypes.byref(fl)) == OK
+    args = dict(g=FAKE, ldg=32, x=FAKE, ldx=64, w=FAKE, ldw=64, m=16, n=32, k=64, cap=8, fws=FAKE,
+                fwsb=fl.bytes, gx=FAKE, ldgx=64, gw=FAKE, ldgw=64, ws=FAKE, wsb=lay.bytes)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.i8mp_linear_backward(a["g"], a["ldg"], a["x"], a["ldx"], a["w"], a["ldw"], a["m"], a["n"],
+                                      a["k"], a["cap"], a["fws"], a["fwsb"], a["gx"], a["ldgx"], a["gw"],
+                                      a["ldgw"], a["ws"], a["wsb"], None)
+
+    assert call(g=None) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(ldg=31) == EINVAL
+    assert call(ldw=63) == EINVAL
+    assert call(ldx=63) == EINVAL
+    assert call(ldgx=63) == EINVAL
+    assert call(ldgw=63) == EINVAL
+    assert call(ldgw=MAX_LD + 1, gx=None) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(cap=-1) == EINVAL
+    assert call(m=133145) == ERANGE
+    assert call(n=133145, ldg=133145) == ERANGE
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=lay.bytes - 1) == EWORKSPACE
+    assert call(fwsb=fl.bytes - 1) == EWORKSPACE
+    assert call(gx=None, gw=None) == OK
+    assert call(m=0, gw=None) == OK
+    assert call(n=0, gx=None) == OK
+    # w is only needed for grad_x, x only for grad_w
+    if not _has_gpu():
+        assert call(w=None, gx=None) == EDEVICE
+        assert call(x=None, gw=None) == EDEVICE
+
+    cq = L.i8mp_int8_colwise_quant
+    wsb = L.i8mp_colwise_quant_workspace_bytes(100, 70)
+    assert wsb >= 70 * 4 and L.i8mp_colwise_quant_workspace_bytes(-1, 70) == 0
+    assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, 99, FAKE, FAKE, wsb, None) == EINVAL   # ldqt < rows
+    assert cq(FAKE, 100, 70, 69, None, None, 0, FAKE, 100, FAKE, FAKE, wsb, None) == EINVAL  # lda < cols
+    assert cq(FAKE, 100, 70, 70, FAKE, None, 4, FAKE, 100, FAKE, FAKE, wsb, None) == EINVAL  # idx without count
+    assert cq(FAKE, 100, 70, 70, None, None, 0, None, 100, FAKE, FAKE, wsb, None) == EINVAL
+    assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, 100, None, FAKE, wsb, None) == EINVAL
+    assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, MAX_LD + 1, FAKE, FAKE, wsb, None) == EINVAL
+    assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, 100, FAKE, FAKE, wsb - 1, None) == EWORKSPACE
+    assert cq(FAKE, 100, 0, 70, None, None, 0, FAKE, 100, FAKE, None, 0, None) == OK
+    if not _has_gpu():
+        assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, 100, FAKE, FAKE, wsb, None) == EDEVICE
+
+
 def _has_gpu():
     try:
         import torch
