@@ -288,6 +288,193 @@ def dequant_run(steps: int, warmup: int) -> int:
     return 0
 
 
+def backward_run(args) -> int:
+    """The backward through every layer of a prefill workload: grad_x and
+    grad_w of each linear for a seeded upstream gradient, with the forward's
+    outlier list (from its quantization of x, untimed) and the fp16 weight
+    kept for training.  One JSON line; the dominant kernel is the fused int8
+    GEMM (two per layer), timed alone on the same operands."""
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+    from synth import draw_grad, make_layer
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs, kind = workload_specs(args.workload)
+    if kind != "prefill":
+        raise SystemExit("--mode backward takes a prefill workload")
+    cap = args.cap
+    base = []
+    per_copy = 0
+    for s in specs:
+        log(f"layer {s.name}: m={s.m} k={s.k} n={s.n} outliers={s.n_outlier}")
+        L = make_layer(s)
+        x = torch.from_numpy(L.x).to(dev)
+        w = torch.from_numpy(L.w).to(dev)
+        g = torch.from_numpy(draw_grad(s.m, s.n, seed=(s.config_id, s.layer_id, s.variant_id))).to(dev)
+        fws = i8.LinearWorkspace.create(s.m, s.n, s.k, cap, dev)
+        i8.linear_quantize(x, fws, s.tau)
+        bws = i8.BackwardWorkspace.create(s.m, s.n, s.k, cap, dev)
+        base.append((s, x, w, g, fws))
+        per_copy += 2 * (x.numel() + w.numel() + g.numel()) + bws.buf.numel() + 2 * (s.m + s.n) * s.k
+    copies = int(min(64, max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))))
+    log(f"rotation copies: {copies} ({per_copy / 2**20:.1f} MiB each)")
+    sets = []
+    for c in range(copies):
+        layer_sets = []
+        for s, x, w, g, fws in base:
+            if c > 0:
+                x, w, g = x.clone(), w.clone(), g.clone()
+                fws2 = i8.LinearWorkspace.create(s.m, s.n, s.k, cap, dev)
+                i8.linear_quantize(x, fws2, s.tau)
+                fws = fws2
+            bws = i8.BackwardWorkspace.create(s.m, s.n, s.k, cap, dev)
+            gx = torch.empty((s.m, s.k), dtype=torch.float16, device=dev)
+            gw = torch.empty((s.n, s.k), dtype=torch.float16, device=dev)
+            layer_sets.append((s, x, w, g, fws, bws, gx, gw))
+        sets.append(layer_sets)
+    torch.cuda.synchronize()
+    for s, x, w, g, fws, *_ in sets[0]:
+        if fws.outlier_overflow():
+            raise SystemExit(f"layer {s.name}: more outlier columns than cap={cap}")
+
+    def step(c: int) -> None:
+        for s, x, w, g, fws, bws, gx, gw in sets[c]:
+            i8.linear_backward(g, x, w, fws, True, True, bws, gx, gw)
+
+    for i in range(max(args.warmup, copies)):
+        step(i % copies)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    log(f"eager: {eager_ms * 1e3:.2f} us/step")
+    ms, launch, graph_ms = eager_ms, "eager", None
+    if args.graph == "on":
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+
+        def capture(nsteps):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(gr, stream=st):
+                    for c in range(nsteps):
+                        step(c)
+            return gr
+
+        g_all = capture(copies)
+        rem = args.steps % copies
+        g_rem = capture(rem) if rem else None
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // copies)):
+            g_all.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps // copies):
+            g_all.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        log(f"graph replay: {graph_ms * 1e3:.2f} us/step")
+        if graph_ms < ms:
+            ms, launch = graph_ms, "hipGraph replay"
+
+    # the two gradient GEMMs of each layer alone: the same fused kernel on the
+    # same operands, reached through the forward's quantize -> matmul-dequant
+    # entries (the row-wise codes of g^T are the column-wise codes of g)
+    gemm_sets = []
+    for s, x, w, g, fws, bws, gx, gw in sets[0]:
+        wt_q, wt_s = i8.colwise_quant(w)
+        ws_x = i8.LinearWorkspace.create(s.m, s.k, s.n, 0, dev)
+        i8.linear_quantize(g, ws_x, 0.0)
+        xt_q, xt_s = i8.colwise_quant(x, fws.idx(), fws.count())
+        ws_w = i8.LinearWorkspace.create(s.n, s.k, s.m, 0, dev)
+        i8.linear_quantize(g.t().contiguous(), ws_w, 0.0)
+        gemm_sets.append((s, (ws_x, wt_q, wt_s, gx), (ws_w, xt_q, xt_s, gw)))
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    gemm_us = {}
+    reps = max(10, args.steps // 2)
+    with torch.cuda.stream(st):
+        for s, gx_args, gw_args in gemm_sets:
+            for tag, (wsq, bq, bs, out) in (("grad_x", gx_args), ("grad_w", gw_args)):
+                for _ in range(3):
+                    i8.linear_matmul_dequant(wsq, bq, bs, None, out)
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=st):
+                    for _ in range(4):
+                        i8.linear_matmul_dequant(wsq, bq, bs, None, out)
+                gr.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for _ in range(reps):
+                    gr.replay()
+                e1.record(st)
+                torch.cuda.synchronize()
+                gemm_us[f"{s.name}.{tag}"] = e0.elapsed_time(e1) * 1e3 / (reps * 4)
+                log(f"gemm {s.name} {tag}: {gemm_us[f'{s.name}.{tag}']:.2f} us/launch")
+
+    ops = sum(4 * s.m * s.n * s.k for s in specs)
+    value = ops / (ms * 1e-3) / 1e12
+    g_time = sum(gemm_us.values()) * 1e-6
+    achieved = ops / g_time / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_OPS / 1e12, "unit": "TFLOP/s",
+            "frac": round(achieved / (PEAK_INT8_OPS / 1e12), 4), "traffic": None,
+            "kernel": "fused int8 GEMM + dequant epilogue (gemm_dtl_kernel), grad_x and grad_w launches",
+            "per_launch_us": {k: round(v, 3) for k, v in gemm_us.items()},
+            "timing": "HIP events around graph replays of each gradient GEMM's launches"}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle  # only this leg of the benchmark touches the oracle
+        log(f"cpu oracle for ~{args.cpu_seconds:.0f} s")
+        rows = 256
+        prepared = []
+        for s in specs:
+            L = make_layer(s, m=rows)
+            gg = draw_grad(s.m, s.n, seed=(s.config_id, s.layer_id, s.variant_id))[:rows]
+            prepared.append((s, L, gg, oracle.outlier_columns(L.x, s.tau)))
+        done, reps_c, t0 = 0.0, 0, time.perf_counter()
+        while True:
+            for s, L, gg, cols in prepared:
+                oracle.linear_backward(gg, L.x, L.w, cols)
+                done += 4.0 * rows * s.n * s.k
+            reps_c += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps_c >= 1000:
+                break
+        try:
+            from threadpoolctl import threadpool_info
+            threads = sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas")
+        except Exception:  # pragma: no cover
+            threads = 1
+        cpu = {"value": done / el / 1e12, "unit": "TOPS", "cores": max(threads, 1), "kind": "oracle",
+               "sample": f"{reps_c} passes of the backward over the workload's layers with {rows} of each "
+                         f"layer's rows (outlier set from the sampled rows)", "seconds": round(el, 2)}
+
+    print(json.dumps({
+        "metric": "int8 linear backward TOPS (grad_x + grad_w, 4*m*n*k per layer) & % int8-MFMA peak",
+        "value": round(value, 4), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+f16", "data": "synthetic (seeded layers and upstream gradients)",
+        "config": {"workload": args.workload + "_backward",
+                   "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n, "outlier_cols": s.n_outlier}
+                              for s in specs],
+                   "threshold": specs[0].tau, "cap": cap, "launch": launch,
+                   "eager_ms_per_step": round(eager_ms, 6),
+                   "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
+                   "rotation_copies": copies, "device": torch.cuda.get_device_name(dev)},
+        "roofline": roof, "cpu_baseline": cpu}), flush=True)
+    return 0
+
+
 def copy_run(launches: int) -> int:
     """A plain copy of known size (COPY_MB MiB read, COPY_MB MiB written) for counter calibration."""
     import torch
@@ -312,9 +499,10 @@ def main() -> int:
     ap.add_argument("--graph", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward"), default="bench",
                     help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
-                         "dequant: the int8 dequantize op on a 65B weight")
+                         "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
+                         "every layer of a prefill workload")
     ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
@@ -339,6 +527,8 @@ def main() -> int:
         return copy_run(args.launches)
     if args.mode == "dequant":
         return dequant_run(args.steps, args.warmup)
+    if args.mode == "backward":
+        return backward_run(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     specs, kind = workload_specs(args.workload)

@@ -408,6 +408,7 @@ def linear_backward(grad_out: torch.Tensor, x: torch.Tensor, w: Optional[torch.T
                     forward_workspace: Optional[LinearWorkspace] = None,
                     need_grad_x: bool = True, need_grad_w: bool = True,
                     workspace: Optional[BackwardWorkspace] = None,
+                    out_x: Optional[torch.Tensor] = None, out_w: Optional[torch.Tensor] = None,
                     ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Both gradients of ``linear`` for dL/dout = grad_out: (grad_x fp16 [m, k], grad_w fp16 [n, k]).
 
@@ -437,8 +438,15 @@ def linear_backward(grad_out: torch.Tensor, x: torch.Tensor, w: Optional[torch.T
         workspace = BackwardWorkspace.create(m, n, k, cap, dev)
     elif (workspace.m, workspace.n, workspace.k, workspace.cap) != (m, n, k, cap):
         raise ValueError("backward workspace was created for another shape or capacity")
-    gx = torch.empty((m, k), dtype=torch.float16, device=dev) if need_grad_x else None
-    gw = torch.empty((n, k), dtype=torch.float16, device=dev) if need_grad_w else None
+    gx = gw = None
+    if need_grad_x:
+        gx = torch.empty((m, k), dtype=torch.float16, device=dev) if out_x is None else out_x
+        if tuple(gx.shape) != (m, k) or not gx.is_contiguous() or gx.dtype != torch.float16:
+            raise ValueError("out_x must be a contiguous fp16 [m, k] tensor")
+    if need_grad_w:
+        gw = torch.empty((n, k), dtype=torch.float16, device=dev) if out_w is None else out_w
+        if tuple(gw.shape) != (n, k) or not gw.is_contiguous() or gw.dtype != torch.float16:
+            raise ValueError("out_w must be a contiguous fp16 [n, k] tensor")
     fws = None if forward_workspace is None else forward_workspace.buf
     with torch.cuda.device(dev):
         check(lib().i8mp_linear_backward(_ptr(grad_out), ldg, _ptr(x), ldx, _ptr(w if need_grad_x else None), ldw,

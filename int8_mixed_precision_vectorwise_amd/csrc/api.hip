@@ -83,7 +83,7 @@ void backward_layout(int64_t m, int64_t n, int64_t k, int32_t cap, i8mp_backward
     if (colquant_scratch_bytes(m, k) > colmax) colmax = colquant_scratch_bytes(m, k);
     L->scratch_offset = off;
     const size_t acc_at = align_up(colmax);
-    L->scratch_bytes = acc_at + fix_acc_bytes(n, cap);
+    L->scratch_bytes = acc_at + fix_part_bytes(m, n, cap);
     off = align_up(off + L->scratch_bytes);
     L->bytes = off;
 }
@@ -488,7 +488,19 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
         const char* fws = static_cast<const char*>(fwd_workspace);
         const int32_t* idx = fws ? reinterpret_cast<const int32_t*>(fws + F.idx_offset) : nullptr;
         const int32_t* count = fws ? reinterpret_cast<const int32_t*>(fws + F.count_offset) : nullptr;
-        // g and x column-wise, x's outlier columns zeroed (CAt), then the GEMM
+        // g and x column-wise, x's outlier columns zeroed (CAt), then the GEMM;
+        // the pass over g also sums the fp16 outlier columns per row block
+        FixArgs f{};
+        if (fws && cap > 0) {
+            f.x_out = reinterpret_cast<const half_bits*>(fws + F.xo_offset);
+            f.ldo = F.cap_pad;
+            f.idx = idx;
+            f.count = count;
+            f.cap = cap;
+            f.part = reinterpret_cast<float*>(ws + L.scratch_offset + (L.scratch_bytes - fix_part_bytes(m, n, cap)));
+            f.grad_w = static_cast<half_bits*>(grad_w);
+            f.ldgw = ldgw;
+        }
         ColQuantArgs c{};
         c.x = g;
         c.rows = m;
@@ -498,7 +510,9 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
         c.ldqt = L.ld_m;
         c.col_absmax = reinterpret_cast<float*>(ws + L.gts_offset);
         c.partial = colmax;
+        c.fix = f;
         if (i8mp_status s = launched(launch_colwise_quant(c, stream)); s != I8MP_OK) return s;
+        c.fix = FixArgs{};
         c.x = static_cast<const half_bits*>(x);
         c.cols = k;
         c.lda = ldx;
@@ -522,22 +536,7 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
         G.out = static_cast<half_bits*>(grad_w);
         G.ldout = ldgw;
         if (i8mp_status s = launched(launch_gemm_fused(G, stream)); s != I8MP_OK) return s;
-        if (fws && cap > 0) {
-            FixArgs f{};
-            f.g = g;
-            f.ldg = ldg;
-            f.m = m;
-            f.n = n;
-            f.x_out = reinterpret_cast<const half_bits*>(fws + F.xo_offset);
-            f.ldo = F.cap_pad;
-            f.idx = idx;
-            f.count = count;
-            f.cap = cap;
-            f.acc = reinterpret_cast<float*>(ws + L.scratch_offset + (L.scratch_bytes - fix_acc_bytes(n, cap)));
-            f.grad_w = static_cast<half_bits*>(grad_w);
-            f.ldgw = ldgw;
-            if (i8mp_status s = launched(launch_outlier_grad(f, stream)); s != I8MP_OK) return s;
-        }
+        if (i8mp_status s = launched(launch_outlier_store(f, m, n, stream)); s != I8MP_OK) return s;
     }
     return I8MP_OK;
 }

@@ -53,9 +53,83 @@ __device__ inline void load_lane_rows(const ColQuantArgs& a, int64_t r0, int64_t
     }
 }
 
+// Block sums of the fp16 outlier columns of grad_w while g's rows are in
+// registers: part[blockIdx.y][s][col] = sum over the block's rows r of
+// g[r, col] * x_out[r, s] in fp32, in a fixed order: each lane takes its 16
+// rows in pairs with v_dot2_f32_f16 (two exact fp16 products added into an
+// fp32 accumulator), lane pairs one row-lane apart are added (DPP), then the
+// 16 row groups of the workgroup in order.  Slots go 8 at a time.
+__device__ inline float dpp_ror8(float v) {  // lane i <- lane (i + 8) mod 16 of its row: lane i ^ 8
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf,
+                                                                 false));
+}
+
+__device__ inline void fix_block_sums(const ColQuantArgs& a, const uint4 (&v)[kLaneRows], int64_t r0, int cc,
+                                      int rl, int wave, int tid) {
+    const FixArgs& f = a.fix;
+    int32_t cnt = *f.count;
+    if (cnt > f.cap) cnt = f.cap;
+    __shared__ float red[16][8][kStripCols];  // [row group][slot][column of the strip]
+    for (int32_t s0 = 0; s0 < cnt; s0 += 8) {
+        float acc[8][8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[s][e] = 0.0f;
+#pragma unroll
+        for (int jp = 0; jp < kLaneRows / 2; ++jp) {
+            uint32_t xw[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t r = r0 + 2 * jp + h;
+                // x_out has ldo >= round_up(cap, 8) columns, zero past the count
+                const uint4 xv = r < a.rows ? *reinterpret_cast<const uint4*>(f.x_out + r * f.ldo + s0)
+                                            : make_uint4(0, 0, 0, 0);
+                xw[h][0] = xv.x; xw[h][1] = xv.y; xw[h][2] = xv.z; xw[h][3] = xv.w;
+            }
+            const uint4 g0 = v[2 * jp], g1 = v[2 * jp + 1];
+            const uint32_t gw[2][4] = {{g0.x, g0.y, g0.z, g0.w}, {g1.x, g1.y, g1.z, g1.w}};
+            // (value of row 2jp, value of row 2jp + 1) per slot and per column
+            h2_t xp[8], gp[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                xp[2 * w] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(xw[1][w], xw[0][w], 0x05040100u));
+                xp[2 * w + 1] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(xw[1][w], xw[0][w], 0x07060302u));
+                gp[2 * w] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(gw[1][w], gw[0][w], 0x05040100u));
+                gp[2 * w + 1] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(gw[1][w], gw[0][w], 0x07060302u));
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[s][e] = __builtin_amdgcn_fdot2(gp[e], xp[s], acc[s][e], false);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[s][e] += dpp_ror8(acc[s][e]);
+        if ((rl & 1) == 0) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[wave * 4 + (rl >> 1)][s][cc * 8 + e] = acc[s][e];
+        }
+        __syncthreads();
+        for (int o = tid; o < 8 * kStripCols; o += 256) {
+            const int s = o / kStripCols, ci = o % kStripCols;
+            float t = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) t += red[q][s][ci];
+            const int64_t col = (int64_t)blockIdx.x * kStripCols + ci;
+            if (s0 + s < cnt && col < a.cols)
+                f.part[((int64_t)blockIdx.y * f.cap + s0 + s) * a.cols_pad + col] = t;
+        }
+        __syncthreads();
+    }
+}
+
 // Pass 1: maxima of |x| per column over each 512-row block,
-// partial[blockIdx.y][col] (fp32, exact).
-template <bool kVec>
+// partial[blockIdx.y][col] (fp32, exact); kFix: also the block sums above.
+template <bool kVec, bool kFix>
 __global__ __launch_bounds__(256) void colmax_kernel(ColQuantArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cc = lane & 7, rl = lane >> 3;
@@ -81,6 +155,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(ColQuantArgs a) {
         const int64_t col = (int64_t)blockIdx.x * kStripCols + tid;
         if (col < a.cols) a.partial[(int64_t)blockIdx.y * a.cols_pad + col] = h2f(half_at(m, e));
     }
+    if constexpr (kFix) fix_block_sums(a, v, r0, cc, rl, wave, tid);
 }
 
 // Pass 2: codes of x^T.  Column scale s = max over the partial maxima, inv =
@@ -159,66 +234,18 @@ __global__ __launch_bounds__(256) void colquant_kernel(ColQuantArgs a) {
     }
 }
 
-// ---- fp16 outlier columns of the weight gradient ---------------------------
-
-constexpr int kFixCols = 2;      // columns of g per thread
-constexpr int kFixGroup = 8;     // outlier slots per pass over the rows
-
-// acc[s][n] = 0 for the slots s < min(count, cap)
-__global__ __launch_bounds__(256) void fix_zero_kernel(FixArgs f) {
+// grad_w[col, idx[s]] = fp16(sum over the row blocks of the block sums), in
+// row-block order
+__global__ __launch_bounds__(256) void fix_store_kernel(FixArgs f, int64_t n, int64_t cols_pad, int64_t row_blocks) {
     int32_t cnt = *f.count;
     if (cnt > f.cap) cnt = f.cap;
-    const int64_t total = (int64_t)cnt * f.n_pad;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256)
-        f.acc[t] = 0.0f;
-}
-
-// acc[s][n] += sum over this workgroup's rows i of g[i, n] * x_out[i, s]
-// (fp32, one atomic add per slot and column per workgroup)
-__global__ __launch_bounds__(256) void fix_partial_kernel(FixArgs f) {
-    int32_t cnt = *f.count;
-    if (cnt > f.cap) cnt = f.cap;
-    const int64_t n0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kFixCols;
-    if (n0 >= f.n) return;
-    const int64_t i0 = (int64_t)blockIdx.y * f.rows_per_block;
-    const int64_t i1 = i0 + f.rows_per_block < f.m ? i0 + f.rows_per_block : f.m;
-    const bool pair = n0 + 1 < f.n;
-    for (int s0 = 0; s0 < cnt; s0 += kFixGroup) {
-        float acc[kFixGroup][kFixCols];
-#pragma unroll
-        for (int s = 0; s < kFixGroup; ++s) acc[s][0] = acc[s][1] = 0.0f;
-#pragma unroll 4
-        for (int64_t i = i0; i < i1; ++i) {
-            const half_bits* gr = f.g + i * f.ldg + n0;
-            const float g0 = h2f(gr[0]);
-            const float g1 = pair ? h2f(gr[1]) : 0.0f;
-            const half_bits* xr = f.x_out + i * f.ldo + s0;   // slots past cnt hold zeros
-#pragma unroll
-            for (int s = 0; s < kFixGroup; ++s) {
-                const float xv = h2f(xr[s]);
-                acc[s][0] = fmaf(g0, xv, acc[s][0]);
-                acc[s][1] = fmaf(g1, xv, acc[s][1]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < kFixGroup; ++s) {
-            if (s0 + s < cnt) {
-                float* dst = f.acc + (int64_t)(s0 + s) * f.n_pad + n0;
-                unsafeAtomicAdd(dst, acc[s][0]);
-                if (pair) unsafeAtomicAdd(dst + 1, acc[s][1]);
-            }
-        }
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= n) return;
+    for (int32_t s = blockIdx.y; s < cnt; s += gridDim.y) {
+        float t = 0.0f;
+        for (int64_t rb = 0; rb < row_blocks; ++rb) t += f.part[(rb * f.cap + s) * cols_pad + col];
+        f.grad_w[col * f.ldgw + f.idx[s]] = f2h(t);
     }
-}
-
-// grad_w[n, idx[s]] = fp16(acc[s][n]) for s < min(count, cap)
-__global__ __launch_bounds__(256) void fix_store_kernel(FixArgs f) {
-    int32_t cnt = *f.count;
-    if (cnt > f.cap) cnt = f.cap;
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= f.n) return;
-    for (int32_t s = 0; s < cnt; ++s)
-        f.grad_w[n * f.ldgw + f.idx[s]] = f2h(f.acc[(int64_t)s * f.n_pad + n]);
 }
 
 __global__ __launch_bounds__(256) void fill_f16_kernel(half_bits* out, int64_t rows, int64_t cols, int64_t ld) {
@@ -248,10 +275,15 @@ hipError_t launch_colwise_quant(const ColQuantArgs& in, hipStream_t stream) {
     const unsigned gx = (unsigned)ceil_div(a.cols, kStripCols);
     if (a.rows > 0) {
         const dim3 grid(gx, (unsigned)a.row_blocks);
-        if (vec_in)
-            hipLaunchKernelGGL(colmax_kernel<true>, grid, dim3(256), 0, stream, a);
+        const bool fix = a.fix.x_out != nullptr && a.fix.cap > 0;
+        if (vec_in && fix)
+            hipLaunchKernelGGL((colmax_kernel<true, true>), grid, dim3(256), 0, stream, a);
+        else if (vec_in)
+            hipLaunchKernelGGL((colmax_kernel<true, false>), grid, dim3(256), 0, stream, a);
+        else if (fix)
+            hipLaunchKernelGGL((colmax_kernel<false, true>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL(colmax_kernel<false>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((colmax_kernel<false, false>), grid, dim3(256), 0, stream, a);
     } else {
         // no rows: every column scale is 0 (one zero partial row)
         a.row_blocks = 0;
@@ -269,29 +301,11 @@ hipError_t launch_colwise_quant(const ColQuantArgs& in, hipStream_t stream) {
     return hipGetLastError();
 }
 
-FixArgs fix_geometry(FixArgs f) {
-    f.n_pad = round_up(f.n, 2);
-    const int64_t gx = ceil_div(f.n, 256 * kFixCols);
-    int64_t rb = ceil_div(2048, gx);                 // about 2048 workgroups
-    const int64_t max_rb = ceil_div(f.m, 32);        // at least 32 rows each
-    if (rb > max_rb) rb = max_rb;
-    if (rb < 1) rb = 1;
-    f.rows_per_block = ceil_div(f.m, rb);
-    f.row_blocks = ceil_div(f.m, f.rows_per_block);
-    return f;
-}
-
-size_t fix_acc_bytes(int64_t n, int32_t cap) { return (size_t)(cap > 0 ? cap : 1) * (size_t)round_up(n, 2) * 4; }
-
-hipError_t launch_outlier_grad(const FixArgs& in, hipStream_t stream) {
-    const FixArgs f = fix_geometry(in);
-    if (f.cap <= 0 || f.m <= 0 || f.n <= 0) return hipSuccess;
-    int64_t zero_blocks = ceil_div((int64_t)f.cap * f.n_pad, 256);
-    if (zero_blocks > 2048) zero_blocks = 2048;     // grid-stride beyond
-    hipLaunchKernelGGL(fix_zero_kernel, dim3((unsigned)zero_blocks), dim3(256), 0, stream, f);
-    hipLaunchKernelGGL(fix_partial_kernel, dim3((unsigned)ceil_div(f.n, 256 * kFixCols), (unsigned)f.row_blocks),
-                       dim3(256), 0, stream, f);
-    hipLaunchKernelGGL(fix_store_kernel, dim3((unsigned)ceil_div(f.n, 256)), dim3(256), 0, stream, f);
+hipError_t launch_outlier_store(const FixArgs& f, int64_t m, int64_t n, hipStream_t stream) {
+    if (!f.x_out || f.cap <= 0 || m <= 0 || n <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)(f.cap < 32 ? f.cap : 32));
+    hipLaunchKernelGGL(fix_store_kernel, grid, dim3(256), 0, stream, f, n, round_up(n, kStripCols),
+                       colquant_row_blocks(m));
     return hipGetLastError();
 }
 
