@@ -334,6 +334,50 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
                                  void* grad_x, int64_t ldgx, void* grad_w, int64_t ldgw,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Blockwise 4-bit weights (the page "Loading an LLM in 4 bits using
+ * bitsandbytes", sections "Normalized Float" and "Double Quantization"): fp4
+ * with 1 sign bit, 2 exponent bits and 1 mantissa bit (E2M1: magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6), blocks of 64 weights with an fp32 scale each, and
+ * double quantization of those scales to 8 bits in groups of 256.  Readings:
+ *  - a block is 64 consecutive weights of a row of W [n x k], k a multiple of
+ *    64; its scale A = max |w| over the block (fp32, exact);
+ *  - code = sign bit of w (bit 3) | magnitude code (bits 0..2) of the E2M1
+ *    value nearest to fl32(|w| * fl32(6 / A)) (ties to the even mantissa bit,
+ *    saturating at 6); two codes per byte, element 2j in the low nibble of
+ *    byte j of the row;
+ *  - double quantization over the flattened block scales, groups of 256 (the
+ *    last may be shorter): s2 = group max, c8 = clamp(rne(fl32(A * fl32(255 / s2))),
+ *    0, 255); the scale used is then fl32(c8 * fl32(s2 / 255));
+ *  - w' = fl32(E2M1 value * fl32(A / 6)).
+ * The nf4 type has no value table on the pages and is not provided.
+ */
+
+/* codes uint8 [n x ldc], ldc >= k/2; absmax fp32 [n * k/64] (row-major blocks).
+ * k must be a positive multiple of 64 (else I8MP_EINVAL); n == 0 is a no-op. */
+i8mp_status i8mp_fp4_quantize(const void* w, int64_t n, int64_t k, int64_t ldw, uint8_t* codes, int64_t ldc,
+                              float* absmax, hipStream_t stream);
+
+/* c8 uint8 [nb], s2 fp32 [ceil(nb / 256)] from the block scales absmax fp32 [nb]. */
+i8mp_status i8mp_fp4_double_quant(const float* absmax, int64_t nb, uint8_t* c8, float* s2, hipStream_t stream);
+
+/* out [n x ldout], ldout >= k: w' as fp16 (I8MP_DTYPE_F16, rounded once from
+ * the fp32 w') or fp32.  Scales: absmax (non-NULL, c8 and s2 NULL) or the
+ * double-quantized c8 / s2 (absmax NULL). */
+i8mp_status i8mp_fp4_dequantize(const uint8_t* codes, int64_t ldc, int64_t n, int64_t k, const float* absmax,
+                                const uint8_t* c8, const float* s2, int32_t out_dtype, void* out, int64_t ldout,
+                                hipStream_t stream);
+
+/* The 4-bit linear for decode-sized batches:
+ *   out[i, r] = fp16( sum_j x[i, j] * w'[r, j] + bias[r] )   (fp32 sums)
+ * x fp16 [m x ldx] 16-byte aligned with ldx a multiple of 8; codes 16-byte
+ * aligned with ldc a multiple of 16; scales as for the dequantize; bias
+ * optional fp16 [n]; out fp16 [m x ldout], ldout >= n.  Any m >= 0: every four
+ * rows of x read the weights once. */
+i8mp_status i8mp_fp4_linear(const void* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* codes, int64_t ldc,
+                            const float* absmax, const uint8_t* c8, const float* s2, int64_t n, const void* bias,
+                            void* out, int64_t ldout, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

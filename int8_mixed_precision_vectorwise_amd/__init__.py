@@ -44,6 +44,11 @@ __all__ = [
     "colwise_quant",
     "linear_backward",
     "BackwardWorkspace",
+    "Fp4Weight",
+    "fp4_quantize",
+    "fp4_double_quant",
+    "fp4_dequantize",
+    "fp4_linear",
     "I8mpError",
 ]
 
@@ -455,4 +460,92 @@ def linear_backward(grad_out: torch.Tensor, x: torch.Tensor, w: Optional[torch.T
                                          _stream(dev)),
               "i8mp_linear_backward")
     return gx, gw
+
+
+@dataclass
+class Fp4Weight:
+    """A weight in blockwise 4-bit E2M1 form: packed codes [n, ldc] (ldc = k/2
+    rounded up to 16 bytes), and either fp32 block scales [n, k/64] or their
+    8-bit double quantization (c8 [n * k/64], s2 [ceil(n * k/64 / 256)])."""
+
+    codes: torch.Tensor
+    k: int
+    absmax: Optional[torch.Tensor] = None
+    c8: Optional[torch.Tensor] = None
+    s2: Optional[torch.Tensor] = None
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[0]
+
+    def scale_ptrs(self):
+        if self.absmax is not None:
+            return _ptr(self.absmax), None, None
+        return None, _ptr(self.c8), _ptr(self.s2)
+
+
+def fp4_quantize(w: torch.Tensor, double_quant: bool = False) -> Fp4Weight:
+    """Blockwise 4-bit E2M1 quantization of an fp16 weight [n, k] (k a multiple of 64)."""
+    dev = _device_of(w)
+    ldw = _rowmajor(w, "w", torch.float16)
+    n, k = w.shape
+    if k % 64 or k == 0:
+        raise ValueError("k must be a positive multiple of 64")
+    ldc = (k // 2 + 15) // 16 * 16
+    codes = torch.zeros((n, ldc), dtype=torch.uint8, device=dev)
+    absmax = torch.empty((n, k // 64), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_fp4_quantize(_ptr(w), n, k, ldw, _ptr(codes), ldc, _ptr(absmax), _stream(dev)),
+              "i8mp_fp4_quantize")
+    fw = Fp4Weight(codes, k, absmax)
+    return fp4_double_quant(fw) if double_quant else fw
+
+
+def fp4_double_quant(fw: Fp4Weight) -> Fp4Weight:
+    """The same weight with its block scales quantized to 8 bits in groups of 256."""
+    if fw.absmax is None:
+        raise ValueError("already double-quantized")
+    dev = _device_of(fw.codes, fw.absmax)
+    nb = fw.absmax.numel()
+    c8 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    s2 = torch.empty(max((nb + 255) // 256, 1), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        check(lib().i8mp_fp4_double_quant(_ptr(fw.absmax), nb, _ptr(c8), _ptr(s2), _stream(dev)),
+              "i8mp_fp4_double_quant")
+    return Fp4Weight(fw.codes, fw.k, None, c8, s2[: (nb + 255) // 256])
+
+
+def fp4_dequantize(fw: Fp4Weight, dtype: torch.dtype = torch.float16) -> torch.Tensor:
+    """w' [n, k] = E2M1 value * (block scale / 6), as fp16 or fp32."""
+    if dtype not in (torch.float16, torch.float32):
+        raise ValueError("dtype must be torch.float16 or torch.float32")
+    dev = _device_of(fw.codes)
+    out = torch.empty((fw.n, fw.k), dtype=dtype, device=dev)
+    a, c8, s2 = fw.scale_ptrs()
+    with torch.cuda.device(dev):
+        check(lib().i8mp_fp4_dequantize(_ptr(fw.codes), fw.codes.stride(0), fw.n, fw.k, a, c8, s2,
+                                        0 if dtype == torch.float16 else 1, _ptr(out), fw.k, _stream(dev)),
+              "i8mp_fp4_dequantize")
+    return out
+
+
+def fp4_linear(x: torch.Tensor, fw: Fp4Weight, bias: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The 4-bit linear for decode-sized batches: fp16 out [m, n] = x . w'^T + bias."""
+    dev = _device_of(x, fw.codes, bias, out)
+    ldx = _rowmajor(x, "x", torch.float16)
+    m, k = x.shape
+    if k != fw.k:
+        raise ValueError("x and the weight differ in k")
+    if bias is not None:
+        _vec(bias, "bias", torch.float16, fw.n)
+    if out is None:
+        out = torch.empty((m, fw.n), dtype=torch.float16, device=dev)
+    ldout = _rowmajor(out, "out", torch.float16)
+    a, c8, s2 = fw.scale_ptrs()
+    with torch.cuda.device(dev):
+        check(lib().i8mp_fp4_linear(_ptr(x), m, k, ldx, _ptr(fw.codes), fw.codes.stride(0), a, c8, s2, fw.n,
+                                    _ptr(bias), _ptr(out), ldout, _stream(dev)),
+              "i8mp_fp4_linear")
+    return out
 

@@ -35,6 +35,10 @@ EXPORTS = (
     "i8mp_int8_colwise_quant",
     "i8mp_linear_backward_workspace_query",
     "i8mp_linear_backward",
+    "i8mp_fp4_quantize",
+    "i8mp_fp4_double_quant",
+    "i8mp_fp4_dequantize",
+    "i8mp_fp4_linear",
 )
 
 
@@ -130,6 +134,16 @@ def _declare(lib):
                                          c_int64, c_int64, c_int32, c_void_p, c_size_t, c_void_p, c_int64,
                                          c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
     lib.i8mp_linear_backward.restype = c_int32
+    lib.i8mp_fp4_quantize.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p]
+    lib.i8mp_fp4_quantize.restype = c_int32
+    lib.i8mp_fp4_double_quant.argtypes = [c_void_p, c_int64, c_void_p, c_void_p, c_void_p]
+    lib.i8mp_fp4_double_quant.restype = c_int32
+    lib.i8mp_fp4_dequantize.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_int32,
+                                        c_void_p, c_int64, c_void_p]
+    lib.i8mp_fp4_dequantize.restype = c_int32
+    lib.i8mp_fp4_linear.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
+                                    c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p]
+    lib.i8mp_fp4_linear.restype = c_int32
 
 
 def lib():

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libi8mp.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip", "dequant.hip", "backward.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip", "dequant.hip", "backward.hip", "fp4.hip"]
 
 # -packed-fp32-ops: no v_pk_*_f32 generation.  Correctly rounded fp32 division:
 # the quantizer's 127/absmax must be the IEEE quotient.  No fast-math anywhere.

@@ -541,4 +541,84 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
     return I8MP_OK;
 }
 
+namespace {
+bool fp4_scales_ok(const float* absmax, const uint8_t* c8, const float* s2) {
+    return absmax ? (!c8 && !s2) : (c8 && s2);
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+}  // namespace
+
+i8mp_status i8mp_fp4_quantize(const void* w, int64_t n, int64_t k, int64_t ldw, uint8_t* codes, int64_t ldc,
+                              float* absmax, hipStream_t stream) {
+    if (n < 0 || k < 64 || k % 64 || ldw < k || ldc < k / 2) return I8MP_EINVAL;
+    if (n == 0) return I8MP_OK;
+    if (!w || !codes || !absmax) return I8MP_EINVAL;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    Fp4Args a{};
+    a.w = static_cast<const half_bits*>(w);
+    a.ldw = ldw;
+    a.codes_out = codes;
+    a.ldc = ldc;
+    a.absmax_out = absmax;
+    a.n = n;
+    a.k = k;
+    return launched(launch_fp4_quantize(a, stream));
+}
+
+i8mp_status i8mp_fp4_double_quant(const float* absmax, int64_t nb, uint8_t* c8, float* s2, hipStream_t stream) {
+    if (nb < 0) return I8MP_EINVAL;
+    if (nb == 0) return I8MP_OK;
+    if (!absmax || !c8 || !s2) return I8MP_EINVAL;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    return launched(launch_fp4_double_quant(absmax, nb, c8, s2, stream));
+}
+
+i8mp_status i8mp_fp4_dequantize(const uint8_t* codes, int64_t ldc, int64_t n, int64_t k, const float* absmax,
+                                const uint8_t* c8, const float* s2, int32_t out_dtype, void* out, int64_t ldout,
+                                hipStream_t stream) {
+    if (n < 0 || k < 64 || k % 64 || ldc < k / 2 || ldout < k) return I8MP_EINVAL;
+    if (out_dtype != I8MP_DTYPE_F16 && out_dtype != I8MP_DTYPE_F32) return I8MP_EINVAL;
+    if (n == 0) return I8MP_OK;
+    if (!codes || !out || !fp4_scales_ok(absmax, c8, s2)) return I8MP_EINVAL;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    Fp4Args a{};
+    a.codes = codes;
+    a.ldc = ldc;
+    a.absmax = absmax;
+    a.c8 = c8;
+    a.s2 = s2;
+    a.out = out;
+    a.ldout = ldout;
+    a.half_out = out_dtype == I8MP_DTYPE_F16;
+    a.n = n;
+    a.k = k;
+    return launched(launch_fp4_dequantize(a, stream));
+}
+
+i8mp_status i8mp_fp4_linear(const void* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* codes, int64_t ldc,
+                            const float* absmax, const uint8_t* c8, const float* s2, int64_t n, const void* bias,
+                            void* out, int64_t ldout, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 64 || k % 64 || ldx < k || ldx % 8 || ldc < k / 2 || ldc % 16 || ldout < n)
+        return I8MP_EINVAL;
+    if (m == 0 || n == 0) return I8MP_OK;
+    if (!x || !codes || !out || !fp4_scales_ok(absmax, c8, s2)) return I8MP_EINVAL;
+    if (!aligned16(x) || !aligned16(codes)) return I8MP_EINVAL;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    Fp4Args a{};
+    a.x = static_cast<const half_bits*>(x);
+    a.ldx = ldx;
+    a.m = m;
+    a.codes = codes;
+    a.ldc = ldc;
+    a.absmax = absmax;
+    a.c8 = c8;
+    a.s2 = s2;
+    a.bias = static_cast<const half_bits*>(bias);
+    a.out = out;
+    a.ldout = ldout;
+    a.n = n;
+    a.k = k;
+    return launched(launch_fp4_linear(a, stream));
+}
+
 }  // extern "C"

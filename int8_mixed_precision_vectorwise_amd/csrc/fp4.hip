@@ -1,0 +1,254 @@
+// Blockwise 4-bit (FP4, E2M1) weights: quantization in blocks of 64 with an
+// fp32 absmax per block, 8-bit double quantization of the block scales in
+// groups of 256, dequantization, and the decode linear (one to four rows of
+// x against 4-bit weights).  The format and the two block sizes are those of
+// the page "Loading an LLM in 4 bits using bitsandbytes" (sections "Normalized
+// Float" and "Double Quantization"): 1 sign bit, 2 exponent bits, 1 mantissa bit.
+#include "common.h"
+#include "quant_util.h"
+
+namespace i8mp {
+
+namespace {
+
+constexpr int kBlk = 64;     // weights per block scale
+constexpr int kDqGroup = 256;  // block scales per double-quantization group
+
+typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+
+// Magnitude code (0..7) of a non-negative fp32 value: the nearest of 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6, ties to the even code (the mantissa bit), saturating at
+// 6.  A value exactly between two neighbours goes up only where the upper
+// neighbour's code is even (0.75, 1.75, 3.5).
+__device__ inline uint32_t e2m1_mag(float v) {
+    return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) + (uint32_t)(v >= 1.75f) +
+           (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) + (uint32_t)(v > 5.0f);
+}
+
+// fp32 value of a 4-bit code from its bits: exponent field e (bias 1), mantissa m
+__device__ inline float e2m1_f32(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u);
+    return __uint_as_float(mag | ((c & 8u) << 28));
+}
+
+// Block scale A of block blk (flattened): the fp32 absmax, or the double-
+// quantized fl32(c8 * fl32(s2 / 255)).
+__device__ inline float block_scale(const Fp4Args& a, int64_t blk) {
+    if (a.absmax) return a.absmax[blk];
+    const float step = a.s2[blk / kDqGroup] / 255.0f;
+    return (float)a.c8[blk] * step;
+}
+
+// One lane per 8 weights, 8 lanes per block: absmax, codes, packed nibbles
+// (element 2j in the low nibble of byte j).
+template <bool kVec>
+__global__ __launch_bounds__(256) void fp4_quant_kernel(Fp4Args a) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t kb = a.k / kBlk;
+    const int64_t blk = t >> 3;
+    const int part = (int)(t & 7);
+    const bool live = blk < a.n * kb;
+    const int64_t row = live ? blk / kb : 0, b = live ? blk % kb : 0;
+    const int64_t col = b * kBlk + part * 8;
+    const uint4 v = live ? load8<kVec>(a.w + row * a.ldw, col, a.k) : make_uint4(0, 0, 0, 0);
+    float mx = chunk_absmax(v);
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));   // the 8 lanes of a block are 8 consecutive lanes
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+    if (!live) return;
+    const float inv = mx > 0.0f ? 6.0f / mx : 0.0f;  // IEEE division
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const half_bits h = half_at(v, e);
+        const float f = fabsf(h2f(h)) * inv;
+        packed |= (e2m1_mag(f) | ((uint32_t)(h >> 15) << 3)) << (4 * e);
+    }
+    uint8_t* dst = a.codes_out + row * a.ldc + col / 2;
+    if (kVec) {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = (uint8_t)(packed >> (8 * j));
+    }
+    if (part == 0) a.absmax_out[blk] = mx;
+}
+
+// One workgroup per group of 256 block scales.
+__global__ __launch_bounds__(256) void fp4_dq_kernel(const float* absmax, int64_t nb, uint8_t* c8, float* s2) {
+    const int64_t i = (int64_t)blockIdx.x * kDqGroup + threadIdx.x;
+    const float v = i < nb ? absmax[i] : 0.0f;
+    __shared__ float red[4];
+    const float w = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    __syncthreads();
+    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = s > 0.0f ? 255.0f / s : 0.0f;  // IEEE division
+    if (i < nb) c8[i] = (uint8_t)fminf(fmaxf(__builtin_rintf(v * inv), 0.0f), 255.0f);
+    if (threadIdx.x == 0) s2[blockIdx.x] = s;
+}
+
+// One lane per 8 weights: w' = fl32(E2M1 value * fl32(A / 6)), stored as fp32
+// or rounded to fp16.
+__global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t kb = a.k / kBlk;
+    const int64_t blk = t >> 3;
+    if (blk >= a.n * kb) return;
+    const int64_t row = blk / kb, col = (blk % kb) * kBlk + (t & 7) * 8;
+    const uint8_t* src = a.codes + row * a.ldc + col / 2;
+    const uint32_t packed = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) |
+                            ((uint32_t)src[3] << 24);
+    const float d = block_scale(a, blk) / 6.0f;
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = e2m1_f32((packed >> (4 * e)) & 15u) * d;
+    if (a.half_out) {
+        half_bits* o = static_cast<half_bits*>(a.out) + row * a.ldout + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f2h(w[e]);
+    } else {
+        float* o = static_cast<float*>(a.out) + row * a.ldout + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = w[e];
+    }
+}
+
+// The decode linear: out[i, n] = fp16(sum_k x[i, k] * w'[n, k] + bias[n]) for
+// M rows of x.  A wave takes 4 weight rows at a time; lane l takes the 16-byte
+// code chunks l, l + 64, ... (32 weights, half a block) of each of them.  The
+// hardware conversion turns a code byte into two exact fp16 E2M1 values (scale
+// 1); v_dot2_f32_f16 adds their products with x into an fp32 sum per half
+// block, which is then scaled by fl32(A / 6).  kLds: x staged in LDS.
+template <int M, bool kLds>
+__global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
+    extern __shared__ __attribute__((aligned(16))) uint4 xs[];  // [M][k / 8] when kLds
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t k8 = a.k / 8, chunks = a.k / 32, kb = a.k / kBlk;
+    if (kLds) {
+        for (int64_t i = tid; i < M * k8; i += 256) {
+            const int64_t r = i / k8, q = i % k8;
+            xs[i] = *reinterpret_cast<const uint4*>(a.x + r * a.ldx + q * 8);
+        }
+        __syncthreads();
+    }
+    const int64_t groups = (a.n + 3) / 4;
+    for (int64_t rg = (int64_t)blockIdx.x * 4 + wave; rg < groups; rg += (int64_t)gridDim.x * 4) {
+        const int64_t n0 = rg * 4;
+        float acc[4][M];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+        for (int64_t c = lane; c < chunks; c += 64) {
+            uint4 xv[M][4];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xv[m][q] = kLds ? xs[m * k8 + c * 4 + q]
+                                    : *reinterpret_cast<const uint4*>(a.x + m * a.ldx + c * 32 + q * 8);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = n0 + r;
+                if (row >= a.n) break;  // the same for the whole wave
+                const uint4 cv = *reinterpret_cast<const uint4*>(a.codes + row * a.ldc + c * 16);
+                const float d = block_scale(a, row * kb + c / 2) / 6.0f;
+                const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+                float part[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) part[m] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    hh2 wv[4];
+                    wv[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 0);
+                    wv[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 1);
+                    wv[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 2);
+                    wv[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 3);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const uint32_t xq[4] = {xv[m][q].x, xv[m][q].y, xv[m][q].z, xv[m][q].w};
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            part[m] = __builtin_amdgcn_fdot2(wv[b], __builtin_bit_cast(hh2, xq[b]), part[m], false);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] = fmaf(part[m], d, acc[r][m]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float s = wave_sum_f32(acc[r][m]);
+                const int64_t row = n0 + r;
+                if (lane == 0 && row < a.n) {
+                    const float b = a.bias ? h2f(a.bias[row]) : 0.0f;
+                    static_cast<half_bits*>(a.out)[m * a.ldout + row] = f2h(s + b);
+                }
+            }
+        }
+    }
+}
+
+template <int M>
+hipError_t launch_gemv_m(const Fp4Args& a, hipStream_t stream) {
+    const int64_t groups = (a.n + 3) / 4;
+    int64_t blocks = (groups + 3) / 4;
+    if (blocks > 1024) blocks = 1024;
+    const size_t lds = (size_t)M * (size_t)a.k * 2;
+    if (M > 1 && lds <= 64 * 1024)
+        hipLaunchKernelGGL((fp4_gemv_kernel<M, true>), dim3((unsigned)blocks), dim3(256), lds, stream, a);
+    else
+        hipLaunchKernelGGL((fp4_gemv_kernel<M, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp4_quantize(const Fp4Args& a, hipStream_t stream) {
+    const int64_t lanes = a.n * (a.k / kBlk) * 8;
+    if (lanes == 0) return hipSuccess;
+    const bool vec = a.ldw % 8 == 0 && (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && a.ldc % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.codes_out) & 3) == 0;
+    const dim3 grid((unsigned)ceil_div(lanes, 256));
+    if (vec)
+        hipLaunchKernelGGL(fp4_quant_kernel<true>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(fp4_quant_kernel<false>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp4_double_quant(const float* absmax, int64_t nb, uint8_t* c8, float* s2, hipStream_t stream) {
+    if (nb <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fp4_dq_kernel, dim3((unsigned)ceil_div(nb, kDqGroup)), dim3(256), 0, stream, absmax, nb, c8,
+                       s2);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp4_dequantize(const Fp4Args& a, hipStream_t stream) {
+    const int64_t lanes = a.n * (a.k / kBlk) * 8;
+    if (lanes == 0) return hipSuccess;
+    hipLaunchKernelGGL(fp4_dequant_kernel, dim3((unsigned)ceil_div(lanes, 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp4_linear(const Fp4Args& in, hipStream_t stream) {
+    // groups of at most four rows of x, each a launch over all the weights
+    for (int64_t i0 = 0; i0 < in.m; i0 += 4) {
+        Fp4Args a = in;
+        a.x = in.x + i0 * in.ldx;
+        a.out = static_cast<half_bits*>(in.out) + i0 * in.ldout;
+        const int64_t mm = in.m - i0 < 4 ? in.m - i0 : 4;
+        hipError_t e = mm == 1 ? launch_gemv_m<1>(a, stream)
+                     : mm == 2 ? launch_gemv_m<2>(a, stream)
+                     : mm == 3 ? launch_gemv_m<3>(a, stream)
+                               : launch_gemv_m<4>(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace i8mp
