@@ -475,6 +475,127 @@ def backward_run(args) -> int:
     return 0
 
 
+def fp4_run(args) -> int:
+    """The 4-bit (FP4 E2M1, double-quantized block scales) decode linear over
+    a decode workload's layers (the same shapes as the int8 decode workload);
+    one JSON line with its HBM roofline.  Bytes per layer: packed codes,
+    8-bit scales and their group maxima, x and the fp16 output."""
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+    from synth import make_layer
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs, kind = workload_specs(args.workload)
+    if kind != "decode":
+        raise SystemExit("--mode fp4 takes a decode workload (llama13b_decode_m1, _m4, _m16)")
+    base = []
+    per_copy = 0
+    for s in specs:
+        L = make_layer(s)
+        fw = i8.fp4_quantize(torch.from_numpy(L.w).to(dev), double_quant=True)
+        x = torch.from_numpy(L.x).to(dev)
+        base.append((s, x, fw))
+        per_copy += fw.codes.numel() + fw.c8.numel() + 4 * fw.s2.numel()
+    copies = int(min(64, max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))))
+    log(f"rotation copies: {copies} ({per_copy / 2**20:.1f} MiB of 4-bit weights each)")
+    sets = []
+    for c in range(copies):
+        layer_sets = []
+        for s, x, fw in base:
+            fwc = fw if c == 0 else i8.Fp4Weight(fw.codes.clone(), fw.k, None, fw.c8.clone(), fw.s2.clone())
+            out = torch.empty((s.m, s.n), dtype=torch.float16, device=dev)
+            layer_sets.append((s, x, fwc, out))
+        sets.append(layer_sets)
+    torch.cuda.synchronize()
+
+    def step(c: int) -> None:
+        for s, x, fwc, out in sets[c]:
+            i8.fp4_linear(x, fwc, None, out)
+
+    for i in range(max(args.warmup, copies)):
+        step(i % copies)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for c in range(copies):
+                step(c)
+        g.replay()
+        reps = max(1, args.steps // copies)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    # per-layer launch time (same stream, graph replays of that layer alone)
+    per_us = {}
+    with torch.cuda.stream(st):
+        for li, s in enumerate(specs):
+            gl = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gl, stream=st):
+                for c in range(copies):
+                    _, x, fwc, out = sets[c][li]
+                    i8.fp4_linear(x, fwc, None, out)
+            gl.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                gl.replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            per_us[s.name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            log(f"fp4 linear {s.name}: {per_us[s.name]:.2f} us/launch")
+
+    def layer_bytes(s, fw):
+        return fw.n * fw.k // 2 + fw.c8.numel() + 4 * fw.s2.numel() + 2 * s.m * s.k + 2 * s.m * s.n
+
+    byts = sum(layer_bytes(s, fw) for s, _, fw in base)
+    gbs = byts / (ms * 1e-3) / 1e9
+    k_time = sum(per_us.values()) * 1e-6
+    achieved = byts / k_time / 1e9
+    cpu = None
+    if not args.no_cpu:
+        from oracle import fp4 as fp4_oracle  # only this leg of the benchmark touches the oracle
+        rows = 1024
+        prepared = []
+        for s in specs:
+            L = make_layer(s)
+            c, a = fp4_oracle.fp4_quantize(L.w[:rows])
+            c8, s2 = fp4_oracle.double_quant(a)
+            prepared.append((s, L.x, c, fp4_oracle.double_dequant(c8, s2)))
+        done, reps_c, t0 = 0.0, 0, time.perf_counter()
+        while True:
+            for s, x, c, sc in prepared:
+                fp4_oracle.fp4_linear(x, c, sc)
+                done += rows * s.k // 2 + rows * s.k // 64 + 2 * s.m * s.k + 2 * s.m * rows
+            reps_c += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 10.0) or reps_c >= 1000:
+                break
+        cpu = {"value": done / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps_c} passes over the layers with {rows} weight rows each (scales from those rows)",
+               "seconds": round(el, 2)}
+    print(json.dumps({
+        "metric": "4-bit (FP4 E2M1, blocks of 64, double-quantized scales) decode linear GB/s & % HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps * copies, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4+f16", "data": "synthetic (seeded layers)",
+        "config": {"workload": args.workload + "_fp4",
+                   "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n} for s in specs],
+                   "rotation_copies": copies, "launch": "hipGraph replay",
+                   "device": torch.cuda.get_device_name(dev)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": None,
+                     "kernel": "fp4_gemv_kernel", "per_launch_us": {k: round(v, 3) for k, v in per_us.items()},
+                     "timing": "HIP events around graph replays of each layer's launches"},
+        "cpu_baseline": cpu}), flush=True)
+    return 0
+
+
 def copy_run(launches: int) -> int:
     """A plain copy of known size (COPY_MB MiB read, COPY_MB MiB written) for counter calibration."""
     import torch
@@ -499,10 +620,10 @@ def main() -> int:
     ap.add_argument("--graph", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward", "fp4"), default="bench",
                     help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
                          "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
-                         "every layer of a prefill workload")
+                         "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
     ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
@@ -529,6 +650,8 @@ def main() -> int:
         return dequant_run(args.steps, args.warmup)
     if args.mode == "backward":
         return backward_run(args)
+    if args.mode == "fp4":
+        return fp4_run(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     specs, kind = workload_specs(args.workload)

@@ -116,93 +116,127 @@ __global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
 }
 
 // The decode linear: out[i, n] = fp16(sum_k x[i, k] * w'[n, k] + bias[n]) for
-// M rows of x.  A wave takes 4 weight rows at a time; lane l takes the 16-byte
-// code chunks l, l + 64, ... (32 weights, half a block) of each of them.  The
-// hardware conversion turns a code byte into two exact fp16 E2M1 values (scale
-// 1); v_dot2_f32_f16 adds their products with x into an fp32 sum per half
-// block, which is then scaled by fl32(A / 6).  kLds: x staged in LDS.
-template <int M, bool kLds>
-__global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
-    extern __shared__ __attribute__((aligned(16))) uint4 xs[];  // [M][k / 8] when kLds
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t k8 = a.k / 8, chunks = a.k / 32, kb = a.k / kBlk;
-    if (kLds) {
-        for (int64_t i = tid; i < M * k8; i += 256) {
-            const int64_t r = i / k8, q = i % k8;
-            xs[i] = *reinterpret_cast<const uint4*>(a.x + r * a.ldx + q * 8);
+// M rows of x.  A workgroup takes kRows weight rows; its 256 lanes split each
+// row into 16-byte code chunks (32 weights, half a block), lane t taking chunks
+// t, t + 256, ..., the same chunks of all kRows rows, so the lane's x chunk is
+// read once for them.  The next chunk's codes are requested before the current
+// one is used.  The hardware conversion turns a code byte into two exact fp16
+// E2M1 values (scale 1); v_dot2_f32_f16 adds their products with x into an
+// fp32 sum per half block, which is then scaled by fl32(A / 6).  Lane sums are
+// reduced in the wave (DPP), then over the 4 waves in LDS.
+constexpr int kRows = 8;
+
+// Everything one chunk needs, loaded together: the codes of the kRows rows,
+// the lane's x chunk, and the raw block-scale values (converted only where
+// they are used, so that no load is waited for early).
+template <int M>
+struct Fp4Chunk {
+    uint4 cv[kRows];
+    uint4 xv[M][4];
+    float sa[kRows];      // absmax, or the group maximum s2 when double-quantized
+    uint32_t c8[kRows];   // double-quantized scale code
+};
+
+template <int M>
+__device__ inline void fp4_load(const Fp4Args& a, int64_t n0, int64_t c, int64_t kb, Fp4Chunk<M>& t) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t.xv[m][q] = *reinterpret_cast<const uint4*>(a.x + m * a.ldx + c * 32 + q * 8);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const bool live = n0 + r < a.n;
+        const int64_t blk = live ? (n0 + r) * kb + c / 2 : 0;
+        t.cv[r] = live ? *reinterpret_cast<const uint4*>(a.codes + (n0 + r) * a.ldc + c * 16) : make_uint4(0, 0, 0, 0);
+        if (a.absmax) {
+            t.sa[r] = a.absmax[blk];
+            t.c8[r] = 0;
+        } else {
+            t.sa[r] = a.s2[blk / kDqGroup];
+            t.c8[r] = a.c8[blk];
         }
-        __syncthreads();
     }
-    const int64_t groups = (a.n + 3) / 4;
-    for (int64_t rg = (int64_t)blockIdx.x * 4 + wave; rg < groups; rg += (int64_t)gridDim.x * 4) {
-        const int64_t n0 = rg * 4;
-        float acc[4][M];
+}
+
+template <int M>
+__device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M>& t, int64_t n0, float (&acc)[kRows][M]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kRows; ++r) {
+        if (n0 + r >= a.n) break;  // the same for the whole workgroup
+        // block scale A (the absmax, or fl32(c8 * fl32(s2 / 255))), then fl32(A / 6)
+        const float A = a.absmax ? t.sa[r] : (float)t.c8[r] * (t.sa[r] / 255.0f);
+        const float d = A / 6.0f;
+        const uint32_t cw[4] = {t.cv[r].x, t.cv[r].y, t.cv[r].z, t.cv[r].w};
+        float part[M];
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-        for (int64_t c = lane; c < chunks; c += 64) {
-            uint4 xv[M][4];
+        for (int m = 0; m < M; ++m) part[m] = 0.0f;
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    xv[m][q] = kLds ? xs[m * k8 + c * 4 + q]
-                                    : *reinterpret_cast<const uint4*>(a.x + m * a.ldx + c * 32 + q * 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = n0 + r;
-                if (row >= a.n) break;  // the same for the whole wave
-                const uint4 cv = *reinterpret_cast<const uint4*>(a.codes + row * a.ldc + c * 16);
-                const float d = block_scale(a, row * kb + c / 2) / 6.0f;
-                const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
-                float part[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) part[m] = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    hh2 wv[4];
-                    wv[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 0);
-                    wv[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 1);
-                    wv[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 2);
-                    wv[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 3);
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const uint32_t xq[4] = {xv[m][q].x, xv[m][q].y, xv[m][q].z, xv[m][q].w};
-#pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            part[m] = __builtin_amdgcn_fdot2(wv[b], __builtin_bit_cast(hh2, xq[b]), part[m], false);
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < M; ++m) acc[r][m] = fmaf(part[m], d, acc[r][m]);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int q = 0; q < 4; ++q) {
+            hh2 wv[4];
+            wv[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 0);
+            wv[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 1);
+            wv[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 2);
+            wv[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 3);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const float s = wave_sum_f32(acc[r][m]);
-                const int64_t row = n0 + r;
-                if (lane == 0 && row < a.n) {
-                    const float b = a.bias ? h2f(a.bias[row]) : 0.0f;
-                    static_cast<half_bits*>(a.out)[m * a.ldout + row] = f2h(s + b);
-                }
+                const uint32_t xq[4] = {t.xv[m][q].x, t.xv[m][q].y, t.xv[m][q].z, t.xv[m][q].w};
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    part[m] = __builtin_amdgcn_fdot2(wv[b], __builtin_bit_cast(hh2, xq[b]), part[m], false);
             }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(part[m], d, acc[r][m]);
+    }
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t chunks = a.k / 32, kb = a.k / kBlk;
+    const int64_t n0 = (int64_t)blockIdx.x * kRows;
+    float acc[kRows][M];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    int64_t c = tid;
+    if (c < chunks) {
+        Fp4Chunk<M> cur, nxt;
+        fp4_load(a, n0, c, kb, cur);
+        for (;;) {
+            const int64_t cn = c + 256;
+            const bool more = cn < chunks;
+            if (more) fp4_load(a, n0, cn, kb, nxt);  // issued before the current chunk is used
+            fp4_compute(a, cur, n0, acc);
+            if (!more) break;
+            cur = nxt;
+            c = cn;
+        }
+    }
+    __shared__ float red[4][kRows * M];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float s = wave_sum_f32(acc[r][m]);
+            if (lane == 0) red[wave][r * M + m] = s;
+        }
+    __syncthreads();
+    if (tid < kRows * M) {
+        const int r = tid / M, m = tid % M;
+        const int64_t row = n0 + r;
+        if (row < a.n) {
+            const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+            const float b = a.bias ? h2f(a.bias[row]) : 0.0f;
+            static_cast<half_bits*>(a.out)[m * a.ldout + row] = f2h(s + b);
         }
     }
 }
 
 template <int M>
 hipError_t launch_gemv_m(const Fp4Args& a, hipStream_t stream) {
-    const int64_t groups = (a.n + 3) / 4;
-    int64_t blocks = (groups + 3) / 4;
-    if (blocks > 1024) blocks = 1024;
-    const size_t lds = (size_t)M * (size_t)a.k * 2;
-    if (M > 1 && lds <= 64 * 1024)
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, true>), dim3((unsigned)blocks), dim3(256), lds, stream, a);
-    else
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fp4_gemv_kernel<M>), dim3((unsigned)ceil_div(a.n, kRows)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
