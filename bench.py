@@ -328,18 +328,32 @@ def backward_run(args) -> int:
                 i8.linear_quantize(x, fws2, s.tau)
                 fws = fws2
             bws = i8.BackwardWorkspace.create(s.m, s.n, s.k, cap, dev)
+            bws2 = i8.BackwardWorkspace.create(s.m, s.n, s.k, cap, dev) if args.bwd_streams == 2 else None
             gx = torch.empty((s.m, s.k), dtype=torch.float16, device=dev)
             gw = torch.empty((s.n, s.k), dtype=torch.float16, device=dev)
-            layer_sets.append((s, x, w, g, fws, bws, gx, gw))
+            layer_sets.append((s, x, w, g, fws, bws, gx, gw, bws2))
         sets.append(layer_sets)
     torch.cuda.synchronize()
     for s, x, w, g, fws, *_ in sets[0]:
         if fws.outlier_overflow():
             raise SystemExit(f"layer {s.name}: more outlier columns than cap={cap}")
 
+    side = torch.cuda.Stream() if args.bwd_streams == 2 else None  # default priority
+
     def step(c: int) -> None:
-        for s, x, w, g, fws, bws, gx, gw in sets[c]:
-            i8.linear_backward(g, x, w, fws, True, True, bws, gx, gw)
+        if side is None:
+            for s, x, w, g, fws, bws, gx, gw, _ in sets[c]:
+                i8.linear_backward(g, x, w, fws, True, True, bws, gx, gw)
+            return
+        # grad_x of every layer on the current stream, grad_w on a second one
+        # (own workspaces), joined at the end of the step
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        for s, x, w, g, fws, bws, gx, gw, bws2 in sets[c]:
+            i8.linear_backward(g, x, w, fws, True, False, bws, gx, None)
+            with torch.cuda.stream(side):
+                i8.linear_backward(g, x, None, fws, False, True, bws2, None, gw)
+        main.wait_stream(side)
 
     for i in range(max(args.warmup, copies)):
         step(i % copies)
@@ -389,7 +403,7 @@ def backward_run(args) -> int:
     # same operands, reached through the forward's quantize -> matmul-dequant
     # entries (the row-wise codes of g^T are the column-wise codes of g)
     gemm_sets = []
-    for s, x, w, g, fws, bws, gx, gw in sets[0]:
+    for s, x, w, g, fws, bws, gx, gw, _ in sets[0]:
         wt_q, wt_s = i8.colwise_quant(w)
         ws_x = i8.LinearWorkspace.create(s.m, s.k, s.n, 0, dev)
         i8.linear_quantize(g, ws_x, 0.0)
@@ -468,6 +482,7 @@ def backward_run(args) -> int:
                    "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n, "outlier_cols": s.n_outlier}
                               for s in specs],
                    "threshold": specs[0].tau, "cap": cap, "launch": launch,
+                   "streams": args.bwd_streams,
                    "eager_ms_per_step": round(eager_ms, 6),
                    "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
                    "rotation_copies": copies, "device": torch.cuda.get_device_name(dev)},
@@ -625,6 +640,8 @@ def main() -> int:
                          "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
                          "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
     ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
+    ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=2,
+                    help="--mode backward: grad_x and grad_w on one stream, or on two")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
     args = ap.parse_args()
