@@ -190,3 +190,39 @@ def test_linear_backward_llama7b_full_size(layer):
     ref_x, ref_w = _sampled_backward(g, Lr.x, Lr.w, cols, rows_x, rows_w)
     assert_fp16_close(gx[torch.from_numpy(rows_x).cuda()], ref_x, "grad_x rows")
     assert_fp16_close(gw[torch.from_numpy(rows_w).cuda()], ref_w, "grad_w rows")
+
+
+def test_backward_graph_replays_match_eager():
+    # the backward is deterministic (fixed-order sums, no atomics): every
+    # replay of a captured call equals the eager call bit for bit, whatever the
+    # workspace held before
+    m, n, k, cap = 300, 520, 640, 32
+    L = make_inputs(m, k, n, n_outlier=6, seed=(86, 0, 0))
+    g = draw_grad(m, n, seed=(86, 0, 0))
+    xt, gt_, wt_ = dev(L.x), dev(g), dev(L.w)
+    say("linear_backward graph capture")
+    fws = _run_forward(xt, n, k, cap)
+    bws = i8.BackwardWorkspace.create(m, n, k, cap, "cuda")
+    ex, ew = i8.linear_backward(gt_, xt, wt_, fws, workspace=bws)
+    ex, ew = ex.clone(), ew.clone()
+    gx = torch.empty_like(ex)
+    gw = torch.empty_like(ew)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            i8.linear_backward(gt_, xt, wt_, fws, True, True, bws, gx, gw)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        gx.fill_(7.0)
+        gw.fill_(-3.0)
+        bws.buf.fill_(0x5a)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gx.view(torch.int16), ex.view(torch.int16)), rep
+        assert torch.equal(gw.view(torch.int16), ew.view(torch.int16)), rep
+    ref = oracle.linear_backward(g, L.x, L.w, oracle.outlier_columns(L.x, TAU)[:cap])
+    assert_fp16_close(gw, ref.gw, "grad_w after replays")

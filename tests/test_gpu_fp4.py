@@ -130,3 +130,28 @@ def test_fp4_linear_llama13b_decode_full_size(layer, m):
     sc = fp4.double_dequant(c8, s2).reshape(n, k // 64)[rows]
     _, y = fp4.fp4_linear(L.x, ref_c, sc)
     assert_fp16_close(out[:, torch.from_numpy(rows).cuda()], y, "fp4 linear rows")
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_fp4_linear_graph_replays_match_eager(m):
+    n, k = 200, 1024
+    L = make_inputs(m, k, n, seed=(95, m, 0), bias_std=0.05)
+    say(f"fp4_linear graph capture m={m}")
+    fw = i8.fp4_quantize(dev(L.w), double_quant=True)
+    x, b = dev(L.x), dev(L.bias)
+    eager = i8.fp4_linear(x, fw, b).clone()
+    out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            i8.fp4_linear(x, fw, b, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
