@@ -591,7 +591,12 @@ def fp4_run(args) -> int:
             el = time.perf_counter() - t0
             if el >= min(args.cpu_seconds, 10.0) or reps_c >= 1000:
                 break
-        cpu = {"value": done / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        try:
+            from threadpoolctl import threadpool_info
+            threads = sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas")
+        except Exception:  # pragma: no cover
+            threads = 1
+        cpu = {"value": done / el / 1e9, "unit": "GB/s", "cores": max(threads, 1), "kind": "oracle",
                "sample": f"{reps_c} passes over the layers with {rows} weight rows each (scales from those rows)",
                "seconds": round(el, 2)}
     print(json.dumps({
