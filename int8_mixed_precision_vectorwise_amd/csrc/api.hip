@@ -5,6 +5,8 @@
 #include <cstring>
 
 #include "common.h"
+#include "backward.h"
+#include "fp4.h"
 
 using namespace i8mp;
 

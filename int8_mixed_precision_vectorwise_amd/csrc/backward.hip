@@ -9,6 +9,7 @@
 // The two gradient GEMMs themselves are the forward's int8 GEMM with its
 // dequant epilogue (gemm.hip), called from api.hip.
 #include "common.h"
+#include "backward.h"
 #include "quant_util.h"
 
 namespace i8mp {

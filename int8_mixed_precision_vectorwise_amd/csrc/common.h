@@ -89,73 +89,6 @@ hipError_t launch_gemm_fused(const GemmArgs& g, hipStream_t stream);
 bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g);
 hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream);
 
-// ---- backward: column-wise quantization and the outlier weight gradient ----
-// The fp16 outlier columns of grad_w: sum_i g[i, n] * x_out[i, s], summed
-// per 512-row block by the column-maximum pass over g (part), then over the
-// blocks into grad_w[n, idx[s]] for s < min(count, cap).
-struct FixArgs {
-    const half_bits* x_out;      // nullable: off.  The forward's gathered outlier columns [m x ldo],
-    int64_t ldo;                 // zero past the count; ldo >= round_up(cap, 8), a multiple of 8
-    const int32_t* idx;          // [cap] outlier columns
-    const int32_t* count;        // [1]
-    int32_t cap;
-    float* part;                 // [row blocks x cap x cols_pad] fp32 block sums
-    half_bits* grad_w;           // [n x ldgw]
-    int64_t ldgw;
-};
-
-struct ColQuantArgs {
-    const half_bits* x;          // [rows x lda]
-    int64_t rows, cols, lda;
-    const int32_t* zero_idx;     // nullable: columns whose codes are zeroed
-    const int32_t* zero_count;   // [1], used with zero_idx
-    int32_t cap;                 // entries of zero_idx considered: min(count, cap)
-    int8_t* qt;                  // [cols x ldqt] transposed codes, rows .. ldqt - 1 written as 0
-    int64_t ldqt;
-    float* col_absmax;           // [cols]
-    float* partial;              // [row blocks x cols_pad] column maxima of 512-row blocks
-    FixArgs fix;                 // x = g: also the block sums of the outlier columns of grad_w
-    int64_t cols_pad;            // set by the launcher
-    int64_t row_blocks;          // set by the launcher
-};
-
-int64_t colquant_row_blocks(int64_t rows);
-// bytes of ColQuantArgs::partial for a rows x cols input
-inline size_t colquant_scratch_bytes(int64_t rows, int64_t cols) {
-    return (size_t)colquant_row_blocks(rows) * (size_t)round_up(cols > 0 ? cols : 1, 64) * 4;
-}
-// bytes of FixArgs::part for g [m x n] and capacity cap
-inline size_t fix_part_bytes(int64_t m, int64_t n, int32_t cap) {
-    return (size_t)colquant_row_blocks(m) * (size_t)(cap > 0 ? cap : 1) * (size_t)round_up(n > 0 ? n : 1, 64) * 4;
-}
-hipError_t launch_colwise_quant(const ColQuantArgs& a, hipStream_t stream);
-// grad_w[n, idx[s]] = fp16(sum of the block sums) for s < min(count, cap), once
-// the column pass over g [m x n] has written them
-hipError_t launch_outlier_store(const FixArgs& f, int64_t m, int64_t n, hipStream_t stream);
-// out[i, j] = +0 for an fp16 rows x cols matrix (an empty contraction)
-hipError_t launch_fill_f16(half_bits* out, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
-
-// ---- blockwise 4-bit (FP4 E2M1) weights ------------------------------------
-struct Fp4Args {
-    const half_bits* w; int64_t ldw;     // quantize: fp16 weights [n x ldw]
-    uint8_t* codes_out;                  // quantize: packed codes [n x ldc]
-    float* absmax_out;                   // quantize: fp32 block absmax [n * k / 64]
-    const uint8_t* codes; int64_t ldc;   // packed codes, element 2j in the low nibble of byte j
-    const float* absmax;                 // block scales, or null with c8 / s2 (double-quantized)
-    const uint8_t* c8;                   // [n * k / 64]
-    const float* s2;                     // [ceil(n * k / 64 / 256)]
-    const half_bits* x; int64_t ldx, m;  // linear: x [m x ldx]
-    const half_bits* bias;               // linear: nullable
-    void* out; int64_t ldout;
-    bool half_out;                       // dequantize: fp16 (else fp32)
-    int64_t n, k;                        // k a multiple of 64
-};
-hipError_t launch_fp4_quantize(const Fp4Args& a, hipStream_t stream);
-hipError_t launch_fp4_double_quant(const float* absmax, int64_t nb, uint8_t* c8, float* s2, hipStream_t stream);
-hipError_t launch_fp4_dequantize(const Fp4Args& a, hipStream_t stream);
-// x 16-byte aligned with ldx a multiple of 8, codes rows 16-byte aligned (ldc a multiple of 16)
-hipError_t launch_fp4_linear(const Fp4Args& a, hipStream_t stream);
-
 struct DequantArgs {
     const int32_t* c; int64_t ldc;
     const float* row_absmax;

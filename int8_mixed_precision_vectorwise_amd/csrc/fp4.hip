@@ -5,6 +5,7 @@
 // the page "Loading an LLM in 4 bits using bitsandbytes" (sections "Normalized
 // Float" and "Double Quantization"): 1 sign bit, 2 exponent bits, 1 mantissa bit.
 #include "common.h"
+#include "fp4.h"
 #include "quant_util.h"
 
 namespace i8mp {
