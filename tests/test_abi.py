@@ -244,6 +244,40 @@ def test_backward_validation(L):
         assert cq(FAKE, 100, 70, 70, None, None, 0, FAKE, 100, FAKE, FAKE, wsb, None) == EDEVICE
 
 
+def test_fp4_validation(L):
+    q, dqf, dq, lin = L.i8mp_fp4_quantize, L.i8mp_fp4_double_quant, L.i8mp_fp4_dequantize, L.i8mp_fp4_linear
+    # quantize: k a positive multiple of 64, ld checks, n == 0 no-op
+    assert q(FAKE, 4, 100, 100, FAKE, 64, FAKE, None) == EINVAL
+    assert q(FAKE, 4, 0, 64, FAKE, 64, FAKE, None) == EINVAL
+    assert q(FAKE, 4, 128, 127, FAKE, 64, FAKE, None) == EINVAL
+    assert q(FAKE, 4, 128, 128, FAKE, 63, FAKE, None) == EINVAL
+    assert q(None, 4, 128, 128, FAKE, 64, FAKE, None) == EINVAL
+    assert q(FAKE, 4, 128, 128, FAKE, 64, None, None) == EINVAL
+    assert q(None, 0, 128, 128, None, 64, None, None) == OK
+    assert dqf(FAKE, -1, FAKE, FAKE, None) == EINVAL
+    assert dqf(None, 0, None, None, None) == OK
+    assert dqf(None, 10, FAKE, FAKE, None) == EINVAL
+    # dequantize: exactly one kind of scales, a known dtype
+    assert dq(FAKE, 64, 4, 128, FAKE, FAKE, FAKE, 0, FAKE, 128, None) == EINVAL
+    assert dq(FAKE, 64, 4, 128, None, FAKE, None, 0, FAKE, 128, None) == EINVAL
+    assert dq(FAKE, 64, 4, 128, None, None, None, 0, FAKE, 128, None) == EINVAL
+    assert dq(FAKE, 64, 4, 128, FAKE, None, None, 7, FAKE, 128, None) == EINVAL
+    assert dq(FAKE, 64, 4, 128, FAKE, None, None, 0, FAKE, 127, None) == EINVAL
+    assert dq(FAKE, 64, 0, 128, FAKE, None, None, 1, FAKE, 128, None) == OK
+    # linear: x and codes 16-byte aligned, ldx a multiple of 8, ldc of 16
+    A16 = ctypes.c_void_p(0x1000)
+    assert lin(A16, 2, 128, 132, A16, 64, FAKE, None, None, 8, None, A16, 8, None) == EINVAL   # ldx % 8
+    assert lin(A16, 2, 128, 128, A16, 72, FAKE, None, None, 8, None, A16, 8, None) == EINVAL   # ldc % 16
+    assert lin(ctypes.c_void_p(0x1008), 2, 128, 128, A16, 64, FAKE, None, None, 8, None, A16, 8, None) == EINVAL
+    assert lin(A16, 2, 128, 128, A16, 64, FAKE, FAKE, FAKE, 8, None, A16, 8, None) == EINVAL   # both scales
+    assert lin(A16, 2, 128, 128, A16, 64, FAKE, None, None, 8, None, A16, 7, None) == EINVAL   # ldout < n
+    assert lin(A16, 2, 100, 128, A16, 64, FAKE, None, None, 8, None, A16, 8, None) == EINVAL   # k % 64
+    assert lin(None, 0, 128, 128, None, 64, FAKE, None, None, 8, None, None, 8, None) == OK
+    if not _has_gpu():
+        assert lin(A16, 2, 128, 128, A16, 64, FAKE, None, None, 8, None, A16, 8, None) == EDEVICE
+        assert q(FAKE, 4, 128, 128, FAKE, 64, FAKE, None) == EDEVICE
+
+
 def _has_gpu():
     try:
         import torch
