@@ -37,6 +37,9 @@ DEFAULT_WORKLOAD = "opt350m_mlp_pair_m512"
 GEMM_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
              for f in ("gemm.hip", "decode.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+FP4_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
+            for f in ("fp4.hip", "fp4.h", "quant_util.h", "common.h")]
+FP4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp4_traffic.json")
 GEMM_KERNELS = ("i8mp::gemm", "i8mp::gemv")  # kernel-name parts of the fused GEMM launches
 COPY_MB = 256              # calibration copy: 256 MiB read + 256 MiB written
 
@@ -80,6 +83,13 @@ def _code_only(text: str) -> str:
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
     return "\n".join(ln for ln in lines if ln)
+
+
+def fp4_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in FP4_SRCS:
+        h.update(_code_only(open(f).read()).encode())
+    return h.hexdigest()[:16]
 
 
 def src_sha() -> str:
@@ -599,6 +609,13 @@ def fp4_run(args) -> int:
         cpu = {"value": done / el / 1e9, "unit": "GB/s", "cores": max(threads, 1), "kind": "oracle",
                "sample": f"{reps_c} passes over the layers with {rows} weight rows each (scales from those rows)",
                "seconds": round(el, 2)}
+    traffic = None
+    try:
+        t = json.load(open(FP4_TRAFFIC_FILE))
+        if t.get("fp4_source_sha") == fp4_src_sha():
+            traffic = t.get("per_step_bytes", {}).get(args.workload)
+    except (OSError, ValueError):
+        pass
     print(json.dumps({
         "metric": "4-bit (FP4 E2M1, blocks of 64, double-quantized scales) decode linear GB/s & % HBM peak",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps * copies, "warmup": args.warmup,
@@ -609,7 +626,7 @@ def fp4_run(args) -> int:
                    "rotation_copies": copies, "launch": "hipGraph replay",
                    "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": None,
+                     "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": traffic,
                      "kernel": "fp4_gemv_kernel", "per_launch_us": {k: round(v, 3) for k, v in per_us.items()},
                      "timing": "HIP events around graph replays of each layer's launches"},
         "cpu_baseline": cpu}), flush=True)
