@@ -125,27 +125,30 @@ __global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
 // E2M1 values (scale 1); v_dot2_f32_f16 adds their products with x into an
 // fp32 sum per half block, which is then scaled by fl32(A / 6).  Lane sums are
 // reduced in the wave (DPP), then over the 4 waves in LDS.
-constexpr int kRows = 8;
+// weight rows per workgroup: 4 for three or more rows of x in the pipelined form
+// (two chunk buffers), 8 otherwise
+template <int M, bool kOne>
+constexpr int fp4_rows() { return M >= 3 && !kOne ? 4 : 8; }
 
 // Everything one chunk needs, loaded together: the codes of the kRows rows,
 // the lane's x chunk, and the raw block-scale values (converted only where
 // they are used, so that no load is waited for early).
-template <int M>
+template <int M, int R>
 struct Fp4Chunk {
-    uint4 cv[kRows];
+    uint4 cv[R];
     uint4 xv[M][4];
-    float sa[kRows];      // absmax, or the group maximum s2 when double-quantized
-    uint32_t c8[kRows];   // double-quantized scale code
+    float sa[R];          // absmax, or the group maximum s2 when double-quantized
+    uint32_t c8[R];       // double-quantized scale code
 };
 
-template <int M>
-__device__ inline void fp4_load(const Fp4Args& a, int64_t n0, int64_t c, int64_t kb, Fp4Chunk<M>& t) {
+template <int M, int R>
+__device__ inline void fp4_load(const Fp4Args& a, int64_t n0, int64_t c, int64_t kb, Fp4Chunk<M, R>& t) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int q = 0; q < 4; ++q) t.xv[m][q] = *reinterpret_cast<const uint4*>(a.x + m * a.ldx + c * 32 + q * 8);
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < R; ++r) {
         const bool live = n0 + r < a.n;
         const int64_t blk = live ? (n0 + r) * kb + c / 2 : 0;
         t.cv[r] = live ? *reinterpret_cast<const uint4*>(a.codes + (n0 + r) * a.ldc + c * 16) : make_uint4(0, 0, 0, 0);
@@ -159,10 +162,10 @@ __device__ inline void fp4_load(const Fp4Args& a, int64_t n0, int64_t c, int64_t
     }
 }
 
-template <int M>
-__device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M>& t, int64_t n0, float (&acc)[kRows][M]) {
+template <int M, int R>
+__device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M, R>& t, int64_t n0, float (&acc)[R][M]) {
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < R; ++r) {
         if (n0 + r >= a.n) break;  // the same for the whole workgroup
         // block scale A (the absmax, or fl32(c8 * fl32(s2 / 255))), then A / 6 as
         // A * fl32(1 / 6): within one ulp of the IEEE quotient the dequantize op
@@ -200,6 +203,7 @@ __device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M>& t, int64
 // measured faster (14.0 against 16.6 us).
 template <int M, bool kOne>
 __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
+    constexpr int kRows = fp4_rows<M, kOne>();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t chunks = a.k / 32, kb = a.k / kBlk;
     const int64_t n0 = (int64_t)blockIdx.x * kRows;
@@ -211,12 +215,12 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
     int64_t c = tid;
     if (kOne) {
         if (c < chunks) {
-            Fp4Chunk<M> cur;
+            Fp4Chunk<M, kRows> cur;
             fp4_load(a, n0, c, kb, cur);
             fp4_compute(a, cur, n0, acc);
         }
     } else if (c < chunks) {
-        Fp4Chunk<M> cur, nxt;
+        Fp4Chunk<M, kRows> cur, nxt;
         fp4_load(a, n0, c, kb, cur);
         for (;;) {
             const int64_t cn = c + 256;
@@ -250,11 +254,12 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
 
 template <int M>
 hipError_t launch_gemv_m(const Fp4Args& a, hipStream_t stream) {
-    const dim3 grid((unsigned)ceil_div(a.n, kRows));
     if (M > 1 && a.k / 32 <= 256)
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((fp4_gemv_kernel<M, true>), dim3((unsigned)ceil_div(a.n, fp4_rows<M, true>())),
+                           dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((fp4_gemv_kernel<M, false>), dim3((unsigned)ceil_div(a.n, fp4_rows<M, false>())),
+                           dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
