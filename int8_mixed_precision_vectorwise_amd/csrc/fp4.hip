@@ -125,10 +125,10 @@ __global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
 // E2M1 values (scale 1); v_dot2_f32_f16 adds their products with x into an
 // fp32 sum per half block, which is then scaled by fl32(A / 6).  Lane sums are
 // reduced in the wave (DPP), then over the 4 waves in LDS.
-// weight rows per workgroup: 4 for three or more rows of x in the pipelined form
-// (two chunk buffers), 8 otherwise
+// weight rows per workgroup: 4 for three or more rows of x (fewer registers,
+// two waves per SIMD at four rows of x), 8 otherwise
 template <int M, bool kOne>
-constexpr int fp4_rows() { return M >= 3 && !kOne ? 4 : 8; }
+constexpr int fp4_rows() { return M >= 3 ? 4 : 8; }
 
 // Everything one chunk needs, loaded together: the codes of the kRows rows,
 // the lane's x chunk, and the raw block-scale values (converted only where
