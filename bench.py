@@ -165,13 +165,13 @@ def capture_gemm_graphs(torch, i8, sets, specs, copies):
     with torch.cuda.stream(st):
         for li in range(len(specs)):
             for c in range(copies):  # eager warm-up of this layer's launches
-                _, _, wqc, wac, b, ws, out = sets[c][li]
-                i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+                _, xc, wqc, wac, b, ws, out = sets[c][li]
+                i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=st):
                 for c in range(copies):
-                    _, _, wqc, wac, b, ws, out = sets[c][li]
-                    i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+                    _, xc, wqc, wac, b, ws, out = sets[c][li]
+                    i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
             graphs.append(g)
     torch.cuda.synchronize()
     return graphs, st
@@ -345,8 +345,8 @@ def backward_run(args) -> int:
         sets.append(layer_sets)
     torch.cuda.synchronize()
     for s, x, w, g, fws, *_ in sets[0]:
-        if fws.outlier_overflow():
-            raise SystemExit(f"layer {s.name}: more outlier columns than cap={cap}")
+        if fws.outliers_past_cap():
+            log(f"layer {s.name}: more outlier columns than cap={cap} (those past it take the slow path)")
 
     side = torch.cuda.Stream() if args.bwd_streams == 2 else None  # default priority
 
@@ -419,8 +419,9 @@ def backward_run(args) -> int:
         i8.linear_quantize(g, ws_x, 0.0)
         xt_q, xt_s = i8.colwise_quant(x, fws.idx(), fws.count())
         ws_w = i8.LinearWorkspace.create(s.n, s.k, s.m, 0, dev)
-        i8.linear_quantize(g.t().contiguous(), ws_w, 0.0)
-        gemm_sets.append((s, (ws_x, wt_q, wt_s, gx), (ws_w, xt_q, xt_s, gw)))
+        gt = g.t().contiguous()
+        i8.linear_quantize(gt, ws_w, 0.0)
+        gemm_sets.append((s, (g, ws_x, wt_q, wt_s, gx), (gt, ws_w, xt_q, xt_s, gw)))
     torch.cuda.synchronize()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -428,13 +429,13 @@ def backward_run(args) -> int:
     reps = max(10, args.steps // 2)
     with torch.cuda.stream(st):
         for s, gx_args, gw_args in gemm_sets:
-            for tag, (wsq, bq, bs, out) in (("grad_x", gx_args), ("grad_w", gw_args)):
+            for tag, (xq, wsq, bq, bs, out) in (("grad_x", gx_args), ("grad_w", gw_args)):
                 for _ in range(3):
-                    i8.linear_matmul_dequant(wsq, bq, bs, None, out)
+                    i8.linear_matmul_dequant(xq, wsq, bq, bs, None, out)
                 gr = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(gr, stream=st):
                     for _ in range(4):
-                        i8.linear_matmul_dequant(wsq, bq, bs, None, out)
+                        i8.linear_matmul_dequant(xq, wsq, bq, bs, None, out)
                 gr.replay()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(st)
@@ -734,10 +735,10 @@ def main() -> int:
         # exactly args.launches GEMM dispatches per layer, layer after layer
         for li, s in enumerate(specs):
             for i in range(args.launches):
-                _, _, wqc, wac, b, ws, out = sets[i % copies][li]
+                _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
                 if i < copies:
-                    i8.linear_quantize(sets[i % copies][li][1], ws, s.tau)
-                i8.linear_matmul_dequant(ws, wqc, wac, b, out)
+                    i8.linear_quantize(xc, ws, s.tau)
+                i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
         torch.cuda.synchronize()
         print(json.dumps({"workload": args.workload, "gemm_launches_per_layer": args.launches}))
         return 0
@@ -747,8 +748,8 @@ def main() -> int:
         step(c)
     torch.cuda.synchronize()
     for s, xc, wqc, wac, b, ws, out in sets[0]:
-        if ws.outlier_overflow():
-            raise SystemExit(f"layer {s.name}: more outlier columns than cap={cap}")
+        if ws.outliers_past_cap():
+            log(f"layer {s.name}: more outlier columns than cap={cap} (those past it take the slow path)")
 
     # ---- eager timing ------------------------------------------------------------
     def timed(run, steps, warmup):

@@ -29,7 +29,8 @@
  *  - Sizes: m, n >= 0, k >= 1; k <= I8MP_MAX_K so that int32 accumulation of
  *    int8 products is exact.  m == 0 or n == 0 is a valid empty call.
  *    Leading dimensions of the GEMM operands and outputs (lda, ldb, ldw, ldc,
- *    ldout) and the outlier capacity are at most I8MP_MAX_LD elements.
+ *    ldout), of the linear's input (ldx) and the outlier capacity are at most
+ *    I8MP_MAX_LD elements.
  *  - Calls that share a workspace or outputs and overlap in time race; calls
  *    on one stream are ordered.
  *
@@ -117,8 +118,11 @@ i8mp_status i8mp_int8_vectorwise_quant(const void* x, int64_t m, int64_t k, int6
  *   outlier_bitmap  uint32 [ceil(k/32)] as written by i8mp_int8_vectorwise_quant
  *   cap             capacity (>= 0) of idx and of the columns of x_out
  *   idx             int32 [cap] output: ascending outlier columns, -1 past the count
- *   count           int32 [1] output: the number of outlier columns (may exceed cap;
- *                   then only the first cap columns are listed and gathered)
+ *   count           int32 [1] output: the number of outlier columns.  It may
+ *                   exceed cap: then only the first cap columns are listed and
+ *                   gathered, and a caller building the linear from the
+ *                   separate ops must extract again with cap >= count (cap = k
+ *                   always suffices) for the method's result
  *   x_out           optional fp16 [m x ldo] output, ldo >= cap: x_out[i, s] =
  *                   x[i, idx[s]] for s < min(count, cap), 0 for the other s < cap
  */
@@ -188,15 +192,17 @@ i8mp_status i8mp_int8_vectorwise_dequant(const int8_t* q, int64_t ldq, int64_t m
 /* The whole mixed-precision linear, fused: quantize + detect, extract, int8
  * MFMA GEMM with the dequant, outlier sub-matmul and bias in its epilogue.
  *
- *   x          fp16 [m x k], ldx >= k
+ *   x          fp16 [m x k], ldx >= k (ldx at most I8MP_MAX_LD)
  *   w_q        int8 [n x ldw], ldw >= k   (from i8mp_int8_vectorwise_quant, threshold <= 0)
  *   w_absmax   fp32 [n]
  *   bias       optional fp16 [n]
  *   threshold  outlier threshold (<= 0: pure int8)
- *   cap        outlier capacity (>= 0).  If the call finds more than cap outlier
- *              columns, only the first cap take the fp16 path and the others are
- *              dropped from both parts: out is then NOT the method's result.  The
- *              true count is left in the workspace (see the layout query).
+ *   cap        capacity (>= 0) of the gathered outlier columns X_O in the
+ *              workspace.  Every outlier column takes the fp16 path whatever
+ *              the count: the epilogue reads the x values of the first cap
+ *              outlier columns from X_O and those of any further column from x
+ *              through the index list (slower).  The index list always holds
+ *              every outlier column and the count is exact.
  *   out        fp16 [m x ldout] output, ldout >= n
  *   workspace  at least i8mp_linear_workspace(...).bytes bytes; contents on entry
  *              are ignored; after the call it holds the intermediates at the
@@ -208,12 +214,15 @@ typedef struct i8mp_linear_workspace {
     int64_t ldq;           /* leading dimension of the codes                      */
     size_t absmax_offset;  /* fp32 [m] row absmax                                 */
     size_t bitmap_offset;  /* uint32 [ceil(k/32)] outlier bitmap                  */
-    size_t idx_offset;     /* int32 [cap_pad] outlier columns, -1 past the count  */
+    size_t idx_offset;     /* int32 [idx_len] outlier columns, ascending, -1 past
+                              the count                                           */
     size_t count_offset;   /* int32 [1] outlier count                             */
-    size_t xo_offset;      /* fp16 [m x cap_pad] gathered outlier columns         */
+    size_t xo_offset;      /* fp16 [m x cap_pad]: x of the first min(count, cap)
+                              outlier columns, zero past them                     */
     int32_t cap_pad;       /* cap rounded up to the fp16 MFMA depth               */
     size_t scratch_offset; /* private: partial outlier bitmaps of the detection   */
     size_t scratch_bytes;
+    int64_t idx_len;       /* entries of the index list: k rounded up to 32       */
 } i8mp_linear_workspace;
 
 i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t cap,
@@ -229,16 +238,16 @@ i8mp_status i8mp_linear_workspace_query(int64_t m, int64_t n, int64_t k, int32_t
  * outlier extraction of x into the workspace (arguments as for the forward).
  * i8mp_linear_matmul_dequant: the int8 MFMA GEMM of the workspace codes with
  * w_q and the fused epilogue (row/column absmax, outlier sub-matmul, bias);
- * m, k and cap must be those of the i8mp_linear_quantize call that filled the
- * workspace. */
+ * x, m, k and cap must be those of the i8mp_linear_quantize call that filled
+ * the workspace (x is read for outlier columns past cap). */
 i8mp_status i8mp_linear_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
                                  int32_t cap, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
-i8mp_status i8mp_linear_matmul_dequant(const void* workspace, size_t workspace_bytes, int64_t m,
-                                       int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
-                                       const float* w_absmax, int64_t n, const void* bias, void* out,
-                                       int64_t ldout, hipStream_t stream);
+i8mp_status i8mp_linear_matmul_dequant(const void* x, int64_t ldx, const void* workspace,
+                                       size_t workspace_bytes, int64_t m, int64_t k, int32_t cap,
+                                       const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+                                       const void* bias, void* out, int64_t ldout, hipStream_t stream);
 
 i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx,
                                 const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
@@ -317,10 +326,10 @@ i8mp_status i8mp_linear_backward_workspace_query(int64_t m, int64_t n, int64_t k
  *              required when grad_x is requested)
  *   cap, fwd_workspace   the forward's outlier capacity and its workspace (from
  *              i8mp_linear_forward or i8mp_linear_quantize on this x with this
- *              m, k and cap), read for its outlier index, count and gathered
- *              outlier columns; NULL = no outlier columns.  As in the forward,
- *              with more than cap outlier columns only the first cap take the
- *              fp16 path.
+ *              m, k and cap), read for its outlier bitmap, index list, count
+ *              and gathered outlier columns; NULL = no outlier columns.  As in
+ *              the forward, every outlier column takes the fp16 path; those
+ *              past cap are summed from grad_out and x directly (slower).
  *   grad_x     optional fp16 [m x ldgx] output, ldgx >= k (NULL: not computed)
  *   grad_w     optional fp16 [n x ldgw] output, ldgw >= k (NULL: not computed)
  *   workspace  at least the query's bytes

@@ -115,13 +115,22 @@ def quantize_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     return q, absmax
 
 
-def outlier_extract(x: torch.Tensor, bitmap: torch.Tensor, cap: int
+def outlier_extract(x: torch.Tensor, bitmap: torch.Tensor, cap: Optional[int] = None, strict: bool = True
                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """extract_outliers: (idx int32 [cap], count int32 [1], x_out fp16 [m, cap])."""
+    """extract_outliers: (idx int32 [cap], count int32 [1], x_out fp16 [m, cap]).
+
+    ``cap`` defaults to k, which holds every outlier column.  With a smaller
+    cap and more outlier columns than it, only the first cap are listed;
+    ``strict`` (default) then raises instead, reading the count back (a
+    synchronization), since the sparse decomposition built from such a list
+    would drop columns.
+    """
     dev = _device_of(x, bitmap)
     ldx = _rowmajor(x, "x", torch.float16)
     m, k = x.shape
     _vec(bitmap, "bitmap", torch.int32, (k + 31) // 32)
+    if cap is None:
+        cap = k
     idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int32, device=dev)
     xo = torch.empty((m, max(cap, 1)), dtype=torch.float16, device=dev)
@@ -129,6 +138,10 @@ def outlier_extract(x: torch.Tensor, bitmap: torch.Tensor, cap: int
         check(lib().i8mp_outlier_extract(_ptr(x), m, k, ldx, _ptr(bitmap), cap, _ptr(idx), _ptr(count),
                                          _ptr(xo), max(cap, 1), _stream(dev)),
               "i8mp_outlier_extract")
+    if strict and cap < k:
+        found = int(count.item())
+        if found > cap:
+            raise ValueError(f"{found} outlier columns found, more than cap={cap}: extract with a larger cap")
     return idx[:cap], count, xo[:, :cap]
 
 
@@ -221,7 +234,8 @@ class LinearWorkspace:
         return self._view(self.layout.bitmap_offset, (self.k + 31) // 32, torch.int32)
 
     def idx(self) -> torch.Tensor:
-        return self._view(self.layout.idx_offset, max(self.layout.cap_pad, 1), torch.int32)[: self.cap]
+        """Every outlier column, ascending, -1 past the count (idx_len entries)."""
+        return self._view(self.layout.idx_offset, self.layout.idx_len, torch.int32)
 
     def count(self) -> torch.Tensor:
         return self._view(self.layout.count_offset, 1, torch.int32)
@@ -230,8 +244,11 @@ class LinearWorkspace:
         cp = self.layout.cap_pad
         return self._view(self.layout.xo_offset, self.m * cp, torch.float16).view(self.m, cp)[:, : self.cap]
 
-    def outlier_overflow(self) -> bool:
-        """True if the last call found more outlier columns than cap (synchronizes)."""
+    def outliers_past_cap(self) -> bool:
+        """True if the last call found more outlier columns than cap (synchronizes).
+
+        The output is the method's either way; the columns past cap read their
+        x values through the index list, which is slower."""
         return int(self.count().item()) > self.cap
 
 
@@ -261,7 +278,10 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_absmax: torch.Tensor,
            bias: Optional[torch.Tensor] = None, threshold: float = DEFAULT_THRESHOLD,
            cap: int = DEFAULT_CAP, workspace: Optional[LinearWorkspace] = None,
            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The fused mixed-precision linear: fp16 out [m, n] = x . dequant(w)^T + bias."""
+    """The fused mixed-precision linear: fp16 out [m, n] = x . dequant(w)^T + bias.
+
+    Every outlier column takes the fp16 path for any count; ``cap`` sizes the
+    workspace's gathered copy of the outlier columns (the fast path)."""
     dev = _device_of(x, w_q, w_absmax, bias, out)
     ldx = _rowmajor(x, "x", torch.float16)
     ldw = _rowmajor(w_q, "w_q", torch.int8)
@@ -303,15 +323,18 @@ def linear_quantize(x: torch.Tensor, workspace: LinearWorkspace,
               "i8mp_linear_quantize")
 
 
-def linear_matmul_dequant(workspace: LinearWorkspace, w_q: torch.Tensor, w_absmax: torch.Tensor,
-                          bias: Optional[torch.Tensor] = None,
+def linear_matmul_dequant(x: torch.Tensor, workspace: LinearWorkspace, w_q: torch.Tensor,
+                          w_absmax: torch.Tensor, bias: Optional[torch.Tensor] = None,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Second half of ``linear``: fused int8 GEMM + dequant epilogue from the workspace."""
-    dev = _device_of(workspace.buf, w_q, w_absmax, bias, out)
+    """Second half of ``linear``: fused int8 GEMM + dequant epilogue from the
+    workspace that ``linear_quantize(x, workspace)`` filled (x is read for
+    outlier columns past the workspace's cap)."""
+    dev = _device_of(x, workspace.buf, w_q, w_absmax, bias, out)
+    ldx = _rowmajor(x, "x", torch.float16)
     ldw = _rowmajor(w_q, "w_q", torch.int8)
     n, k = w_q.shape
-    if k != workspace.k:
-        raise ValueError("w_q and the workspace differ in k")
+    if k != workspace.k or tuple(x.shape) != (workspace.m, workspace.k):
+        raise ValueError("x, w_q and the workspace differ in shape")
     _vec(w_absmax, "w_absmax", torch.float32, n)
     if bias is not None:
         _vec(bias, "bias", torch.float16, n)
@@ -320,7 +343,8 @@ def linear_matmul_dequant(workspace: LinearWorkspace, w_q: torch.Tensor, w_absma
         out = torch.empty((m, n), dtype=torch.float16, device=dev)
     ldout = _rowmajor(out, "out", torch.float16)
     with torch.cuda.device(dev):
-        check(lib().i8mp_linear_matmul_dequant(_ptr(workspace.buf), workspace.buf.numel(), m, k, workspace.cap,
+        check(lib().i8mp_linear_matmul_dequant(_ptr(x), ldx, _ptr(workspace.buf), workspace.buf.numel(), m, k,
+                                               workspace.cap,
                                                _ptr(w_q), ldw, _ptr(w_absmax), n, _ptr(bias), _ptr(out),
                                                ldout, _stream(dev)),
               "i8mp_linear_matmul_dequant")

@@ -55,6 +55,7 @@ class LinearWorkspaceLayout(Structure):
         ("cap_pad", c_int32),
         ("scratch_offset", c_size_t),
         ("scratch_bytes", c_size_t),
+        ("idx_len", c_int64),
     ]
 
 
@@ -118,8 +119,8 @@ def _declare(lib):
     lib.i8mp_linear_quantize.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_float, c_int32, c_void_p,
                                          c_size_t, c_void_p]
     lib.i8mp_linear_quantize.restype = c_int32
-    lib.i8mp_linear_matmul_dequant.argtypes = [c_void_p, c_size_t, c_int64, c_int64, c_int32, c_void_p,
-                                               c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+    lib.i8mp_linear_matmul_dequant.argtypes = [c_void_p, c_int64, c_void_p, c_size_t, c_int64, c_int64, c_int32,
+                                               c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                                c_void_p]
     lib.i8mp_linear_matmul_dequant.restype = c_int32
     lib.i8mp_colwise_quant_workspace_bytes.argtypes = [c_int64, c_int64]

@@ -40,6 +40,7 @@ void forward_layout(int64_t m, int64_t k, int32_t cap, i8mp_linear_workspace* L)
     std::memset(L, 0, sizeof(*L));
     L->ldq = round_up(k, 128);
     L->cap_pad = (int32_t)round_up(cap, 32);
+    L->idx_len = round_up(k, 32);   // room for every column: the list is never cut
     size_t off = 0;
     L->scratch_offset = off;
     L->scratch_bytes = quant_scratch_bytes(k);
@@ -47,7 +48,7 @@ void forward_layout(int64_t m, int64_t k, int32_t cap, i8mp_linear_workspace* L)
     L->bitmap_offset = off;
     off = align_up(off + (size_t)ceil_div(k, 32) * 4);
     L->idx_offset = off;
-    off = align_up(off + (size_t)(L->cap_pad > 0 ? L->cap_pad : 1) * 4);
+    off = align_up(off + (size_t)L->idx_len * 4);
     L->count_offset = off;
     off = align_up(off + 4);
     L->absmax_offset = off;
@@ -106,7 +107,7 @@ const char* i8mp_status_string(i8mp_status s) {
     }
 }
 
-int32_t i8mp_abi_version(void) { return (2 << 16) | 0; }
+int32_t i8mp_abi_version(void) { return (3 << 16) | 0; }
 
 size_t i8mp_quant_workspace_bytes(int64_t m, int64_t k) {
     if (m <= 0 || k < 1 || k > I8MP_MAX_K) return 0;
@@ -272,7 +273,7 @@ QuantArgs forward_quant_args(const void* x, int64_t m, int64_t k, int64_t ldx, f
     a.idx_out = reinterpret_cast<int32_t*>(ws + L.idx_offset);
     a.count_out = reinterpret_cast<int32_t*>(ws + L.count_offset);
     a.cap = cap;
-    a.idx_len = L.cap_pad;
+    a.idx_len = (int32_t)L.idx_len;
     a.x_out = L.cap_pad > 0 ? reinterpret_cast<half_bits*>(ws + L.xo_offset) : nullptr;
     a.ldo = L.cap_pad;
     a.xo_cols = L.cap_pad;
@@ -285,9 +286,10 @@ i8mp_status enqueue_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, f
     return launched(launch_quantize(forward_quant_args(x, m, k, ldx, threshold, cap, L, ws), stream));
 }
 
-// Arguments of the fused GEMM + dequant epilogue reading the forward workspace.
-GemmArgs forward_gemm_args(const i8mp_linear_workspace& L, const char* ws, int64_t m, int64_t k, int32_t cap,
-                           const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+// Arguments of the fused GEMM + dequant epilogue reading the forward workspace
+// (and x itself for outlier slots past cap).
+GemmArgs forward_gemm_args(const i8mp_linear_workspace& L, const char* ws, const void* x, int64_t ldx, int64_t m,
+                           int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
                            const void* bias, void* out, int64_t ldout) {
     GemmArgs g{};
     g.a = reinterpret_cast<const int8_t*>(ws + L.q_offset);
@@ -304,19 +306,22 @@ GemmArgs forward_gemm_args(const i8mp_linear_workspace& L, const char* ws, int64
     g.x_out = L.cap_pad > 0 ? reinterpret_cast<const half_bits*>(ws + L.xo_offset) : nullptr;
     g.ldo = L.cap_pad;
     g.idx = reinterpret_cast<const int32_t*>(ws + L.idx_offset);
+    g.idx_len = (int32_t)L.idx_len;
     g.count = reinterpret_cast<const int32_t*>(ws + L.count_offset);
     g.cap = cap;
+    g.x = static_cast<const half_bits*>(x);
+    g.ldx = ldx;
     g.out = static_cast<half_bits*>(out);
     g.ldout = ldout;
     return g;
 }
 
-i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* ws, int64_t m,
-                                   int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
+i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* ws, const void* x, int64_t ldx,
+                                   int64_t m, int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
                                    const float* w_absmax, int64_t n, const void* bias, void* out,
                                    int64_t ldout, hipStream_t stream) {
     return launched(launch_gemm_fused(
-        forward_gemm_args(L, ws, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout), stream));
+        forward_gemm_args(L, ws, x, ldx, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout), stream));
 }
 
 }  // namespace
@@ -324,7 +329,7 @@ i8mp_status enqueue_matmul_dequant(const i8mp_linear_workspace& L, const char* w
 i8mp_status i8mp_linear_quantize(const void* x, int64_t m, int64_t k, int64_t ldx, float threshold,
                                  int32_t cap, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-    if (m < 0 || bad_k(k) || ldx < k || cap < 0 || bad_ld(cap)) return I8MP_EINVAL;
+    if (m < 0 || bad_k(k) || ldx < k || cap < 0 || bad_ld(cap) || bad_ld(ldx)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0) return I8MP_OK;
     if (!x) return I8MP_EINVAL;
@@ -335,20 +340,20 @@ i8mp_status i8mp_linear_quantize(const void* x, int64_t m, int64_t k, int64_t ld
     return enqueue_quantize(x, m, k, ldx, threshold, cap, L, static_cast<char*>(workspace), stream);
 }
 
-i8mp_status i8mp_linear_matmul_dequant(const void* workspace, size_t workspace_bytes, int64_t m,
-                                       int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
+i8mp_status i8mp_linear_matmul_dequant(const void* x, int64_t ldx, const void* workspace, size_t workspace_bytes,
+                                       int64_t m, int64_t k, int32_t cap, const int8_t* w_q, int64_t ldw,
                                        const float* w_absmax, int64_t n, const void* bias, void* out,
                                        int64_t ldout, hipStream_t stream) {
-    if (m < 0 || n < 0 || bad_k(k) || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
-    if (bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
+    if (m < 0 || n < 0 || bad_k(k) || ldx < k || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
+    if (bad_ld(ldx) || bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0 || n == 0) return I8MP_OK;
-    if (!w_q || !w_absmax || !out) return I8MP_EINVAL;
+    if (!x || !w_q || !w_absmax || !out) return I8MP_EINVAL;
     i8mp_linear_workspace L;
     forward_layout(m, k, cap, &L);
     if (!workspace || workspace_bytes < L.bytes) return I8MP_EWORKSPACE;
     if (i8mp_status s = check_device(); s != I8MP_OK) return s;
-    return enqueue_matmul_dequant(L, static_cast<const char*>(workspace), m, k, cap, w_q, ldw, w_absmax,
+    return enqueue_matmul_dequant(L, static_cast<const char*>(workspace), x, ldx, m, k, cap, w_q, ldw, w_absmax,
                                   n, bias, out, ldout, stream);
 }
 
@@ -358,7 +363,7 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
                                 int64_t ldout, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
     if (m < 0 || n < 0 || bad_k(k) || ldx < k || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
-    if (bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
+    if (bad_ld(ldx) || bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
     if (m == 0 || n == 0) return I8MP_OK;
     if (!x || !w_q || !w_absmax || !out) return I8MP_EINVAL;
@@ -369,7 +374,7 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
     char* ws = static_cast<char*>(workspace);
     // one to four rows: quantization inside the GEMV's workgroups, one launch
     const QuantArgs qa = forward_quant_args(x, m, k, ldx, threshold, cap, L, ws);
-    const GemmArgs g = forward_gemm_args(L, ws, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout);
+    const GemmArgs g = forward_gemm_args(L, ws, x, ldx, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout);
     if (decode_forward_fits(qa, g)) return launched(launch_decode_forward(qa, g, stream));
     if (i8mp_status s = launched(launch_quantize(qa, stream)); s != I8MP_OK) return s;
     return launched(launch_gemm_fused(g, stream));
@@ -488,20 +493,25 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
             return launched(launch_fill_f16(static_cast<half_bits*>(grad_w), n, k, ldgw, stream));
         }
         const char* fws = static_cast<const char*>(fwd_workspace);
-        const int32_t* idx = fws ? reinterpret_cast<const int32_t*>(fws + F.idx_offset) : nullptr;
-        const int32_t* count = fws ? reinterpret_cast<const int32_t*>(fws + F.count_offset) : nullptr;
-        // g and x column-wise, x's outlier columns zeroed (CAt), then the GEMM;
-        // the pass over g also sums the fp16 outlier columns per row block
+        // g and x column-wise, every outlier column of x zeroed (CAt), then
+        // the GEMM; the pass over g also sums the fp16 outlier columns that
+        // the forward gathered per row block, and the store after the GEMM
+        // writes every outlier column of grad_w
         FixArgs f{};
-        if (fws && cap > 0) {
-            f.x_out = reinterpret_cast<const half_bits*>(fws + F.xo_offset);
+        if (fws) {
+            f.x_out = cap > 0 ? reinterpret_cast<const half_bits*>(fws + F.xo_offset) : nullptr;
             f.ldo = F.cap_pad;
-            f.idx = idx;
-            f.count = count;
+            f.idx = reinterpret_cast<const int32_t*>(fws + F.idx_offset);
+            f.idx_len = (int32_t)F.idx_len;
+            f.count = reinterpret_cast<const int32_t*>(fws + F.count_offset);
             f.cap = cap;
             f.part = reinterpret_cast<float*>(ws + L.scratch_offset + (L.scratch_bytes - fix_part_bytes(m, n, cap)));
             f.grad_w = static_cast<half_bits*>(grad_w);
             f.ldgw = ldgw;
+            f.g = g;
+            f.ldg = ldg;
+            f.x = static_cast<const half_bits*>(x);
+            f.ldx = ldx;
         }
         ColQuantArgs c{};
         c.x = g;
@@ -518,9 +528,7 @@ i8mp_status i8mp_linear_backward(const void* grad_out, int64_t ldg, const void* 
         c.x = static_cast<const half_bits*>(x);
         c.cols = k;
         c.lda = ldx;
-        c.zero_idx = cap > 0 ? idx : nullptr;
-        c.zero_count = count;
-        c.cap = cap;
+        c.zero_bitmap = fws ? reinterpret_cast<const uint32_t*>(fws + F.bitmap_offset) : nullptr;
         c.qt = reinterpret_cast<int8_t*>(ws + L.xtq_offset);
         c.col_absmax = reinterpret_cast<float*>(ws + L.xts_offset);
         if (i8mp_status s = launched(launch_colwise_quant(c, stream)); s != I8MP_OK) return s;

@@ -6,18 +6,22 @@
 namespace i8mp {
 
 // ---- backward: column-wise quantization and the outlier weight gradient ----
-// The fp16 outlier columns of grad_w: sum_i g[i, n] * x_out[i, s], summed
-// per 512-row block by the column-maximum pass over g (part), then over the
-// blocks into grad_w[n, idx[s]] for s < min(count, cap).
+// The fp16 outlier columns of grad_w, grad_w[n, idx[s]] = sum_i g[i, n] * x[i, idx[s]]
+// for every slot s < count: for s < cap summed per 512-row block by the
+// column-maximum pass over g from the forward's gathered columns (part), then
+// over the blocks; past cap summed over the rows of g and x directly.
 struct FixArgs {
-    const half_bits* x_out;      // nullable: off.  The forward's gathered outlier columns [m x ldo],
+    const half_bits* x_out;      // nullable (cap == 0).  The forward's gathered outlier columns [m x ldo],
     int64_t ldo;                 // zero past the count; ldo >= round_up(cap, 8), a multiple of 8
-    const int32_t* idx;          // [cap] outlier columns
+    const int32_t* idx;          // nullable: off.  [idx_len] outlier columns, ascending
+    int32_t idx_len;
     const int32_t* count;        // [1]
     int32_t cap;
     float* part;                 // [row blocks x cap x cols_pad] fp32 block sums
     half_bits* grad_w;           // [n x ldgw]
     int64_t ldgw;
+    const half_bits* g; int64_t ldg;   // [m x ldg] upstream gradient (slots past cap)
+    const half_bits* x; int64_t ldx;   // [m x ldx] layer input (slots past cap)
 };
 
 struct ColQuantArgs {
@@ -26,6 +30,7 @@ struct ColQuantArgs {
     const int32_t* zero_idx;     // nullable: columns whose codes are zeroed
     const int32_t* zero_count;   // [1], used with zero_idx
     int32_t cap;                 // entries of zero_idx considered: min(count, cap)
+    const uint32_t* zero_bitmap; // nullable: columns whose bit is set get zero codes too
     int8_t* qt;                  // [cols x ldqt] transposed codes, rows .. ldqt - 1 written as 0
     int64_t ldqt;
     float* col_absmax;           // [cols]
@@ -45,8 +50,8 @@ inline size_t fix_part_bytes(int64_t m, int64_t n, int32_t cap) {
     return (size_t)colquant_row_blocks(m) * (size_t)(cap > 0 ? cap : 1) * (size_t)round_up(n > 0 ? n : 1, 64) * 4;
 }
 hipError_t launch_colwise_quant(const ColQuantArgs& a, hipStream_t stream);
-// grad_w[n, idx[s]] = fp16(sum of the block sums) for s < min(count, cap), once
-// the column pass over g [m x n] has written them
+// grad_w[n, idx[s]] for every outlier slot s, once the column pass over g
+// [m x n] has written the block sums of the slots below cap
 hipError_t launch_outlier_store(const FixArgs& f, int64_t m, int64_t n, hipStream_t stream);
 // out[i, j] = +0 for an fp16 rows x cols matrix (an empty contraction)
 hipError_t launch_fill_f16(half_bits* out, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);

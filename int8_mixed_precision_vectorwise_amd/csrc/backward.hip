@@ -186,6 +186,7 @@ __global__ __launch_bounds__(256) void colquant_kernel(ColQuantArgs a) {
         s[4] = fmaxf(s[4], p1.x); s[5] = fmaxf(s[5], p1.y); s[6] = fmaxf(s[6], p1.z); s[7] = fmaxf(s[7], p1.w);
     }
     uint32_t zmask = 0;
+    if (a.zero_bitmap) zmask = (a.zero_bitmap[c >> 5] >> (c & 31)) & 0xffu;  // c % 8 == 0
     if (a.zero_idx) {
         int32_t nz = *a.zero_count;
         if (nz > a.cap) nz = a.cap;
@@ -235,17 +236,26 @@ __global__ __launch_bounds__(256) void colquant_kernel(ColQuantArgs a) {
     }
 }
 
-// grad_w[col, idx[s]] = fp16(sum over the row blocks of the block sums), in
-// row-block order
-__global__ __launch_bounds__(256) void fix_store_kernel(FixArgs f, int64_t n, int64_t cols_pad, int64_t row_blocks) {
+// grad_w[col, idx[s]]: for s < cap the fp16 of the sum over the row blocks of
+// the block sums, in row-block order; past cap (more outlier columns than the
+// forward gathered) the fp32 sum over the rows, in row order, of g[i, col] *
+// x[i, idx[s]] (exact fp16 products)
+__global__ __launch_bounds__(256) void fix_store_kernel(FixArgs f, int64_t m, int64_t n, int64_t cols_pad,
+                                                        int64_t row_blocks) {
     int32_t cnt = *f.count;
-    if (cnt > f.cap) cnt = f.cap;
+    cnt = cnt < 0 ? 0 : (cnt > f.idx_len ? f.idx_len : cnt);
+    const int32_t kept = cnt < f.cap ? cnt : f.cap;
     const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (col >= n) return;
     for (int32_t s = blockIdx.y; s < cnt; s += gridDim.y) {
+        const int32_t j = f.idx[s];
         float t = 0.0f;
-        for (int64_t rb = 0; rb < row_blocks; ++rb) t += f.part[(rb * f.cap + s) * cols_pad + col];
-        f.grad_w[col * f.ldgw + f.idx[s]] = f2h(t);
+        if (s < kept) {
+            for (int64_t rb = 0; rb < row_blocks; ++rb) t += f.part[(rb * f.cap + s) * cols_pad + col];
+        } else {
+            for (int64_t i = 0; i < m; ++i) t = fmaf(h2f(f.g[i * f.ldg + col]), h2f(f.x[i * f.ldx + j]), t);
+        }
+        f.grad_w[col * f.ldgw + j] = f2h(t);
     }
 }
 
@@ -303,9 +313,10 @@ hipError_t launch_colwise_quant(const ColQuantArgs& in, hipStream_t stream) {
 }
 
 hipError_t launch_outlier_store(const FixArgs& f, int64_t m, int64_t n, hipStream_t stream) {
-    if (!f.x_out || f.cap <= 0 || m <= 0 || n <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(n, 256), (unsigned)(f.cap < 32 ? f.cap : 32));
-    hipLaunchKernelGGL(fix_store_kernel, grid, dim3(256), 0, stream, f, n, round_up(n, kStripCols),
+    if (!f.idx || m <= 0 || n <= 0) return hipSuccess;
+    // the count is on the device: 32 slot strides cover any count
+    const dim3 grid((unsigned)ceil_div(n, 256), 32u);
+    hipLaunchKernelGGL(fix_store_kernel, grid, dim3(256), 0, stream, f, m, n, round_up(n, kStripCols),
                        colquant_row_blocks(m));
     return hipGetLastError();
 }

@@ -47,10 +47,10 @@ struct QuantArgs {
     int64_t kpad;               // codes in [k, kpad) are written as 0
     float* absmax;              // nullable iff q is null
     uint32_t* bitmap_out;       // nullable
-    int32_t* idx_out;           // nullable
+    int32_t* idx_out;           // nullable: the outlier columns, ascending
     int32_t* count_out;         // nullable
-    int32_t cap;                // capacity of idx_out / x_out columns
-    int32_t idx_len;            // idx entries written (>= cap, -1 padded)
+    int32_t cap;                // x_out holds the values of the first cap outlier columns
+    int32_t idx_len;            // idx entries written: the first idx_len columns, -1 past the count
     half_bits* x_out;           // nullable
     int64_t ldo;
     int32_t xo_cols;            // x_out columns written per row (>= cap, zero padded)
@@ -72,12 +72,27 @@ struct GemmArgs {
     const float* row_absmax;
     const float* col_absmax;
     const half_bits* bias;               // nullable
-    const half_bits* x_out; int64_t ldo; // nullable: no outlier term
-    const int32_t* idx;
+    // outlier sub-matmul, on iff count is non-null: slot s < count has column
+    // idx[s] (idx holds idx_len >= count entries); its x values come from
+    // x_out[:, s] for s < cap (zero from the count to ldo), from x[:, idx[s]]
+    // past cap
     const int32_t* count;
+    const int32_t* idx; int32_t idx_len;
+    const half_bits* x_out; int64_t ldo; // nullable iff cap == 0
     int32_t cap;
+    const half_bits* x; int64_t ldx;     // the layer input
     half_bits* out; int64_t ldout;
 };
+
+// x value of outlier slot s of activation row r (see GemmArgs)
+__device__ inline float outlier_x(const GemmArgs& g, int64_t r, int s) {
+    return h2f(s < g.cap ? g.x_out[r * g.ldo + s] : g.x[r * g.ldx + g.idx[s]]);
+}
+// number of outlier slots of the fused epilogue: the device count, bounded by
+// the index list it is read from
+__device__ inline int outlier_count(const GemmArgs& g, int c) {
+    return c < 0 ? 0 : (c > g.idx_len ? g.idx_len : c);
+}
 
 hipError_t launch_gemm_i32(const GemmArgs& g, hipStream_t stream);
 // m <= 16, 16-byte aligned operands, A covering whole 128-byte K chunks

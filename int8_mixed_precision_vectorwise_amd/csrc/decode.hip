@@ -132,14 +132,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     int ocol_lane = 0x7fffffff;  // lane s: column of slot s
     v4f_t p = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (kFused) {
-        if (g.x_out) {
-            cnt = *g.count;
-            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
-        }
+        if (g.count) cnt = outlier_count(g, *g.count);
         n_ring = cnt < kDecOutl ? cnt : kDecOutl;
         for (int t = threadIdx.x; t < kRows * kDecOutl; t += 256) {
             const int r = t / kDecOutl, s2 = t % kDecOutl;
-            xo[t] = (r < g.m && s2 < n_ring) ? h2f(g.x_out[r * g.ldo + s2]) : 0.0f;
+            xo[t] = (r < g.m && s2 < n_ring) ? outlier_x(g, r, s2) : 0.0f;
         }
         if (lane < n_ring) ocol_lane = g.idx[lane];
         if (n_ring > 0) ocol = __builtin_amdgcn_readfirstlane(ocol_lane);
@@ -211,10 +208,20 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         int64_t arow = lane & 15;
         if (arow >= g.m) arow = g.m - 1;
         const int64_t bcol = col < g.n ? col : g.n - 1;
-        // columns past the ring's kDecOutl: gathered (kDecOutl is a multiple of 32)
+        // columns past the ring's kDecOutl: gathered (kDecOutl is a multiple of
+        // 32); x values as 8-slot vectors from X_O below xo_lim (zero from the
+        // count to ldo), past it slot by slot
+        const int xo_lim = cnt <= g.cap ? (int)g.ldo : g.cap;
         for (int s0 = n_ring; s0 < cnt; s0 += 32) {
             const int s1 = s0 + (lane >> 4) * 8;
-            const v8h xa = *reinterpret_cast<const v8h*>(g.x_out + arow * g.ldo + s1);
+            v8h xa;
+            if (s1 + 8 <= xo_lim) {
+                xa = *reinterpret_cast<const v8h*>(g.x_out + arow * g.ldo + s1);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xa[e] = s1 + e < cnt ? (_Float16)outlier_x(g, arow, s1 + e) : (_Float16)0.0f;
+            }
             v8h wb;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -312,11 +319,11 @@ __device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L]) {
 }
 
 // Quantize the chunks of load_x_chunks into the LDS activation rows xs
-// [M][kr] (kr >= k, zeros past k and in rows past m); the first kGvOutl kept
+// [M][kr] (kr >= k, zeros past k and in rows past m); the first kGvOutl
 // outlier columns and their values go to oidx / oval; the bitmap, its prefix
-// and the row absmax to q.  Returns the outlier count (the kept columns are
-// that count capped at a.cap).  Every thread calls; one workgroup barrier
-// between the local pass and the codes, two inside the prefix.
+// and the row absmax to q.  Returns the outlier count.  Every thread calls;
+// one workgroup barrier between the local pass and the codes, two inside the
+// prefix.
 template <int M, int L, int T>
 __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)[L], int64_t kr, int8_t* xs,
                                             int32_t* oidx, float* oval, const GvQuantLds& q) {
@@ -401,9 +408,8 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
         }
     }
     const int32_t total = outl ? bitmap_prefix(q.bm, q.pre, a.words, q.wave_tot) : 0;
-    // the first kGvOutl kept outlier columns and their values, in slot order
-    const int32_t kept = total < a.cap ? total : a.cap;
-    const int32_t lc = kept < kGvOutl ? kept : kGvOutl;
+    // the first kGvOutl outlier columns and their values, in slot order
+    const int32_t lc = total < kGvOutl ? total : kGvOutl;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
         const uint32_t ob = obits[qq];
@@ -428,15 +434,15 @@ __device__ inline int32_t quantize_rows_lds(const QuantArgs& a, const uint4 (&v)
 
 // The forward's intermediates into the workspace, spread over the grid (each
 // thread writes at most a few entries): codes (the LDS rows, kpad == ldq),
-// absmax, bitmap, count, index list (-1 past the kept columns) and gathered
-// outlier values (zero past the kept columns).  The first kGvOutl slots come
+// absmax, bitmap, count, index list (-1 past the count) and gathered outlier
+// values (the first cap slots, zero past them).  The first kGvOutl slots come
 // from the stream's LDS list (columns, and values as fp32 that convert back
 // to the same fp16); later slots, if any, from the bitmap and x.  After the
 // barrier that follows quantize_rows_lds.
 template <int M, int T>
 __device__ inline void publish_spread(const QuantArgs& a, int64_t kx, const int8_t* xs, const GvQuantLds& q,
-                                      const int32_t* oidx, const float* oval, bool any, int32_t total,
-                                      int32_t kept) {
+                                      const int32_t* oidx, const float* oval, bool any, int32_t total) {
+    const int32_t kept = total < a.cap ? total : a.cap;   // slots with gathered x values
     const int64_t gt = (int64_t)blockIdx.x * T + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * T;
     const int64_t units = a.ldq / 16;  // 16-byte units per code row (ldq <= kx, zeros past k)
@@ -448,27 +454,27 @@ __device__ inline void publish_spread(const QuantArgs& a, int64_t kx, const int8
     if (gt == 0 && a.count_out) *a.count_out = total;
     if (a.bitmap_out)
         for (int64_t w = gt; w < a.words; w += stride) a.bitmap_out[w] = any ? q.bm[w] : 0u;
-    const int32_t lc = kept < kGvOutl ? kept : kGvOutl;
+    const int32_t lc = total < kGvOutl ? total : kGvOutl;
     if (a.idx_out)
         for (int64_t s = gt; s < a.idx_len; s += stride)
             if (s < lc) a.idx_out[s] = oidx[s];
-            else if (s >= kept) a.idx_out[s] = -1;
+            else if (s >= total) a.idx_out[s] = -1;
     if (a.x_out)
         for (int64_t f = gt; f < a.m * a.xo_cols; f += stride) {
             const int64_t r = f / a.xo_cols, s = f - r * a.xo_cols;
-            if (s < lc) a.x_out[r * a.ldo + s] = f2h(oval[r * kGvOutl + s]);
+            if (s < lc && s < kept) a.x_out[r * a.ldo + s] = f2h(oval[r * kGvOutl + s]);
             else if (s >= kept) a.x_out[r * a.ldo + s] = 0;
         }
-    if (kept > kGvOutl)  // slots from kGvOutl on: walk the bitmap words
+    if (total > kGvOutl)  // slots from kGvOutl on: walk the bitmap words
         for (int64_t w = gt; w < a.words; w += stride) {
             uint32_t bits = q.bm[w];
             int32_t slot = bits ? q.pre[w] : 0;
             while (bits) {
                 const int64_t j = w * 32 + (__ffs(bits) - 1);
                 bits &= bits - 1u;
-                if (slot >= kGvOutl && slot < kept) {
-                    if (a.idx_out) a.idx_out[slot] = (int32_t)j;
-                    if (a.x_out)
+                if (slot >= kGvOutl && slot < total) {
+                    if (a.idx_out && slot < a.idx_len) a.idx_out[slot] = (int32_t)j;
+                    if (a.x_out && slot < kept)
                         for (int64_t r = 0; r < a.m; ++r) a.x_out[r * a.ldo + slot] = a.x[r * a.ldx + j];
                 }
                 ++slot;
@@ -565,18 +571,18 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
                 ++r;
             }
         }
-        if (kFused && g.x_out) {
-            cnt = *g.count;
-            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
-            // thread t < kGvOutl: idx[t]; thread t < M kGvOutl: x_out[t / kGvOutl, t % kGvOutl]
-            // (past cap or m: zeros through the range checks; masked by the count below)
+        if (kFused && g.count) {
+            cnt = outlier_count(g, *g.count);
+            // thread t < M kGvOutl: slot s2 = t % kGvOutl of row r = t / kGvOutl,
+            // idx[s2] and, below cap, x_out[r, s2] (past the list, cap or m:
+            // zeros through the range checks; masked by the count below)
             const int t = threadIdx.x;
-            const __amdgpu_buffer_rsrc_t ri = rsrc(g.idx, (int64_t)g.cap * 4);
-            const __amdgpu_buffer_rsrc_t ro = rsrc(g.x_out, (int64_t)g.m * g.ldo * 2);
+            const __amdgpu_buffer_rsrc_t ri = rsrc(g.idx, (int64_t)g.idx_len * 4);
+            const __amdgpu_buffer_rsrc_t ro = rsrc(g.x_out, g.x_out ? (int64_t)g.m * g.ldo * 2 : 0);
             const int r = t / kGvOutl, s2 = t % kGvOutl;
-            idx_t = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, t < kGvOutl ? t * 4 : (int)0x80000000, 0, 0);
+            idx_t = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, t < M * kGvOutl ? s2 * 4 : (int)0x80000000, 0, 0);
             oval_bits = __builtin_amdgcn_raw_buffer_load_b16(
-                ro, t < M * kGvOutl && r < g.m ? (int)((r * g.ldo + s2) * 2) : (int)0x80000000, 0, 0);
+                ro, t < M * kGvOutl && r < g.m && s2 < g.cap ? (int)((r * g.ldo + s2) * 2) : (int)0x80000000, 0, 0);
         }
     }
     const float r127 = 1.0f / 127.0f;
@@ -602,20 +608,26 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
     // activations (rows >= m and bytes past K as zeros), outlier columns / values
     if constexpr (kQuant) {
         const int32_t total = quantize_rows_lds<M, kQuantL, 64 * W>(qa, xv, kx, xs, oidx, oval, ql);
-        cnt = total < qa.cap ? total : qa.cap;
+        cnt = total;   // every outlier column takes the fp16 path
         __syncthreads();
-        publish_spread<M, 64 * W>(qa, kx, xs, ql, oidx, oval, total > 0, total, cnt);
+        publish_spread<M, 64 * W>(qa, kx, xs, ql, oidx, oval, total > 0, total);
     } else {
 #pragma unroll
         for (int i = 0; i < kCL; ++i) {
             const int f = (int)threadIdx.x + 64 * W * i;
             if (f < M * (int)per_row) *reinterpret_cast<v4i_t*>(xs + f * 16) = cv[i];  // row f / per_row, chunk f % per_row
         }
-        if (kFused && g.x_out) {
+        if (kFused && g.count) {
             const int lc0 = cnt < kGvOutl ? cnt : kGvOutl;
             const int t = threadIdx.x;
             if (t < kGvOutl) oidx[t] = t < lc0 ? idx_t : 0x7fffffff;
-            if (t < M * kGvOutl) oval[t] = t % kGvOutl < lc0 ? h2f((half_bits)oval_bits) : 0.0f;
+            if (t < M * kGvOutl) {
+                const int r = t / kGvOutl, s2 = t % kGvOutl;
+                float v = 0.0f;
+                if (s2 < lc0)  // past X_O's capacity: from x through the index list
+                    v = s2 < g.cap ? h2f((half_bits)oval_bits) : (r < g.m ? h2f(g.x[r * g.ldx + idx_t]) : 0.0f);
+                oval[t] = v;
+            }
         } else {
             for (int t = threadIdx.x; t < kGvOutl; t += 64 * W) oidx[t] = 0x7fffffff;
             for (int t = threadIdx.x; t < M * kGvOutl; t += 64 * W) oval[t] = 0.0f;
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemmArgs g, QuantArgs qa, 
                         const float wv = (float)g.b[n * g.ldb + g.idx[s2]];
 #pragma unroll
                         for (int r = 0; r < M; ++r)
-                            if (r < g.m) pacc[r] += wv * h2f(g.x_out[r * g.ldo + s2]);
+                            if (r < g.m) pacc[r] += wv * outlier_x(g, r, s2);
                     }
                 }
 #pragma unroll

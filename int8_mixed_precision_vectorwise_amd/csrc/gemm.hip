@@ -148,8 +148,8 @@ __device__ inline void epi_prefetch(const GemmArgs& g, int64_t m0, int64_t n0, E
         const __amdgpu_buffer_rsrc_t cs = make_rsrc(g.col_absmax + n0, (g.n - n0) * 4);
         for (int c = wave; c < BM / 64; c += 4) dma4(rs, e.sx + c * 64, (c * 64 + lane) * 4);
         for (int c = wave; c < BN / 64; c += 4) dma4(cs, e.sw + c * 64, (c * 64 + lane) * 4);
-        if (g.x_out) {
-            if (wave == 0) dma4(make_rsrc(g.idx, (int64_t)g.cap * 4), e.idx, lane * 4);
+        if (g.count) {
+            if (wave == 0) dma4(make_rsrc(g.idx, (int64_t)g.idx_len * 4), e.idx, lane * 4);
             if (wave == 1) dma4(make_rsrc(g.count, 4), e.cnt, 0);
         }
     }
@@ -164,7 +164,8 @@ __device__ inline void epi_prefetch(const GemmArgs& g, int64_t m0, int64_t n0, E
 //
 // Fused: acc becomes float(C) * row_absmax / 127 in place, the outlier
 // sub-matmul accumulates into it on v_mfma_f32_32x32x16_f16 (16 outlier
-// columns per step: X_O from the workspace, weight bytes gathered through the
+// columns per step: x values from X_O in the workspace, or for slots past its
+// capacity from x through the index list; weight bytes gathered through the
 // index list), then out = col_absmax / 127 * acc + bias in fp16.
 template <int BM, int BN, int FM, int FN, bool kFused, int kStageBytes>
 __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t m0, int64_t n0, int wr0, int wc0,
@@ -198,15 +199,16 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
                 _Float16, __builtin_amdgcn_raw_buffer_load_b16(rbias, (wc0 + 32 * j + l32) * 2, 0, 0));
 
         int cnt = 0;
-        if (g.x_out) {
-            cnt = e.cnt[0];
-            cnt = cnt > g.cap ? g.cap : cnt;
-            cnt = cnt < 0 ? 0 : cnt;
-        }
+        if (g.count) cnt = outlier_count(g, e.cnt[0]);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
-        const __amdgpu_buffer_rsrc_t rxo = make_rsrc(g.x_out + m0 * g.ldo, g.x_out ? rows_left * g.ldo * 2 : 0);
+        // slots below xo_lim read their x values from X_O as 8-slot vectors
+        // (X_O is zero from the count to ldo); past it, slot by slot
+        const int xo_lim = cnt <= g.cap ? (int)g.ldo : g.cap;
+        const __amdgpu_buffer_rsrc_t rxo = make_rsrc(g.x_out ? g.x_out + m0 * g.ldo : nullptr,
+                                                     g.x_out ? rows_left * g.ldo * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x ? g.x + m0 * g.ldx : nullptr, g.x ? rows_left * g.ldx * 2 : 0);
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.b + n0 * g.ldb, (cols_left - 1) * g.ldb + g.k);
-        const __amdgpu_buffer_rsrc_t ridx = make_rsrc(g.idx, g.x_out ? (int64_t)g.cap * 4 : 0);
+        const __amdgpu_buffer_rsrc_t ridx = make_rsrc(g.idx, g.count ? (int64_t)g.idx_len * 4 : 0);
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(g.out + m0 * g.ldout + n0, ((rows_left - 1) * g.ldout + cols_left) * 2);
 
@@ -238,8 +240,10 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
         constexpr bool kPreW = !(BM == 256 && BN == 256);
         constexpr int kWIns = 16 * WN / 64;   // weight-byte copies: entry q*64 + lane -> slot, column
         const int npre = cnt < 16 ? cnt : 16;
-        const bool pre_ok = kPreW || npre <= n_stash;   // every slot below npre has LDS operands
-        if (npre > 0) {
+        // every slot below npre has LDS operands: X_O holds it, and so does
+        // the stash where the weight bytes come from there
+        const bool pre_ok = npre > 0 && npre <= g.cap && (kPreW || npre <= n_stash);
+        if (pre_ok) {
             int ixv[kPreW ? kWIns : 1];
             if constexpr (kPreW) {
                 // index reads first: an LDS read issued after a copy to LDS waits for it
@@ -282,7 +286,7 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
                     for (int r = 0; r < 16; ++r) f[ii][j][r] = (float)acc[i][j][r] * sxr[r];
             }
 
-            if (ic == 0 && npre > 0) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the LDS copies landed
+            if (ic == 0 && pre_ok) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the LDS copies landed
             for (int s0 = 0; s0 < cnt; s0 += 16) {
                 const int sb = s0 + 8 * hi;   // this lane's 8 outlier slots
                 if (s0 == 0 && pre_ok) {
@@ -326,11 +330,28 @@ __device__ inline void epilogue(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t 
 #pragma unroll
                 for (int t = 0; t < 8; ++t) ix[t] = sb + t < cnt ? ix[t] : -1;
                 v8h xa[IC];
+                if (sb + 8 <= xo_lim) {
 #pragma unroll
-                for (int ii = 0; ii < IC; ++ii) {
-                    const int lrow = wr0 + 32 * (ic + ii) + l32;
-                    xa[ii] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rxo, (lrow * (int)g.ldo + sb) * 2, 0, 0));
+                    for (int ii = 0; ii < IC; ++ii) {
+                        const int lrow = wr0 + 32 * (ic + ii) + l32;
+                        xa[ii] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rxo, (lrow * (int)g.ldo + sb) * 2, 0, 0));
+                    }
+                } else {
+                    // slots past X_O's capacity: x[row, idx[slot]] one by one
+#pragma unroll
+                    for (int ii = 0; ii < IC; ++ii) {
+                        const int lrow = wr0 + 32 * (ic + ii) + l32;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            const int slot = sb + t;
+                            const uint16_t h =
+                                slot < g.cap ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (lrow * (int)g.ldo + slot) * 2, 0, 0)
+                                             : __builtin_amdgcn_raw_buffer_load_b16(
+                                                   rx, ix[t] >= 0 ? (lrow * (int)g.ldx + ix[t]) * 2 : (int)0x80000000, 0, 0);
+                            xa[ii][t] = __builtin_bit_cast(_Float16, h);
+                        }
+                    }
                 }
                 uint32_t wby[FN][8];
                 if (sb + 8 <= n_stash) {
@@ -793,9 +814,8 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
     int n_st = 0, st_next = 0;
     int64_t st_col = INT64_MAX;
     if constexpr (stash_on<BM, BN, kFused>()) {
-        if (g.x_out) {
-            int cnt = epi.cnt[0];
-            cnt = cnt > g.cap ? g.cap : (cnt < 0 ? 0 : cnt);
+        if (g.count) {
+            const int cnt = outlier_count(g, epi.cnt[0]);
             n_st = __builtin_amdgcn_readfirstlane(cnt < kStash ? cnt : kStash);
             if (n_st > 0) st_col = __builtin_amdgcn_readfirstlane(epi.idx[0]);
         }

@@ -98,25 +98,25 @@ __device__ inline int32_t bitmap_prefix(const uint32_t* bm, int32_t* pre, int64_
 }
 
 
-// Workgroup 0 publishes the bitmap, the count and the ascending index list.
+// Workgroup 0 publishes the bitmap, the count and the ascending index list
+// (its first idx_len entries, -1 past the count).
 __device__ inline void publish(const QuantArgs& a, const uint32_t* bm, const int32_t* pre, int32_t total,
                                bool outl) {
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
-    const int32_t kept = total < a.cap ? total : a.cap;
     if (a.bitmap_out)
         for (int64_t w = tid; w < a.words; w += nt) a.bitmap_out[w] = outl ? bm[w] : 0u;
     if (a.count_out && tid == 0) *a.count_out = total;
     if (a.idx_out) {
         for (int32_t s = tid; s < a.idx_len; s += nt)
-            if (s >= kept) a.idx_out[s] = -1;
+            if (s >= total) a.idx_out[s] = -1;
         if (outl) {
             for (int64_t w = tid; w < a.words; w += nt) {
                 uint32_t v = bm[w];
                 int32_t slot = pre[w];
                 while (v) {
                     const int b = __ffs(v) - 1;
-                    if (slot < a.cap) a.idx_out[slot] = (int32_t)(w * 32 + b);
+                    if (slot < a.idx_len) a.idx_out[slot] = (int32_t)(w * 32 + b);
                     ++slot;
                     v &= v - 1u;
                 }

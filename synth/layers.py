@@ -51,6 +51,7 @@ class LayerSpec:
     bias_std: Optional[float] = None
     tau: float = TAU_DEFAULT
     variant_id: int = 0
+    truncate: bool = True         # False: the bulk keeps its raw tail (stress input)
 
     @property
     def ops(self) -> int:
@@ -87,6 +88,12 @@ def _workloads() -> Dict[str, List[LayerSpec]]:
     w["llama65b_prefill_m4096"] = [
         LayerSpec(5, 0, "up", 4096, 8192, 22016, 20, 6.0, 100.0, bulk="t3"),
         LayerSpec(5, 1, "down", 4096, 22016, 8192, 20, 6.0, 100.0, bulk="t3"),
+    ]
+    # the same layers with the heavy tail left untruncated: nearly every
+    # column reaches the threshold somewhere, so the linear is almost all fp16
+    w["llama65b_prefill_m4096_stress"] = [
+        LayerSpec(5, 0, "up", 4096, 8192, 22016, 20, 6.0, 100.0, bulk="t3", variant_id=1, truncate=False),
+        LayerSpec(5, 1, "down", 4096, 22016, 8192, 20, 6.0, 100.0, bulk="t3", variant_id=1, truncate=False),
     ]
     return w
 
@@ -198,7 +205,7 @@ def make_layer(spec: LayerSpec, *, with_weight: bool = True, m: Optional[int] = 
     seed = (spec.config_id, spec.layer_id, spec.variant_id)
     mm = spec.m if m is None else m
     x, cols = draw_activations(mm, spec.k, spec.n_outlier, spec.outlier_lo, spec.outlier_hi,
-                               bulk=spec.bulk, tau=spec.tau, seed=seed)
+                               bulk=spec.bulk, tau=spec.tau, seed=seed, truncate=spec.truncate)
     w = draw_weight(spec.n, spec.k, seed=seed) if with_weight else np.zeros((0, spec.k), np.float16)
     b = draw_bias(spec.n, seed=seed, std=spec.bias_std) if spec.bias_std is not None else None
     return Layer(spec, x, w, b, cols, (spec.config_id, spec.layer_id, -1, spec.variant_id))

@@ -45,7 +45,7 @@ def test_exports_match_header(L):
 def test_status_strings(L):
     for s in (OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE, -5):
         assert len(L.i8mp_status_string(s)) > 0
-    assert L.i8mp_abi_version() >> 16 == 2
+    assert L.i8mp_abi_version() >> 16 == 3
 
 
 def test_workspace_queries(L):
@@ -56,6 +56,8 @@ def test_workspace_queries(L):
     assert L.i8mp_linear_workspace_query(2048, 4096, 4096, 20, ctypes.byref(lay)) == OK
     assert lay.ldq % 128 == 0 and lay.ldq >= 4096
     assert lay.cap_pad == 32
+    assert lay.idx_len == 4096                       # every column fits the index list
+    assert lay.count_offset - lay.idx_offset >= 4 * lay.idx_len
     offs = [lay.scratch_offset, lay.bitmap_offset, lay.idx_offset, lay.count_offset,
             lay.absmax_offset, lay.q_offset, lay.xo_offset]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
@@ -158,6 +160,7 @@ def test_forward_validation(L):
     assert call(m=0) == OK
     assert call(n=0) == OK
     assert call(ldw=MAX_LD + 1) == EINVAL
+    assert call(ldx=MAX_LD + 1) == EINVAL
     assert call(ldo=MAX_LD + 1) == EINVAL
     assert call(cap=MAX_LD + 1) == EINVAL
     assert L.i8mp_linear_workspace_query(16, 32, 64, MAX_LD + 1, ctypes.byref(lay)) == EINVAL
@@ -170,12 +173,15 @@ def test_forward_validation(L):
     assert qz(FAKE, 16, 133145, 133145, 6.0, 8, FAKE, 1 << 40, None) == ERANGE
     assert qz(None, 0, 64, 64, 6.0, 8, None, 0, None) == OK
     md = L.i8mp_linear_matmul_dequant
-    assert md(FAKE, lay.bytes, 16, 64, 8, None, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL
-    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 63, FAKE, 32, None, FAKE, 32, None) == EINVAL
-    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 31, None) == EINVAL
-    assert md(None, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
-    assert md(FAKE, lay.bytes - 1, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
-    assert md(FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 0, None, FAKE, 32, None) == OK
+    assert md(FAKE, 64, FAKE, lay.bytes, 16, 64, 8, None, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL
+    assert md(FAKE, 64, FAKE, lay.bytes, 16, 64, 8, FAKE, 63, FAKE, 32, None, FAKE, 32, None) == EINVAL
+    assert md(FAKE, 64, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 31, None) == EINVAL
+    assert md(None, 64, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL  # x
+    assert md(FAKE, 63, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL  # ldx < k
+    assert md(FAKE, MAX_LD + 1, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EINVAL
+    assert md(FAKE, 64, None, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
+    assert md(FAKE, 64, FAKE, lay.bytes - 1, 16, 64, 8, FAKE, 64, FAKE, 32, None, FAKE, 32, None) == EWORKSPACE
+    assert md(FAKE, 64, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 0, None, FAKE, 32, None) == OK
 
 
 def test_backward_validation(L):

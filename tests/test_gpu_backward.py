@@ -83,7 +83,8 @@ BWD_CASES = [
     (130, 250, 300, 4, 32),
     (200, 33, 513, 5, 256),
     (512, 1024, 768, 7, 256),
-    (333, 257, 1000, 12, 8),      # more outlier columns than cap: the first cap take the fp16 path
+    (333, 257, 1000, 12, 8),      # more outlier columns than cap: those past it summed from g and x
+    (300, 200, 500, 20, 0),       # no gathered columns at all
     (1100, 640, 2048, 20, 32),    # three row blocks of the column maxima
     (700, 3000, 96, 2, 16),       # long grad_x contraction, short grad_w one
 ]
@@ -103,7 +104,7 @@ def test_linear_backward(case):
     x, w = L.x, L.w
     g = draw_grad(m, n, seed=(82, m % 101, n % 103))
     cols = oracle.outlier_columns(x, TAU)
-    used = cols[:cap]
+    used = cols   # every outlier column takes the fp16 path, whatever cap
     say(f"linear_backward m={m} n={n} k={k} outliers={len(cols)} cap={cap}")
     xt, gt_, wt_ = dev(x), dev(g), dev(w)
     fws = _run_forward(xt, n, k, cap)
@@ -224,5 +225,33 @@ def test_backward_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(gx.view(torch.int16), ex.view(torch.int16)), rep
         assert torch.equal(gw.view(torch.int16), ew.view(torch.int16)), rep
-    ref = oracle.linear_backward(g, L.x, L.w, oracle.outlier_columns(L.x, TAU)[:cap])
+    ref = oracle.linear_backward(g, L.x, L.w, oracle.outlier_columns(L.x, TAU))
     assert_fp16_close(gw, ref.gw, "grad_w after replays")
+
+
+@pytest.mark.parametrize("tau", [6.0, 6.001])
+def test_linear_backward_threshold_edge(tau):
+    """The backward takes the forward's outlier list at the threshold's edge:
+    a column whose only large element is exactly 6.0 is an outlier at tau = 6
+    (zeroed in CAt, fp16 column of grad_w) and not at tau = 6.001; one at the
+    largest fp16 below 6 never is."""
+    m, n, k = 200, 96, 300
+    L = make_inputs(m, k, n, seed=(87, 0, 0))
+    L.x[17, 40] = np.float16(6.0)
+    L.x[3, 41] = np.float16(-6.0)
+    L.x[150, 99] = np.float16(5.99609375)
+    L.x[151, 200] = np.float16(6.00390625)
+    g = draw_grad(m, n, seed=(87, 0, 0))
+    cols = oracle.outlier_columns(L.x, tau)
+    assert cols.tolist() == ([40, 41, 200] if tau == 6.0 else [200])
+    say(f"linear_backward threshold edge tau={tau}")
+    xt = dev(L.x)
+    fws = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
+    i8.linear_quantize(xt, fws, threshold=tau)
+    bws = i8.BackwardWorkspace.create(m, n, k, 32, "cuda")
+    gx, gw = i8.linear_backward(dev(g), xt, dev(L.w), fws, workspace=bws)
+    torch.cuda.synchronize()
+    ref = oracle.linear_backward(g, L.x, L.w, cols)
+    assert_equal(bws.xt_q(), ref.xt_q, "column-wise codes of x, outlier columns zeroed")
+    assert_fp16_close(gx, ref.gx, "grad_x")
+    assert_fp16_close(gw, ref.gw, "grad_w")

@@ -110,3 +110,43 @@ def test_vectorwise_dequant_65b_weight():
     # the weight codes themselves are the oracle's
     wq_ref, ws_ref = oracle.quantize_weight(L.w[rows])
     assert_equal(wq[ridx], wq_ref, "weight codes")
+
+
+STRESS = layer_specs("llama65b_prefill_m4096_stress")
+
+
+@pytest.mark.parametrize("spec,cap", [(STRESS[0], CAP), (STRESS[0], 8192), (STRESS[1], CAP)],
+                         ids=["up-cap256", "up-capk", "down-cap256"])
+def test_llama65b_stress_untruncated(spec, cap):
+    """The 65B layers on their untruncated Student-t input: nearly every column
+    is an outlier, so the linear is almost all fp16.  With cap 256 all but 256
+    outlier columns read x through the index list; with cap = k all come from
+    the gathered copy.  Codes, absmax, bitmap and the whole index list in full,
+    the output on sampled rows (outlier set from the full input)."""
+    say(f"stress {spec.name} m={spec.m} k={spec.k} n={spec.n} cap={cap}")
+    L = make_layer(spec)
+    qr = oracle.vectorwise_quant(L.x, spec.tau)
+    assert qr.cols.size > 0.99 * spec.k
+    xd = dev(L.x)
+    wq_g, ws_g = i8.quantize_weight(dev(L.w))
+    wsp = i8.LinearWorkspace.create(spec.m, spec.n, spec.k, cap, "cuda")
+    out = i8.linear(xd, wq_g, ws_g, None, spec.tau, cap, wsp)
+    torch.cuda.synchronize()
+    assert int(wsp.count().item()) == qr.cols.size
+    assert_equal(wsp.bitmap().view(torch.int32), qr.bitmap.view(np.int32), "bitmap")
+    assert_equal(wsp.absmax(), qr.absmax, "absmax")
+    assert_equal(wsp.codes(), qr.q, "codes")
+    ridx, _, _ = oracle.outlier_extract(L.x, qr.cols, int(wsp.layout.idx_len))
+    assert_equal(wsp.idx(), ridx, "idx")
+    wq = wq_g.cpu().numpy()
+    ws = ws_g.cpu().numpy()
+    rows = _sample_rows(spec.m, count=24, seed=spec.layer_id + 11)
+    xs = L.x[rows]
+    s = oracle.row_absmax(xs, qr.cols)
+    q = oracle.quantize_rows(xs, s, qr.cols)
+    c = oracle.int8_linear_matmul(q, wq)
+    p = oracle.outlier_matmul(xs, qr.cols, wq)
+    ref = oracle.mm_dequant(c, s, ws, None, p)
+    assert_fp16_close(out[torch.from_numpy(rows).cuda()], ref, f"{spec.name} stress sampled rows")
+    wq_ref, ws_ref = oracle.quantize_weight(L.w[:64])
+    assert_equal(wq_g[:64], wq_ref, "weight codes (first rows)")

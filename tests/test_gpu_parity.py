@@ -85,13 +85,14 @@ def test_weight_quant_bit_exact(n, k):
 
 
 @pytest.mark.parametrize("m,k,o,cap", [(5, 100, 3, 8), (64, 4096, 7, 32), (16, 1024, 0, 8),
-                                       (4, 200, 12, 5), (1, 70, 2, 0)])
+                                       (4, 200, 12, 5), (1, 70, 2, 0), (7, 300, 9, None)])
 def test_outlier_extract_bit_exact(m, k, o, cap):
     L = _quant_layer(m, k, o, 0.6, 9)
     say(f"outlier_extract m={m} k={k} o={o} cap={cap}")
     xd = dev(L.x)
     _, _, bm = i8.vectorwise_quant(xd, TAU)
-    idx, count, xo = i8.outlier_extract(xd, bm, cap)
+    idx, count, xo = i8.outlier_extract(xd, bm, cap, strict=False)
+    cap = k if cap is None else cap
     torch.cuda.synchronize()
     ref = oracle.vectorwise_quant(L.x, TAU)
     ridx, rcount, rxo = oracle.outlier_extract(L.x, ref.cols, cap)
@@ -224,6 +225,19 @@ FWD_CASES = [
 ]
 
 
+def _check_workspace(wsp, x, ref, cap):
+    """Codes, absmax, bitmap, count, the whole index list and the first cap
+    gathered columns of a forward workspace, bit for bit."""
+    assert_equal(wsp.codes(), ref.q, "codes")
+    assert_equal(wsp.absmax(), ref.absmax, "absmax")
+    assert_equal(wsp.bitmap().view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+    assert int(host(wsp.count())[0]) == ref.cols.size
+    ridx, _, _ = oracle.outlier_extract(x, ref.cols, int(wsp.layout.idx_len))
+    assert_equal(wsp.idx(), ridx, "idx (every outlier column)")
+    _, _, rxo = oracle.outlier_extract(x, ref.cols, cap)
+    assert_equal(wsp.x_out().contiguous().view(torch.int16), rxo.view(np.int16), "x_out")
+
+
 def _check_forward(L, wq, ws, tau, cap, what):
     ref = oracle.linear_forward(L.x, wq, ws, L.bias, tau)
     m, k = L.x.shape
@@ -232,13 +246,7 @@ def _check_forward(L, wq, ws, tau, cap, what):
     wsp = i8.LinearWorkspace.create(m, n, k, cap, "cuda")
     out = i8.linear(dev(L.x), dev(wq), dev(ws), dev(L.bias) if L.bias is not None else None, tau, cap, wsp)
     torch.cuda.synchronize()
-    assert_equal(wsp.codes(), ref.quant.q, "codes")
-    assert_equal(wsp.absmax(), ref.quant.absmax, "absmax")
-    assert_equal(wsp.bitmap().view(torch.int32), ref.quant.bitmap.view(np.int32), "bitmap")
-    assert int(host(wsp.count())[0]) == ref.quant.cols.size
-    ridx, _, rxo = oracle.outlier_extract(L.x, ref.quant.cols, cap)
-    assert_equal(wsp.idx(), ridx, "idx")
-    assert_equal(wsp.x_out().contiguous().view(torch.int16), rxo.view(np.int16), "x_out")
+    _check_workspace(wsp, L.x, ref.quant, cap)
     assert_fp16_close(out, ref.out)
     return out, ref
 
@@ -295,17 +303,56 @@ def test_linear_forward_zero_rows_and_zero_input():
     assert np.array_equal(host(out), np.repeat(L.bias[None, :], 20, 0))
 
 
-def test_linear_forward_capacity_overflow_reports_count():
-    L = make_inputs(8, 512, 64, n_outlier=12, seed=(78, 0, 0))
+PAST_CAP_CASES = [
+    # m, k, n, o, frac, bias, cap: more outlier columns than the gathered
+    # capacity; every path must still give the method's result
+    (8, 512, 64, 12, 1.0, False, 4),          # prefill 64 x 64 tiles
+    (300, 520, 600, 11, 0.3, True, 0),        # no gathered columns at all
+    (768, 256, 6144, 30, 0.5, True, 4),       # 256 x 128: operands of the first 16 slots not copied early
+    (1536, 384, 6144, 40, 0.5, False, 8),     # 256 x 256: stash for 24 slots, X_O for 8, x past them
+    (1536, 256, 6144, 20, 1.0, True, 17),     # 256 x 256: a 16-slot group straddling cap
+    (768, 250, 6144, 20, 0.5, True, 5),       # register-staged kernel (unaligned weight rows)
+    (40, 2100, 300, 5, 1.0, True, 2),         # two K pipelines
+    (1, 4096, 300, 70, 0.5, True, 8),         # one-launch GEMV forward, past the stream's 64 columns
+    (3, 2000, 130, 9, 1.0, False, 4),         # one-launch GEMV forward, m = 3
+    (4, 8192, 200, 70, 1.0, False, 0),        # one-launch GEMV forward, no gathered columns
+    (9, 3000, 200, 33, 1.0, True, 4),         # MFMA decode kernel: ring 32, then gathered
+    (16, 1024, 256, 40, 0.5, False, 0),       # MFMA decode kernel, no gathered columns
+    (4, 13824, 300, 12, 0.5, True, 2),        # m <= 4 past the GEMV's LDS: MFMA decode kernel
+]
+
+
+@pytest.mark.parametrize("case", PAST_CAP_CASES, ids=lambda c: "m%d_k%d_n%d_o%d_f%g_b%d_c%d" % c)
+def test_linear_forward_past_cap(case):
+    """The fused forward gives the oracle's result for any outlier count: the
+    columns past cap read x through the index list.  The index list holds
+    every outlier column, X_O the first cap."""
+    m, k, n, o, frac, bias, cap = case
+    L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01 if bias else None, seed=(78, m, k),
+                    outlier_row_frac=frac)
     wq, ws = oracle.quantize_weight(L.w)
-    say("forward cap overflow")
-    wsp = i8.LinearWorkspace.create(8, 64, 512, 4, "cuda")
-    i8.linear(dev(L.x), dev(wq), dev(ws), None, TAU, 4, wsp)
+    out, ref = _check_forward(L, wq, ws, TAU, cap, f"past cap {case}")
+    assert ref.quant.cols.size == o > cap
+
+
+@pytest.mark.parametrize("case", [(2, 4096, 264, 40, 4), (3, 2000, 130, 70, 0), (12, 3000, 200, 45, 8),
+                                  (520, 300, 1000, 30, 3)], ids=lambda c: "m%d_k%d_n%d_o%d_c%d" % c)
+def test_two_launch_forward_past_cap(case):
+    """linear_quantize + linear_matmul_dequant (the GEMV of m <= 4 reading the
+    workspace codes, the MFMA decode kernel, a prefill tile) past cap."""
+    m, k, n, o, cap = case
+    L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01, seed=(78, 1, m), outlier_row_frac=0.5)
+    wq, ws = oracle.quantize_weight(L.w)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    x = dev(L.x)
+    wsp = i8.LinearWorkspace.create(m, n, k, cap, "cuda")
+    say(f"two-launch forward past cap {case}")
+    i8.linear_quantize(x, wsp, TAU)
+    out = i8.linear_matmul_dequant(x, wsp, dev(wq), dev(ws), dev(L.bias))
     torch.cuda.synchronize()
-    assert int(host(wsp.count())[0]) == 12
-    assert wsp.outlier_overflow()
-    ref = oracle.vectorwise_quant(L.x, TAU)
-    assert_equal(wsp.idx(), ref.cols[:4].astype(np.int32), "first cap indices")
+    assert wsp.outliers_past_cap()
+    _check_workspace(wsp, L.x, ref.quant, cap)
+    assert_fp16_close(out, ref.out)
 
 
 def _workspace_state(wsp):
@@ -328,17 +375,16 @@ def test_decode_forward_matches_two_launches(m, k, n, o, cap):
     torch.cuda.synchronize()
     say(f"two-launch forward m={m} k={k} n={n} o={o} cap={cap}")
     i8.linear_quantize(x, wb, TAU)
-    two = i8.linear_matmul_dequant(wb, w, s, b)
+    two = i8.linear_matmul_dequant(x, wb, w, s, b)
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
     for name, a, c in zip(("codes", "absmax", "bitmap", "idx", "count", "x_out"),
                           _workspace_state(wa), _workspace_state(wb)):
         assert torch.equal(a.view(torch.uint8), c.view(torch.uint8)), name
     assert int(host(wa.count())[0]) == o
-    assert wa.outlier_overflow() == (o > cap)
-    if o <= cap:
-        ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
-        assert_fp16_close(one, ref.out)
+    assert wa.outliers_past_cap() == (o > cap)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_fp16_close(one, ref.out)
 
 
 @pytest.mark.parametrize("m", [1, 4])
@@ -359,7 +405,7 @@ def test_gemv_outlier_columns_sharing_a_lane(m):
     one = i8.linear(x, w, s_, b, TAU, 32, wa)
     wb = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
     i8.linear_quantize(x, wb, TAU)
-    two = i8.linear_matmul_dequant(wb, w, s_, b)
+    two = i8.linear_matmul_dequant(x, wb, w, s_, b)
     torch.cuda.synchronize()
     assert_fp16_close(one, ref.out)
     assert_fp16_close(two, ref.out)
@@ -504,4 +550,137 @@ def test_graph_capture_replays_match_eager(m):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
     ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    assert_fp16_close(out, ref.out)
+
+
+def test_outlier_extract_strict_raises_past_cap():
+    L = _quant_layer(6, 300, 9, 1.0, 11)
+    xd = dev(L.x)
+    _, _, bm = i8.vectorwise_quant(xd, TAU)
+    say("outlier_extract strict past cap")
+    with pytest.raises(ValueError):
+        i8.outlier_extract(xd, bm, 4)
+    idx, count, _ = i8.outlier_extract(xd, bm)     # cap = k: every column
+    torch.cuda.synchronize()
+    assert int(host(count)[0]) == 9
+
+
+# ---- the threshold's edge: |x| >= tau decides, in fp32 on both sides --------
+
+BELOW6 = np.float16(5.99609375)    # largest fp16 below 6
+ABOVE6 = np.float16(6.00390625)    # smallest fp16 above 6
+
+
+def _edge_input(m, k, n, seed):
+    """Seeded layer (bulk below 6) with columns planted at the threshold's
+    edge, each large in a single row only: +6.0 (col a), -6.0 (col a2),
+    the largest fp16 below 6 (col b, in two rows with both signs), the
+    smallest above 6 (col c).  Columns straddle 8-column chunks and 32-column
+    bitmap words.  Returns the layer and the columns."""
+    L = make_inputs(m, k, n, bias_std=0.01, seed=(86, m, k))
+    rng = np.random.default_rng([86, m, k, n])
+    cols = np.sort(rng.choice(np.arange(1, k - 1), size=4, replace=False))
+    a, a2, b, c = (int(v) for v in rng.permutation(cols))
+    rows = rng.integers(0, m, size=5)
+    L.x[rows[0], a] = np.float16(6.0)
+    L.x[rows[1], a2] = np.float16(-6.0)
+    L.x[rows[2], b] = BELOW6
+    L.x[rows[3], b] = -BELOW6
+    L.x[rows[4], c] = ABOVE6
+    return L, (a, a2, b, c)
+
+
+EDGE_CASES = [
+    # m, k, n, tau: tau = 6.001 is not an fp16 value (6.0 is then below it)
+    (1, 1000, 77, 6.0),        # one-launch GEMV forward (detection in its prologue)
+    (1, 1000, 77, 6.001),
+    (3, 2048, 130, 6.0),
+    (9, 3000, 200, 6.0),       # quantizer kernels + MFMA decode kernel
+    (9, 3000, 200, 6.001),
+    (300, 1024, 520, 6.0),     # detect + quantize kernels + prefill tile
+    (300, 1024, 520, 6.001),
+    (2, 33000, 64, 6.0),       # single-workgroup quantizer (two rows), MFMA decode kernel
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "m%d_k%d_n%d_t%g" % c)
+def test_threshold_edge_forward(case):
+    m, k, n, tau = case
+    L, (a, a2, b, c) = _edge_input(m, k, n, seed=0)
+    wq, ws = oracle.quantize_weight(L.w)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, tau)
+    want = {c} | ({a, a2} if tau == 6.0 else set())
+    assert set(ref.quant.cols.tolist()) == want     # the oracle's own decision at the edge
+    _check_forward(L, wq, ws, tau, 32, f"threshold edge {case}")
+
+
+@pytest.mark.parametrize("m,k,tau", [(2, 1000, 6.0), (2, 1000, 6.001), (40, 3000, 6.0), (300, 20000, 6.0),
+                                     (300, 20000, 6.001)])
+def test_threshold_edge_quant(m, k, tau):
+    """int8_vectorwise_quant on its own: the two-row single-workgroup kernel,
+    and detect + quantize with a wavefront or a workgroup per row."""
+    L, _ = _edge_input(m, k, 1, seed=1)
+    say(f"vectorwise_quant threshold edge m={m} k={k} tau={tau}")
+    q, s, bm = i8.vectorwise_quant(dev(L.x), tau)
+    torch.cuda.synchronize()
+    ref = oracle.vectorwise_quant(L.x, tau)
+    assert_equal(q, ref.q, "codes")
+    assert_equal(s, ref.absmax, "absmax")
+    assert_equal(bm.view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+
+
+# ---- int32 accumulation at the largest k (k * 127^2 < 2^31) ------------------
+
+def test_linear_matmul_int32_bound():
+    k = i8.I8MP_MAX_K
+    a = np.full((3, k), 127, np.int8)
+    a[1] = -127
+    a[2, 1::2] = -127
+    b = np.full((2, k), 127, np.int8)
+    b[1] = -127
+    say(f"linear_matmul k={k} all +-127")
+    c = i8.linear_matmul(dev(a), dev(b))
+    torch.cuda.synchronize()
+    ref = oracle.int8_linear_matmul(a, b)
+    assert ref[0, 0] == 2147479576 and ref[1, 0] == -2147479576
+    assert_equal(c, ref, "C at k = 133144")
+    c1 = i8.linear_matmul(dev(a[:1]), dev(b[:1]))
+    torch.cuda.synchronize()
+    assert int(host(c1)[0, 0]) == 2147479576
+
+
+def test_linear_matmul_int32_bound_tiles():
+    """Random codes at the largest k through a prefill tile (ragged m and n)."""
+    k = i8.I8MP_MAX_K
+    rng = np.random.default_rng(87)
+    a = rng.integers(-127, 128, (40, k), dtype=np.int16).astype(np.int8)
+    a[0] = 127
+    b = rng.integers(-127, 128, (70, k), dtype=np.int16).astype(np.int8)
+    b[0] = 127
+    say(f"linear_matmul 40 x 70 x {k}")
+    c = i8.linear_matmul(dev(a), dev(b))
+    torch.cuda.synchronize()
+    ref = oracle.int8_linear_matmul(a, b)
+    assert ref[0, 0] == 2147479576
+    assert_equal(c, ref, "C")
+
+
+@pytest.mark.parametrize("m", [1, 3, 300])
+def test_linear_forward_largest_k(m):
+    """The fused forward at k = 133144: x = 1 and w = 2^-10 everywhere give
+    all-127 codes on both sides (C = (k - o) * 127^2 near 2^31), plus three
+    outlier columns of 7.0 in the fp16 part."""
+    k, n = i8.I8MP_MAX_K, 64
+    x = np.ones((m, k), np.float16)
+    x[:, [5, 70000, k - 1]] = np.float16(7.0)
+    w = np.full((n, k), np.float16(2.0 ** -10))
+    w[1::2, ::3] = np.float16(-(2.0 ** -10))
+    wq, ws = oracle.quantize_weight(w)
+    ref = oracle.linear_forward(x, wq, ws, None, TAU)
+    assert ref.c[0, 0] == (k - 3) * 127 * 127
+    say(f"linear_forward m={m} k={k}")
+    wsp = i8.LinearWorkspace.create(m, n, k, 8, "cuda")
+    out = i8.linear(dev(x), dev(wq), dev(ws), None, TAU, 8, wsp)
+    torch.cuda.synchronize()
+    _check_workspace(wsp, x, ref.quant, 8)
     assert_fp16_close(out, ref.out)
