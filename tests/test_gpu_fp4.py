@@ -89,7 +89,9 @@ LINEAR_CASES = [
     (4, 64, 4096, True, True),
     (5, 31, 2048, False, False),    # two launches: rows 0-3, then row 4
     (9, 100, 1024, True, True),
-    (4, 50, 13824, False, False),   # x too large for LDS: read from memory
+    (4, 50, 13824, False, False),   # more than 256 chunks of 32 weights per row: the pipelined form
+    (3, 37, 13824, True, True),     # pipelined, four weight rows per workgroup, the last workgroup partial
+    (2, 9, 9216, False, True),      # pipelined at m = 2, the last workgroup partial
     (1, 1000, 5120, True, False),
 ]
 

@@ -182,3 +182,19 @@ def test_linear_brute_force_tiny(seed):
         for r in range(n):
             exact = sum((Fraction(float(x[i, j])) * wq[r][j] for j in range(k)), Fraction(0)) + Fraction(float(b[r]))
             assert abs(Fraction(float(y[i, r])) - exact) <= abs(exact) * Fraction(1, 2**50) + Fraction(1, 2**60)
+
+
+def test_double_dequant_exact_rationals():
+    """The reconstructed scale fl32(c8 * fl32(s2 / 255)) for every code 0..255
+    under a set of group maxima, against exact rationals rounded to binary32
+    twice, as F4 reads.  A one-rounding (float64) evaluation of the same
+    product differs on this set, so the pin tells the two apart."""
+    rng = np.random.default_rng(24)
+    s2 = np.concatenate([rng.uniform(1e-4, 1.0, 6), [0.1, 0.2, 1.0 / 3.0]]).astype(np.float32)
+    c8 = np.tile(np.arange(256, dtype=np.uint8), s2.size)
+    r = fp4.double_dequant(c8, s2)
+    for j in range(c8.size):
+        step = f32(Fraction(float(s2[j // 256])) / 255)
+        assert Fraction(float(r[j])) == f32(Fraction(int(c8[j])) * step), j
+    one_rounding = (c8.astype(np.float64) * (np.repeat(s2.astype(np.float64), 256) / 255.0)).astype(np.float32)
+    assert not np.array_equal(one_rounding, r)
