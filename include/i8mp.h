@@ -65,6 +65,7 @@ typedef int32_t i8mp_status;
 #define I8MP_EWORKSPACE -3 /* workspace NULL or smaller than the query returned   */
 #define I8MP_EDEVICE -4    /* current device is not gfx950, or no device          */
 #define I8MP_ELAUNCH -5    /* a kernel launch failed (hipGetLastError)            */
+#define I8MP_ESCRATCH -6   /* the call needs more than the fixed scratch array    */
 
 /* floor((2^31 - 1) / 127^2): largest k whose worst-case int8 dot product fits int32. */
 #define I8MP_MAX_K 133144
@@ -254,6 +255,22 @@ i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx
                                 const void* bias, float threshold, int32_t cap, void* out,
                                 int64_t ldout, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): i8mp_linear_forward
+ * with the same arguments except the workspace, which is a fixed device array
+ * inside the library of I8MP_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * acquired on the first call on that GPU and held until the process ends.
+ * The call allocates nothing.  A shape whose workspace (the layout query's
+ * bytes for m, k and cap) exceeds the array returns I8MP_ESCRATCH and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race, and the
+ * intermediates of a call are overwritten by the next one. */
+#define I8MP_NOALLOC_SCRATCH_BYTES (32u << 20)
+i8mp_status i8mp_linear_forward_noalloc(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                        const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+                                        const void* bias, float threshold, int32_t cap, void* out,
+                                        int64_t ldout, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Backward pass through the int8 linear (training with the fp16 weight kept).

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     BackwardWorkspaceLayout,
     I8MP_MAX_K,
+    I8MP_NOALLOC_SCRATCH_BYTES,
     I8mpError,
     LinearWorkspaceLayout,
     check,
@@ -38,6 +39,7 @@ __all__ = [
     "mm_dequant",
     "vectorwise_dequant",
     "linear",
+    "linear_forward_noalloc",
     "linear_quantize",
     "linear_matmul_dequant",
     "LinearWorkspace",
@@ -306,6 +308,33 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_absmax: torch.Tensor,
                                         threshold, cap, _ptr(out), ldout, _ptr(workspace.buf),
                                         workspace.buf.numel(), _stream(dev)),
               "i8mp_linear_forward")
+    return out
+
+
+def linear_forward_noalloc(x: torch.Tensor, w_q: torch.Tensor, w_absmax: torch.Tensor, out: torch.Tensor,
+                           bias: Optional[torch.Tensor] = None, threshold: float = DEFAULT_THRESHOLD,
+                           cap: int = DEFAULT_CAP) -> torch.Tensor:
+    """``linear`` into a caller-owned ``out`` with the library's fixed scratch
+    array as workspace: the call allocates nothing (for graph capture and
+    serving loops).  Shapes whose workspace exceeds the array raise; calls
+    that overlap on one GPU share the array and race."""
+    dev = _device_of(x, w_q, w_absmax, bias, out)
+    ldx = _rowmajor(x, "x", torch.float16)
+    ldw = _rowmajor(w_q, "w_q", torch.int8)
+    m, k = x.shape
+    n, kw = w_q.shape
+    if kw != k:
+        raise ValueError("x and w_q differ in k")
+    _vec(w_absmax, "w_absmax", torch.float32, n)
+    if bias is not None:
+        _vec(bias, "bias", torch.float16, n)
+    ldout = _rowmajor(out, "out", torch.float16)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(dev):
+        check(lib().i8mp_linear_forward_noalloc(_ptr(x), m, k, ldx, _ptr(w_q), ldw, _ptr(w_absmax), n, _ptr(bias),
+                                                threshold, cap, _ptr(out), ldout, _stream(dev)),
+              "i8mp_linear_forward_noalloc")
     return out
 
 

@@ -15,7 +15,9 @@ I8MP_ERANGE = -2
 I8MP_EWORKSPACE = -3
 I8MP_EDEVICE = -4
 I8MP_ELAUNCH = -5
+I8MP_ESCRATCH = -6
 I8MP_MAX_K = 133144
+I8MP_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/i8mp.h declares.
 EXPORTS = (
@@ -31,6 +33,7 @@ EXPORTS = (
     "i8mp_linear_quantize",
     "i8mp_linear_matmul_dequant",
     "i8mp_linear_forward",
+    "i8mp_linear_forward_noalloc",
     "i8mp_colwise_quant_workspace_bytes",
     "i8mp_int8_colwise_quant",
     "i8mp_linear_backward_workspace_query",
@@ -116,6 +119,9 @@ def _declare(lib):
                                         c_int64, c_void_p, c_float, c_int32, c_void_p, c_int64, c_void_p,
                                         c_size_t, c_void_p]
     lib.i8mp_linear_forward.restype = c_int32
+    lib.i8mp_linear_forward_noalloc.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p,
+                                                c_int64, c_void_p, c_float, c_int32, c_void_p, c_int64, c_void_p]
+    lib.i8mp_linear_forward_noalloc.restype = c_int32
     lib.i8mp_linear_quantize.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_float, c_int32, c_void_p,
                                          c_size_t, c_void_p]
     lib.i8mp_linear_quantize.restype = c_int32

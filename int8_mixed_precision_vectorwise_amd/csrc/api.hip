@@ -3,6 +3,7 @@
 // device memory; every launch goes to the caller's stream.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 #include "backward.h"
@@ -103,6 +104,7 @@ const char* i8mp_status_string(i8mp_status s) {
         case I8MP_EWORKSPACE: return "workspace missing or too small";
         case I8MP_EDEVICE: return "no gfx950 device is current";
         case I8MP_ELAUNCH: return "kernel launch failed";
+        case I8MP_ESCRATCH: return "the call needs more than the library's fixed scratch array holds";
         default: return "unknown status";
     }
 }
@@ -357,27 +359,109 @@ i8mp_status i8mp_linear_matmul_dequant(const void* x, int64_t ldx, const void* w
                                   n, bias, out, ldout, stream);
 }
 
-i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx,
-                                const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
-                                const void* bias, float threshold, int32_t cap, void* out,
-                                int64_t ldout, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+namespace {
+
+// Checks shared by the forward entry points; I8MP_OK with *empty set when
+// there is nothing to do.
+i8mp_status check_forward_args(const void* x, int64_t m, int64_t k, int64_t ldx, const int8_t* w_q, int64_t ldw,
+                               const float* w_absmax, int64_t n, int32_t cap, const void* out, int64_t ldout,
+                               bool* empty) {
+    *empty = false;
     if (m < 0 || n < 0 || bad_k(k) || ldx < k || ldw < k || ldout < n || cap < 0) return I8MP_EINVAL;
     if (bad_ld(ldx) || bad_ld(ldw) || bad_ld(ldout) || bad_ld(cap)) return I8MP_EINVAL;
     if (k > I8MP_MAX_K) return I8MP_ERANGE;
-    if (m == 0 || n == 0) return I8MP_OK;
+    if (m == 0 || n == 0) {
+        *empty = true;
+        return I8MP_OK;
+    }
     if (!x || !w_q || !w_absmax || !out) return I8MP_EINVAL;
-    i8mp_linear_workspace L;
-    forward_layout(m, k, cap, &L);
-    if (!workspace || workspace_bytes < L.bytes) return I8MP_EWORKSPACE;
-    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
-    char* ws = static_cast<char*>(workspace);
+    return I8MP_OK;
+}
+
+// The forward's launches with its workspace at ws (layout L).
+i8mp_status enqueue_forward(const void* x, int64_t m, int64_t k, int64_t ldx, const int8_t* w_q, int64_t ldw,
+                            const float* w_absmax, int64_t n, const void* bias, float threshold, int32_t cap,
+                            void* out, int64_t ldout, const i8mp_linear_workspace& L, char* ws,
+                            hipStream_t stream) {
     // one to four rows: quantization inside the GEMV's workgroups, one launch
     const QuantArgs qa = forward_quant_args(x, m, k, ldx, threshold, cap, L, ws);
     const GemmArgs g = forward_gemm_args(L, ws, x, ldx, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout);
     if (decode_forward_fits(qa, g)) return launched(launch_decode_forward(qa, g, stream));
     if (i8mp_status s = launched(launch_quantize(qa, stream)); s != I8MP_OK) return s;
     return launched(launch_gemm_fused(g, stream));
+}
+
+}  // namespace
+
+i8mp_status i8mp_linear_forward(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                const int8_t* w_q, int64_t ldw, const float* w_absmax, int64_t n,
+                                const void* bias, float threshold, int32_t cap, void* out,
+                                int64_t ldout, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    bool empty = false;
+    if (i8mp_status s = check_forward_args(x, m, k, ldx, w_q, ldw, w_absmax, n, cap, out, ldout, &empty);
+        s != I8MP_OK || empty)
+        return s;
+    i8mp_linear_workspace L;
+    forward_layout(m, k, cap, &L);
+    if (!workspace || workspace_bytes < L.bytes) return I8MP_EWORKSPACE;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    return enqueue_forward(x, m, k, ldx, w_q, ldw, w_absmax, n, bias, threshold, cap, out, ldout, L,
+                           static_cast<char*>(workspace), stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The forward for callers that cannot allocate: its workspace is this
+// file-scope device array, one per GPU, held until the process ends.  In host
+// code the name `scratch` is a host-side stand-in, not device memory; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device (with that device current) on the entry point's first call
+// there, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[I8MP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array.
+i8mp_status scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return I8MP_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return I8MP_EDEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return I8MP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+i8mp_status i8mp_linear_forward_noalloc(const void* x, int64_t m, int64_t k, int64_t ldx, const int8_t* w_q,
+                                        int64_t ldw, const float* w_absmax, int64_t n, const void* bias,
+                                        float threshold, int32_t cap, void* out, int64_t ldout,
+                                        hipStream_t stream) {
+    bool empty = false;
+    if (i8mp_status s = check_forward_args(x, m, k, ldx, w_q, ldw, w_absmax, n, cap, out, ldout, &empty);
+        s != I8MP_OK || empty)
+        return s;
+    i8mp_linear_workspace L;
+    forward_layout(m, k, cap, &L);
+    if (L.bytes > (size_t)I8MP_NOALLOC_SCRATCH_BYTES) return I8MP_ESCRATCH;
+    if (i8mp_status s = check_device(); s != I8MP_OK) return s;
+    void* ws = nullptr;
+    if (i8mp_status s = scratch_on_current_device(&ws); s != I8MP_OK) return s;
+    // every intermediate is written before it is read: nothing to clear
+    return enqueue_forward(x, m, k, ldx, w_q, ldw, w_absmax, n, bias, threshold, cap, out, ldout, L,
+                           static_cast<char*>(ws), stream);
 }
 
 size_t i8mp_colwise_quant_workspace_bytes(int64_t rows, int64_t cols) {

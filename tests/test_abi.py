@@ -184,6 +184,22 @@ def test_forward_validation(L):
     assert md(FAKE, 64, FAKE, lay.bytes, 16, 64, 8, FAKE, 64, FAKE, 0, None, FAKE, 32, None) == OK
 
 
+def test_noalloc_forward_validation(L):
+    f = L.i8mp_linear_forward_noalloc
+    ESCRATCH = _lib.I8MP_ESCRATCH
+    assert len(L.i8mp_status_string(ESCRATCH)) > 0
+    # the workspace of 4096 x 22016 (90 MB of codes) does not fit the fixed array
+    assert f(FAKE, 4096, 22016, 22016, FAKE, 22016, FAKE, 64, None, 6.0, 256, FAKE, 64, None) == ESCRATCH
+    lay = _lib.LinearWorkspaceLayout()
+    for m, k, cap in ((2048, 11008, 256), (16, 13824, 256), (1, 133144, 256)):
+        assert L.i8mp_linear_workspace_query(m, 64, k, cap, ctypes.byref(lay)) == OK
+        assert lay.bytes <= _lib.I8MP_NOALLOC_SCRATCH_BYTES, (m, k)
+    assert f(None, 16, 64, 64, FAKE, 64, FAKE, 32, None, 6.0, 8, FAKE, 32, None) == EINVAL
+    assert f(FAKE, 16, 64, 63, FAKE, 64, FAKE, 32, None, 6.0, 8, FAKE, 32, None) == EINVAL
+    assert f(FAKE, 16, 133145, 133145, FAKE, 133145, FAKE, 32, None, 6.0, 8, FAKE, 32, None) == ERANGE
+    assert f(None, 0, 64, 64, None, 64, None, 32, None, 6.0, 8, None, 32, None) == OK   # empty
+
+
 def test_backward_validation(L):
     lay = _lib.BackwardWorkspaceLayout()
     assert L.i8mp_linear_backward_workspace_query(2048, 4096, 11008, 20, ctypes.byref(lay)) == OK
