@@ -925,6 +925,393 @@ __global__ __launch_bounds__(256 * KS, MINW) void gemm_dtl_kernel(GemmArgs g) {
                                                       st_next);
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles on 8 waves in ping-pong: two waves per SIMD.
+//
+// With one wave per SIMD (gemm_dtl_kernel), a wave whose DMA instruction the
+// memory pipeline cannot take yet stalls, and the MFMAs behind it in its
+// in-order stream wait with it.  Here each SIMD holds two waves of 128 x 64
+// int32 accumulators (128 of them per lane).  The waves form two groups of
+// four (waves w and w + 4 share SIMD w % 4) that alternate between a memory
+// phase (this stage's fragments LDS -> registers, this wave's share of the
+// DMA of the stage three ahead) and an MFMA phase (16 MFMAs on the
+// fragments), separated by workgroup barriers: group 1 runs one barrier
+// behind group 0, so while one group issues memory instructions the other
+// keeps the matrix cores busy, and a stalled DMA issue delays only the
+// memory phase.  K goes in 64-byte stages, four in LDS: a stage's DMA is
+// requested three stages ahead and waited for (by the wave that issued it)
+// one stage ahead, so every wave's part has landed at the barrier before
+// any wave reads it.  The MFMA phase runs at raised wave priority.
+//
+// The MFMAs take the weight fragment as their first operand, so lane l
+// holds row l % 32 of a 32 x 32 block and four consecutive columns per
+// group of four accumulators: the epilogue stores fp16 (or int32) results
+// straight from registers, 8 (or 16) bytes per store.
+namespace {
+constexpr int kPpBK = 64;                  // K bytes per stage
+constexpr int kPpStages = 4;
+constexpr int kPpWaves = 8;
+constexpr int kPpStage = (256 + 256) * kPpBK;
+constexpr int kPpLds = kPpStages * kPpStage + (int)sizeof(EpiLds<256, 256>) + kStash * 256 * 4;
+static_assert(kPpLds <= 160 * 1024, "ping-pong tile does not fit LDS");
+
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_h2(float a, float b) {
+    const h2_t h = {(_Float16)a, (_Float16)b};   // round to nearest even
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Epilogue of the transposed layout.  Accumulator (i, j, r) of lane l holds
+// row wr0 + 32 i + l % 32 and column wc0 + 32 j + 8 (r / 4) + 4 (l / 32) +
+// r % 4 of the tile at (m0, n0).  Loads and stores go through buffer
+// resources, so rows past m need no branch; columns past n are masked.
+//
+// fp16 results are staged through this wave's LDS area (stage, at least
+// 2 * 32 * (FN * 64 + 16) bytes, free of other use): each lane writes its
+// four-column quads (8 bytes), then reads back 16 contiguous bytes of a row,
+// so that every global store covers whole 128-byte row segments.
+template <int BM, int BN, int FM, int FN, bool kFused>
+__device__ inline void epilogue_tr(const GemmArgs& g, v16i (&acc)[FM][FN], int64_t m0, int64_t n0, int wr0, int wc0,
+                                   int lane, const EpiLds<BM, BN>& e, const int32_t* stash, int n_stash,
+                                   int8_t* stage) {
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int64_t rows_left = g.m - m0, cols_left = g.n - n0;
+    if constexpr (!kFused) {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.c + m0 * g.ldc + n0, ((rows_left - 1) * g.ldc + cols_left) * 4);
+        const bool vec = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wr0 + 32 * i + l32;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = wc0 + 32 * j + 8 * q + 4 * hi;
+                    const int off = (row * (int)g.ldc + col) * 4;
+                    if (vec && col + 4 <= cols_left) {
+                        const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][4 * q + t], rc,
+                                                                  col + t < cols_left ? off + 4 * t : (int)0x80000000, 0, 0);
+                    }
+                }
+        }
+    } else {
+        const float r127 = 1.0f / 127.0f;
+        int cnt = 0;
+        if (g.count) cnt = outlier_count(g, e.cnt[0]);
+        cnt = __builtin_amdgcn_readfirstlane(cnt);
+        const int xo_lim = cnt <= g.cap ? (int)g.ldo : g.cap;
+        const __amdgpu_buffer_rsrc_t rxo = make_rsrc(g.x_out ? g.x_out + m0 * g.ldo : nullptr,
+                                                     g.x_out ? rows_left * g.ldo * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x ? g.x + m0 * g.ldx : nullptr, g.x ? rows_left * g.ldx * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.b + n0 * g.ldb, (cols_left - 1) * g.ldb + g.k);
+        const __amdgpu_buffer_rsrc_t ridx = make_rsrc(g.idx, g.count ? (int64_t)g.idx_len * 4 : 0);
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(g.out + m0 * g.ldout + n0, ((rows_left - 1) * g.ldout + cols_left) * 2);
+        const __amdgpu_buffer_rsrc_t rbias = make_rsrc(g.bias ? g.bias + n0 : nullptr, g.bias ? cols_left * 2 : 0);
+        const bool vec = (g.ldout & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+
+        // the x values of the first 16 outlier slots for every row of the
+        // wave, and the bias, go out first: their latency hides behind the
+        // conversion
+        v8h xa0[FM];
+        const bool xa0_vec = cnt > 0 && 8 * hi + 8 <= xo_lim;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int lrow = wr0 + 32 * i + l32;
+            xa0[i] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rxo, xa0_vec ? (lrow * (int)g.ldo + 8 * hi) * 2 : (int)0x80000000, 0, 0));
+        }
+        // (two dword loads per four columns: this compiler folds the second
+        // dword of an 8-byte buffer load's result onto the first)
+        uint32_t braw[FN][4][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int d = 0; d < 2; ++d)
+                    braw[j][q][d] = __builtin_amdgcn_raw_buffer_load_b32(rbias, (wc0 + 32 * j + 8 * q + 4 * hi) * 2 + 4 * d, 0, 0);
+
+        // x values of 8 outlier slots (from sb) of tile row lrow: X_O as a
+        // vector below xo_lim, else slot by slot (X_O or x through idx)
+        auto x_slots = [&](int sb, int lrow, const int (&ix)[8]) -> v8h {
+            if (sb + 8 <= xo_lim)
+                return __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rxo, (lrow * (int)g.ldo + sb) * 2, 0, 0));
+            v8h v;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int slot = sb + t;
+                const uint16_t h = slot < g.cap ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (lrow * (int)g.ldo + slot) * 2, 0, 0)
+                                                : __builtin_amdgcn_raw_buffer_load_b16(
+                                                      rx, ix[t] >= 0 ? (lrow * (int)g.ldx + ix[t]) * 2 : (int)0x80000000, 0, 0);
+                v[t] = __builtin_bit_cast(_Float16, h);
+            }
+            return v;
+        };
+
+        constexpr int IC = 2;   // rows of blocks per pass: 32 fp32 results per block and lane
+        static_assert(FM % IC == 0, "row blocks in pairs");
+#pragma unroll
+        for (int ic = 0; ic < FM; ic += IC) {
+            v16f f[IC][FN];
+#pragma unroll
+            for (int ii = 0; ii < IC; ++ii) {
+                const float sxr = e.sx[wr0 + 32 * (ic + ii) + l32] * r127;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) f[ii][j][r] = (float)acc[ic + ii][j][r] * sxr;
+            }
+            // outlier sub-matmul: 16 slots per step; weight bytes (first
+            // operand: this lane's column) from the stash or gathered
+            for (int s0 = 0; s0 < cnt; s0 += 16) {
+                const int sb = s0 + 8 * hi;
+                int ix[8];
+                if (s0 + 16 <= kEpiIdx) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) ix[t] = e.idx[sb + t];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) ix[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(ridx, (sb + t) * 4, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ix[t] = sb + t < cnt ? ix[t] : -1;
+                v8h xa[IC];
+#pragma unroll
+                for (int ii = 0; ii < IC; ++ii)
+                    xa[ii] = (s0 == 0 && xa0_vec) ? xa0[ic + ii] : x_slots(sb, wr0 + 32 * (ic + ii) + l32, ix);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int lcol = wc0 + 32 * j + l32;
+                    v8h wb;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int slot = sb + t;
+                        uint32_t w;
+                        if (slot < n_stash) {
+                            w = (uint32_t)stash[slot * BN + lcol];
+                        } else {
+                            const int off = ix[t] >= 0 ? lcol * (int)g.ldb + ix[t] : (int)0x80000000;
+                            w = __builtin_amdgcn_raw_buffer_load_b8(rw, off, 0, 0);
+                        }
+                        wb[t] = (_Float16)(float)(int8_t)(uint8_t)w;
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < IC; ++ii)
+                        f[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb, xa[ii], f[ii][j], 0, 0, 0);
+                }
+            }
+            // out = fp16(sw / 127 * f + bias): each lane's four-column quads
+            // into the staging area (row pitch kPitch), then rows back out
+            constexpr int WN = FN * 32;
+            constexpr int kPitch = WN * 2 + 16;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ccol = 32 * j + 8 * q + 4 * hi;   // column within the wave's block
+                    const v4f sw4 = *reinterpret_cast<const v4f*>(&e.sw[wc0 + ccol]);
+                    const h2_t b01 = __builtin_bit_cast(h2_t, braw[j][q][0]);
+                    const h2_t b23 = __builtin_bit_cast(h2_t, braw[j][q][1]);
+                    const float bb[4] = {(float)b01[0], (float)b01[1], (float)b23[0], (float)b23[1]};
+#pragma unroll
+                    for (int ii = 0; ii < IC; ++ii) {
+                        float y[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) y[t] = sw4[t] * r127 * f[ii][j][4 * q + t] + bb[t];
+                        const v2u_t v = {pack_h2(y[0], y[1]), pack_h2(y[2], y[3])};
+                        *reinterpret_cast<v2u_t*>(stage + (32 * ii + l32) * kPitch + ccol * 2) = v;
+                    }
+                }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+            constexpr int CPR = WN / 8;          // 16-byte chunks per row
+            constexpr int RPI = 64 / CPR;        // rows per store instruction
+#pragma unroll
+            for (int it = 0; it < IC * 32 / RPI; ++it) {
+                const int crow = it * RPI + lane / CPR;
+                const int c = lane % CPR;
+                const v4i v = *reinterpret_cast<const v4i*>(stage + crow * kPitch + c * 16);
+                const int trow = wr0 + 32 * ic + crow;   // tile row (rows past m are dropped by the range)
+                const int tcol = wc0 + 8 * c;
+                const int off = (trow * (int)g.ldout + tcol) * 2;
+                if (vec && tcol + 8 <= cols_left) {
+                    // streaming (nt): every tile writes its output at the end, nothing here reads it back
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ro, off, 0, 2);
+                } else if (tcol < cols_left) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t h = ((uint32_t)v[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h, ro,
+                                                              tcol + t < cols_left ? off + 2 * t : (int)0x80000000, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the area is written again
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+}  // namespace
+
+template <bool kFused>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BKS = kPpBK, NSTAGE = kPpStages;
+    constexpr int FM = 4, FN = 2;                 // 128 x 64 per wave
+    constexpr int STAGE_A = BM * BKS, STAGE = kPpStage;
+    constexpr int INS = 4;                        // DMA instructions per wave per stage (2 A, 2 B)
+    constexpr bool kSt = kFused;                  // stash the outlier columns' weight bytes
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kPpLds];
+    EpiLds<BM, BN>& epi = *reinterpret_cast<EpiLds<BM, BN>*>(smem + NSTAGE * STAGE);
+    int32_t* stash = reinterpret_cast<int32_t*>(smem + NSTAGE * STAGE + sizeof(EpiLds<BM, BN>));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7; SIMD wave % 4
+    const int group = wave >> 2;
+    const int wm = wave & 1, wn = wave >> 1;                     // 2 x 4 blocks of 128 x 64
+
+    const int64_t tiles_m = (g.m + BM - 1) / BM;
+    const int64_t tiles_n = (g.n + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_coords<group_m<BM, BN>()>(blockIdx.x, (int64_t)gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    epi_prefetch<BM, BN, kFused>(g, m0, n0, epi, wave, lane);
+
+    const int64_t kr = (g.k + BKS - 1) / BKS * BKS;
+    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(g.a + m0 * g.lda, (g.m - m0 - 1) * g.lda + kr);
+    const __amdgpu_buffer_rsrc_t rb_src = make_rsrc(g.b + n0 * g.ldb, (g.n - n0 - 1) * g.ldb + ((g.k + 3) & ~(int64_t)3));
+    const __amdgpu_buffer_rsrc_t r_none = make_rsrc(g.a, 0);
+    // DMA: wave w writes 1 KB blocks 2w, 2w + 1 of the A and of the B part of
+    // a stage (16 rows of 64 bytes each; lane i -> row i / 4, slot i % 4,
+    // holding the global chunk slot ^ ((row >> 2) & 3))
+    int a_off[2], b_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = (wave * 2 + q) * 16 + (lane >> 2);
+        const int gchunk = (lane & 3) ^ ((row >> 2) & 3);
+        a_off[q] = (int)(row * g.lda + gchunk * 16);
+        b_off[q] = (int)(row * g.ldb + gchunk * 16);
+    }
+    const int64_t ktiles = kr / BKS;
+    // Stages past the last read through a zero-length range: nothing is
+    // fetched, zeros land in a stage that is not read again, and every
+    // vmcnt wait stays a constant.
+    auto dma_stage = [&](int64_t t) {
+        const bool real = t < ktiles;
+        const int kb = real ? (int)(t * BKS) : 0;
+        int8_t* base = smem + (int)(t % NSTAGE) * STAGE;
+        const __amdgpu_buffer_rsrc_t sa = real ? ra_src : r_none;
+        const __amdgpu_buffer_rsrc_t sb = real ? rb_src : r_none;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) dma16(sa, base + (wave * 2 + q) * 1024, a_off[q] + kb, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) dma16(sb, base + STAGE_A + (wave * 2 + q) * 1024, b_off[q] + kb, 0);
+    };
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int64_t t) {
+        const int8_t* base = smem + (int)(t % NSTAGE) * STAGE;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[s][i] = *reinterpret_cast<const v4i*>(base + swz_k<BKS>(wm * 128 + 32 * i + (lane & 31), ch));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[s][j] = *reinterpret_cast<const v4i*>(base + STAGE_A + swz_k<BKS>(wn * 64 + 32 * j + (lane & 31), ch));
+        }
+    };
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    auto barrier = [&]() {
+        // the wave's LDS reads done, then s_barrier; nothing is scheduled
+        // across it (the signal fences keep memory accesses, the scheduling
+        // barriers everything else on their side)
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    dma_stage(0);
+    dma_stage(1);
+    dma_stage(2);
+    wait_vm(2 * INS);   // this wave's part of stage 0 landed
+    barrier();          // ... everyone's, and the epilogue operands
+
+    // Outlier columns' weight bytes: the first n_st slots (ascending columns)
+    // are copied into the stash by group 0 (64 weight rows per wave) next to
+    // the DMA of the stage that holds them, so the lines are on their way
+    // through L2 anyway.
+    int n_st = 0, st_next = 0;
+    int64_t st_col = INT64_MAX;
+    if constexpr (kSt) {
+        if (g.count) {
+            const int cnt = outlier_count(g, epi.cnt[0]);
+            n_st = __builtin_amdgcn_readfirstlane(cnt < kStash ? cnt : kStash);
+            if (n_st > 0) st_col = __builtin_amdgcn_readfirstlane(epi.idx[0]);
+        }
+    }
+    auto stash_upto = [&](int64_t col_end) {
+        while (st_col < col_end) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb_src, (__attribute__((address_space(3))) void*)(stash + st_next * BN + wave * 64), 1,
+                (int)((wave * 64 + lane) * g.ldb + st_col), 0, 0, 0);
+            ++st_next;
+            st_col = st_next < n_st ? (int64_t)__builtin_amdgcn_readfirstlane(epi.idx[st_next]) : INT64_MAX;
+        }
+    };
+    if constexpr (kSt)
+        if (group == 0) stash_upto(3 * BKS);
+
+    if (group == 1) barrier();   // group 1 runs one phase behind
+    for (int64_t t = 0; t < ktiles; ++t) {
+        // memory phase: fragments of stage t, DMA of stage t + 3 (into the
+        // stage both groups finished reading before the last barrier)
+        read_frags(t);
+        dma_stage(t + 3);
+        if constexpr (kSt)
+            if (group == 0) stash_upto((t + 4) * BKS);
+        wait_vm(2 * INS);   // this wave's part of stage t + 1 landed (t + 2, t + 3 in flight)
+        barrier();
+        // MFMA phase
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+        barrier();
+    }
+    if (group == 0) barrier();   // both groups have passed the same number of barriers
+
+    wait_vm(0);          // the DMA of the stages past the last and the stash
+    __syncthreads();     // the K stages are free: each wave stages its results in its own part
+    constexpr int kEpiArea = 2 * 32 * (FN * 64 + 16);
+    static_assert(kPpWaves * kEpiArea <= NSTAGE * STAGE, "output staging does not fit the K stages");
+    epilogue_tr<BM, BN, FM, FN, kFused>(g, acc, m0, n0, wm * 128, wn * 64, lane, epi, stash, n_st,
+                                        smem + wave * kEpiArea);
+}
+
 namespace {
 
 // Launch one tile shape: the pipelined direct-to-LDS kernel (128-byte K
@@ -945,7 +1332,9 @@ hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t
     constexpr int kStages2 = kFit2 > 4 ? 4 : kFit2;
     constexpr bool kCanSplit = !stash_on<BM, BN, kFused>() && kStages2 >= 2;
     const bool split = kCanSplit && tiles <= 256 && (g.k + 127) / 128 >= 16;
-    if (staged && split) {
+    if (staged && BM == 256 && BN == 256) {
+        hipLaunchKernelGGL((gemm_pp_kernel<kFused>), grid, dim3(512), 0, stream, g);
+    } else if (staged && split) {
         if constexpr (kCanSplit)
             hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, 128, kStages2, kFused, 1, 2>), grid, dim3(512), 0, stream, g);
     } else if (staged)

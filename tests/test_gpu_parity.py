@@ -125,7 +125,8 @@ def test_quant_workspace_reuse(m, k):
 MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128), (300, 600, 300),
              (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100),
              (3, 777, 1280), (2, 513, 640), (4, 100, 13824),
-             (200, 300, 2560), (130, 190, 2176)]  # two K pipelines per workgroup (17 K tiles: one pipeline's last is empty)
+             (200, 300, 2560), (130, 190, 2176),  # two K pipelines per workgroup (17 K tiles: one pipeline's last is empty)
+             (2100, 5000, 512), (2100, 5000, 640), (1800, 6000, 128)]  # 256 x 256 ping-pong tiles, ragged m and n
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -206,6 +207,7 @@ FWD_CASES = [
     # weights with rows of 250 bytes (not 16-byte aligned): the register-staged kernel
     (768, 250, 6144, 20, 0.5, True, TAU, 64),     # 256 x 128: copies in the wave's staging area
     (1536, 250, 6144, 30, 0.5, False, TAU, 64),   # 256 x 256 without a stash: every slot gathered
+    (2100, 1000, 5000, 9, 0.5, True, TAU, 64),    # 256 x 256 ping-pong, ragged m, n and k
     # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
     (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
     (2, 4096, 264, 5, 0.5, False, TAU, 32),
