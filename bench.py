@@ -32,7 +32,7 @@ import numpy as np  # noqa: E402
 METRIC = "int8 linear TOPS & % int8-MFMA peak (prefill); GB/s & % HBM peak (decode)"
 PEAK_INT8_OPS = 5.0e15     # MI355X dense int8 MFMA
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
-DEFAULT_WORKLOAD = "opt350m_mlp_pair_m512"
+DEFAULT_WORKLOAD = "llama65b_prefill_m4096"
 # sources of the GEMM-side kernels (prefill tiles, decode kernels, shared helpers)
 GEMM_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
              for f in ("gemm.hip", "decode.hip", "common.h")]
@@ -198,46 +198,73 @@ def time_gemm_launches(torch, i8, sets, specs, copies, launches):
     return out
 
 
-def traffic_summary(directory: str, workload: str, launches: int) -> int:
-    """Per-launch HBM bytes of the fused GEMM from rocprofv3 --pmc runs.
+# rocprofv3 --pmc passes behind the traffic and MFMA figures (one pass each; a
+# pass holds at most 4 TCC and 8 SQ counters)
+RD_COUNTERS = ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B", "TCC_EA0_RDREQ")
+WR_COUNTERS = ("TCC_EA0_WRREQ_64B", "TCC_EA0_WRREQ")
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_I8", "GRBM_GUI_ACTIVE",
+                 "SQ_WAVES", "SQ_CYCLES")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma.json")
+N_CUS = 256
 
-    ``directory`` holds four rocprofv3 output folders: gemm_fetch, gemm_write
-    (``bench.py --mode gemm``) and copy_fetch, copy_write (``bench.py --mode
-    copy``).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what
-    the same counters read for the copy kernel, whose true bytes are known."""
+
+def _per_dispatch(directory: str, folder: str, counter: str, name_part: tuple):
+    """Counter value per dispatch (summed over the rows rocprofv3 writes for it) of
+    the kernels whose name contains one of name_part, in dispatch order."""
     import csv
     import glob
+    vals = {}
+    for f in glob.glob(os.path.join(directory, folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in name_part):
+                d = int(r["Dispatch_Id"])
+                vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+    return [vals[d] for d in sorted(vals)]
+
+
+def _read_bytes(directory, folder, name_part):
+    """L2 -> fabric read bytes per dispatch: 32, 64 and 128-byte requests by size."""
+    n32, n64, n128, nall = (_per_dispatch(directory, folder, c, name_part) for c in RD_COUNTERS)
+    return [32 * a + 64 * b + 128 * c for a, b, c in zip(n32, n64, n128)], \
+        [t - a - b - c for a, b, c, t in zip(n32, n64, n128, nall)]
+
+
+def _write_bytes(directory, folder, name_part):
+    """L2 -> fabric write bytes per dispatch: 64-byte requests and 32-byte ones."""
+    n64, nall = (_per_dispatch(directory, folder, c, name_part) for c in WR_COUNTERS)
+    return [64 * a + 32 * (t - a) for a, t in zip(n64, nall)]
+
+
+def traffic_summary(directory: str, workload: str, launches: int) -> int:
+    """Per-launch HBM (L2 -> fabric) bytes of the fused GEMM from rocprofv3 --pmc runs.
+
+    ``directory`` holds four rocprofv3 output folders: gemm_rd, gemm_wr (``bench.py
+    --mode gemm``) and copy_rd, copy_wr (``bench.py --mode copy``), with RD_COUNTERS
+    and WR_COUNTERS.  Read bytes are the request counts by size times their sizes;
+    the copy kernel, whose true bytes are known, checks the counting (its scale is
+    reported and applied)."""
     specs, _ = workload_specs(workload)
-
-    def per_dispatch(folder: str, counter: str, name_part: tuple):
-        vals = {}
-        for f in glob.glob(os.path.join(directory, folder, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in name_part):
-                    d = int(r["Dispatch_Id"])
-                    vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"]) * 1024.0
-        return [vals[d] for d in sorted(vals)]
-
-    copy_f = per_dispatch("copy_fetch", "FETCH_SIZE", ("elementwise",))
-    copy_w = per_dispatch("copy_write", "WRITE_SIZE", ("elementwise",))
     copy_bytes = COPY_MB * 2**20
-    if not copy_f or not copy_w:
+    cr, c_other = _read_bytes(directory, "copy_rd", ("elementwise",))
+    cw = _write_bytes(directory, "copy_wr", ("elementwise",))
+    if not cr or not cw:
         raise SystemExit("no copy-kernel counters found")
-    f_scale = copy_bytes / (sum(copy_f) / len(copy_f))
-    w_scale = copy_bytes / (sum(copy_w) / len(copy_w))
-    gf = per_dispatch("gemm_fetch", "FETCH_SIZE", GEMM_KERNELS)
-    gw = per_dispatch("gemm_write", "WRITE_SIZE", GEMM_KERNELS)
-    if len(gf) < len(specs) * launches or len(gw) < len(specs) * launches:
-        raise SystemExit(f"expected {len(specs) * launches} GEMM dispatches, got {len(gf)} / {len(gw)}")
+    f_scale = copy_bytes / (sum(cr) / len(cr))
+    w_scale = copy_bytes / (sum(cw) / len(cw))
+    gr, g_other = _read_bytes(directory, "gemm_rd", GEMM_KERNELS)
+    gw = _write_bytes(directory, "gemm_wr", GEMM_KERNELS)
+    if len(gr) < len(specs) * launches or len(gw) < len(specs) * launches:
+        raise SystemExit(f"expected {len(specs) * launches} GEMM dispatches, got {len(gr)} / {len(gw)}")
     layers = {}
     tot = 0.0
     for li, s in enumerate(specs):
-        f = gf[li * launches:(li + 1) * launches]
+        f = gr[li * launches:(li + 1) * launches]
         w = gw[li * launches:(li + 1) * launches]
         fb = sum(f) / len(f) * f_scale
         wb = sum(w) / len(w) * w_scale
         layers[s.name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
-                          "algorithmic_bytes": gemm_alg_bytes(s)}
+                          "algorithmic_bytes": gemm_alg_bytes(s),
+                          "ratio": round((fb + wb) / gemm_alg_bytes(s), 3)}
         tot += fb + wb
     try:
         d = json.load(open(TRAFFIC_FILE))
@@ -248,11 +275,61 @@ def traffic_summary(directory: str, workload: str, launches: int) -> int:
     d["gemm_source_sha"] = src_sha()
     d.setdefault("per_launch_bytes", {})[workload] = round(tot)
     d.setdefault("layers", {})[workload] = layers
-    d["calibration"] = {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    d["calibration"] = {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                        "counters": list(RD_COUNTERS + WR_COUNTERS),
+                        "read_requests_of_other_sizes": [sum(c_other), sum(g_other)]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(d, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
     print(json.dumps({"workload": workload, "traffic_bytes": round(tot), "layers": layers,
                       "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}))
+    return 0
+
+
+def mfma_summary(directory: str, workload: str, launches: int) -> int:
+    """MFMA utilisation of the fused GEMM from a rocprofv3 --pmc pass with
+    MFMA_COUNTERS (folder gemm_mfma, ``bench.py --mode gemm``) and the bench line
+    of a kernel-trace run of the same workload (trace_bench.json: per-launch us).
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums the matrix-core busy cycles of all 1024 SIMDs
+    (each v_mfma_i32_32x32x32_i8 adds 32); GRBM_GUI_ACTIVE sums the GPU-active
+    cycles of the 8 XCDs.  So the shader clock during the launch is
+    GRBM_GUI_ACTIVE / 8 / duration, and the busy share of the SIMD-cycles is
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024).  ops =
+    SQ_INSTS_VALU_MFMA_MOPS_I8 * 512, to match 2 m n k."""
+    specs, _ = workload_specs(workload)
+    vals = {c: _per_dispatch(directory, "gemm_mfma", c, GEMM_KERNELS) for c in MFMA_COUNTERS}
+    if any(len(v) < len(specs) * launches for v in vals.values()):
+        raise SystemExit("missing MFMA counter dispatches")
+    try:
+        per_us = json.load(open(os.path.join(directory, "trace_bench.json")))["roofline"]["per_launch_us"]
+    except (OSError, ValueError, KeyError):
+        per_us = {}
+    layers = {}
+    for li, s in enumerate(specs):
+        sl = slice(li * launches, (li + 1) * launches)
+        avg = {c: sum(v[sl]) / launches for c, v in vals.items()}
+        xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8
+        rec = {"mfma_busy": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 4 * N_CUS), 4),
+               "mops_i8_x512": round(avg["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512),
+               "two_mnk": 2 * s.m * s.n * s.k,
+               "counters": {c: round(v) for c, v in avg.items()}}
+        if s.name in per_us:
+            us = per_us[s.name]
+            clk = xcd_cycles / (us * 1e-6)
+            rec.update({"launch_us": us, "clock_ghz": round(clk / 1e9, 3),
+                        "int8_peak_at_clock_tops": round(N_CUS * 8192 * clk / 1e12, 1),
+                        "achieved_tops": round(2 * s.m * s.n * s.k / (us * 1e-6) / 1e12, 1)})
+        layers[s.name] = rec
+    try:
+        d = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        d = {}
+    d[workload] = {"gemm_source_sha": src_sha(), "layers": layers,
+                   "normalisation": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 1024 SIMDs); "
+                                    "clock = GRBM_GUI_ACTIVE / 8 / launch duration"}
+    os.makedirs(os.path.dirname(MFMA_FILE), exist_ok=True)
+    json.dump(d, open(MFMA_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps({"workload": workload, "layers": layers}))
     return 0
 
 
@@ -647,61 +724,14 @@ def copy_run(launches: int) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cap", type=int, default=256)
-    ap.add_argument("--rotate-mb", type=float, default=1024.0)
-    ap.add_argument("--graph", choices=("on", "off"), default="on")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward", "fp4"), default="bench",
-                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
-                         "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
-                         "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
-    ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
-    ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=2,
-                    help="--mode backward: grad_x and grad_w on one stream, or on two")
-    ap.add_argument("--traffic-summary", metavar="DIR",
-                    help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
-    args = ap.parse_args()
-
-    if args.traffic_summary:
-        return traffic_summary(args.traffic_summary, args.workload, args.launches)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the multi-GPU path is not built (one GPU per box); "
-              "run with --gpus 1", file=sys.stderr)
-        return 2
-
-    import torch
-    import int8_mixed_precision_vectorwise_amd as i8
+def prepare_sets(torch, i8, specs, cap, rotate_mb, dev):
+    """Inputs resident in HBM and weights quantized once (untimed), rotated over
+    enough copies that the working set exceeds the last-level caches."""
     from synth import make_layer
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    if args.mode == "copy":
-        return copy_run(args.launches)
-    if args.mode == "dequant":
-        return dequant_run(args.steps, args.warmup)
-    if args.mode == "backward":
-        return backward_run(args)
-    if args.mode == "fp4":
-        return fp4_run(args)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    specs, kind = workload_specs(args.workload)
-    cap = args.cap
-
-    # ---- inputs resident in HBM, weights quantized once (untimed) -----------------
     base = []
     per_copy = 0
     for s in specs:
-        log(f"layer {s.name}: m={s.m} k={s.k} n={s.n} outliers={s.n_outlier}")
+        log(f"layer {s.name}: m={s.m} k={s.k} n={s.n} planted outliers={s.n_outlier}")
         L = make_layer(s)
         x = torch.from_numpy(L.x).to(dev)
         w = torch.from_numpy(L.w).to(dev)
@@ -711,7 +741,7 @@ def main() -> int:
         ws = i8.LinearWorkspace.create(s.m, s.n, s.k, cap, dev)
         base.append((s, x, wq, wabs, b))
         per_copy += x.numel() * 2 + wq.numel() + ws.buf.numel() + s.m * s.n * 2
-    copies = int(min(64, max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))))
+    copies = int(min(64, max(2, math.ceil(rotate_mb * 2**20 / per_copy))))
     log(f"rotation copies: {copies} ({per_copy / 2**20:.1f} MiB each)")
     sets = []
     for c in range(copies):
@@ -726,53 +756,35 @@ def main() -> int:
             layer_sets.append((s, xc, wqc, wac, b, ws, out))
         sets.append(layer_sets)
     torch.cuda.synchronize()
+    return sets, copies
 
+
+def time_steps(torch, i8, sets, cap, copies, steps, warmup, graph):
+    """Eager and hipGraph-replay time per step (ms), the faster labelled."""
     def step(c: int) -> None:
         for s, xc, wqc, wac, b, ws, out in sets[c]:
             i8.linear(xc, wqc, wac, b, s.tau, cap, ws, out)
 
-    if args.mode == "gemm":
-        # exactly args.launches GEMM dispatches per layer, layer after layer
-        for li, s in enumerate(specs):
-            for i in range(args.launches):
-                _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
-                if i < copies:
-                    i8.linear_quantize(xc, ws, s.tau)
-                i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
-        torch.cuda.synchronize()
-        print(json.dumps({"workload": args.workload, "gemm_launches_per_layer": args.launches}))
-        return 0
-
-    # first call: check for outlier-capacity overflow once (outside timing)
     for c in range(copies):
         step(c)
     torch.cuda.synchronize()
     for s, xc, wqc, wac, b, ws, out in sets[0]:
-        if ws.outliers_past_cap():
-            log(f"layer {s.name}: more outlier columns than cap={cap} (those past it take the slow path)")
+        n_out = int(ws.count().item())
+        log(f"layer {s.name}: {n_out} outlier columns" + (" (past cap: the slower path)" if n_out > cap else ""))
 
-    # ---- eager timing ------------------------------------------------------------
-    def timed(run, steps, warmup):
-        for i in range(warmup):
-            run(i % copies)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(steps):
-            run(i % copies)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / steps, wall
-
-    eager_ms, _ = timed(step, args.steps, args.warmup)
+    for i in range(warmup):
+        step(i % copies)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
     log(f"eager: {eager_ms * 1e3:.2f} us/step")
-
-    ms = eager_ms
-    launch = "eager"
-    graph_ms = None
-    if args.graph == "on":
+    ms, launch, graph_ms = eager_ms, "eager", None
+    if graph:
         # one graph holds a whole rotation (steps over copies 0 .. copies-1),
         # so a replay costs one graph launch per `copies` steps; a second graph
         # holds the remainder, so exactly `steps` steps run in the timed region
@@ -788,44 +800,33 @@ def main() -> int:
             return g
 
         g_all = capture(copies)
-        rem = args.steps % copies
+        rem = steps % copies
         g_rem = capture(rem) if rem else None
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup // copies)):
+        for _ in range(max(1, warmup // copies)):
             g_all.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(args.steps // copies):
+        for _ in range(steps // copies):
             g_all.replay()
         if g_rem is not None:
             g_rem.replay()
         e1.record()
         torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / args.steps
+        graph_ms = e0.elapsed_time(e1) / steps
         log(f"graph replay: {graph_ms * 1e3:.2f} us/step ({copies} steps per graph)")
         if graph_ms < ms:
             ms, launch = graph_ms, "hipGraph replay"
+    return ms, eager_ms, graph_ms, launch
 
-    # ---- dominant kernel: the fused GEMM, timed alone with events on its stream -----
-    gemm_us = time_gemm_launches(torch, i8, sets, specs, copies, max(args.steps, 50))
-    for s in specs:
-        log(f"gemm {s.name}: {gemm_us[s.name]:.2f} us/launch")
 
-    ops = sum(2 * s.m * s.n * s.k for s in specs)
-    byts = sum(alg_bytes(s) for s in specs)
-    if kind == "prefill":
-        value, unit = ops / (ms * 1e-3) / 1e12, "TOPS"
-    else:
-        value, unit = byts / (ms * 1e-3) / 1e9, "GB/s"
-
-    # roofline of the fused GEMM kernel over the step's launches
+def gemm_roofline(specs, gemm_us, workload):
+    """Roofline of the fused GEMM kernel over the step's launches."""
     g_ops = sum(2 * s.m * s.n * s.k for s in specs)
     g_bytes = sum(gemm_alg_bytes(s) for s in specs)
     g_time = sum(gemm_us[s.name] for s in specs) * 1e-6
-    t_mfma = g_ops / PEAK_INT8_OPS
-    t_hbm = g_bytes / PEAK_HBM
-    if t_mfma >= t_hbm:
+    if g_ops / PEAK_INT8_OPS >= g_bytes / PEAK_HBM:
         achieved = g_ops / g_time / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_OPS / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved / (PEAK_INT8_OPS / 1e12), 4)}
@@ -834,10 +835,129 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
     roof["kernel"] = ("fused int8 GEMM + dequant epilogue, the GEMM half of the linear run alone "
-                      "(gemm_dtl_kernel for prefill; gemv_kernel for m <= 4, gemm_decode_kernel for m <= 16)")
+                      "(gemm_pp_kernel / gemm_dtl_kernel for prefill; gemv_kernel for m <= 4, "
+                      "gemm_decode_kernel for m <= 16)")
     roof["per_launch_us"] = {k: round(v, 3) for k, v in gemm_us.items()}
     roof["timing"] = "HIP events around graph replays of the layer's GEMM launches"
-    roof["traffic"] = read_traffic(args.workload)
+    roof["traffic"] = read_traffic(workload)
+    return roof
+
+
+def decode_record(torch, i8, dev, args):
+    """13B decode layers (up and down, 8 outlier columns) at m = 1, 4 and 16:
+    whole-linear GB/s of algorithmic bytes and the fraction of 8 TB/s."""
+    out = {}
+    for m in (1, 4, 16):
+        wl = f"llama13b_decode_m{m}"
+        specs, _ = workload_specs(wl)
+        sets, copies = prepare_sets(torch, i8, specs, 256, args.rotate_mb, dev)
+        ms, _, _, launch = time_steps(torch, i8, sets, 256, copies, max(args.steps, 100), args.warmup,
+                                      args.graph == "on")
+        byts = sum(alg_bytes(s) for s in specs)
+        gbs = byts / (ms * 1e-3) / 1e9
+        out[f"m{m}"] = {"value": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / (PEAK_HBM / 1e9), 4),
+                        "ms_per_step": round(ms, 6), "launch": launch, "workload": wl}
+        log(f"decode m={m}: {gbs:.0f} GB/s ({ms * 1e3:.2f} us/step)")
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cap", type=int, default=None,
+                    help="outlier capacity of the workspaces (default 256; the stress workload: k)")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0)
+    ap.add_argument("--graph", choices=("on", "off"), default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode", choices=("on", "off"), default="on",
+                    help="with a prefill workload: also measure the 13B decode layers at m = 1, 4, 16")
+    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward", "fp4"), default="bench",
+                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
+                         "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
+                         "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
+    ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
+    ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=2,
+                    help="--mode backward: grad_x and grad_w on one stream, or on two")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="write profiles/gemm_mfma.json from a rocprofv3 --pmc output in DIR")
+    args = ap.parse_args()
+
+    if args.traffic_summary:
+        return traffic_summary(args.traffic_summary, args.workload, args.launches)
+    if args.mfma_summary:
+        return mfma_summary(args.mfma_summary, args.workload, args.launches)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the multi-GPU path is not built (one GPU per box); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.cap is None:
+        # the stress input makes nearly every column an outlier: capacity k
+        # keeps them all on the gathered (fast) path
+        stress = args.workload.endswith("_stress")
+        args.cap = max(s.k for s in workload_specs(args.workload)[0]) if stress else 256
+    if args.mode == "copy":
+        return copy_run(args.launches)
+    if args.mode == "dequant":
+        return dequant_run(args.steps, args.warmup)
+    if args.mode == "backward":
+        return backward_run(args)
+    if args.mode == "fp4":
+        return fp4_run(args)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs, kind = workload_specs(args.workload)
+    cap = args.cap
+    sets, copies = prepare_sets(torch, i8, specs, cap, args.rotate_mb, dev)
+
+    if args.mode == "gemm":
+        # exactly args.launches GEMM dispatches per layer, layer after layer
+        for li, s in enumerate(specs):
+            for i in range(args.launches):
+                _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
+                if i < copies:
+                    i8.linear_quantize(xc, ws, s.tau)
+                i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "gemm_launches_per_layer": args.launches}))
+        return 0
+
+    ms, eager_ms, graph_ms, launch = time_steps(torch, i8, sets, cap, copies, args.steps, args.warmup,
+                                                args.graph == "on")
+
+    # ---- dominant kernel: the fused GEMM, timed alone with events on its stream -----
+    gemm_us = time_gemm_launches(torch, i8, sets, specs, copies, max(args.steps, 50))
+    for s in specs:
+        log(f"gemm {s.name}: {gemm_us[s.name]:.2f} us/launch")
+    del sets
+    torch.cuda.empty_cache()
+
+    ops = sum(2 * s.m * s.n * s.k for s in specs)
+    byts = sum(alg_bytes(s) for s in specs)
+    if kind == "prefill":
+        value, unit = ops / (ms * 1e-3) / 1e12, "TOPS"
+    else:
+        value, unit = byts / (ms * 1e-3) / 1e9, "GB/s"
+    roof = gemm_roofline(specs, gemm_us, args.workload)
+
+    decode = None
+    if kind == "prefill" and args.decode == "on" and not args.workload.endswith("_stress"):
+        decode = decode_record(torch, i8, dev, args)
 
     cpu = None
     if not args.no_cpu:
@@ -859,7 +979,7 @@ def main() -> int:
         "data": "synthetic (seeded layers; no datasets or trained weights)",
         "config": {
             "workload": args.workload,
-            "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n, "outlier_cols": s.n_outlier,
+            "layers": [{"name": s.name, "m": s.m, "k": s.k, "n": s.n, "planted_outlier_cols": s.n_outlier,
                         "bias": s.bias_std is not None} for s in specs],
             "threshold": specs[0].tau,
             "cap": cap,
@@ -872,6 +992,10 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if kind == "prefill":
+        line["int8_peak_frac"] = round(value / (PEAK_INT8_OPS / 1e12), 4)
+    if decode is not None:
+        line["decode"] = decode
     print(json.dumps(line), flush=True)
     return 0
 
