@@ -37,6 +37,8 @@
 
 namespace i8mp {
 
+typedef unsigned v2u_q __attribute__((ext_vector_type(2)));
+
 namespace {
 // whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
 bool vector_rows(const QuantArgs& a) {
@@ -120,11 +122,16 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
     // chunk indices (8 columns each) fit 32 bits: k <= 133144
     const int32_t nchunks = (int32_t)((a.k + 7) / 8);
     uint4 v[kBatch];
+    // kVec: buffer loads (chunks past k read 0) with no branch per chunk
     auto load_batch = [&](const half_bits* __restrict__ xr, int32_t b) {
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xr, kVec ? a.k * 2 : 0);
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int32_t ch = b * P * kBatch + pid + P * c;
-            v[c] = ch < nchunks ? load8<kVec>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
+            if constexpr (kVec)
+                v[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ch * 16, 0, 0));
+            else
+                v[c] = ch < nchunks ? load8<false>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
         }
     };
     if (preload) load_batch(a.x + r_first * a.ldx, 0);
@@ -189,6 +196,10 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
         const float inv = s > 0.0f ? 127.0f / s : 0.0f;  // IEEE division; 0 for a zero row
         if (a.q) {
             int8_t* qr = a.q + r * a.ldq;
+            // kVec: whole 8-byte chunks (checked by the launcher) through one
+            // buffer range up to kpad (chunks past it dropped), no branch per
+            // chunk; the chunks past k hold zeros, so they write the padding
+            const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qr, kVec ? a.kpad : 0);
             for (int32_t b = 0; b < nbatch; ++b) {
                 if (nbatch > 1) {  // one batch: still in registers, masked
                     load_batch(xr, b);
@@ -197,19 +208,20 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 #pragma unroll
                 for (int c = 0; c < kBatch; ++c) {
                     const int32_t ch = b * P * kBatch + pid + P * c;
-                    if (ch >= nchunks) continue;
                     const int64_t col = (int64_t)ch * 8;
                     const uint2 code = codes8_plain(v[c], inv);
-                    if (kVec) {  // whole chunks, 8-byte aligned code rows (checked by the launcher)
-                        *reinterpret_cast<uint2*>(qr + col) = code;
+                    if constexpr (kVec) {
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_q, code), rq, ch * 8, 0, 0);
                     } else {
+                        if (ch >= nchunks) continue;
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             if (col + e < a.k) qr[col + e] = (int8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
                     }
                 }
             }
-            for (int64_t j = a.k + pid; j < a.kpad; j += P) qr[j] = 0;
+            const int64_t pad0 = kVec ? (int64_t)nbatch * P * kBatch * 8 : a.k;
+            for (int64_t j = pad0 + pid; j < a.kpad; j += P) qr[j] = 0;
             if (pid == 0) a.absmax[r] = s;
         }
         // the row's outlier values into their slots of the compact matrix
@@ -232,6 +244,230 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// One read of x for prefill-sized inputs (threshold > 0), three launches:
+//   zero_words_kernel  clears kMaxRowBlocks partial outlier bitmaps in the
+//                      scratch (a kernel, not a memset node, so that the call
+//                      can be captured in a graph);
+//   quant1_kernel      reads each row once: the outlier bits of its elements
+//                      (into the workgroup's LDS bitmap, then OR-ed into partial
+//                      bitmap blockIdx % kMaxRowBlocks with atomics on the
+//                      words that have any), the
+//                      row maximum m over the elements below the threshold, and
+//                      the codes with fl32(127 / m), 0 at elements at or above
+//                      the threshold;
+//   quant2_kernel      with the whole outlier set (the OR of the partials): the
+//                      bitmap, index list and count;
+//                      per row the gather of its outlier-column values, zero
+//                      codes in the outlier columns, and the check of the row
+//                      scale.  The scale is the maximum over the columns outside
+//                      the set, which is m unless m is reached only inside the
+//                      set: when the largest element of an outlier column below
+//                      the threshold equals m, the row is quantized again from
+//                      the bitmap (exact; rare: every element of a planted
+//                      outlier column is above the threshold).
+// The codes of such a check are the two-launch quantizer's own: the same
+// masked chunk maxima, the same IEEE quotient and rounding.
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ w, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) w[i] = 0u;
+}
+
+template <bool kVec, bool kBlockRow, int kBatch>
+__global__ __launch_bounds__(256) void quant1_kernel(QuantArgs a, uint32_t* __restrict__ gbm) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* bm = smem;   // [words] this workgroup's outlier bits
+    __shared__ float rmax[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    constexpr int P = kBlockRow ? 256 : 64;   // threads sharing a row
+    const int pid = kBlockRow ? tid : lane;
+    const int64_t rr0 = kBlockRow ? 0 : wave;
+    const int64_t rstep = kBlockRow ? 1 : 4;
+    const int32_t nchunks = (int32_t)((a.k + 7) / 8);
+    const int32_t nbatch = (nchunks + P * kBatch - 1) / (P * kBatch);
+    const float tau = a.threshold;
+
+    uint4 v[kBatch], vn[kBatch];
+    // kVec: buffer loads (chunks past k read 0) with no branch per chunk
+    auto load_batch = [&](uint4 (&dst)[kBatch], const half_bits* __restrict__ xr, int32_t b) {
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xr, kVec ? a.k * 2 : 0);
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int32_t ch = b * P * kBatch + pid + P * c;
+            if constexpr (kVec)
+                dst[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ch * 16, 0, 0));
+            else
+                dst[c] = ch < nchunks ? load8<false>(xr, (int64_t)ch * 8, a.k) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    // a batch's outlier bits into LDS and the elements at or above the
+    // threshold set to 0; returns the maximum of the rest
+    auto detect_mask = [&](int32_t b, bool record) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int32_t ch = b * P * kBatch + pid + P * c;
+            const float cm = chunk_absmax(v[c]);   // chunks past k are 0
+            if (cm >= tau) {
+                const uint32_t ob = outlier_bits8(v[c], tau);
+                if (record) atomicOr(&bm[ch >> 2], ob << ((ch & 3) * 8));
+                v[c] = mask_outliers(v[c], ob);
+                mx = fmaxf(mx, chunk_absmax(v[c]));
+            } else {
+                mx = fmaxf(mx, cm);
+            }
+        }
+        return mx;
+    };
+
+    const int64_t r_first = (int64_t)blockIdx.x * a.rows_per_block + rr0;
+    if (rr0 < a.rows_per_block && r_first < a.m) load_batch(v, a.x + r_first * a.ldx, 0);
+    for (int64_t w = tid; w < a.words; w += 256) bm[w] = 0u;
+    __syncthreads();
+
+    for (int64_t rr = rr0; rr < a.rows_per_block; rr += rstep) {
+        const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
+        if (r >= a.m) break;
+        const half_bits* __restrict__ xr = a.x + r * a.ldx;
+        const int64_t rn = r + rstep;
+        const bool next = rr + rstep < a.rows_per_block && rn < a.m;
+        float mx = 0.0f;
+        for (int32_t b = 0; b < nbatch; ++b) {
+            if (b > 0) load_batch(v, xr, b);   // batch 0 is in v
+            mx = fmaxf(mx, detect_mask(b, true));
+        }
+        // a row of one batch: the next row's loads go out before this row's
+        // reduction and codes
+        if (nbatch == 1 && next) load_batch(vn, a.x + rn * a.ldx, 0);
+        float s = wave_max_uniform(mx);
+        if constexpr (kBlockRow) {
+            if (lane == 0) rmax[wave] = s;
+            __syncthreads();
+            s = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
+            __syncthreads();
+        }
+        const float inv = s > 0.0f ? 127.0f / s : 0.0f;   // IEEE division; 0 for a zero row
+        int8_t* qr = a.q + r * a.ldq;
+        // kVec: the row's codes and its zero padding to kpad through one
+        // buffer range (chunks past kpad are dropped), no branch per chunk
+        const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qr, kVec ? a.kpad : 0);
+        for (int32_t b = 0; b < nbatch; ++b) {
+            if (nbatch > 1) {   // longer rows: read again (L2 / infinity cache)
+                load_batch(v, xr, b);
+                detect_mask(b, false);
+            }
+#pragma unroll
+            for (int c = 0; c < kBatch; ++c) {
+                const int32_t ch = b * P * kBatch + pid + P * c;
+                const int64_t col = (int64_t)ch * 8;
+                const uint2 code = codes8_plain(v[c], inv);   // chunks past k are 0: codes 0
+                if constexpr (kVec) {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_q, code), rq, ch * 8, 0, 0);
+                } else {
+                    if (ch >= nchunks) continue;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < a.k) qr[col + e] = (int8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+                }
+            }
+        }
+        // padding past the chunks written above (kVec writes whole batches)
+        const int64_t pad0 = kVec ? (int64_t)nbatch * P * kBatch * 8 : a.k;
+        for (int64_t j = pad0 + pid; j < a.kpad; j += P) qr[j] = 0;
+        if (pid == 0) a.absmax[r] = s;
+        if (nbatch == 1 && next) {
+#pragma unroll
+            for (int c = 0; c < kBatch; ++c) v[c] = vn[c];
+        } else if (next) {
+            load_batch(v, a.x + rn * a.ldx, 0);
+        }
+    }
+    __syncthreads();
+    // Every workgroup finds much the same outlier columns, and atomics on
+    // one word serialize at L2: the workgroups spread over kMaxRowBlocks
+    // partial bitmaps.  The atomics return nothing, so no wave waits for them
+    // (a wait here would also wait for the row's code stores).
+    uint32_t* part = gbm + (int64_t)(blockIdx.x % kMaxRowBlocks) * a.words;
+    for (int64_t w = tid; w < a.words; w += 256) {
+        const uint32_t b = bm[w];
+        if (b) atomicOr(&part[w], b);
+    }
+}
+
+// A wave per row.  kVec: 16-byte chunks of x and 8-byte code stores.
+template <bool kVec>
+__global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t* __restrict__ gbm) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* bm = smem;                                       // [words]
+    int32_t* pre = reinterpret_cast<int32_t*>(smem + a.words);  // [words]
+    __shared__ int32_t wave_tot[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int64_t w = tid; w < a.words; w += 256) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int p = 0; p < kMaxRowBlocks; ++p) b |= gbm[(int64_t)p * a.words + w];
+        bm[w] = b;
+    }
+    __syncthreads();
+    const int32_t total = bitmap_prefix(bm, pre, a.words, wave_tot);
+    const int32_t kept = total < a.cap ? total : a.cap;
+    if (blockIdx.x == 0) publish(a, bm, pre, total, true);
+    const float tau = a.threshold;
+    const uint8_t* bmb = reinterpret_cast<const uint8_t*>(bm);
+    const int32_t nchunks = (int32_t)((a.k + 7) / 8);
+    for (int64_t rr = wave; rr < a.rows_per_block; rr += 4) {
+        const int64_t r = (int64_t)blockIdx.x * a.rows_per_block + rr;
+        if (r >= a.m) break;
+        const half_bits* __restrict__ xr = a.x + r * a.ldx;
+        // the row's outlier-column values: the gather, zero codes there, and
+        // their largest magnitude below the threshold
+        float t = 0.0f;
+        if (total > 0)
+            for (int64_t w = lane; w < a.words; w += 64) {
+                uint32_t bits = bm[w];
+                int32_t slot = bits ? pre[w] : 0;
+                while (bits) {
+                    const int64_t j = w * 32 + (__ffs(bits) - 1);
+                    bits &= bits - 1u;
+                    const half_bits h = xr[j];
+                    if (a.x_out && slot < a.cap) a.x_out[r * a.ldo + slot] = h;
+                    const float f = fabsf(h2f(h));
+                    if (f < tau) t = fmaxf(t, f);
+                    if (a.q) a.q[r * a.ldq + j] = 0;
+                    ++slot;
+                }
+            }
+        if (a.x_out)
+            for (int32_t s2 = kept + lane; s2 < a.xo_cols; s2 += 64) a.x_out[r * a.ldo + s2] = 0;
+        t = wave_max_uniform(t);
+        if (!a.q || !(t > 0.0f) || t < a.absmax[r]) continue;
+        // the row maximum below the threshold sits in an outlier column:
+        // the scale over the columns outside the set, and the codes again
+        float mx = 0.0f;
+        for (int32_t ch = lane; ch < nchunks; ch += 64) {
+            const uint4 v = mask_outliers(load8<kVec>(xr, (int64_t)ch * 8, a.k), (uint32_t)bmb[ch]);
+            mx = fmaxf(mx, chunk_absmax(v));
+        }
+        const float s = wave_max_uniform(mx);
+        const float inv = s > 0.0f ? 127.0f / s : 0.0f;   // IEEE division
+        int8_t* qr = a.q + r * a.ldq;
+        for (int32_t ch = lane; ch < nchunks; ch += 64) {
+            const int64_t col = (int64_t)ch * 8;
+            const uint2 code = codes8_plain(mask_outliers(load8<kVec>(xr, col, a.k), (uint32_t)bmb[ch]), inv);
+            if (kVec) {
+                *reinterpret_cast<uint2*>(qr + col) = code;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < a.k) qr[col + e] = (int8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+            }
+        }
+        if (lane == 0) a.absmax[r] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // One or two rows (decode): one workgroup of 1024 threads holds all of x in
 // registers and so sees the whole outlier set itself: detection, calibration,
 // quantization and extraction in one launch, x read once.  Chunk f = tid +
@@ -239,6 +475,9 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 // more rows one workgroup's memory pipeline measured slower than the two
 // kernels, which spread the rows over the CUs.)
 constexpr int kSmallThreads = 1024;
+// rows from which the quantizer reads x once (three launches) instead of twice
+// (detection, then quantization: two launches)
+constexpr int64_t kSingleReadMinRows = 1024;
 constexpr int kSmallMaxL = 8;
 constexpr int kSmallMaxRows = 2;
 
@@ -388,6 +627,64 @@ hipError_t launch_quant_rows(const QuantArgs& in, hipStream_t stream) {
                      : launch_rows<false, false>(a, blocks, lds, stream);
 }
 
+namespace {
+
+template <bool kVec, bool kBlockRow>
+hipError_t launch_pass1(const QuantArgs& a, int64_t blocks, uint32_t* gbm, hipStream_t stream) {
+    constexpr int P = kBlockRow ? 256 : 64;
+    const int64_t per_lane = ceil_div(ceil_div(a.k, 8), P);
+    const dim3 grid((unsigned)blocks), block(256);
+    const size_t lds = (size_t)a.words * sizeof(uint32_t);
+    if (per_lane <= 2)
+        hipLaunchKernelGGL((quant1_kernel<kVec, kBlockRow, 2>), grid, block, lds, stream, a, gbm);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL((quant1_kernel<kVec, kBlockRow, 4>), grid, block, lds, stream, a, gbm);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL((quant1_kernel<kVec, kBlockRow, 8>), grid, block, lds, stream, a, gbm);
+    else
+        hipLaunchKernelGGL((quant1_kernel<kVec, kBlockRow, 16>), grid, block, lds, stream, a, gbm);
+    return hipGetLastError();
+}
+
+// threshold > 0: zero the partial bitmaps (scratch), the single read of x,
+// then the pass over the outlier set
+hipError_t launch_single_read(const QuantArgs& in, hipStream_t stream) {
+    QuantArgs a = in;
+    uint32_t* gbm = a.partial;   // kMaxRowBlocks x words
+    const int64_t pwords = kMaxRowBlocks * a.words;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(pwords > 8192 ? 16 : 1)), dim3(256), 0, stream, gbm,
+                       pwords);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const bool vec = vector_rows(a) && ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
+    const int64_t cpr = (a.k + 7) / 8;
+    const bool block_row = cpr > 512 || (cpr >= 256 && a.m <= 512);
+    int64_t blocks;
+    if (block_row) {
+        a.rows_per_block = ceil_div(a.m, 1024);
+        blocks = ceil_div(a.m, a.rows_per_block);
+    } else {
+        a.rows_per_block = 4 * ceil_div(a.m, 4 * 512);
+        blocks = ceil_div(a.m, a.rows_per_block);
+    }
+    hipError_t e = vec ? (block_row ? launch_pass1<true, true>(a, blocks, gbm, stream)
+                                    : launch_pass1<true, false>(a, blocks, gbm, stream))
+                       : (block_row ? launch_pass1<false, true>(a, blocks, gbm, stream)
+                                    : launch_pass1<false, false>(a, blocks, gbm, stream));
+    if (e != hipSuccess) return e;
+    // a wave per row, up to 512 workgroups
+    QuantArgs b = in;
+    b.rows_per_block = 4 * ceil_div(a.m, 4 * 512);
+    const int64_t blocks2 = ceil_div(a.m, b.rows_per_block);
+    const size_t lds2 = (size_t)a.words * 2 * sizeof(uint32_t);
+    if (vec)
+        hipLaunchKernelGGL((quant2_kernel<true>), dim3((unsigned)blocks2), dim3(256), lds2, stream, b, gbm);
+    else
+        hipLaunchKernelGGL((quant2_kernel<false>), dim3((unsigned)blocks2), dim3(256), lds2, stream, b, gbm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
     QuantArgs a = in;
     const bool vec = vector_rows(a);
@@ -397,6 +694,7 @@ hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
         const size_t lds = ((size_t)a.words * 2 + (size_t)a.m * 2) * sizeof(uint32_t);
         return vec ? launch_small<true>(a, per_thread, lds, stream) : launch_small<false>(a, per_thread, lds, stream);
     }
+    if (a.threshold > 0.0f && a.m >= kSingleReadMinRows && a.q) return launch_single_read(a, stream);
     if (a.threshold > 0.0f && a.m > 0) {
         // detect: 256 or 64 columns x RB rows per workgroup, at most
         // kMaxRowBlocks row blocks (RB >= 8), about 1024 workgroups when the

@@ -35,6 +35,16 @@ __device__ inline uint4 load8(const half_bits* __restrict__ row, int64_t col, in
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Buffer resource over bytes [base, base + bytes): loads past the end return
+// 0 and stores past it are dropped, so loops over chunks need no branch per
+// access (which would make the compiler's vmcnt waits conservative; on gfx9
+// vmcnt also counts stores).
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+    if (bytes < 0) bytes = 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ inline half_bits half_at(const uint4& v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return (half_bits)((w >> (16 * (e & 1))) & 0xffffu);

@@ -686,3 +686,38 @@ def test_linear_forward_largest_k(m):
     torch.cuda.synchronize()
     _check_workspace(wsp, x, ref.quant, 8)
     assert_fp16_close(out, ref.out)
+
+
+@pytest.mark.parametrize("m,k", [(64, 2048), (40, 300), (300, 20000), (1100, 512)])
+def test_quant_row_max_inside_outlier_columns(m, k):
+    """Rows whose largest element below the threshold sits in an outlier column
+    (large in another row): the row scale must come from the other columns.
+    Row 5: max 5.5 in outlier column 3, next 4.0 elsewhere; row 6: 5.5 in the
+    outlier column and 5.5 in an ordinary column (tie); row 7: every ordinary
+    element 0 (zero scale)."""
+    L = make_inputs(m, k, 1, seed=(88, m, k), with_weight=False)
+    x = (L.x.astype(np.float32) * 0.5).astype(np.float16)
+    x[0, 3] = np.float16(50.0)
+    x[1, k - 2] = np.float16(-7.0)
+    x[5] = np.clip(x[5], -3.5, 3.5)
+    x[5, 3] = np.float16(5.5)
+    x[5, 10] = np.float16(-4.0)
+    x[6] = np.clip(x[6], -3.5, 3.5)
+    x[6, 3] = np.float16(-5.5)
+    x[6, k - 1] = np.float16(5.5)
+    x[7] = 0
+    x[7, 3] = np.float16(2.0)
+    x[7, k - 2] = np.float16(1.0)
+    ref = oracle.vectorwise_quant(x, TAU)
+    assert ref.cols.tolist() == [3, k - 2]
+    assert ref.absmax[5] == np.float32(4.0) and ref.absmax[6] == np.float32(5.5) and ref.absmax[7] == 0
+    say(f"vectorwise_quant row max inside outlier columns m={m} k={k}")
+    q, s, bm = i8.vectorwise_quant(dev(x), TAU)
+    torch.cuda.synchronize()
+    assert_equal(q, ref.q, "codes")
+    assert_equal(s, ref.absmax, "absmax")
+    assert_equal(bm.view(torch.int32), ref.bitmap.view(np.int32), "bitmap")
+    wsp = i8.LinearWorkspace.create(m, 8, k, 1, "cuda")
+    i8.linear_quantize(dev(x), wsp, TAU)
+    torch.cuda.synchronize()
+    _check_workspace(wsp, x, ref, 1)
