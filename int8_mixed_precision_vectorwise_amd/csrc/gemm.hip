@@ -1350,26 +1350,78 @@ hipError_t launch_tile(const GemmArgs& g, bool aligned, bool staged, hipStream_t
 // MI355X: a workgroup costs a fixed ~3 us (first stage in flight, epilogue)
 // plus k-tiles x the per-128-byte-K-tile time of its shape; workgroups run in
 // rounds over the CUs (two 64 x 64 workgroups fit one CU's LDS).
-int pick_tile(int64_t m, int64_t n, int64_t k) {
-    constexpr int64_t kCUs = 256;
-    struct Cand { int bm, bn, per_cu; double tk, tk_shared; };
-    const Cand cands[6] = {{256, 256, 1, 1.71, 1.71}, {256, 128, 1, 0.97, 0.97}, {128, 128, 1, 0.50, 0.50},
-                           {128, 64, 1, 0.30, 0.30},   {64, 128, 1, 0.33, 0.33},  {64, 64, 2, 0.26, 0.38}};
-    const double ktiles = (double)((k + 127) / 128);
+struct TileCand { int bm, bn, per_cu; double tk, tk_shared; };
+constexpr int kCands = 6;
+constexpr TileCand kTileCands[kCands] = {{256, 256, 1, 1.71, 1.71}, {256, 128, 1, 0.97, 0.97},
+                                         {128, 128, 1, 0.50, 0.50}, {128, 64, 1, 0.30, 0.30},
+                                         {64, 128, 1, 0.33, 0.33},  {64, 64, 2, 0.26, 0.38}};
+constexpr int64_t kCUs = 256;
+// the host-side gap between two launches on one stream, in the same units (us)
+constexpr double kLaunchGap = 4.0;
+
+int64_t cand_tiles(int c, int64_t m, int64_t n) {
+    return ((m + kTileCands[c].bm - 1) / kTileCands[c].bm) * ((n + kTileCands[c].bn - 1) / kTileCands[c].bn);
+}
+double cand_cost(int c, int64_t m, int64_t n, int64_t k) {
+    const int64_t tiles = cand_tiles(c, m, n);
+    const int64_t slots = kCUs * kTileCands[c].per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double tk = tiles > kCUs ? kTileCands[c].tk_shared : kTileCands[c].tk;
+    return (double)rounds * (3.0 + (double)((k + 127) / 128) * tk);
+}
+int pick_tile(int64_t m, int64_t n, int64_t k, double* cost = nullptr) {
     int best = 0;
     double best_t = 1e300;
-    for (int c = 0; c < 6; ++c) {
-        const int64_t tiles = ((m + cands[c].bm - 1) / cands[c].bm) * ((n + cands[c].bn - 1) / cands[c].bn);
-        const int64_t slots = kCUs * cands[c].per_cu;
-        const int64_t rounds = (tiles + slots - 1) / slots;
-        const double tk = tiles > kCUs ? cands[c].tk_shared : cands[c].tk;
-        const double t = (double)rounds * (3.0 + ktiles * tk);
+    for (int c = 0; c < kCands; ++c) {
+        const double t = cand_cost(c, m, n, k);
         if (t < best_t * 0.999) {
             best_t = t;
             best = c;
         }
     }
+    if (cost) *cost = best_t;
     return best;
+}
+
+// A launch plan: tile `main` over output columns [0, n_main), and, when the
+// last round of `main` would leave CUs idle, tile `tail` over the columns
+// [n_main, n) in a second launch.  The split is on whole tile columns of the
+// main shape that fill whole rounds (65B up, 4096 x 22016: 1280 tiles of
+// 256 x 256 in five rounds, then 4096 x 1536 in smaller tiles, instead of a
+// sixth round with 96 of 256 CUs busy).
+struct TilePlan { int main; int64_t n_main; int tail; };
+TilePlan plan_tiles(int64_t m, int64_t n, int64_t k) {
+    double single;
+    TilePlan plan{pick_tile(m, n, k, &single), n, 0};
+    double best_t = single;
+    for (int c = 0; c < kCands; ++c) {
+        const int64_t slots = kCUs * kTileCands[c].per_cu;
+        const int64_t tm = (m + kTileCands[c].bm - 1) / kTileCands[c].bm;
+        const int64_t full = cand_tiles(c, m, n) / slots;   // whole rounds
+        const int64_t cols = full * slots / tm;              // whole tile columns in them
+        const int64_t n_main = cols * kTileCands[c].bn;
+        if (cols <= 0 || n_main >= n) continue;
+        double tail_t;
+        const int tail = pick_tile(m, n - n_main, k, &tail_t);
+        const double t = cand_cost(c, m, n_main, k) + kLaunchGap + tail_t;
+        if (t < best_t * 0.97) {
+            best_t = t;
+            plan = TilePlan{c, n_main, tail};
+        }
+    }
+    return plan;
+}
+
+template <bool kFused>
+hipError_t launch_shape(int c, const GemmArgs& g, bool aligned, bool staged, hipStream_t stream) {
+    switch (c) {
+        case 0: return launch_tile<256, 256, kFused>(g, aligned, staged, stream);
+        case 1: return launch_tile<256, 128, kFused>(g, aligned, staged, stream);
+        case 2: return launch_tile<128, 128, kFused>(g, aligned, staged, stream);
+        case 3: return launch_tile<128, 64, kFused>(g, aligned, staged, stream);
+        case 4: return launch_tile<64, 128, kFused>(g, aligned, staged, stream);
+        default: return launch_tile<64, 64, kFused>(g, aligned, staged, stream);
+    }
 }
 
 template <bool kFused>
@@ -1380,14 +1432,25 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     // the staged kernels read whole 128-byte K stages: A must be zero past k
     const bool staged = aligned && ((g.k & 127) == 0 || g.a_zero_padded);
     if (staged && g.m <= 16) return launch_decode(g, kFused, stream);
-    switch (pick_tile(g.m, g.n, g.k)) {
-        case 0: return launch_tile<256, 256, kFused>(g, aligned, staged, stream);
-        case 1: return launch_tile<256, 128, kFused>(g, aligned, staged, stream);
-        case 2: return launch_tile<128, 128, kFused>(g, aligned, staged, stream);
-        case 3: return launch_tile<128, 64, kFused>(g, aligned, staged, stream);
-        case 4: return launch_tile<64, 128, kFused>(g, aligned, staged, stream);
-        default: return launch_tile<64, 64, kFused>(g, aligned, staged, stream);
+    const TilePlan plan = plan_tiles(g.m, g.n, g.k);
+    if (plan.n_main >= g.n) return launch_shape<kFused>(plan.main, g, aligned, staged, stream);
+    GemmArgs head = g;
+    head.n = plan.n_main;
+    hipError_t e = launch_shape<kFused>(plan.main, head, aligned, staged, stream);
+    if (e != hipSuccess) return e;
+    // the remaining columns: every column operand moves by n_main (the weight
+    // rows keep 16-byte alignment: n_main is a multiple of the tile width)
+    GemmArgs tail = g;
+    tail.n = g.n - plan.n_main;
+    tail.b = g.b + plan.n_main * g.ldb;
+    if (kFused) {
+        tail.col_absmax = g.col_absmax + plan.n_main;
+        if (g.bias) tail.bias = g.bias + plan.n_main;
+        tail.out = g.out + plan.n_main;
+    } else {
+        tail.c = g.c + plan.n_main;
     }
+    return launch_shape<kFused>(plan.tail, tail, aligned, staged, stream);
 }
 
 }  // namespace

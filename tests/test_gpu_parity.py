@@ -126,7 +126,9 @@ MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128
              (512, 256, 1024), (1, 4096, 5120), (16, 13824, 640), (257, 259, 4100),
              (3, 777, 1280), (2, 513, 640), (4, 100, 13824),
              (200, 300, 2560), (130, 190, 2176),  # two K pipelines per workgroup (17 K tiles: one pipeline's last is empty)
-             (2100, 5000, 512), (2100, 5000, 640), (1800, 6000, 128)]  # 256 x 256 ping-pong tiles, ragged m and n
+             (2100, 5000, 512), (2100, 5000, 640), (1800, 6000, 128),  # 256 x 256 ping-pong tiles, ragged m and n
+             # whole rounds of 256 x 256 tiles, the remaining columns in a second launch of smaller tiles
+             (2048, 9000, 512), (2100, 9000, 512)]
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -208,6 +210,9 @@ FWD_CASES = [
     (768, 250, 6144, 20, 0.5, True, TAU, 64),     # 256 x 128: copies in the wave's staging area
     (1536, 250, 6144, 30, 0.5, False, TAU, 64),   # 256 x 256 without a stash: every slot gathered
     (2100, 1000, 5000, 9, 0.5, True, TAU, 64),    # 256 x 256 ping-pong, ragged m, n and k
+    # 256 x 256 tiles over whole rounds, then the remaining columns in a second launch
+    (2048, 512, 9000, 9, 0.5, True, TAU, 64),     # tail of 128 x 64 tiles: bias and outliers offset
+    (2100, 512, 9000, 30, 0.5, False, TAU, 64),   # tail of 128 x 128 tiles, ragged m, slots past 16
     # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
     (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
     (2, 4096, 264, 5, 0.5, False, TAU, 32),
