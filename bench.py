@@ -222,6 +222,35 @@ def _per_dispatch(directory: str, folder: str, counter: str, name_part: tuple):
     return [vals[d] for d in sorted(vals)]
 
 
+LAYER_MARK = "FillFunctor"   # the kernel --mode gemm runs after each layer's launches
+
+
+def _per_layer(directory: str, folder: str, counter: str, launches: int):
+    """Counter value per GEMM launch of each layer, from a --mode gemm run: the
+    GEMM dispatches (one or two per launch: a main and a tail launch) between
+    consecutive layer marks, summed and divided by the launches."""
+    import csv
+    import glob
+    vals, names = {}, {}
+    for f in glob.glob(os.path.join(directory, folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            names[d] = r["Kernel_Name"]
+            vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+    layers, cur, n = [], 0.0, 0
+    for d in sorted(vals):
+        if LAYER_MARK in names[d]:
+            if n:
+                layers.append(cur / launches)
+            cur, n = 0.0, 0
+        elif any(p in names[d] for p in GEMM_KERNELS):
+            cur += vals[d]
+            n += 1
+    return layers
+
+
 def _read_bytes(directory, folder, name_part):
     """L2 -> fabric read bytes per dispatch: 32, 64 and 128-byte requests by size."""
     n32, n64, n128, nall = (_per_dispatch(directory, folder, c, name_part) for c in RD_COUNTERS)
@@ -251,17 +280,16 @@ def traffic_summary(directory: str, workload: str, launches: int) -> int:
         raise SystemExit("no copy-kernel counters found")
     f_scale = copy_bytes / (sum(cr) / len(cr))
     w_scale = copy_bytes / (sum(cw) / len(cw))
-    gr, g_other = _read_bytes(directory, "gemm_rd", GEMM_KERNELS)
-    gw = _write_bytes(directory, "gemm_wr", GEMM_KERNELS)
-    if len(gr) < len(specs) * launches or len(gw) < len(specs) * launches:
-        raise SystemExit(f"expected {len(specs) * launches} GEMM dispatches, got {len(gr)} / {len(gw)}")
+    n32, n64, n128, nall = (_per_layer(directory, "gemm_rd", c, launches) for c in RD_COUNTERS)
+    w64, wall = (_per_layer(directory, "gemm_wr", c, launches) for c in WR_COUNTERS)
+    if min(len(n32), len(w64)) < len(specs):
+        raise SystemExit(f"expected GEMM launches of {len(specs)} layers, got {len(n32)} / {len(w64)}")
+    g_other = [t - a - b - c for a, b, c, t in zip(n32, n64, n128, nall)]
     layers = {}
     tot = 0.0
     for li, s in enumerate(specs):
-        f = gr[li * launches:(li + 1) * launches]
-        w = gw[li * launches:(li + 1) * launches]
-        fb = sum(f) / len(f) * f_scale
-        wb = sum(w) / len(w) * w_scale
+        fb = (32 * n32[li] + 64 * n64[li] + 128 * n128[li]) * f_scale
+        wb = (64 * w64[li] + 32 * (wall[li] - w64[li])) * w_scale
         layers[s.name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
                           "algorithmic_bytes": gemm_alg_bytes(s),
                           "ratio": round((fb + wb) / gemm_alg_bytes(s), 3)}
@@ -297,8 +325,8 @@ def mfma_summary(directory: str, workload: str, launches: int) -> int:
     SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024).  ops =
     SQ_INSTS_VALU_MFMA_MOPS_I8 * 512, to match 2 m n k."""
     specs, _ = workload_specs(workload)
-    vals = {c: _per_dispatch(directory, "gemm_mfma", c, GEMM_KERNELS) for c in MFMA_COUNTERS}
-    if any(len(v) < len(specs) * launches for v in vals.values()):
+    vals = {c: _per_layer(directory, "gemm_mfma", c, launches) for c in MFMA_COUNTERS}
+    if any(len(v) < len(specs) for v in vals.values()):
         raise SystemExit("missing MFMA counter dispatches")
     try:
         per_us = json.load(open(os.path.join(directory, "trace_bench.json")))["roofline"]["per_launch_us"]
@@ -306,8 +334,7 @@ def mfma_summary(directory: str, workload: str, launches: int) -> int:
         per_us = {}
     layers = {}
     for li, s in enumerate(specs):
-        sl = slice(li * launches, (li + 1) * launches)
-        avg = {c: sum(v[sl]) / launches for c, v in vals.items()}
+        avg = {c: v[li] for c, v in vals.items()}
         xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8
         rec = {"mfma_busy": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 4 * N_CUS), 4),
                "mops_i8_x512": round(avg["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512),
@@ -926,13 +953,16 @@ def main() -> int:
     sets, copies = prepare_sets(torch, i8, specs, cap, args.rotate_mb, dev)
 
     if args.mode == "gemm":
-        # exactly args.launches GEMM dispatches per layer, layer after layer
+        # exactly args.launches GEMM launches per layer, layer after layer, each
+        # layer followed by a one-element fill (the mark the counter summaries
+        # split the dispatches at: a launch may be two kernels)
         for li, s in enumerate(specs):
             for i in range(args.launches):
                 _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
                 if i < copies:
                     i8.linear_quantize(xc, ws, s.tau)
                 i8.linear_matmul_dequant(xc, ws, wqc, wac, b, out)
+            torch.full((1,), li, dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
         print(json.dumps({"workload": args.workload, "gemm_launches_per_layer": args.launches}))
         return 0

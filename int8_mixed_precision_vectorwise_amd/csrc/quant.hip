@@ -396,11 +396,16 @@ __global__ __launch_bounds__(256) void quant1_kernel(QuantArgs a, uint32_t* __re
 }
 
 // A wave per row.  kVec: 16-byte chunks of x and 8-byte code stores.
+// outlier columns whose slot -> column list quant2_kernel keeps in LDS (more:
+// each row walks the bitmap words)
+constexpr int kQ2Cols = 2048;
+
 template <bool kVec>
 __global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t* __restrict__ gbm) {
     extern __shared__ uint32_t smem[];
     uint32_t* bm = smem;                                       // [words]
     int32_t* pre = reinterpret_cast<int32_t*>(smem + a.words);  // [words]
+    int32_t* cols = pre + a.words;                             // [kQ2Cols] column of each slot
     __shared__ int32_t wave_tot[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int64_t w = tid; w < a.words; w += 256) {
@@ -413,6 +418,18 @@ __global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t
     const int32_t total = bitmap_prefix(bm, pre, a.words, wave_tot);
     const int32_t kept = total < a.cap ? total : a.cap;
     if (blockIdx.x == 0) publish(a, bm, pre, total, true);
+    const bool listed = total <= kQ2Cols;
+    if (listed && total > 0) {
+        for (int64_t w = tid; w < a.words; w += 256) {
+            uint32_t bits = bm[w];
+            int32_t slot = pre[w];
+            while (bits) {
+                cols[slot++] = (int32_t)(w * 32 + (__ffs(bits) - 1));
+                bits &= bits - 1u;
+            }
+        }
+        __syncthreads();
+    }
     const float tau = a.threshold;
     const uint8_t* bmb = reinterpret_cast<const uint8_t*>(bm);
     const int32_t nchunks = (int32_t)((a.k + 7) / 8);
@@ -423,7 +440,30 @@ __global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t
         // the row's outlier-column values: the gather, zero codes there, and
         // their largest magnitude below the threshold
         float t = 0.0f;
-        if (total > 0)
+        if (listed) {
+            // slots lane, lane + 64, ...: the loads of a batch go out together
+            constexpr int B = 4;
+            for (int32_t s0 = 0; s0 < total; s0 += 64 * B) {
+                int32_t j[B];
+                half_bits h[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int32_t slot = s0 + 64 * b + lane;
+                    j[b] = slot < total ? cols[slot] : -1;
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) h[b] = j[b] >= 0 ? xr[j[b]] : (half_bits)0;
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    if (j[b] < 0) continue;
+                    const int32_t slot = s0 + 64 * b + lane;
+                    if (a.x_out && slot < a.cap) a.x_out[r * a.ldo + slot] = h[b];
+                    const float f = fabsf(h2f(h[b]));
+                    if (f < tau) t = fmaxf(t, f);
+                    if (a.q) a.q[r * a.ldq + j[b]] = 0;
+                }
+            }
+        } else
             for (int64_t w = lane; w < a.words; w += 64) {
                 uint32_t bits = bm[w];
                 int32_t slot = bits ? pre[w] : 0;
@@ -675,7 +715,7 @@ hipError_t launch_single_read(const QuantArgs& in, hipStream_t stream) {
     QuantArgs b = in;
     b.rows_per_block = 4 * ceil_div(a.m, 4 * 512);
     const int64_t blocks2 = ceil_div(a.m, b.rows_per_block);
-    const size_t lds2 = (size_t)a.words * 2 * sizeof(uint32_t);
+    const size_t lds2 = ((size_t)a.words * 2 + kQ2Cols) * sizeof(uint32_t);
     if (vec)
         hipLaunchKernelGGL((quant2_kernel<true>), dim3((unsigned)blocks2), dim3(256), lds2, stream, b, gbm);
     else
