@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kRows = 16;     // weight rows per group
 constexpr int kWaves = 4;     // waves per workgroup
-constexpr int kStages = 8;    // per-wave ring depth
+constexpr int kStages = 4;    // per-wave ring depth
 constexpr int kChunk = 128;   // K bytes per stage
 constexpr int kStageBytes = kRows * kChunk;  // weight rows only
 constexpr int kRsrcWord3 = 0x00020000;

@@ -23,7 +23,9 @@
 //
 // One or two rows of at most 65536 columns (decode) take quant_small_kernel:
 // one workgroup of 1024 threads holds all of x in registers and does every
-// step in one launch.
+// step in one launch.  Three to sixteen rows take two launches over column
+// slices (cs1_kernel, cs2_kernel); from 1024 rows x is read once
+// (quant1_kernel, quant2_kernel).
 //
 // (A single kernel with a grid-wide meeting point instead of the second
 // launch measured slower on MI355X: the device-scope release / acquire round
@@ -508,6 +510,178 @@ __global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t
 }
 
 // ---------------------------------------------------------------------------
+// A few rows (decode, 3 to 16 rows), two launches over 256-column slices: a
+// workgroup holds every row of its slice, so what it sees of the outlier set
+// (the OR over the rows of each column) is final, and so is its share of each
+// row's maximum over the non-outlier columns.
+//   cs1_kernel  the slice's outlier bits (scratch bitmap, and the output
+//               bitmap) and per row the maximum |x| over its non-outlier
+//               columns (scratch, [slice x m]);
+//   cs2_kernel  per row the absmax (the maximum over the slices), the codes of
+//               the slice, and its outlier columns' slots (popcounts of the
+//               words before it): index list entries and the gathered values.
+//               Workgroup 0 writes the count, absmax, the index list's -1
+//               tail and the zero padding of the gathered values.
+// Thread t holds chunk t % 32 (8 columns) of rows t / 32 and t / 32 + 8.
+constexpr int kCsRows = 16;
+constexpr int kCsCols = 256;
+
+template <bool kVec>
+__device__ inline void cs_load(const QuantArgs& a, uint4 (&v)[2], int rl, int64_t col) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t r = rl + 8 * h;
+        v[h] = (r < a.m && col < a.k) ? load8<kVec>(a.x + r * a.ldx, col, a.k) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void cs1_kernel(QuantArgs a, uint32_t* __restrict__ sbits,
+                                                  float* __restrict__ spart) {
+    const int tid = threadIdx.x, c = tid & 31, rl = tid >> 5;
+    const int64_t col = (int64_t)blockIdx.x * kCsCols + c * 8;
+    uint4 v[2];
+    cs_load<kVec>(a, v, rl, col);
+    __shared__ uint32_t red[256];
+    red[tid] = outlier_bits8(v[0], a.threshold) | outlier_bits8(v[1], a.threshold);
+    __syncthreads();
+    uint32_t cb = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cb |= red[q * 32 + c];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float mx = chunk_absmax(mask_outliers(v[h], cb));
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));   // the 32 chunks
+        const int64_t r = rl + 8 * h;
+        if (c == 0 && r < a.m) spart[(int64_t)blockIdx.x * a.m + r] = mx;
+    }
+    if (tid < kCsCols / 32) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint32_t mm = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) mm |= red[q * 32 + tid * 4 + q4];
+            word |= (mm & 0xffu) << (8 * q4);
+        }
+        const int64_t w = (int64_t)blockIdx.x * (kCsCols / 32) + tid;
+        if (w < a.words) {
+            sbits[w] = word;
+            if (a.bitmap_out) a.bitmap_out[w] = word;
+        }
+    }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void cs2_kernel(QuantArgs a, const uint32_t* __restrict__ sbits,
+                                                  const float* __restrict__ spart, int64_t nslices) {
+    const int tid = threadIdx.x, c = tid & 31, rl = tid >> 5, lane = tid & 63, wave = tid >> 6;
+    const int64_t col = (int64_t)blockIdx.x * kCsCols + c * 8;
+    uint4 v[2];
+    cs_load<kVec>(a, v, rl, col);
+    __shared__ float s_row[kCsRows];
+    __shared__ uint32_t sb[kCsCols / 32];
+    __shared__ int32_t wsum[2][4];
+    // row absmax: 16 lanes per row over the slices
+    {
+        const int64_t r = tid >> 4;
+        const int u = tid & 15;
+        float pm = 0.0f;
+        if (r < a.m)
+            for (int64_t sl = u; sl < nslices; sl += 16) pm = fmaxf(pm, spart[sl * a.m + r]);
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) pm = fmaxf(pm, __shfl_xor(pm, off, 64));
+        if (u == 0 && r < kCsRows) s_row[r] = pm;
+    }
+    // outlier columns before this slice, and in all
+    const int64_t w0 = (int64_t)blockIdx.x * (kCsCols / 32);
+    int32_t before = 0, tot = 0;
+    for (int64_t w = tid; w < a.words; w += 256) {
+        const int32_t p = __popc(sbits[w]);
+        tot += p;
+        before += w < w0 ? p : 0;
+    }
+    before = wave_sum_i32(before);
+    tot = wave_sum_i32(tot);
+    if (lane == 0) {
+        wsum[0][wave] = before;
+        wsum[1][wave] = tot;
+    }
+    if (tid < kCsCols / 32) sb[tid] = w0 + tid < a.words ? sbits[w0 + tid] : 0u;
+    __syncthreads();
+    const int32_t base = wsum[0][0] + wsum[0][1] + wsum[0][2] + wsum[0][3];
+    const int32_t total = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
+    const uint32_t cb = (sb[c >> 2] >> (8 * (c & 3))) & 0xffu;
+    int32_t slot0 = base + __popc(sb[c >> 2] & ((1u << (8 * (c & 3))) - 1u));
+    for (int w = 0; w < (c >> 2); ++w) slot0 += __popc(sb[w]);
+
+    const bool vec_q = ((a.ldq & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t r = rl + 8 * h;
+        if (r >= a.m) continue;
+        if (a.q && col < a.kpad) {
+            const float sr = s_row[r];
+            const float inv = sr > 0.0f ? 127.0f / sr : 0.0f;   // IEEE division
+            const uint2 code = codes8_plain(mask_outliers(v[h], cb), inv);
+            int8_t* qr = a.q + r * a.ldq + col;
+            if (vec_q && col + 8 <= a.kpad) {
+                *reinterpret_cast<uint2*>(qr) = code;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < a.kpad) qr[e] = (int8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+            }
+        }
+        if (cb) {
+            int32_t slot = slot0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!((cb >> e) & 1u)) continue;
+                if (a.x_out && slot < a.cap) a.x_out[r * a.ldo + slot] = half_at(v[h], e);
+                if (h == 0 && rl == 0 && a.idx_out && slot < a.idx_len) a.idx_out[slot] = (int32_t)(col + e);
+                ++slot;
+            }
+        }
+    }
+    if (blockIdx.x == 0) {
+        if (a.count_out && tid == 0) *a.count_out = total;
+        if (a.absmax && tid < a.m) a.absmax[tid] = s_row[tid];
+        if (a.idx_out)
+            for (int32_t sl = total + tid; sl < a.idx_len; sl += 256) a.idx_out[sl] = -1;
+        if (a.x_out) {
+            const int32_t kept = total < a.cap ? total : a.cap;
+            const int32_t pad = a.xo_cols - kept;
+            for (int32_t i = tid; i < (int32_t)a.m * pad; i += 256)
+                a.x_out[(int64_t)(i / pad) * a.ldo + kept + i % pad] = 0;
+        }
+    }
+}
+
+// the two launches; false when the scratch cannot hold the slice data
+bool launch_col_slices(const QuantArgs& a, hipStream_t stream, hipError_t* err) {
+    const int64_t span = a.kpad > a.k ? a.kpad : a.k;
+    const int64_t nslices = ceil_div(span, kCsCols);
+    const size_t need = (size_t)ceil_div(span, 32) * 4 + (size_t)nslices * a.m * 4;
+    if (a.m > kCsRows || need > quant_scratch_bytes(a.k)) return false;
+    uint32_t* sbits = a.partial;
+    float* spart = reinterpret_cast<float*>(a.partial + ceil_div(span, 32));
+    const bool vec = vector_rows(a);
+    if (vec)
+        hipLaunchKernelGGL((cs1_kernel<true>), dim3((unsigned)nslices), dim3(256), 0, stream, a, sbits, spart);
+    else
+        hipLaunchKernelGGL((cs1_kernel<false>), dim3((unsigned)nslices), dim3(256), 0, stream, a, sbits, spart);
+    if ((*err = hipGetLastError()) != hipSuccess) return true;
+    if (vec)
+        hipLaunchKernelGGL((cs2_kernel<true>), dim3((unsigned)nslices), dim3(256), 0, stream, a, sbits, spart, nslices);
+    else
+        hipLaunchKernelGGL((cs2_kernel<false>), dim3((unsigned)nslices), dim3(256), 0, stream, a, sbits, spart, nslices);
+    *err = hipGetLastError();
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // One or two rows (decode): one workgroup of 1024 threads holds all of x in
 // registers and so sees the whole outlier set itself: detection, calibration,
 // quantization and extraction in one launch, x read once.  Chunk f = tid +
@@ -735,6 +909,10 @@ hipError_t launch_quantize(const QuantArgs& in, hipStream_t stream) {
         return vec ? launch_small<true>(a, per_thread, lds, stream) : launch_small<false>(a, per_thread, lds, stream);
     }
     if (a.threshold > 0.0f && a.m >= kSingleReadMinRows && a.q) return launch_single_read(a, stream);
+    if (a.threshold > 0.0f && a.m > kSmallMaxRows && a.m <= kCsRows) {
+        hipError_t e;
+        if (launch_col_slices(a, stream, &e)) return e;
+    }
     if (a.threshold > 0.0f && a.m > 0) {
         // detect: 256 or 64 columns x RB rows per workgroup, at most
         // kMaxRowBlocks row blocks (RB >= 8), about 1024 workgroups when the

@@ -101,7 +101,7 @@ def test_outlier_extract_bit_exact(m, k, o, cap):
     assert_equal(xo.view(torch.int16), rxo.view(np.int16), "x_out")
 
 
-@pytest.mark.parametrize("m,k", [(512, 1024), (300, 20000)], ids=["wave_rows", "block_rows"])
+@pytest.mark.parametrize("m,k", [(512, 1024), (300, 20000), (6, 5000)], ids=["wave_rows", "block_rows", "col_slices"])
 def test_quant_workspace_reuse(m, k):
     """Three calls on one workspace, each with other outlier columns: every
     result is the oracle's (nothing carries over from the previous call)."""
@@ -693,7 +693,7 @@ def test_linear_forward_largest_k(m):
     assert_fp16_close(out, ref.out)
 
 
-@pytest.mark.parametrize("m,k", [(64, 2048), (40, 300), (300, 20000), (1100, 512)])
+@pytest.mark.parametrize("m,k", [(64, 2048), (40, 300), (300, 20000), (1100, 512), (8, 300), (16, 13824)])
 def test_quant_row_max_inside_outlier_columns(m, k):
     """Rows whose largest element below the threshold sits in an outlier column
     (large in another row): the row scale must come from the other columns.
