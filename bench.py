@@ -41,6 +41,11 @@ FP4_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
             for f in ("fp4.hip", "fp4.h", "quant_util.h", "common.h")]
 FP4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp4_traffic.json")
 GEMM_KERNELS = ("i8mp::gemm", "i8mp::gemv")  # kernel-name parts of the fused GEMM launches
+# kernel-name parts of the quantize half (every launch it makes)
+QUANT_KERNELS = ("i8mp::quant", "i8mp::detect", "i8mp::zero_words", "i8mp::cs1", "i8mp::cs2")
+QUANT_SRCS = [os.path.join(ROOT, "int8_mixed_precision_vectorwise_amd", "csrc", f)
+              for f in ("quant.hip", "quant_util.h", "common.h")]
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_traffic.json")
 COPY_MB = 256              # calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -78,6 +83,11 @@ def gemm_alg_bytes(s) -> int:
     return b
 
 
+def quant_alg_bytes(s) -> int:
+    """Bytes of the quantize half alone: x read, codes and row absmax written."""
+    return 2 * s.m * s.k + s.m * s.k + 4 * s.m
+
+
 def _code_only(text: str) -> str:
     """The source without comments and blank lines: what a compiler sees."""
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -88,6 +98,13 @@ def _code_only(text: str) -> str:
 def fp4_src_sha() -> str:
     h = hashlib.sha256()
     for f in FP4_SRCS:
+        h.update(_code_only(open(f).read()).encode())
+    return h.hexdigest()[:16]
+
+
+def quant_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in QUANT_SRCS:
         h.update(_code_only(open(f).read()).encode())
     return h.hexdigest()[:16]
 
@@ -225,10 +242,11 @@ def _per_dispatch(directory: str, folder: str, counter: str, name_part: tuple):
 LAYER_MARK = "FillFunctor"   # the kernel --mode gemm runs after each layer's launches
 
 
-def _per_layer(directory: str, folder: str, counter: str, launches: int):
-    """Counter value per GEMM launch of each layer, from a --mode gemm run: the
-    GEMM dispatches (one or two per launch: a main and a tail launch) between
-    consecutive layer marks, summed and divided by the launches."""
+def _per_layer(directory: str, folder: str, counter: str, launches: int, kernels=GEMM_KERNELS):
+    """Counter value per launch of each layer, from a --mode gemm (or quant)
+    run: the dispatches of `kernels` (several per call: a GEMM's main and tail
+    launches, the quantizer's passes) between consecutive layer marks, summed
+    and divided by the launches."""
     import csv
     import glob
     vals, names = {}, {}
@@ -245,7 +263,7 @@ def _per_layer(directory: str, folder: str, counter: str, launches: int):
             if n:
                 layers.append(cur / launches)
             cur, n = 0.0, 0
-        elif any(p in names[d] for p in GEMM_KERNELS):
+        elif any(p in names[d] for p in kernels):
             cur += vals[d]
             n += 1
     return layers
@@ -310,6 +328,48 @@ def traffic_summary(directory: str, workload: str, launches: int) -> int:
     json.dump(d, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
     print(json.dumps({"workload": workload, "traffic_bytes": round(tot), "layers": layers,
                       "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}))
+    return 0
+
+
+def _copy_scales(directory: str):
+    copy_bytes = COPY_MB * 2**20
+    cr, _ = _read_bytes(directory, "copy_rd", ("elementwise",))
+    cw = _write_bytes(directory, "copy_wr", ("elementwise",))
+    if not cr or not cw:
+        raise SystemExit("no copy-kernel counters found")
+    return copy_bytes / (sum(cr) / len(cr)), copy_bytes / (sum(cw) / len(cw))
+
+
+def quant_traffic_summary(directory: str, workload: str, launches: int) -> int:
+    """Per-call HBM bytes of the quantize half (all of its launches) from the
+    quant_rd / quant_wr folders of --mode quant runs, scaled like the GEMM's by
+    the copy kernel's factors (copy_rd, copy_wr)."""
+    specs, _ = workload_specs(workload)
+    f_scale, w_scale = _copy_scales(directory)
+    n32, n64, n128 = (_per_layer(directory, "quant_rd", c, launches, QUANT_KERNELS) for c in RD_COUNTERS[:3])
+    w64, wall = (_per_layer(directory, "quant_wr", c, launches, QUANT_KERNELS) for c in WR_COUNTERS)
+    if min(len(n32), len(w64)) < len(specs):
+        raise SystemExit(f"expected quantize calls of {len(specs)} layers, got {len(n32)} / {len(w64)}")
+    layers = {}
+    for li, s in enumerate(specs):
+        fb = (32 * n32[li] + 64 * n64[li] + 128 * n128[li]) * f_scale
+        wb = (64 * w64[li] + 32 * (wall[li] - w64[li])) * w_scale
+        layers[s.name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                          "algorithmic_bytes": quant_alg_bytes(s),
+                          "ratio": round((fb + wb) / quant_alg_bytes(s), 3)}
+    try:
+        d = json.load(open(QUANT_TRAFFIC_FILE))
+        if d.get("quant_source_sha") != quant_src_sha():
+            d = {}
+    except (OSError, ValueError):
+        d = {}
+    d["quant_source_sha"] = quant_src_sha()
+    d.setdefault("layers", {})[workload] = layers
+    d["calibration"] = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                        "counters": list(RD_COUNTERS[:3] + WR_COUNTERS)}
+    os.makedirs(os.path.dirname(QUANT_TRAFFIC_FILE), exist_ok=True)
+    json.dump(d, open(QUANT_TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps({"workload": workload, "quant_layers": layers}))
     return 0
 
 
@@ -904,19 +964,24 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode", choices=("on", "off"), default="on",
                     help="with a prefill workload: also measure the 13B decode layers at m = 1, 4, 16")
-    ap.add_argument("--mode", choices=("bench", "gemm", "copy", "dequant", "backward", "fp4"), default="bench",
-                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); copy: calibration copy; "
+    ap.add_argument("--mode", choices=("bench", "gemm", "quant", "copy", "dequant", "backward", "fp4"), default="bench",
+                    help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); quant: only the quantize "
+                         "calls; copy: calibration copy; "
                          "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
                          "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
-    ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / copy")
+    ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / quant / copy")
     ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=2,
                     help="--mode backward: grad_x and grad_w on one stream, or on two")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="write profiles/gemm_mfma.json from a rocprofv3 --pmc output in DIR")
+    ap.add_argument("--quant-traffic-summary", metavar="DIR",
+                    help="write profiles/quant_traffic.json from rocprofv3 --pmc outputs in DIR")
     args = ap.parse_args()
 
+    if args.quant_traffic_summary:
+        return quant_traffic_summary(args.quant_traffic_summary, args.workload, args.launches)
     if args.traffic_summary:
         return traffic_summary(args.traffic_summary, args.workload, args.launches)
     if args.mfma_summary:
@@ -951,6 +1016,17 @@ def main() -> int:
     specs, kind = workload_specs(args.workload)
     cap = args.cap
     sets, copies = prepare_sets(torch, i8, specs, cap, args.rotate_mb, dev)
+
+    if args.mode == "quant":
+        # args.launches quantize calls per layer, each layer followed by a mark
+        for li, s in enumerate(specs):
+            for i in range(args.launches):
+                _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
+                i8.linear_quantize(xc, ws, s.tau)
+            torch.full((1,), li, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "quantize_calls_per_layer": args.launches}))
+        return 0
 
     if args.mode == "gemm":
         # exactly args.launches GEMM launches per layer, layer after layer, each

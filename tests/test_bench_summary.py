@@ -48,3 +48,25 @@ def test_per_layer_groups_split_launches(tmp_path):
     _write(tmp_path, "gemm_x", rows)
     got = bench._per_layer(str(tmp_path), "gemm_x", "C", launches)
     assert got == [120.0, 71.0]
+
+
+def test_per_layer_quant_kernels(tmp_path):
+    """The quantize half's passes (zero, single read, finishing pass) count as one call."""
+    rows, d = [], 0
+
+    def disp(name, value):
+        nonlocal d
+        d += 1
+        rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "C", "Counter_Value": value})
+
+    for i in range(2):
+        disp("i8mp::zero_words_kernel(unsigned int*, long)", 1.0)
+        disp(QUANT, 10.0)
+        disp("void i8mp::quant2_kernel<true>(i8mp::QuantArgs, unsigned int const*)", 3.0)
+    disp(MARK, 0.0)
+    for i in range(2):
+        disp("void i8mp::cs1_kernel<true>(i8mp::QuantArgs, unsigned int*, float*)", 2.0)
+        disp("void i8mp::cs2_kernel<true>(i8mp::QuantArgs, unsigned int const*, float const*, long)", 4.0)
+    disp(MARK, 0.0)
+    _write(tmp_path, "quant_x", rows)
+    assert bench._per_layer(str(tmp_path), "quant_x", "C", 2, bench.QUANT_KERNELS) == [14.0, 6.0]
