@@ -373,6 +373,46 @@ def quant_traffic_summary(directory: str, workload: str, launches: int) -> int:
     return 0
 
 
+STALL_COUNTERS = ("TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "GRBM_GUI_ACTIVE",
+                  "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "TCC_HIT_sum", "TCC_MISS_sum",
+                  "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")
+STALL_FILE = os.path.join(ROOT, "profiles", "gemm_stalls.json")
+
+
+def stall_summary(directory: str, workload: str, launches: int) -> int:
+    """Where the fused GEMM's memory side spends its time, from one rocprofv3
+    --pmc pass with STALL_COUNTERS (folder gemm_stall, ``bench.py --mode gemm``):
+    the texture addresser's busy share (TA_BUSY_avr, the mean over the 256 TA
+    instances, against GRBM_GUI_ACTIVE / 8, the active cycles of one XCD), the
+    share of it stalled by the L1 (TA_ADDR_STALLED_BY_TC_CYCLES summed over the
+    TAs), the mean L1 -> L2 read latency in cycles, the L2 hit rate, and the
+    share of wave cycles spent waiting on LDS instructions."""
+    specs, _ = workload_specs(workload)
+    vals = {c: _per_layer(directory, "gemm_stall", c, launches) for c in STALL_COUNTERS}
+    if any(len(v) < len(specs) for v in vals.values()):
+        raise SystemExit("missing stall counter dispatches")
+    layers = {}
+    for li, s in enumerate(specs):
+        v = {c: x[li] for c, x in vals.items()}
+        xcd_cycles = v["GRBM_GUI_ACTIVE"] / 8
+        layers[s.name] = {
+            "ta_busy": round(v["TA_BUSY_avr"] / xcd_cycles, 4),
+            "ta_stalled_by_l1": round(v["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / N_CUS / xcd_cycles, 4),
+            "l2_read_latency_cycles": round(v["TCP_TCC_READ_REQ_LATENCY_sum"] / max(v["TCP_TCC_READ_REQ_sum"], 1), 1),
+            "l2_hit_rate": round(v["TCC_HIT_sum"] / max(v["TCC_HIT_sum"] + v["TCC_MISS_sum"], 1), 4),
+            "lds_wait_share": round(v["SQ_WAIT_INST_LDS"] / max(v["SQ_WAVE_CYCLES"], 1), 4),
+            "counters": {c: round(x) for c, x in v.items()}}
+    try:
+        d = json.load(open(STALL_FILE))
+    except (OSError, ValueError):
+        d = {}
+    d[workload] = {"gemm_source_sha": src_sha(), "layers": layers}
+    os.makedirs(os.path.dirname(STALL_FILE), exist_ok=True)
+    json.dump(d, open(STALL_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps({"workload": workload, "stalls": layers}))
+    return 0
+
+
 def mfma_summary(directory: str, workload: str, launches: int) -> int:
     """MFMA utilisation of the fused GEMM from a rocprofv3 --pmc pass with
     MFMA_COUNTERS (folder gemm_mfma, ``bench.py --mode gemm``) and the bench line
@@ -976,10 +1016,14 @@ def main() -> int:
                     help="write profiles/gemm_traffic.json from rocprofv3 --pmc outputs in DIR")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="write profiles/gemm_mfma.json from a rocprofv3 --pmc output in DIR")
+    ap.add_argument("--stall-summary", metavar="DIR",
+                    help="write profiles/gemm_stalls.json from a rocprofv3 --pmc output in DIR")
     ap.add_argument("--quant-traffic-summary", metavar="DIR",
                     help="write profiles/quant_traffic.json from rocprofv3 --pmc outputs in DIR")
     args = ap.parse_args()
 
+    if args.stall_summary:
+        return stall_summary(args.stall_summary, args.workload, args.launches)
     if args.quant_traffic_summary:
         return quant_traffic_summary(args.quant_traffic_summary, args.workload, args.launches)
     if args.traffic_summary:
