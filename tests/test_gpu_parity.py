@@ -229,6 +229,10 @@ FWD_CASES = [
     (9, 3000, 200, 33, 1.0, False, TAU, 64),      # past the ring's 32 columns: the rest gathered
     (3, 1024, 4500, 70, 0.5, False, TAU, 128),    # several rows per wave and the gathered outliers
     (1, 96, 70, 96, 1.0, True, TAU, 96),          # every column an outlier, past the stream's 64
+    # the MFMA decode kernel on long rows: column-slice quantizer, four waves per group
+    (8, 13824, 700, 40, 0.5, True, TAU, 16),      # ring + gathered outliers, past cap
+    (16, 8192, 1000, 5, 1.0, False, TAU, 64),     # n not a multiple of 16
+    (16, 5120, 2000, 8, 1.0, True, TAU, 256),     # two waves per group
 ]
 
 
@@ -726,3 +730,26 @@ def test_quant_row_max_inside_outlier_columns(m, k):
     i8.linear_quantize(dev(x), wsp, TAU)
     torch.cuda.synchronize()
     _check_workspace(wsp, x, ref, 1)
+
+
+def test_decode_gemm_repeats():
+    """The decode GEMM half run three times on one quantized workspace gives the
+    same output each time, and the oracle's (nothing in the workspace is
+    consumed by a GEMM launch)."""
+    m, k, n = 12, 13824, 900
+    L = make_inputs(m, k, n, n_outlier=6, bias_std=0.01, seed=(91, m, k), outlier_row_frac=0.7)
+    wq, ws = oracle.quantize_weight(L.w)
+    ref = oracle.linear_forward(L.x, wq, ws, L.bias, TAU)
+    say(f"decode GEMM repeated m={m} k={k} n={n}")
+    xd = dev(L.x)
+    wsp = i8.LinearWorkspace.create(m, n, k, 64, "cuda")
+    i8.linear_quantize(xd, wsp, TAU)
+    outs = []
+    for _ in range(3):
+        out = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        i8.linear_matmul_dequant(xd, wsp, dev(wq), dev(ws), dev(L.bias), out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for out in outs:
+        assert torch.equal(out, outs[0])
+    assert_fp16_close(outs[0], ref.out)
