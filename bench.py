@@ -246,7 +246,8 @@ def _per_layer(directory: str, folder: str, counter: str, launches: int, kernels
     """Counter value per launch of each layer, from a --mode gemm (or quant)
     run: the dispatches of `kernels` (several per call: a GEMM's main and tail
     launches, the quantizer's passes) between consecutive layer marks, summed
-    and divided by the launches."""
+    and divided by the launches.  Dispatches before the first mark (the
+    set-up's weight quantization) are not counted."""
     import csv
     import glob
     vals, names = {}, {}
@@ -257,13 +258,13 @@ def _per_layer(directory: str, folder: str, counter: str, launches: int, kernels
             d = int(r["Dispatch_Id"])
             names[d] = r["Kernel_Name"]
             vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
-    layers, cur, n = [], 0.0, 0
+    layers, cur, n, started = [], 0.0, 0, False
     for d in sorted(vals):
         if LAYER_MARK in names[d]:
             if n:
                 layers.append(cur / launches)
-            cur, n = 0.0, 0
-        elif any(p in names[d] for p in kernels):
+            cur, n, started = 0.0, 0, True
+        elif started and any(p in names[d] for p in kernels):
             cur += vals[d]
             n += 1
     return layers
@@ -1062,7 +1063,8 @@ def main() -> int:
     sets, copies = prepare_sets(torch, i8, specs, cap, args.rotate_mb, dev)
 
     if args.mode == "quant":
-        # args.launches quantize calls per layer, each layer followed by a mark
+        # args.launches quantize calls per layer, each layer between two marks
+        torch.full((1,), -1, dtype=torch.int32, device=dev)
         for li, s in enumerate(specs):
             for i in range(args.launches):
                 _, xc, wqc, wac, b, ws, out = sets[i % copies][li]
@@ -1074,8 +1076,9 @@ def main() -> int:
 
     if args.mode == "gemm":
         # exactly args.launches GEMM launches per layer, layer after layer, each
-        # layer followed by a one-element fill (the mark the counter summaries
+        # layer between two one-element fills (the marks the counter summaries
         # split the dispatches at: a launch may be two kernels)
+        torch.full((1,), -1, dtype=torch.int32, device=dev)
         for li, s in enumerate(specs):
             for i in range(args.launches):
                 _, xc, wqc, wac, b, ws, out = sets[i % copies][li]

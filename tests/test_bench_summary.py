@@ -59,6 +59,8 @@ def test_per_layer_quant_kernels(tmp_path):
         d += 1
         rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "C", "Counter_Value": value})
 
+    disp("void i8mp::quant_kernel<true, false, 4>(i8mp::QuantArgs)", 99.0)   # set-up: not counted
+    disp(MARK, 0.0)
     for i in range(2):
         disp("i8mp::zero_words_kernel(unsigned int*, long)", 1.0)
         disp(QUANT, 10.0)
