@@ -706,6 +706,63 @@ def backward_run(args) -> int:
     return 0
 
 
+def fp4_counter_run(args) -> int:
+    """--mode fp4gemv: args.launches 4-bit decode linears per layer of a decode
+    workload, each layer between two marks (for rocprofv3 --pmc runs)."""
+    import torch
+    import int8_mixed_precision_vectorwise_amd as i8
+    from synth import make_layer
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs, kind = workload_specs(args.workload)
+    if kind != "decode":
+        raise SystemExit("--mode fp4gemv takes a decode workload (llama13b_decode_m1, _m4, _m16)")
+    layers = []
+    for s in specs:
+        L = make_layer(s)
+        fw = i8.fp4_quantize(torch.from_numpy(L.w).to(dev), double_quant=True)
+        fws = [fw, i8.Fp4Weight(fw.codes.clone(), fw.k, None, fw.c8.clone(), fw.s2.clone())]
+        out = torch.empty((s.m, s.n), dtype=torch.float16, device=dev)
+        layers.append((s, torch.from_numpy(L.x).to(dev), fws, out))
+    torch.cuda.synchronize()
+    torch.full((1,), -1, dtype=torch.int32, device=dev)
+    for li, (s, x, fws, out) in enumerate(layers):
+        for i in range(args.launches):
+            i8.fp4_linear(x, fws[i % 2], None, out)
+        torch.full((1,), li, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": args.workload, "fp4_launches_per_layer": args.launches}))
+    return 0
+
+
+def fp4_traffic_summary(directory: str, workload: str, launches: int) -> int:
+    """Per-launch HBM bytes of the 4-bit decode linear from the fp4_rd / fp4_wr
+    folders of --mode fp4gemv runs, counted and scaled as the GEMM's (copy_rd,
+    copy_wr give the factors)."""
+    specs, _ = workload_specs(workload)
+    f_scale, w_scale = _copy_scales(directory)
+    k4 = ("i8mp::fp4_gemv",)
+    n32, n64, n128 = (_per_layer(directory, "fp4_rd", c, launches, k4) for c in RD_COUNTERS[:3])
+    w64, wall = (_per_layer(directory, "fp4_wr", c, launches, k4) for c in WR_COUNTERS)
+    if min(len(n32), len(w64)) < len(specs):
+        raise SystemExit(f"expected 4-bit launches of {len(specs)} layers, got {len(n32)} / {len(w64)}")
+    per_launch = {}
+    tot = 0.0
+    for li, s in enumerate(specs):
+        fb = (32 * n32[li] + 64 * n64[li] + 128 * n128[li]) * f_scale
+        wb = (64 * w64[li] + 32 * (wall[li] - w64[li])) * w_scale
+        per_launch[s.name] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
+        tot += fb + wb
+    d = {"fp4_source_sha": fp4_src_sha(), "workload": workload,
+         "calibration": {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                         "counters": list(RD_COUNTERS[:3] + WR_COUNTERS)},
+         "per_launch": per_launch, "per_step_bytes": {workload: round(tot)}}
+    os.makedirs(os.path.dirname(FP4_TRAFFIC_FILE), exist_ok=True)
+    json.dump(d, open(FP4_TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps(d))
+    return 0
+
+
 def fp4_run(args) -> int:
     """The 4-bit (FP4 E2M1, double-quantized block scales) decode linear over
     a decode workload's layers (the same shapes as the int8 decode workload);
@@ -1005,11 +1062,13 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode", choices=("on", "off"), default="on",
                     help="with a prefill workload: also measure the 13B decode layers at m = 1, 4, 16")
-    ap.add_argument("--mode", choices=("bench", "gemm", "quant", "copy", "dequant", "backward", "fp4"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "gemm", "quant", "copy", "dequant", "backward", "fp4", "fp4gemv"),
+                    default="bench",
                     help="gemm: only the fused GEMM launches (for rocprofv3 --pmc); quant: only the quantize "
                          "calls; copy: calibration copy; "
                          "dequant: the int8 dequantize op on a 65B weight; backward: both gradients of "
-                         "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload")
+                         "every layer of a prefill workload; fp4: the 4-bit decode linear on a decode workload; "
+                         "fp4gemv: only its launches (for rocprofv3 --pmc)")
     ap.add_argument("--launches", type=int, default=20, help="launches per layer in --mode gemm / quant / copy")
     ap.add_argument("--bwd-streams", type=int, choices=(1, 2), default=2,
                     help="--mode backward: grad_x and grad_w on one stream, or on two")
@@ -1019,12 +1078,16 @@ def main() -> int:
                     help="write profiles/gemm_mfma.json from a rocprofv3 --pmc output in DIR")
     ap.add_argument("--stall-summary", metavar="DIR",
                     help="write profiles/gemm_stalls.json from a rocprofv3 --pmc output in DIR")
+    ap.add_argument("--fp4-traffic-summary", metavar="DIR",
+                    help="write profiles/fp4_traffic.json from rocprofv3 --pmc outputs in DIR")
     ap.add_argument("--quant-traffic-summary", metavar="DIR",
                     help="write profiles/quant_traffic.json from rocprofv3 --pmc outputs in DIR")
     args = ap.parse_args()
 
     if args.stall_summary:
         return stall_summary(args.stall_summary, args.workload, args.launches)
+    if args.fp4_traffic_summary:
+        return fp4_traffic_summary(args.fp4_traffic_summary, args.workload, args.launches)
     if args.quant_traffic_summary:
         return quant_traffic_summary(args.quant_traffic_summary, args.workload, args.launches)
     if args.traffic_summary:
@@ -1054,6 +1117,8 @@ def main() -> int:
         return dequant_run(args.steps, args.warmup)
     if args.mode == "backward":
         return backward_run(args)
+    if args.mode == "fp4gemv":
+        return fp4_counter_run(args)
     if args.mode == "fp4":
         return fp4_run(args)
     dev = torch.device("cuda:0")
