@@ -741,7 +741,7 @@ def fp4_traffic_summary(directory: str, workload: str, launches: int) -> int:
     copy_wr give the factors)."""
     specs, _ = workload_specs(workload)
     f_scale, w_scale = _copy_scales(directory)
-    k4 = ("i8mp::fp4_gemv",)
+    k4 = ("fp4_gemv_kernel",)
     n32, n64, n128 = (_per_layer(directory, "fp4_rd", c, launches, k4) for c in RD_COUNTERS[:3])
     w64, wall = (_per_layer(directory, "fp4_wr", c, launches, k4) for c in WR_COUNTERS)
     if min(len(n32), len(w64)) < len(specs):
