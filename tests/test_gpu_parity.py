@@ -536,8 +536,12 @@ def test_non_default_stream():
     assert_fp16_close(out, ref.out)
 
 
-@pytest.mark.parametrize("m", [128, 2])
+@pytest.mark.parametrize("m", [128, 2, 8, 1100])
 def test_graph_capture_replays_match_eager(m):
+    """m = 2: the one-launch GEMV forward; 8: the column-slice quantizer and the
+    MFMA decode kernel; 128: detection + quantization launches; 1100: the
+    single read of x (bitmap clearing, atomics into the partial bitmaps).
+    Every replay runs on a workspace filled with garbage first."""
     L = make_inputs(m, 1024, 512, n_outlier=5, bias_std=0.01, seed=(81, m, 0))
     wq, ws = oracle.quantize_weight(L.w)
     x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
