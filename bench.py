@@ -657,7 +657,7 @@ def backward_run(args) -> int:
     achieved = ops / g_time / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_OPS / 1e12, "unit": "TFLOP/s",
             "frac": round(achieved / (PEAK_INT8_OPS / 1e12), 4), "traffic": None,
-            "kernel": "fused int8 GEMM + dequant epilogue (gemm_dtl_kernel), grad_x and grad_w launches",
+            "kernel": "fused int8 GEMM + dequant epilogue (gemm_pp_kernel / gemm_dtl_kernel by shape), grad_x and grad_w launches",
             "per_launch_us": {k: round(v, 3) for k, v in gemm_us.items()},
             "timing": "HIP events around graph replays of each gradient GEMM's launches"}
 
