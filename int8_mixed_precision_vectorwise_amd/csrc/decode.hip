@@ -892,7 +892,8 @@ hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStre
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
     // waves per 16-row group: enough K splits that each wave has a long run of
-    // 128-byte chunks, with all groups resident at once (two workgroups per CU)
+    // 128-byte chunks; fewer where that would put more than two workgroups on
+    // each CU and leave the runs short
     const int64_t groups = (g.n + kRows - 1) / kRows;
     const int64_t nchunks = (g.k + kChunk - 1) / kChunk;
     int gsplit = 1;
