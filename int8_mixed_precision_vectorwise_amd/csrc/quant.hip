@@ -525,6 +525,7 @@ __global__ __launch_bounds__(256) void quant2_kernel(QuantArgs a, const uint32_t
 // Thread t holds chunk t % 32 (8 columns) of rows t / 32 and t / 32 + 8.
 constexpr int kCsRows = 16;
 constexpr int kCsCols = 256;
+constexpr int kCsBatch = 8;   // slices per lane whose scratch loads cs2 issues together
 
 template <bool kVec>
 __device__ inline void cs_load(const QuantArgs& a, uint4 (&v)[2], int rl, int64_t col) {
@@ -583,21 +584,48 @@ __global__ __launch_bounds__(256) void cs2_kernel(QuantArgs a, const uint32_t* _
     __shared__ float s_row[kCsRows];
     __shared__ uint32_t sb[kCsCols / 32];
     __shared__ int32_t wsum[2][4];
-    // row absmax: 16 lanes per row over the slices
+    // Every global load of the scratch is issued before the first is used:
+    // the slice maxima (16 lanes per row) and the bitmap words (for the
+    // popcounts) of up to kCsBatch * 16 slices.  Indexes past the end are
+    // clamped to the last entry: a repeated maximum changes nothing, and a
+    // repeated word is not counted.
+    const int64_t w0 = (int64_t)blockIdx.x * (kCsCols / 32);
+    const int64_t r16 = tid >> 4;
+    const int u = tid & 15;
+    const int64_t rr = r16 < a.m ? r16 : a.m - 1;
+    float pv[kCsBatch];
+    uint32_t wv[kCsBatch / 2];
+#pragma unroll
+    for (int i = 0; i < kCsBatch; ++i) {
+        const int64_t sl = u + 16 * i;
+        pv[i] = spart[(sl < nslices ? sl : nslices - 1) * a.m + rr];
+    }
+#pragma unroll
+    for (int i = 0; i < kCsBatch / 2; ++i) {
+        const int64_t w = tid + 256 * i;
+        wv[i] = sbits[w < a.words ? w : a.words - 1];
+    }
+    if (tid < kCsCols / 32) sb[tid] = w0 + tid < a.words ? sbits[w0 + tid] : 0u;
+    // row absmax
     {
-        const int64_t r = tid >> 4;
-        const int u = tid & 15;
         float pm = 0.0f;
-        if (r < a.m)
-            for (int64_t sl = u; sl < nslices; sl += 16) pm = fmaxf(pm, spart[sl * a.m + r]);
+#pragma unroll
+        for (int i = 0; i < kCsBatch; ++i) pm = fmaxf(pm, pv[i]);
+        for (int64_t sl = u + 16 * kCsBatch; sl < nslices; sl += 16) pm = fmaxf(pm, spart[sl * a.m + rr]);
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) pm = fmaxf(pm, __shfl_xor(pm, off, 64));
-        if (u == 0 && r < kCsRows) s_row[r] = pm;
+        if (u == 0 && r16 < a.m) s_row[r16] = pm;
     }
     // outlier columns before this slice, and in all
-    const int64_t w0 = (int64_t)blockIdx.x * (kCsCols / 32);
     int32_t before = 0, tot = 0;
-    for (int64_t w = tid; w < a.words; w += 256) {
+#pragma unroll
+    for (int i = 0; i < kCsBatch / 2; ++i) {
+        const int64_t w = tid + 256 * i;
+        const int32_t p = w < a.words ? __popc(wv[i]) : 0;
+        tot += p;
+        before += w < w0 ? p : 0;
+    }
+    for (int64_t w = tid + 256 * (kCsBatch / 2); w < a.words; w += 256) {
         const int32_t p = __popc(sbits[w]);
         tot += p;
         before += w < w0 ? p : 0;
@@ -608,7 +636,6 @@ __global__ __launch_bounds__(256) void cs2_kernel(QuantArgs a, const uint32_t* _
         wsum[0][wave] = before;
         wsum[1][wave] = tot;
     }
-    if (tid < kCsCols / 32) sb[tid] = w0 + tid < a.words ? sbits[w0 + tid] : 0u;
     __syncthreads();
     const int32_t base = wsum[0][0] + wsum[0][1] + wsum[0][2] + wsum[0][3];
     const int32_t total = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
