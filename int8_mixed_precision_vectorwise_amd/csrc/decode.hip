@@ -10,11 +10,15 @@
 //    p+2G, ...  A workgroup of 4 waves holds 4/G groups; G is chosen so that
 //    each wave streams a long run of chunks and the grid fits the CUs in one
 //    round.
-//  * Each wave streams its weight chunks through a private ring of kStages
-//    LDS stages with buffer_load ... lds (16 bytes per lane, whole 128-byte
-//    lines, 2 KB per stage).  The matching activation fragments (m <= 16 rows,
-//    L2-resident) go to a ring of registers.  The rings are private, so a
-//    wave only waits for its own loads (s_waitcnt vmcnt), never for a
+//  * Each wave streams its chunks through a private ring of kStages LDS
+//    stages with buffer_load ... lds (16 bytes per lane, eight lanes per
+//    whole 128-byte line): the weight rows' chunk (2 KB) and the matching
+//    chunk of the m <= 16 activation rows (2 KB, L2-resident).  Loaded
+//    straight into the MFMA fragment layout, the activations would put four
+//    rows, four cache lines, under every four lanes; the L1 then spends about
+//    four times the cycles of whole-line requests on them, and with two
+//    workgroups on a CU that alone bounded the stream.  The ring is private,
+//    so a wave only waits for its own loads (s_waitcnt vmcnt), never for a
 //    barrier; kStages - 1 chunks stay in flight.
 //  * The G partial 16x16 int32 blocks of a group are summed through LDS and
 //    the group's first wave runs the fused epilogue: row / column absmax, the
@@ -34,7 +38,8 @@ constexpr int kRows = 16;     // weight rows per group
 constexpr int kWaves = 4;     // waves per workgroup
 constexpr int kStages = 4;    // per-wave ring depth
 constexpr int kChunk = 128;   // K bytes per stage
-constexpr int kStageBytes = kRows * kChunk;  // weight rows only
+constexpr int kHalfBytes = kRows * kChunk;       // one operand's chunk
+constexpr int kStageBytes = 2 * kHalfBytes;       // weight rows, then activation rows
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kDecOutl = 32;  // outlier columns the MFMA decode kernel takes from its ring
 
@@ -49,11 +54,13 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
 }
 
 // 16 bytes per lane global -> LDS; the weight is streamed once per call, so
-// its loads carry the nt (non-temporal) cache policy
+// its loads carry the nt (non-temporal) cache policy, while the activations,
+// read by every group, keep the default one
 constexpr int kWeightPolicy = 2;
+template <int kPolicy>
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t src, int8_t* lds, int voffset, int soffset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                             soffset, 0, kWeightPolicy);
+                                             soffset, 0, kPolicy);
 }
 
 // 128-byte LDS rows; lanes 0-15 of a fragment read rows 0-15 at one 16-byte
@@ -86,23 +93,22 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rx = rsrc(g.a, (g.m - 1) * g.lda + kr);
     const __amdgpu_buffer_rsrc_t r_none = rsrc(g.a, 0);
 
-    // DMA lane mapping: instruction j covers weight rows 8j .. 8j+7 (1 KB);
-    // lane i -> row 8j + i/8, LDS slot i%8, which holds global chunk
-    // slot ^ ((row>>1)&7).  Activation fragment of lane l: row l%16, the 32
-    // bytes at (l/16)*32 of the chunk (two 16-byte loads, one per MFMA).
-    int w_off[2];
+    // DMA lane mapping, the same for both operands: instruction j covers rows
+    // 8j .. 8j+7 (1 KB); lane i -> row 8j + i/8, LDS slot i%8, which holds
+    // global chunk slot ^ ((row>>1)&7).  Rows of the activations past m lie
+    // past their range and read zeros.
+    int w_off[2], a_off[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = 8 * j + (lane >> 3);
         const int gchunk = (lane & 7) ^ ((row >> 1) & 7);
         w_off[j] = (int)(row * g.ldb + gchunk * 16);
+        a_off[j] = (int)(row * g.lda + gchunk * 16);
     }
-    const int x_off = (int)((lane & 15) * g.lda + (lane >> 4) * 32);
     int8_t* my_ring = ring + wid * kStages * kStageBytes;
     const int64_t nchunks = kr / kChunk;
     const int64_t mine = (active && nchunks > part) ? (nchunks - part + G - 1) / G : 0;
-    v4i_t xr[kStages][2];
-    // every chunk issues 4 loads (2 weight DMA, 2 activation); past this
+    // every chunk issues 4 loads (2 weight DMA, 2 activation DMA); past this
     // wave's last chunk they read nothing (zero-length range)
     auto issue = [&](int64_t j, int slot) {
         const bool real = j < mine;
@@ -110,10 +116,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         int8_t* st = my_ring + slot * kStageBytes;
         const __amdgpu_buffer_rsrc_t sw = real ? rw : r_none;
         const __amdgpu_buffer_rsrc_t sx = real ? rx : r_none;
-        dma16(sw, st, w_off[0] + kb, 0);
-        dma16(sw, st + 1024, w_off[1] + kb, 0);
-        xr[slot][0] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off + kb, 0, 0));
-        xr[slot][1] = __builtin_bit_cast(v4i_t, __builtin_amdgcn_raw_buffer_load_b128(sx, x_off + 16 + kb, 0, 0));
+        dma16<kWeightPolicy>(sw, st, w_off[0] + kb, 0);
+        dma16<kWeightPolicy>(sw, st + 1024, w_off[1] + kb, 0);
+        dma16<0>(sx, st + kHalfBytes, a_off[0] + kb, 0);
+        dma16<0>(sx, st + kHalfBytes + 1024, a_off[1] + kb, 0);
     };
 
     v4i_t acc = {0, 0, 0, 0};
@@ -164,16 +170,20 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             __builtin_amdgcn_s_waitcnt(0x0f70 | (((kStages - 2) * 4) & 15) | ((((kStages - 2) * 4) >> 4) << 14));
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const int8_t* st = my_ring + u * kStageBytes;
-            v4i_t wf[2];
+            // fragments of lane l: row l % 16, the 32 bytes at 32 (l / 16) of
+            // the chunk in both operands (one 16-byte piece per MFMA)
+            v4i_t wf[2], af[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) wf[t] = *reinterpret_cast<const v4i_t*>(st + swz(row, (lane >> 4) * 2 + t));
+            for (int t = 0; t < 2; ++t) {
+                wf[t] = *reinterpret_cast<const v4i_t*>(st + swz(row, (lane >> 4) * 2 + t));
+                af[t] = *reinterpret_cast<const v4i_t*>(st + kHalfBytes + swz(row, (lane >> 4) * 2 + t));
+            }
             if constexpr (kFused)
                 if (j0 + u < mine) take_outliers(part + (j0 + u) * G, st);
-            const v4i_t x0 = xr[u][0], x1 = xr[u][1];
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             issue(j0 + u + kStages - 1, (u + kStages - 1) % kStages);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, wf[0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, wf[1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0], wf[0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1], wf[1], acc, 0, 0, 0);
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // no DMA left in flight into the ring
