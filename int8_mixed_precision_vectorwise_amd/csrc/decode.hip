@@ -123,8 +123,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     };
 
     v4i_t acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < kStages - 1; ++j) issue(j, j);
     const int row = lane & 15;
 
     // The first kDecOutl outlier columns (ascending) are taken from the ring
@@ -137,16 +135,53 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     int64_t ocol = INT64_MAX;
     int ocol_lane = 0x7fffffff;  // lane s: column of slot s
     v4f_t p = {0.0f, 0.0f, 0.0f, 0.0f};
+    // The ring's outlier operands are loaded before the stream's first chunks
+    // (vector loads complete in order, so waiting for them then does not wait
+    // for the weight): the first index entries and X_O values, bounded by the
+    // lengths of their arrays rather than by the count, which arrives with
+    // them; slots past the count are dropped afterwards.  Unconditional
+    // buffer loads (zeros out of range) keep the waits for them in one place.
+    constexpr int kXoPer = kRows * kDecOutl / 256;
+    int32_t cnt_raw = 0;
+    uint32_t idx_raw = 0;
+    uint16_t xo_raw[kXoPer];
     if constexpr (kFused) {
-        if (g.count) cnt = outlier_count(g, *g.count);
-        n_ring = cnt < kDecOutl ? cnt : kDecOutl;
-        for (int t = threadIdx.x; t < kRows * kDecOutl; t += 256) {
-            const int r = t / kDecOutl, s2 = t % kDecOutl;
-            xo[t] = (r < g.m && s2 < n_ring) ? outlier_x(g, r, s2) : 0.0f;
+        const int lim = (g.count && g.cap > 0) ? (g.cap < kDecOutl ? g.cap : kDecOutl) : 0;
+        // the range is X_O's whole extent, rounded up to a dword (the range
+        // check is per dword)
+        const __amdgpu_buffer_rsrc_t rxo = rsrc(g.x_out, lim > 0 ? (g.m * g.ldo * 2 + 3) & ~(int64_t)3 : 0);
+#pragma unroll
+        for (int i = 0; i < kXoPer; ++i) {
+            const int t = threadIdx.x + 256 * i, r = t / kDecOutl, s2 = t % kDecOutl;
+            // byte offsets < 2^31: at most 16 rows of a short X_O row
+            const int off = (r < g.m && s2 < lim) ? (int)((r * g.ldo + s2) * 2) : (int)0x80000000;
+            xo_raw[i] = __builtin_amdgcn_raw_buffer_load_b16(rxo, off, 0, 0);
         }
-        if (lane < n_ring) ocol_lane = g.idx[lane];
+        const int ilim = g.count ? (g.idx_len < kDecOutl ? g.idx_len : kDecOutl) : 0;
+        const __amdgpu_buffer_rsrc_t ridx = rsrc(g.idx, (int64_t)ilim * 4);
+        idx_raw = __builtin_amdgcn_raw_buffer_load_b32(ridx, lane < ilim ? lane * 4 : (int)0x80000000, 0, 0);
+        if (g.count) cnt_raw = *g.count;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j) issue(j, j);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (kFused) {
+        if (g.count) cnt = outlier_count(g, cnt_raw);
+        n_ring = cnt < kDecOutl ? cnt : kDecOutl;
+#pragma unroll
+        for (int i = 0; i < kXoPer; ++i) {
+            const int t = threadIdx.x + 256 * i, r = t / kDecOutl, s2 = t % kDecOutl;
+            xo[t] = (r < g.m && s2 < n_ring) ? (s2 < g.cap ? h2f(xo_raw[i]) : outlier_x(g, r, s2)) : 0.0f;
+        }
+        if (lane < n_ring) ocol_lane = (int)idx_raw;
         if (n_ring > 0) ocol = __builtin_amdgcn_readfirstlane(ocol_lane);
-        __syncthreads();
+        // this wave's LDS writes done, then s_barrier; a memory fence would
+        // also wait for the ring's DMA, which must stay in flight
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     const int arow0 = 4 * (lane >> 4);
     auto take_outliers = [&](int64_t chunk, const int8_t* st) {
