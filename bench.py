@@ -1020,7 +1020,7 @@ def gemm_roofline(specs, gemm_us, workload):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
     roof["kernel"] = ("fused int8 GEMM + dequant epilogue, the GEMM half of the linear run alone "
-                      "(gemm_pp_kernel / gemm_dtl_kernel for prefill; gemv_kernel for m <= 4, "
+                      "(gemm_pp_kernel / gemm_dtl_kernel for prefill; gemv_kernel for m <= 2, "
                       "gemm_decode_kernel for m <= 16)")
     roof["per_launch_us"] = {k: round(v, 3) for k, v in gemm_us.items()}
     roof["timing"] = "HIP events around graph replays of the layer's GEMM launches"

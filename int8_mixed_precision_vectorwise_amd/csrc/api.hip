@@ -383,7 +383,7 @@ i8mp_status enqueue_forward(const void* x, int64_t m, int64_t k, int64_t ldx, co
                             const float* w_absmax, int64_t n, const void* bias, float threshold, int32_t cap,
                             void* out, int64_t ldout, const i8mp_linear_workspace& L, char* ws,
                             hipStream_t stream) {
-    // one to four rows: quantization inside the GEMV's workgroups, one launch
+    // one or two rows: quantization inside the GEMV's workgroups, one launch
     const QuantArgs qa = forward_quant_args(x, m, k, ldx, threshold, cap, L, ws);
     const GemmArgs g = forward_gemm_args(L, ws, x, ldx, m, k, cap, w_q, ldw, w_absmax, n, bias, out, ldout);
     if (decode_forward_fits(qa, g)) return launched(launch_decode_forward(qa, g, stream));

@@ -98,7 +98,7 @@ hipError_t launch_gemm_i32(const GemmArgs& g, hipStream_t stream);
 // m <= 16, 16-byte aligned operands, A covering whole 128-byte K chunks
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream);
 hipError_t launch_gemm_fused(const GemmArgs& g, hipStream_t stream);
-// The whole forward of one to four rows in one launch (quantization inside the
+// The whole forward of one or two rows in one launch (quantization inside the
 // GEMV's workgroups); qa / g as for launch_quantize / launch_gemm_fused with the
 // same workspace.  Only where decode_forward_fits.
 bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g);

@@ -289,8 +289,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// m <= 4: a dot-product GEMV on the vector ALUs.  With one to four activation
-// rows the matrix cores would idle over zero padding.  The int8 activations
+// m <= 2: a dot-product GEMV on the vector ALUs.  With one or two activation
+// rows the matrix cores would idle over zero padding.  (From three rows on
+// the MFMA decode kernel above streams the weight faster: 13B up at m = 4
+// took 20.4 us here and takes 16.1 us there.)  The int8 activations
 // sit in LDS (rows of kx = K rounded up to 1 KB, zeros past K), and each wave
 // reads R weight rows front to back, one row after the other: a load is one
 // row's next 1 KB of K (lane i: bytes 16 i .. 16 i + 15).  Wave v of the nw
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 // 0 runs the fused epilogue.
 //
 // The whole forward in one launch (kQuantL > 0): every workgroup holds all
-// of the one to four rows of x, so it runs the quantizer's steps itself and
+// of the one or two rows of x, so it runs the quantizer's steps itself and
 // no grid-wide step separates them.  x sits in registers (kQuantL 8-column
 // chunks per thread); chunk maxima come from packed fp16 maxima; a chunk
 // reaching the threshold sets its outlier bits in an LDS bitmap; the row
@@ -357,7 +359,7 @@ __device__ inline void load_x_chunks(const QuantArgs& a, uint4 (&v)[L]) {
 #pragma unroll
         for (int r = 0; r < M; ++r) {
             const int32_t c = tid + T * q;
-            // byte offsets < 2^31: m <= 4 rows of at most I8MP_MAX_LD elements
+            // byte offsets < 2^31: m <= 2 rows of at most I8MP_MAX_LD elements
             const int off = (c < cpr && r < a.m) ? (int)(((int64_t)r * a.ldx + (int64_t)c * 8) * 2) : (int)0x80000000;
             v[q * M + r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
@@ -879,11 +881,10 @@ size_t gemv_lds(int64_t m_pad, int64_t k, int64_t words, int W, bool quant) {
     return lds;
 }
 
-// m <= 4 with the activations in at most 32 KB of LDS (above that, at m = 4
-// and K = 13824, the MFMA kernel measured faster)
+// m <= 2 with the activations in at most 32 KB of LDS
 bool gemv_fits(const GemmArgs& g) {
     const int64_t kx = (g.k + kGvChunk - 1) / kGvChunk * kGvChunk;
-    return g.m >= 1 && g.m <= 4 && (g.m > 2 ? 4 : g.m) * kx <= 32 * 1024;
+    return g.m >= 1 && g.m <= 2 && g.m * kx <= 32 * 1024;
 }
 
 template <int M, bool kFused, int kQuantL, int W>
@@ -900,8 +901,7 @@ template <bool kFused>
 hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
     const QuantArgs none{};
     if (g.m == 1) return launch_gemv_m<1, kFused, 0, 4>(g, none, stream);
-    if (g.m == 2) return launch_gemv_m<2, kFused, 0, 4>(g, none, stream);
-    return launch_gemv_m<4, kFused, 0, 4>(g, none, stream);
+    return launch_gemv_m<2, kFused, 0, 4>(g, none, stream);
 }
 
 // 8-wave workgroups: x is quantized by 512 threads, at most 8 chunks each
@@ -919,9 +919,8 @@ bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g) {
     const bool w_aligned = ((g.ldb & 15) == 0) && ((reinterpret_cast<uintptr_t>(g.b) & 15) == 0);
     // whole 16-byte chunks of x: k and ldx multiples of 8, x 16-byte aligned
     const bool x_vec = ((qa.k & 7) == 0) && ((qa.ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(qa.x) & 15) == 0);
-    // at most 8 chunks of x per thread of 512 (chunk-major over the padded rows)
-    const int64_t m_pad = qa.m > 2 ? 4 : qa.m;
-    const bool x_regs = m_pad * ((qa.k / 8 + 511) / 512) <= 8;
+    // at most 8 chunks of x per thread of 512 (chunk-major over the rows)
+    const bool x_regs = qa.m * ((qa.k / 8 + 511) / 512) <= 8;
     // the codes are copied from the LDS rows in 16-byte units
     const bool q_rows = qa.q && qa.kpad == qa.ldq && (qa.ldq & 15) == 0 &&
                         ((reinterpret_cast<uintptr_t>(qa.q) & 15) == 0);
@@ -930,8 +929,7 @@ bool decode_forward_fits(const QuantArgs& qa, const GemmArgs& g) {
 
 hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStream_t stream) {
     if (g.m == 1) return launch_forward_m<1>(qa, g, stream);
-    if (g.m == 2) return launch_forward_m<2>(qa, g, stream);
-    return launch_forward_m<4>(qa, g, stream);
+    return launch_forward_m<2>(qa, g, stream);
 }
 
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {

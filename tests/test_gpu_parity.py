@@ -213,19 +213,20 @@ FWD_CASES = [
     # 256 x 256 tiles over whole rounds, then the remaining columns in a second launch
     (2048, 512, 9000, 9, 0.5, True, TAU, 64),     # tail of 128 x 64 tiles: bias and outliers offset
     (2100, 512, 9000, 30, 0.5, False, TAU, 64),   # tail of 128 x 128 tiles, ragged m, slots past 16
-    # m <= 4: the dot-product GEMV (outliers taken from the weight stream)
+    # m <= 2: the dot-product GEMV (outliers taken from the weight stream)
     (1, 1000, 77, 3, 1.0, True, TAU, 16),         # unaligned k and n
     (2, 4096, 264, 5, 0.5, False, TAU, 32),
-    (3, 2000, 130, 9, 1.0, True, TAU, 32),
-    (4, 8192, 600, 8, 1.0, False, TAU, 256),      # the largest K the GEMV takes at m = 4
     (1, 13824, 1024, 70, 0.5, True, TAU, 128),    # more outlier columns than the stream handles
     (2, 640, 2048, 0, 1.0, False, TAU, 8),        # no outliers
     (2, 512, 96, 0, 1.0, True, 0.0, 8),           # threshold off
     (1, 2048, 5000, 3, 1.0, True, TAU, 16),       # three weight rows per wave, the last wave short
     (2, 16384, 256, 10, 1.0, True, TAU, 64),      # the one-launch forward's most chunks per thread at m = 2
     (1, 32768, 128, 12, 0.5, False, TAU, 64),     # ... and at m = 1 (32 KB of activations)
-    # 5 <= m <= 16, or m <= 4 past the GEMV's LDS: the MFMA decode kernel (outliers from its ring)
+    # 3 <= m <= 16, or m <= 2 past the GEMV's LDS: the MFMA decode kernel (outliers from its ring)
+    (3, 2000, 130, 9, 1.0, True, TAU, 32),        # k not a multiple of 128, n of 16
+    (4, 8192, 600, 8, 1.0, False, TAU, 256),
     (4, 13824, 300, 12, 0.5, True, TAU, 64),
+    (2, 16512, 200, 6, 1.0, True, TAU, 32),       # m = 2 one chunk past the GEMV's 32 KB
     (9, 3000, 200, 33, 1.0, False, TAU, 64),      # past the ring's 32 columns: the rest gathered
     (3, 1024, 4500, 70, 0.5, False, TAU, 128),    # several rows per wave and the gathered outliers
     (1, 96, 70, 96, 1.0, True, TAU, 96),          # every column an outlier, past the stream's 64
@@ -325,11 +326,13 @@ PAST_CAP_CASES = [
     (768, 250, 6144, 20, 0.5, True, 5),       # register-staged kernel (unaligned weight rows)
     (40, 2100, 300, 5, 1.0, True, 2),         # two K pipelines
     (1, 4096, 300, 70, 0.5, True, 8),         # one-launch GEMV forward, past the stream's 64 columns
-    (3, 2000, 130, 9, 1.0, False, 4),         # one-launch GEMV forward, m = 3
-    (4, 8192, 200, 70, 1.0, False, 0),        # one-launch GEMV forward, no gathered columns
+    (2, 2000, 130, 9, 1.0, False, 4),         # one-launch GEMV forward, m = 2
+    (2, 8192, 200, 70, 1.0, False, 0),        # one-launch GEMV forward, no gathered columns
+    (3, 2000, 130, 9, 1.0, False, 4),         # MFMA decode kernel, m = 3
+    (4, 8192, 200, 70, 1.0, False, 0),        # MFMA decode kernel, every column past the ring gathered
     (9, 3000, 200, 33, 1.0, True, 4),         # MFMA decode kernel: ring 32, then gathered
     (16, 1024, 256, 40, 0.5, False, 0),       # MFMA decode kernel, no gathered columns
-    (4, 13824, 300, 12, 0.5, True, 2),        # m <= 4 past the GEMV's LDS: MFMA decode kernel
+    (4, 13824, 300, 12, 0.5, True, 2),        # MFMA decode kernel, four waves per group
 ]
 
 
@@ -349,7 +352,7 @@ def test_linear_forward_past_cap(case):
 @pytest.mark.parametrize("case", [(2, 4096, 264, 40, 4), (3, 2000, 130, 70, 0), (12, 3000, 200, 45, 8),
                                   (520, 300, 1000, 30, 3)], ids=lambda c: "m%d_k%d_n%d_o%d_c%d" % c)
 def test_two_launch_forward_past_cap(case):
-    """linear_quantize + linear_matmul_dequant (the GEMV of m <= 4 reading the
+    """linear_quantize + linear_matmul_dequant (the GEMV of m <= 2 reading the
     workspace codes, the MFMA decode kernel, a prefill tile) past cap."""
     m, k, n, o, cap = case
     L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01, seed=(78, 1, m), outlier_row_frac=0.5)
@@ -374,8 +377,9 @@ def _workspace_state(wsp):
 @pytest.mark.parametrize("m,k,n,o,cap", [(1, 5120, 384, 8, 256), (2, 4096, 264, 5, 32), (3, 2000, 130, 9, 4),
                                          (4, 8192, 200, 70, 128), (4, 5120, 256, 0, 8), (1, 64, 16, 40, 16)])
 def test_decode_forward_matches_two_launches(m, k, n, o, cap):
-    """One to four rows: the one-launch forward (quantization inside the GEMV)
-    leaves the workspace and the output of quantize + matmul_dequant, bit for bit."""
+    """One or two rows: the one-launch forward (quantization inside the GEMV)
+    leaves the workspace and the output of quantize + matmul_dequant, bit for
+    bit.  Three and four rows take the two launches either way."""
     L = make_inputs(m, k, n, n_outlier=o, bias_std=0.01, seed=(82, m, k), outlier_row_frac=0.5)
     wq, ws = oracle.quantize_weight(L.w)
     x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
@@ -398,7 +402,7 @@ def test_decode_forward_matches_two_launches(m, k, n, o, cap):
     assert_fp16_close(one, ref.out)
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 2])
 def test_gemv_outlier_columns_sharing_a_lane(m):
     """Outlier columns 5, 6, 7, 1029 and 2053 all sit in lane 0's bytes of
     their 1 KB chunks (more than a lane keeps in registers), 100 in lane 6."""
@@ -426,7 +430,7 @@ def test_gemv_outlier_columns_sharing_a_lane(m):
 def test_decode_forward_strided_x(pad):
     """x with a row stride: an aligned one takes the one-launch forward, an odd
     one the two-launch path; both give the oracle's result."""
-    m, k, n = 3, 1536, 256
+    m, k, n = 2, 1536, 256
     L = make_inputs(m, k, n, n_outlier=4, bias_std=0.01, seed=(83, pad, 0))
     wq, ws = oracle.quantize_weight(L.w)
     big = torch.zeros((m, k + pad), dtype=torch.float16, device="cuda")
