@@ -19,7 +19,9 @@
 //    four times the cycles of whole-line requests on them, and with two
 //    workgroups on a CU that alone bounded the stream.  The ring is private,
 //    so a wave only waits for its own loads (s_waitcnt vmcnt), never for a
-//    barrier; kStages - 1 chunks stay in flight.
+//    barrier; kStages - 1 chunks stay in flight.  With m <= 8 the activation
+//    rows 8-15 are zeros written once, so a chunk takes three DMA instead of
+//    four.
 //  * The G partial 16x16 int32 blocks of a group are summed through LDS and
 //    the group's first wave runs the fused epilogue: row / column absmax, the
 //    fp16 outlier-column sub-matmul on v_mfma_f32_16x16x32_f16, bias, fp16
@@ -36,7 +38,6 @@ namespace {
 
 constexpr int kRows = 16;     // weight rows per group
 constexpr int kWaves = 4;     // waves per workgroup
-constexpr int kStages = 4;    // per-wave ring depth
 constexpr int kChunk = 128;   // K bytes per stage
 constexpr int kHalfBytes = kRows * kChunk;       // one operand's chunk
 constexpr int kStageBytes = 2 * kHalfBytes;       // weight rows, then activation rows
@@ -70,8 +71,12 @@ __device__ inline int swz(int row, int chunk) { return row * kChunk + ((chunk ^ 
 
 }  // namespace
 
-template <int G, bool kFused>
+template <int G, bool kFused, bool kHalfA>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+    // per-wave ring depth: with at most 8 activation rows (one activation
+    // DMA per chunk) three stages measured faster than four (13B down m = 4:
+    // 17.5 -> 16.2 us), with 16 rows four
+    constexpr int kStages = kHalfA ? 3 : 4;
     // one LDS array (a second __shared__ object makes the compiler drain every
     // DMA before each LDS read): the rings, then the partial-sum blocks
     __shared__ __attribute__((aligned(1024))) int8_t
@@ -108,8 +113,16 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     int8_t* my_ring = ring + wid * kStages * kStageBytes;
     const int64_t nchunks = kr / kChunk;
     const int64_t mine = (active && nchunks > part) ? (nchunks - part + G - 1) / G : 0;
-    // every chunk issues 4 loads (2 weight DMA, 2 activation DMA); past this
-    // wave's last chunk they read nothing (zero-length range)
+    // kHalfA (m <= 8): activation rows 8-15 are zeros, written into every
+    // stage once here instead of by a DMA per chunk
+    if constexpr (kHalfA) {
+#pragma unroll
+        for (int sl = 0; sl < kStages; ++sl)
+            *reinterpret_cast<v4i_t*>(my_ring + sl * kStageBytes + kHalfBytes + 1024 + lane * 16) = v4i_t{0, 0, 0, 0};
+    }
+    // every chunk issues kLoads loads (2 weight DMA, 2 or 1 activation DMA);
+    // past this wave's last chunk they read nothing (zero-length range)
+    constexpr int kLoads = kHalfA ? 3 : 4;
     auto issue = [&](int64_t j, int slot) {
         const bool real = j < mine;
         const int kb = (int)((part + j * G) * kChunk);
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         dma16<kWeightPolicy>(sw, st, w_off[0] + kb, 0);
         dma16<kWeightPolicy>(sw, st + 1024, w_off[1] + kb, 0);
         dma16<0>(sx, st + kHalfBytes, a_off[0] + kb, 0);
-        dma16<0>(sx, st + kHalfBytes + 1024, a_off[1] + kb, 0);
+        if constexpr (!kHalfA) dma16<0>(sx, st + kHalfBytes + 1024, a_off[1] + kb, 0);
     };
 
     v4i_t acc = {0, 0, 0, 0};
@@ -201,8 +214,9 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     for (int64_t j0 = 0; j0 < mine; j0 += kStages) {
 #pragma unroll
         for (int u = 0; u < kStages; ++u) {
-            // chunk j0+u landed once only the kStages-2 later chunks (4 loads each) remain
-            __builtin_amdgcn_s_waitcnt(0x0f70 | (((kStages - 2) * 4) & 15) | ((((kStages - 2) * 4) >> 4) << 14));
+            // chunk j0+u landed once only the kStages-2 later chunks (kLoads each) remain
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (((kStages - 2) * kLoads) & 15) |
+                                       ((((kStages - 2) * kLoads) >> 4) << 14));
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const int8_t* st = my_ring + u * kStageBytes;
             // fragments of lane l: row l % 16, the 32 bytes at 32 (l / 16) of
@@ -932,6 +946,21 @@ hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStre
     return launch_forward_m<2>(qa, g, stream);
 }
 
+namespace {
+template <bool kHalfA>
+hipError_t launch_decode_g(const GemmArgs& g, int gsplit, bool fused, dim3 grid, hipStream_t stream) {
+    switch (gsplit * 2 + (fused ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((gemm_decode_kernel<1, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        case 3: hipLaunchKernelGGL((gemm_decode_kernel<1, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        case 4: hipLaunchKernelGGL((gemm_decode_kernel<2, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        case 5: hipLaunchKernelGGL((gemm_decode_kernel<2, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        case 8: hipLaunchKernelGGL((gemm_decode_kernel<4, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        default: hipLaunchKernelGGL((gemm_decode_kernel<4, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
     // waves per 16-row group: enough K splits that each wave has a long run of
@@ -943,15 +972,8 @@ hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     while (gsplit < kWaves && nchunks / (2 * gsplit) >= 16) gsplit *= 2;
     while (gsplit > 1 && groups * gsplit / kWaves > 2 * 256 && nchunks / gsplit < 32) gsplit /= 2;
     dim3 grid((unsigned)((groups * gsplit + kWaves - 1) / kWaves));
-    switch (gsplit * 2 + (fused ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((gemm_decode_kernel<1, false>), grid, dim3(256), 0, stream, g); break;
-        case 3: hipLaunchKernelGGL((gemm_decode_kernel<1, true>), grid, dim3(256), 0, stream, g); break;
-        case 4: hipLaunchKernelGGL((gemm_decode_kernel<2, false>), grid, dim3(256), 0, stream, g); break;
-        case 5: hipLaunchKernelGGL((gemm_decode_kernel<2, true>), grid, dim3(256), 0, stream, g); break;
-        case 8: hipLaunchKernelGGL((gemm_decode_kernel<4, false>), grid, dim3(256), 0, stream, g); break;
-        default: hipLaunchKernelGGL((gemm_decode_kernel<4, true>), grid, dim3(256), 0, stream, g); break;
-    }
-    return hipGetLastError();
+    if (g.m <= 8) return launch_decode_g<true>(g, gsplit, fused, grid, stream);
+    return launch_decode_g<false>(g, gsplit, fused, grid, stream);
 }
 
 }  // namespace i8mp
