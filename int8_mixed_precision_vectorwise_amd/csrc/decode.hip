@@ -9,7 +9,9 @@
 //    by G waves that split K: wave part p takes the 128-byte K chunks p, p+G,
 //    p+2G, ...  A workgroup of 4 waves holds 4/G groups; G is chosen so that
 //    each wave streams a long run of chunks and the grid fits the CUs in one
-//    round.
+//    round.  Where that would give some CUs two groups and others one (257
+//    to 512 groups), a group is instead ceil(n / 256) rows, held as NB = 2
+//    blocks of 16 that share the activation fragments, one workgroup per CU.
 //  * Each wave streams its chunks through a private ring of kStages LDS
 //    stages with buffer_load ... lds (16 bytes per lane, eight lanes per
 //    whole 128-byte line): the weight rows' chunk (2 KB) and the matching
@@ -40,7 +42,6 @@ constexpr int kRows = 16;     // weight rows per group
 constexpr int kWaves = 4;     // waves per workgroup
 constexpr int kChunk = 128;   // K bytes per stage
 constexpr int kHalfBytes = kRows * kChunk;       // one operand's chunk
-constexpr int kStageBytes = 2 * kHalfBytes;       // weight rows, then activation rows
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kDecOutl = 32;  // outlier columns the MFMA decode kernel takes from its ring
 
@@ -71,25 +72,31 @@ __device__ inline int swz(int row, int chunk) { return row * kChunk + ((chunk ^ 
 
 }  // namespace
 
-template <int G, bool kFused, bool kHalfA>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+template <int G, bool kFused, bool kHalfA, int NB>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g, int rg) {
     // per-wave ring depth: with at most 8 activation rows (one activation
     // DMA per chunk) three stages measured faster than four (13B down m = 4:
-    // 17.5 -> 16.2 us), with 16 rows four
-    constexpr int kStages = kHalfA ? 3 : 4;
+    // 17.5 -> 16.2 us), with 16 rows four; groups of more than 16 weight rows
+    // take three for room in LDS
+    constexpr int kStages = (kHalfA || NB > 1) ? 3 : 4;
+    constexpr int kWBytes = NB * kRows * kChunk;      // the weight rows of a stage (NB blocks of 16)
+    constexpr int kStBytes = kWBytes + kHalfBytes;    // then the 16 activation rows
+    constexpr int kRingBytes = kStages * kStBytes;    // one wave's ring
+    static_assert(2 * NB * 4 * 64 * 4 <= kRingBytes, "a wave's partial blocks fit its ring");
     // one LDS array (a second __shared__ object makes the compiler drain every
-    // DMA before each LDS read): the rings, then the partial-sum blocks
+    // DMA before each LDS read): the rings, then the outlier values
     __shared__ __attribute__((aligned(1024))) int8_t
-        ring[kWaves * kStages * kStageBytes + 2 * kWaves * 4 * 64 * 4 + (kFused ? kRows * kDecOutl * 4 : 0)];
-    int32_t* red = reinterpret_cast<int32_t*>(ring + kWaves * kStages * kStageBytes);
-    float* pred = reinterpret_cast<float*>(red + kWaves * 4 * 64);
-    float* xo = pred + kWaves * 4 * 64;  // [16 activation rows][kDecOutl] outlier values (fused)
+        ring[kWaves * kRingBytes + (kFused ? kRows * kDecOutl * 4 : 0)];
+    float* xo = reinterpret_cast<float*>(ring + kWaves * kRingBytes);  // [16 activation rows][kDecOutl] (fused)
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wid % G;                 // this wave's share of K
-    const int64_t n0 = ((int64_t)blockIdx.x * (kWaves / G) + wid / G) * kRows;
+    // group: weight rows n0 .. n0 + rg - 1 (rg <= 16 NB), of which
+    // rows_here exist
+    const int64_t n0 = ((int64_t)blockIdx.x * (kWaves / G) + wid / G) * rg;
     const bool active = n0 < g.n;
+    const int rows_here = active ? (int)(g.n - n0 < rg ? g.n - n0 : rg) : 0;
 
     const int64_t kr = (g.k + kChunk - 1) / kChunk * kChunk;
     // the weight's range ends at the last row's k rounded up to a dword (the
@@ -100,17 +107,19 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 
     // DMA lane mapping, the same for both operands: instruction j covers rows
     // 8j .. 8j+7 (1 KB); lane i -> row 8j + i/8, LDS slot i%8, which holds
-    // global chunk slot ^ ((row>>1)&7).  Rows of the activations past m lie
-    // past their range and read zeros.
-    int w_off[2], a_off[2];
+    // global chunk slot ^ ((row>>1)&7).  Weight rows past the group's (the
+    // next group's, or past n) and activation rows past m read nothing.
+    int w_off[2 * NB], a_off[2];
+    bool w_ok[2 * NB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2 * NB; ++j) {
         const int row = 8 * j + (lane >> 3);
         const int gchunk = (lane & 7) ^ ((row >> 1) & 7);
         w_off[j] = (int)(row * g.ldb + gchunk * 16);
-        a_off[j] = (int)(row * g.lda + gchunk * 16);
+        w_ok[j] = row < rows_here;
+        if (j < 2) a_off[j] = (int)(row * g.lda + gchunk * 16);
     }
-    int8_t* my_ring = ring + wid * kStages * kStageBytes;
+    int8_t* my_ring = ring + wid * kRingBytes;
     const int64_t nchunks = kr / kChunk;
     const int64_t mine = (active && nchunks > part) ? (nchunks - part + G - 1) / G : 0;
     // kHalfA (m <= 8): activation rows 8-15 are zeros, written into every
@@ -118,36 +127,41 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     if constexpr (kHalfA) {
 #pragma unroll
         for (int sl = 0; sl < kStages; ++sl)
-            *reinterpret_cast<v4i_t*>(my_ring + sl * kStageBytes + kHalfBytes + 1024 + lane * 16) = v4i_t{0, 0, 0, 0};
+            *reinterpret_cast<v4i_t*>(my_ring + sl * kStBytes + kWBytes + 1024 + lane * 16) = v4i_t{0, 0, 0, 0};
     }
-    // every chunk issues kLoads loads (2 weight DMA, 2 or 1 activation DMA);
-    // past this wave's last chunk they read nothing (zero-length range)
-    constexpr int kLoads = kHalfA ? 3 : 4;
+    // every chunk issues kLoads loads (2 NB weight DMA, 2 or 1 activation
+    // DMA); past this wave's last chunk they read nothing (zero-length range)
+    constexpr int kLoads = 2 * NB + (kHalfA ? 1 : 2);
     auto issue = [&](int64_t j, int slot) {
         const bool real = j < mine;
         const int kb = (int)((part + j * G) * kChunk);
-        int8_t* st = my_ring + slot * kStageBytes;
+        int8_t* st = my_ring + slot * kStBytes;
         const __amdgpu_buffer_rsrc_t sw = real ? rw : r_none;
         const __amdgpu_buffer_rsrc_t sx = real ? rx : r_none;
-        dma16<kWeightPolicy>(sw, st, w_off[0] + kb, 0);
-        dma16<kWeightPolicy>(sw, st + 1024, w_off[1] + kb, 0);
-        dma16<0>(sx, st + kHalfBytes, a_off[0] + kb, 0);
-        if constexpr (!kHalfA) dma16<0>(sx, st + kHalfBytes + 1024, a_off[1] + kb, 0);
+#pragma unroll
+        for (int jj = 0; jj < 2 * NB; ++jj)
+            dma16<kWeightPolicy>(sw, st + jj * 1024, w_ok[jj] ? w_off[jj] + kb : (int)0x80000000, 0);
+        dma16<0>(sx, st + kWBytes, a_off[0] + kb, 0);
+        if constexpr (!kHalfA) dma16<0>(sx, st + kWBytes + 1024, a_off[1] + kb, 0);
     };
 
-    v4i_t acc = {0, 0, 0, 0};
+    v4i_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = v4i_t{0, 0, 0, 0};
     const int row = lane & 15;
 
     // The first kDecOutl outlier columns (ascending) are taken from the ring
-    // as their chunk passes: lane l reads its weight row's byte (row l % 16)
-    // and adds byte * x into p, laid out like acc (activation rows
-    // 4 (l / 16) + r).  ocol is the next such column (wave-uniform); columns
-    // in other waves' chunks are passed over.  Later columns are gathered in
-    // the epilogue.
+    // as their chunk passes: lane l reads its weight rows' bytes (row l % 16
+    // of each block) and adds byte * x into p, laid out like acc (activation
+    // rows 4 (l / 16) + r).  ocol is the next such column (wave-uniform);
+    // columns in other waves' chunks are passed over.  Later columns are
+    // gathered in the epilogue.
     int cnt = 0, n_ring = 0, optr = 0;
     int64_t ocol = INT64_MAX;
     int ocol_lane = 0x7fffffff;  // lane s: column of slot s
-    v4f_t p = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f_t p[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) p[b] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
     // The ring's outlier operands are loaded before the stream's first chunks
     // (vector loads complete in order, so waiting for them then does not wait
     // for the weight): the first index entries and X_O values, bounded by the
@@ -202,9 +216,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         while (ocol < c0 + kChunk) {
             if (ocol >= c0) {
                 const int cb = (int)(ocol - c0);
-                const float wv = (float)st[swz(row, cb >> 4) + (cb & 15)];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] += wv * xo[(arow0 + r) * kDecOutl + optr];
+                for (int b = 0; b < NB; ++b) {
+                    const float wv = (float)st[swz(kRows * b + row, cb >> 4) + (cb & 15)];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) p[b][r] += wv * xo[(arow0 + r) * kDecOutl + optr];
+                }
             }
             ++optr;
             ocol = optr < n_ring ? (int64_t)__builtin_amdgcn_readlane(ocol_lane, optr) : INT64_MAX;
@@ -218,55 +235,74 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             __builtin_amdgcn_s_waitcnt(0x0f70 | (((kStages - 2) * kLoads) & 15) |
                                        ((((kStages - 2) * kLoads) >> 4) << 14));
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int8_t* st = my_ring + u * kStageBytes;
-            // fragments of lane l: row l % 16, the 32 bytes at 32 (l / 16) of
-            // the chunk in both operands (one 16-byte piece per MFMA)
-            v4i_t wf[2], af[2];
+            const int8_t* st = my_ring + u * kStBytes;
+            // fragments of lane l: row l % 16 (of each weight block), the 32
+            // bytes at 32 (l / 16) of the chunk (one 16-byte piece per MFMA)
+            v4i_t wf[NB][2], af[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                wf[t] = *reinterpret_cast<const v4i_t*>(st + swz(row, (lane >> 4) * 2 + t));
-                af[t] = *reinterpret_cast<const v4i_t*>(st + kHalfBytes + swz(row, (lane >> 4) * 2 + t));
+                af[t] = *reinterpret_cast<const v4i_t*>(st + kWBytes + swz(row, (lane >> 4) * 2 + t));
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    wf[b][t] = *reinterpret_cast<const v4i_t*>(st + swz(kRows * b + row, (lane >> 4) * 2 + t));
             }
             if constexpr (kFused)
                 if (j0 + u < mine) take_outliers(part + (j0 + u) * G, st);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             issue(j0 + u + kStages - 1, (u + kStages - 1) % kStages);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0], wf[0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1], wf[1], acc, 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0], wf[b][0], acc[b], 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1], wf[b][1], acc[b], 0, 0, 0);
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // no DMA left in flight into the ring
 
-    // sum each group's partial blocks
+    // sum each group's partial blocks, through the rings (each wave writes
+    // its own, whose DMA is done; the group's first wave reads after the
+    // barrier)
     if (part > 0) {
+        int32_t* red = reinterpret_cast<int32_t*>(my_ring);
+        float* pred = reinterpret_cast<float*>(my_ring + NB * 4 * 64 * 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            red[(wid * 4 + r) * 64 + lane] = acc[r];
-            if (kFused) pred[(wid * 4 + r) * 64 + lane] = p[r];
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                red[(b * 4 + r) * 64 + lane] = acc[b][r];
+                if (kFused) pred[(b * 4 + r) * 64 + lane] = p[b][r];
+            }
     }
     __syncthreads();
     if (part > 0 || !active) return;  // no barrier below
 #pragma unroll
-    for (int w = 1; w < G; ++w)
+    for (int w = 1; w < G; ++w) {
+        const int32_t* red = reinterpret_cast<const int32_t*>(ring + (wid + w) * kRingBytes);
+        const float* pred = reinterpret_cast<const float*>(ring + (wid + w) * kRingBytes + NB * 4 * 64 * 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            acc[r] += red[((wid + w) * 4 + r) * 64 + lane];
-            if (kFused) p[r] += pred[((wid + w) * 4 + r) * 64 + lane];
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[b][r] += red[(b * 4 + r) * 64 + lane];
+                if (kFused) p[b][r] += pred[(b * 4 + r) * 64 + lane];
+            }
+    }
 
-    // acc[r] of lane l: activation row 4*(l/16) + r, weight row n0 + l%16
-    const int64_t col = n0 + (lane & 15);
+    // acc[b][r] of lane l: activation row 4*(l/16) + r, weight row n0 + 16 b + l%16
     const int64_t row0 = 4 * (lane >> 4);
     if constexpr (!kFused) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (row0 + r < g.m && col < g.n) g.c[(row0 + r) * g.ldc + col] = acc[r];
+        for (int b = 0; b < NB; ++b) {
+            const int lr = kRows * b + (lane & 15);
+            const int64_t col = n0 + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (row0 + r < g.m && lr < rows_here) g.c[(row0 + r) * g.ldc + col] = acc[b][r];
+        }
     } else {
         const float r127 = 1.0f / 127.0f;
         int64_t arow = lane & 15;
         if (arow >= g.m) arow = g.m - 1;
-        const int64_t bcol = col < g.n ? col : g.n - 1;
         // columns past the ring's kDecOutl: gathered (kDecOutl is a multiple of
         // 32); x values as 8-slot vectors from X_O below xo_lim (zero from the
         // count to ldo), past it slot by slot
@@ -281,21 +317,31 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
                 for (int e = 0; e < 8; ++e)
                     xa[e] = s1 + e < cnt ? (_Float16)outlier_x(g, arow, s1 + e) : (_Float16)0.0f;
             }
-            v8h wb;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                wb[e] = s1 + e < cnt ? (_Float16)(float)g.b[bcol * g.ldb + g.idx[s1 + e]] : (_Float16)0.0f;
-            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, wb, p, 0, 0, 0);
+            for (int b = 0; b < NB; ++b) {
+                const int lr = kRows * b + (lane & 15);
+                const int64_t bcol = n0 + (lr < rows_here ? lr : 0);
+                v8h wb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wb[e] = s1 + e < cnt ? (_Float16)(float)g.b[bcol * g.ldb + g.idx[s1 + e]] : (_Float16)0.0f;
+                p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, wb, p[b], 0, 0, 0);
+            }
         }
-        if (col < g.n) {
-            const float sw = g.col_absmax[col] * r127;
-            const float bj = g.bias ? h2f(g.bias[col]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = row0 + r;
-                if (row < g.m) {
-                    const float sx = g.row_absmax[row] * r127;
-                    g.out[row * g.ldout + col] = f2h(sw * ((float)acc[r] * sx + p[r]) + bj);
+        for (int b = 0; b < NB; ++b) {
+            const int lr = kRows * b + (lane & 15);
+            if (lr < rows_here) {
+                const int64_t col = n0 + lr;
+                const float sw = g.col_absmax[col] * r127;
+                const float bj = g.bias ? h2f(g.bias[col]) : 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = row0 + r;
+                    if (row < g.m) {
+                        const float sx = g.row_absmax[row] * r127;
+                        g.out[row * g.ldout + col] = f2h(sw * ((float)acc[b][r] * sx + p[b][r]) + bj);
+                    }
                 }
             }
         }
@@ -947,27 +993,54 @@ hipError_t launch_decode_forward(const QuantArgs& qa, const GemmArgs& g, hipStre
 }
 
 namespace {
+constexpr int64_t kDecCUs = 256;   // MI355X compute units
+
+// whole 16-row groups (NB = 1), gsplit waves per group
 template <bool kHalfA>
 hipError_t launch_decode_g(const GemmArgs& g, int gsplit, bool fused, dim3 grid, hipStream_t stream) {
     switch (gsplit * 2 + (fused ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((gemm_decode_kernel<1, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
-        case 3: hipLaunchKernelGGL((gemm_decode_kernel<1, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
-        case 4: hipLaunchKernelGGL((gemm_decode_kernel<2, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
-        case 5: hipLaunchKernelGGL((gemm_decode_kernel<2, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
-        case 8: hipLaunchKernelGGL((gemm_decode_kernel<4, false, kHalfA>), grid, dim3(256), 0, stream, g); break;
-        default: hipLaunchKernelGGL((gemm_decode_kernel<4, true, kHalfA>), grid, dim3(256), 0, stream, g); break;
+        case 2: hipLaunchKernelGGL((gemm_decode_kernel<1, false, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
+        case 3: hipLaunchKernelGGL((gemm_decode_kernel<1, true, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
+        case 4: hipLaunchKernelGGL((gemm_decode_kernel<2, false, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
+        case 5: hipLaunchKernelGGL((gemm_decode_kernel<2, true, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
+        case 8: hipLaunchKernelGGL((gemm_decode_kernel<4, false, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
+        default: hipLaunchKernelGGL((gemm_decode_kernel<4, true, kHalfA, 1>), grid, dim3(256), 0, stream, g, kRows); break;
     }
     return hipGetLastError();
 }
+
+// one workgroup of four waves (splitting K) per group of rg rows, NB blocks
+template <bool kHalfA, int NB>
+hipError_t launch_decode_wide(const GemmArgs& g, int rg, bool fused, hipStream_t stream) {
+    const dim3 grid((unsigned)((g.n + rg - 1) / rg));
+    if (fused)
+        hipLaunchKernelGGL((gemm_decode_kernel<kWaves, true, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
+    else
+        hipLaunchKernelGGL((gemm_decode_kernel<kWaves, false, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
+    const int64_t groups = (g.n + kRows - 1) / kRows;
+    const int64_t nchunks = (g.k + kChunk - 1) / kChunk;
+    // Between one and two 16-row groups per CU, long K and more than four
+    // rows: one workgroup per CU instead, its group ceil(n / 256) <= 32 rows
+    // in two blocks that share the activation fragments.  With whole 16-row
+    // groups the CUs that take two of them set the time (13B down, 320
+    // groups: m = 16 22.1 -> 18.4 us, m = 8 18.5 -> 17.5 us; at m = 4 even).
+    // Groups of three or four blocks (13B up) measured slower: one
+    // workgroup of 122 KB per CU and short runs per wave.
+    if (groups > kDecCUs && groups <= 2 * kDecCUs && nchunks >= 64 && g.m > 4) {
+        const int rg = (int)((g.n + kDecCUs - 1) / kDecCUs);
+        return g.m <= 8 ? launch_decode_wide<true, 2>(g, rg, fused, stream)
+                        : launch_decode_wide<false, 2>(g, rg, fused, stream);
+    }
     // waves per 16-row group: enough K splits that each wave has a long run of
     // 128-byte chunks; fewer where that would put more than two workgroups on
     // each CU and leave the runs short
-    const int64_t groups = (g.n + kRows - 1) / kRows;
-    const int64_t nchunks = (g.k + kChunk - 1) / kChunk;
     int gsplit = 1;
     while (gsplit < kWaves && nchunks / (2 * gsplit) >= 16) gsplit *= 2;
     while (gsplit > 1 && groups * gsplit / kWaves > 2 * 256 && nchunks / gsplit < 32) gsplit /= 2;

@@ -128,7 +128,11 @@ MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128
              (200, 300, 2560), (130, 190, 2176),  # two K pipelines per workgroup (17 K tiles: one pipeline's last is empty)
              (2100, 5000, 512), (2100, 5000, 640), (1800, 6000, 128),  # 256 x 256 ping-pong tiles, ragged m and n
              # whole rounds of 256 x 256 tiles, the remaining columns in a second launch of smaller tiles
-             (2048, 9000, 512), (2100, 9000, 512)]
+             (2048, 9000, 512), (2100, 9000, 512),
+             # m <= 16 with 257 to 512 groups of 16 rows and long K: one workgroup per CU, two blocks
+             (16, 5003, 8192), (7, 4490, 8320), (12, 8000, 8200),
+             # ... and the 16-row groups past that range
+             (5, 9001, 4224), (12, 16000, 4100), (2, 4500, 16512)]
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -234,6 +238,14 @@ FWD_CASES = [
     (8, 13824, 700, 40, 0.5, True, TAU, 16),      # ring + gathered outliers, past cap
     (16, 8192, 1000, 5, 1.0, False, TAU, 64),     # n not a multiple of 16
     (16, 5120, 2000, 8, 1.0, True, TAU, 256),     # two waves per group
+    # 257 to 512 groups of 16 rows, long K, m > 4: one workgroup per CU, groups of ceil(n / 256) rows
+    (16, 8192, 5003, 8, 1.0, True, TAU, 64),      # 20-row groups, the last 3 rows
+    (7, 8320, 4490, 40, 0.5, False, TAU, 16),     # half the activation rows, past the ring and cap, last group 8 rows
+    (12, 8200, 8000, 9, 1.0, True, TAU, 256),     # 32-row groups, k not a multiple of 128
+    # 16-row groups past those ranges
+    (5, 4224, 9001, 40, 0.5, False, TAU, 16),     # past the ring and cap
+    (12, 4100, 16000, 9, 1.0, True, TAU, 256),    # k not a multiple of 128
+    (2, 16512, 4500, 6, 1.0, True, TAU, 32),      # two rows past the GEMV's LDS
 ]
 
 
