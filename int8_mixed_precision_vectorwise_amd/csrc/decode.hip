@@ -9,9 +9,10 @@
 //    by G waves that split K: wave part p takes the 128-byte K chunks p, p+G,
 //    p+2G, ...  A workgroup of 4 waves holds 4/G groups; G is chosen so that
 //    each wave streams a long run of chunks and the grid fits the CUs in one
-//    round.  Where that would give some CUs two groups and others one (257
-//    to 512 groups), a group is instead ceil(n / 256) rows, held as NB = 2
-//    blocks of 16 that share the activation fragments, one workgroup per CU.
+//    round.  Where that would give some CUs more groups than others (257
+//    to 1024 groups), a group is instead ceil(n / 256) or ceil(n / 512) rows,
+//    held as NB = 2 blocks of 16 that share the activation fragments, one
+//    workgroup per CU.
 //  * Each wave streams its chunks through a private ring of kStages LDS
 //    stages with buffer_load ... lds (16 bytes per lane, eight lanes per
 //    whole 128-byte line): the weight rows' chunk (2 KB) and the matching
@@ -1009,14 +1010,15 @@ hipError_t launch_decode_g(const GemmArgs& g, int gsplit, bool fused, dim3 grid,
     return hipGetLastError();
 }
 
-// one workgroup of four waves (splitting K) per group of rg rows, NB blocks
-template <bool kHalfA, int NB>
+// groups of rg rows in NB blocks, G waves (splitting K) per group
+template <bool kHalfA, int NB, int G>
 hipError_t launch_decode_wide(const GemmArgs& g, int rg, bool fused, hipStream_t stream) {
-    const dim3 grid((unsigned)((g.n + rg - 1) / rg));
+    const int64_t groups = (g.n + rg - 1) / rg;
+    const dim3 grid((unsigned)((groups * G + kWaves - 1) / kWaves));
     if (fused)
-        hipLaunchKernelGGL((gemm_decode_kernel<kWaves, true, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
+        hipLaunchKernelGGL((gemm_decode_kernel<G, true, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
     else
-        hipLaunchKernelGGL((gemm_decode_kernel<kWaves, false, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
+        hipLaunchKernelGGL((gemm_decode_kernel<G, false, kHalfA, NB>), grid, dim3(256), 0, stream, g, rg);
     return hipGetLastError();
 }
 
@@ -1026,17 +1028,24 @@ hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
     const int64_t groups = (g.n + kRows - 1) / kRows;
     const int64_t nchunks = (g.k + kChunk - 1) / kChunk;
-    // Between one and two 16-row groups per CU, long K and more than four
-    // rows: one workgroup per CU instead, its group ceil(n / 256) <= 32 rows
-    // in two blocks that share the activation fragments.  With whole 16-row
-    // groups the CUs that take two of them set the time (13B down, 320
-    // groups: m = 16 22.1 -> 18.4 us, m = 8 18.5 -> 17.5 us; at m = 4 even).
-    // Groups of three or four blocks (13B up) measured slower: one
-    // workgroup of 122 KB per CU and short runs per wave.
-    if (groups > kDecCUs && groups <= 2 * kDecCUs && nchunks >= 64 && g.m > 4) {
-        const int rg = (int)((g.n + kDecCUs - 1) / kDecCUs);
-        return g.m <= 8 ? launch_decode_wide<true, 2>(g, rg, fused, stream)
-                        : launch_decode_wide<false, 2>(g, rg, fused, stream);
+    // Between one and four 16-row groups per CU, more than four rows and K
+    // long enough for 16 chunks per wave: one workgroup per CU instead, with
+    // one group of ceil(n / 256) rows (four waves) or two of ceil(n / 512)
+    // (two waves each), each at most 32 rows in two blocks that share the
+    // activation fragments.  With whole 16-row groups the CUs that take more
+    // of them set the time (13B down, 320 groups: m = 16 22.1 -> 18.4 us,
+    // m = 8 18.5 -> 17.5 us; at m = 4 even).  Groups of three or four blocks
+    // measured slower: one workgroup of 122 KB per CU and short runs.
+    if (groups > kDecCUs && groups <= 4 * kDecCUs && g.m > 4) {
+        const bool two = groups > 2 * kDecCUs;
+        if (nchunks / (two ? 2 : 4) >= 16) {
+            const int rg = (int)((g.n + (two ? 2 : 1) * kDecCUs - 1) / ((two ? 2 : 1) * kDecCUs));
+            if (two)
+                return g.m <= 8 ? launch_decode_wide<true, 2, 2>(g, rg, fused, stream)
+                                : launch_decode_wide<false, 2, 2>(g, rg, fused, stream);
+            return g.m <= 8 ? launch_decode_wide<true, 2, 4>(g, rg, fused, stream)
+                            : launch_decode_wide<false, 2, 4>(g, rg, fused, stream);
+        }
     }
     // waves per 16-row group: enough K splits that each wave has a long run of
     // 128-byte chunks; fewer where that would put more than two workgroups on

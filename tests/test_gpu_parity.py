@@ -131,6 +131,8 @@ MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128
              (2048, 9000, 512), (2100, 9000, 512),
              # m <= 16 with 257 to 512 groups of 16 rows and long K: one workgroup per CU, two blocks
              (16, 5003, 8192), (7, 4490, 8320), (12, 8000, 8200),
+             # ... 513 to 1024 groups: two groups per workgroup
+             (16, 9001, 4096), (9, 12000, 4200),
              # ... and the 16-row groups past that range
              (5, 9001, 4224), (12, 16000, 4100), (2, 4500, 16512)]
 
@@ -242,6 +244,9 @@ FWD_CASES = [
     (16, 8192, 5003, 8, 1.0, True, TAU, 64),      # 20-row groups, the last 3 rows
     (7, 8320, 4490, 40, 0.5, False, TAU, 16),     # half the activation rows, past the ring and cap, last group 8 rows
     (12, 8200, 8000, 9, 1.0, True, TAU, 256),     # 32-row groups, k not a multiple of 128
+    (16, 4096, 9001, 12, 0.5, True, TAU, 64),     # 513 to 1024 groups: two 18-row groups per workgroup, the last 1 row
+    (6, 5120, 13824, 40, 1.0, False, TAU, 16),    # two 27-row groups per workgroup, past the ring and cap
+    (9, 4200, 12000, 8, 1.0, True, TAU, 32),      # k not a multiple of 128
     # 16-row groups past those ranges
     (5, 4224, 9001, 40, 0.5, False, TAU, 16),     # past the ring and cap
     (12, 4100, 16000, 9, 1.0, True, TAU, 256),    # k not a multiple of 128
