@@ -75,11 +75,12 @@ __device__ inline int swz(int row, int chunk) { return row * kChunk + ((chunk ^ 
 
 template <int G, bool kFused, bool kHalfA, int NB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g, int rg) {
-    // per-wave ring depth: with at most 8 activation rows (one activation
-    // DMA per chunk) three stages measured faster than four (13B down m = 4:
-    // 17.5 -> 16.2 us), with 16 rows four; groups of more than 16 weight rows
-    // take three for room in LDS
-    constexpr int kStages = (kHalfA || NB > 1) ? 3 : 4;
+    // per-wave ring depth: 16-row groups with at most 8 activation rows (one
+    // activation DMA per chunk) measured faster with three stages than with
+    // four (13B down m = 4: 17.5 -> 16.2 us), with 16 rows with four; groups
+    // of two blocks (one workgroup per CU) with four rather than three, five
+    // or six (13B down m = 8: 17.4 -> 16.0 us)
+    constexpr int kStages = (kHalfA && NB == 1) ? 3 : 4;
     constexpr int kWBytes = NB * kRows * kChunk;      // the weight rows of a stage (NB blocks of 16)
     constexpr int kStBytes = kWBytes + kHalfBytes;    // then the 16 activation rows
     constexpr int kRingBytes = kStages * kStBytes;    // one wave's ring
