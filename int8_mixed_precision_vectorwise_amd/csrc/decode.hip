@@ -1029,15 +1029,15 @@ hipError_t launch_decode(const GemmArgs& g, bool fused, hipStream_t stream) {
     if (gemv_fits(g)) return fused ? launch_gemv<true>(g, stream) : launch_gemv<false>(g, stream);
     const int64_t groups = (g.n + kRows - 1) / kRows;
     const int64_t nchunks = (g.k + kChunk - 1) / kChunk;
-    // Between one and four 16-row groups per CU, more than four rows and K
-    // long enough for 16 chunks per wave: one workgroup per CU instead, with
-    // one group of ceil(n / 256) rows (four waves) or two of ceil(n / 512)
-    // (two waves each), each at most 32 rows in two blocks that share the
-    // activation fragments.  With whole 16-row groups the CUs that take more
-    // of them set the time (13B down, 320 groups: m = 16 22.1 -> 18.4 us,
-    // m = 8 18.5 -> 17.5 us; at m = 4 even).  Groups of three or four blocks
-    // measured slower: one workgroup of 122 KB per CU and short runs.
-    if (groups > kDecCUs && groups <= 4 * kDecCUs && g.m > 4) {
+    // Between one and four 16-row groups per CU and K long enough for 16
+    // chunks per wave: one workgroup per CU instead, with one group of
+    // ceil(n / 256) rows (four waves) or two of ceil(n / 512) (two waves
+    // each), each at most 32 rows in two blocks that share the activation
+    // fragments.  With whole 16-row groups the CUs that take more of them set
+    // the time (13B down, 320 groups: m = 16 22.1 -> 17.9 us, m = 4 16.2 ->
+    // 14.7 us).  Groups of three or four blocks measured slower: one
+    // workgroup of 122 KB per CU and short runs.
+    if (groups > kDecCUs && groups <= 4 * kDecCUs) {
         const bool two = groups > 2 * kDecCUs;
         if (nchunks / (two ? 2 : 4) >= 16) {
             const int rg = (int)((g.n + (two ? 2 : 1) * kDecCUs - 1) / ((two ? 2 : 1) * kDecCUs));

@@ -130,11 +130,11 @@ MM_SHAPES = [(1, 1, 1), (3, 5, 17), (17, 63, 65), (65, 127, 129), (255, 257, 128
              # whole rounds of 256 x 256 tiles, the remaining columns in a second launch of smaller tiles
              (2048, 9000, 512), (2100, 9000, 512),
              # m <= 16 with 257 to 512 groups of 16 rows and long K: one workgroup per CU, two blocks
-             (16, 5003, 8192), (7, 4490, 8320), (12, 8000, 8200),
+             (16, 5003, 8192), (7, 4490, 8320), (12, 8000, 8200), (2, 4500, 16512),
              # ... 513 to 1024 groups: two groups per workgroup
-             (16, 9001, 4096), (9, 12000, 4200),
-             # ... and the 16-row groups past that range
-             (5, 9001, 4224), (12, 16000, 4100), (2, 4500, 16512)]
+             (16, 9001, 4096), (9, 12000, 4200), (5, 9001, 4224), (12, 16000, 4100),
+             # ... and past 1024 groups, whole 16-row groups
+             (4, 17000, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", MM_SHAPES)
@@ -240,17 +240,19 @@ FWD_CASES = [
     (8, 13824, 700, 40, 0.5, True, TAU, 16),      # ring + gathered outliers, past cap
     (16, 8192, 1000, 5, 1.0, False, TAU, 64),     # n not a multiple of 16
     (16, 5120, 2000, 8, 1.0, True, TAU, 256),     # two waves per group
-    # 257 to 512 groups of 16 rows, long K, m > 4: one workgroup per CU, groups of ceil(n / 256) rows
+    # 257 to 512 groups of 16 rows and long K: one workgroup per CU, one group of ceil(n / 256) rows
     (16, 8192, 5003, 8, 1.0, True, TAU, 64),      # 20-row groups, the last 3 rows
     (7, 8320, 4490, 40, 0.5, False, TAU, 16),     # half the activation rows, past the ring and cap, last group 8 rows
     (12, 8200, 8000, 9, 1.0, True, TAU, 256),     # 32-row groups, k not a multiple of 128
-    (16, 4096, 9001, 12, 0.5, True, TAU, 64),     # 513 to 1024 groups: two 18-row groups per workgroup, the last 1 row
-    (6, 5120, 13824, 40, 1.0, False, TAU, 16),    # two 27-row groups per workgroup, past the ring and cap
-    (9, 4200, 12000, 8, 1.0, True, TAU, 32),      # k not a multiple of 128
-    # 16-row groups past those ranges
-    (5, 4224, 9001, 40, 0.5, False, TAU, 16),     # past the ring and cap
-    (12, 4100, 16000, 9, 1.0, True, TAU, 256),    # k not a multiple of 128
     (2, 16512, 4500, 6, 1.0, True, TAU, 32),      # two rows past the GEMV's LDS
+    # 513 to 1024 groups: two groups of ceil(n / 512) rows per workgroup
+    (16, 4096, 9001, 12, 0.5, True, TAU, 64),     # 18-row groups, the last 1 row
+    (6, 5120, 13824, 40, 1.0, False, TAU, 16),    # 27-row groups, past the ring and cap
+    (9, 4200, 12000, 8, 1.0, True, TAU, 32),      # k not a multiple of 128
+    (5, 4224, 9001, 40, 0.5, False, TAU, 16),     # past the ring and cap
+    (4, 4100, 16000, 9, 1.0, True, TAU, 256),     # 32-row groups, k not a multiple of 128
+    # past 1024 groups: whole 16-row groups again
+    (4, 4096, 17000, 9, 1.0, True, TAU, 64),
 ]
 
 
@@ -557,18 +559,20 @@ def test_non_default_stream():
     assert_fp16_close(out, ref.out)
 
 
-@pytest.mark.parametrize("m", [128, 2, 8, 1100])
-def test_graph_capture_replays_match_eager(m):
+@pytest.mark.parametrize("m,k,n", [(128, 1024, 512), (2, 1024, 512), (8, 1024, 512), (1100, 1024, 512),
+                                   (16, 8192, 5003)])
+def test_graph_capture_replays_match_eager(m, k, n):
     """m = 2: the one-launch GEMV forward; 8: the column-slice quantizer and the
-    MFMA decode kernel; 128: detection + quantization launches; 1100: the
-    single read of x (bitmap clearing, atomics into the partial bitmaps).
+    MFMA decode kernel; 16 with 313 groups of 16 rows: the decode kernel's
+    one-workgroup-per-CU groups; 128: detection + quantization launches; 1100:
+    the single read of x (bitmap clearing, atomics into the partial bitmaps).
     Every replay runs on a workspace filled with garbage first."""
-    L = make_inputs(m, 1024, 512, n_outlier=5, bias_std=0.01, seed=(81, m, 0))
+    L = make_inputs(m, k, n, n_outlier=5, bias_std=0.01, seed=(81, m, 0))
     wq, ws = oracle.quantize_weight(L.w)
     x, w, s, b = dev(L.x), dev(wq), dev(ws), dev(L.bias)
-    wsp = i8.LinearWorkspace.create(m, 512, 1024, 32, "cuda")
-    out = torch.empty((m, 512), dtype=torch.float16, device="cuda")
-    say(f"graph capture m={m}")
+    wsp = i8.LinearWorkspace.create(m, n, k, 32, "cuda")
+    out = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    say(f"graph capture m={m} k={k} n={n}")
     eager = i8.linear(x, w, s, b, TAU, 32, wsp).clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
