@@ -639,6 +639,8 @@ EDGE_CASES = [
     (9, 3000, 200, 6.001),
     (300, 1024, 520, 6.0),     # detect + quantize kernels + prefill tile
     (300, 1024, 520, 6.001),
+    (1100, 1024, 130, 6.0),    # single-read quantizer (1024 rows or more) + prefill tile
+    (1100, 1024, 130, 6.001),
     (2, 33000, 64, 6.0),       # single-workgroup quantizer (two rows), MFMA decode kernel
 ]
 
@@ -655,10 +657,11 @@ def test_threshold_edge_forward(case):
 
 
 @pytest.mark.parametrize("m,k,tau", [(2, 1000, 6.0), (2, 1000, 6.001), (40, 3000, 6.0), (300, 20000, 6.0),
-                                     (300, 20000, 6.001)])
+                                     (300, 20000, 6.001), (1100, 3000, 6.0), (1100, 3000, 6.001)])
 def test_threshold_edge_quant(m, k, tau):
     """int8_vectorwise_quant on its own: the two-row single-workgroup kernel,
-    and detect + quantize with a wavefront or a workgroup per row."""
+    detect + quantize with a wavefront or a workgroup per row, and the
+    single-read pair from 1024 rows."""
     L, _ = _edge_input(m, k, 1, seed=1)
     say(f"vectorwise_quant threshold edge m={m} k={k} tau={tau}")
     q, s, bm = i8.vectorwise_quant(dev(L.x), tau)
