@@ -252,6 +252,178 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
     }
 }
 
+// The decode linear with x staged in LDS, taken for one row of x: a grid of
+// one or two workgroups per CU (two when x fits 64 KB), each of 8 waves.  A
+// workgroup copies its M rows of x into LDS once (direct-to-LDS DMA, in 4 KB
+// blocks, zero past the row); then every wave takes whole weight rows (wave v
+// of the grid: rows v, v + nw, ...), so the grid sweeps a band of neighbouring
+// rows at a time.  A lane takes the 16-byte code chunks lane, lane + 64, ...
+// (CPL of them, 32 weights each, half a block) and reads the matching x from
+// LDS; per row the 64 lane sums meet in a DPP reduction and lane 0 writes the
+// M outputs.  As soon as a chunk of the current row has been converted, the
+// same chunk of the wave's next row is requested into its registers, so CPL
+// chunks are always in flight.  Each code byte is read once from HBM and x
+// once per workgroup from L2 (the four-row kernel above reads x from L2 again
+// for every group of weight rows).  Chunks past the row read zero codes
+// through the row's buffer range, against the zeros of the x block's tail.
+constexpr int kFp4Waves = 8;
+typedef unsigned v4u_l __attribute__((ext_vector_type(4)));
+
+// the buffer ranges of one weight row's codes and block scales (empty past n)
+struct Fp4RowSrc {
+    __amdgpu_buffer_rsrc_t codes, scales, s2;
+    int64_t b0;   // first block of the row
+};
+
+template <bool kDq>
+__device__ inline Fp4RowSrc fp4_row_src(const Fp4Args& a, int64_t row, int64_t chunks, int64_t kb) {
+    const bool live = row < a.n;
+    Fp4RowSrc r;
+    r.b0 = live ? row * kb : 0;
+    r.codes = buf_rsrc(a.codes + (live ? row * a.ldc : 0), live ? chunks * 16 : 0);
+    if constexpr (kDq) {
+        r.scales = buf_rsrc(a.c8 + r.b0, live ? kb : 0);
+        r.s2 = buf_rsrc(a.s2, ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4);
+    } else {
+        r.scales = buf_rsrc(a.absmax + r.b0, live ? kb * 4 : 0);
+        r.s2 = r.scales;
+    }
+    return r;
+}
+
+// chunk c of a row: its codes, and its raw block scale (the absmax, or the
+// code c8 and the group maximum s2)
+template <bool kDq>
+__device__ inline void fp4_chunk_load(const Fp4RowSrc& r, int c, uint4& cv, float& sa, uint32_t& c8) {
+    cv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.codes, c * 16, 0, 0));
+    if constexpr (kDq) {
+        c8 = __builtin_amdgcn_raw_buffer_load_b8(r.scales, c >> 1, 0, 0);
+        sa = __builtin_bit_cast(float,
+                                __builtin_amdgcn_raw_buffer_load_b32(r.s2, (int)((r.b0 + (c >> 1)) / kDqGroup) * 4, 0, 0));
+    } else {
+        sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r.scales, (c >> 1) * 4, 0, 0));
+        c8 = 0;
+    }
+}
+
+template <int M, int CPL, bool kDq>
+__global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[CPL * M * 4096];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t chunks = a.k / 32, kb = a.k / kBlk;
+    const int64_t nw = (int64_t)gridDim.x * kFp4Waves;
+    int64_t row = (int64_t)blockIdx.x * kFp4Waves + wave;
+
+    // x -> LDS in 4 KB blocks: block (j, m) holds bytes [4096 j, 4096 j + 4096)
+    // of row m (the x of chunks 64 j .. 64 j + 63, 64 bytes each), zeros past
+    // the row.  1 KB per wave instruction, instruction q by wave q % 8.
+    for (int q = wave; q < CPL * M * 4; q += kFp4Waves) {
+        const int blk = q >> 2, part = q & 3;
+        const int j = blk / M, m = blk % M;
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + m * a.ldx, a.k * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void*)(xs + q * 1024), 16, j * 4096 + part * 1024 + lane * 16, 0,
+            0, 0);
+    }
+    uint4 cv[CPL];
+    float sa[CPL];
+    uint32_t c8[CPL];
+    {
+        const Fp4RowSrc r = fp4_row_src<kDq>(a, row, chunks, kb);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) fp4_chunk_load<kDq>(r, lane + 64 * j, cv[j], sa[j], c8[j]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first row) landed
+    __syncthreads();                      // ... and every wave's
+
+    for (; row < a.n; row += nw) {
+        const Fp4RowSrc rn = fp4_row_src<kDq>(a, row + nw, chunks, kb);   // past n: nothing is read
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lane + 64 * j;
+            // A / 6 as A * fl32(1 / 6), as in the four-row kernel
+            const float A = kDq ? (float)c8[j] * (sa[j] / 255.0f) : sa[j];
+            const float d = A * (1.0f / 6.0f);
+            const uint32_t cw[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+            hh2 wv[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wv[q][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 0);
+                wv[q][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 1);
+                wv[q][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 2);
+                wv[q][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 3);
+            }
+            // the chunk's registers are free: request the same chunk of the next row
+            fp4_chunk_load<kDq>(rn, c, cv[j], sa[j], c8[j]);
+            // this chunk's x: 64 bytes per row at lane * 64 of blocks (j, m).
+            // x is the same for every weight row; with one row of x the
+            // compiler keeps the lane's chunks in registers across the rows (16
+            // per chunk), with more they would not fit: the base is then made
+            // opaque per chunk, so each chunk's x is read where it is used
+            uint32_t xb = (uint32_t)lane * 64u;
+            if constexpr (M > 1) asm volatile("" : "+v"(xb));
+            const __attribute__((address_space(3))) uint8_t* const xl =
+                (const __attribute__((address_space(3))) uint8_t*)xs + xb + j * M * 4096;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float part = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4u_l xv = *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(xl + m * 4096 + q * 16);
+                    const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        part = __builtin_amdgcn_fdot2(wv[q][b], __builtin_bit_cast(hh2, xq[b]), part, false);
+                }
+                acc[m] = fmaf(part, d, acc[m]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the bias through a range that is empty without one (no branch here,
+        // which would let the chunks' arithmetic sink past their barriers)
+        const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias, a.bias ? a.n * 2 : 0);
+        const float bias =
+            h2f((half_bits)__builtin_amdgcn_raw_buffer_load_b16(rbias, (int)row * 2, 0, 0));
+        // lane 0 stores the M outputs; the other lanes' offsets are out of
+        // range (a branch here would also let the arithmetic sink)
+        const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.out, ((M - 1) * a.ldout + a.n) * 2);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float s = wave_sum_f32(acc[m]);
+            const int off = lane == 0 ? (int)(m * a.ldout + row) * 2 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2h(s + bias), ro, off, 0, 0);
+        }
+    }
+}
+
+template <int M, int CPL>
+hipError_t launch_rows_cpl(const Fp4Args& a, hipStream_t stream) {
+    constexpr int kLds = CPL * M * 4096;
+    const int64_t per_cu = kLds <= 64 * 1024 ? 2 : 1;
+    int64_t grid = 256 * per_cu;
+    const int64_t need = (a.n + kFp4Waves - 1) / kFp4Waves;
+    if (need < grid) grid = need;
+    if (a.absmax)
+        hipLaunchKernelGGL((fp4_rows_kernel<M, CPL, false>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fp4_rows_kernel<M, CPL, true>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a);
+    return hipGetLastError();
+}
+
+// k <= 16384 (at most 8 chunks per lane): the LDS-x kernel
+template <int M>
+hipError_t launch_rows_m(const Fp4Args& a, hipStream_t stream) {
+    const int64_t chunks = a.k / 32;
+    if (chunks <= 128) return launch_rows_cpl<M, 2>(a, stream);
+    if (chunks <= 256) return launch_rows_cpl<M, 4>(a, stream);
+    return launch_rows_cpl<M, 8>(a, stream);
+}
+constexpr int64_t kFp4LdsMaxK = 16384;
+
 template <int M>
 hipError_t launch_gemv_m(const Fp4Args& a, hipStream_t stream) {
     if (M > 1 && a.k / 32 <= 256)
@@ -299,10 +471,15 @@ hipError_t launch_fp4_linear(const Fp4Args& in, hipStream_t stream) {
         a.x = in.x + i0 * in.ldx;
         a.out = static_cast<half_bits*>(in.out) + i0 * in.ldout;
         const int64_t mm = in.m - i0 < 4 ? in.m - i0 : 4;
-        hipError_t e = mm == 1 ? launch_gemv_m<1>(a, stream)
-                     : mm == 2 ? launch_gemv_m<2>(a, stream)
-                     : mm == 3 ? launch_gemv_m<3>(a, stream)
-                               : launch_gemv_m<4>(a, stream);
+        // one row of x with k <= 16384: the LDS-x kernel (13B m = 1: 2657 ->
+        // 2986 GB/s).  With more rows its LDS reads of x, 64 bytes per row of
+        // x for every 16 code bytes, outrun the LDS (13B m = 4: 1487 -> 1238
+        // GB/s), and the four-row kernel, which reuses each x chunk for four
+        // weight rows from registers, stays.
+        const hipError_t e = mm == 1 ? (a.k <= kFp4LdsMaxK ? launch_rows_m<1>(a, stream) : launch_gemv_m<1>(a, stream))
+                           : mm == 2 ? launch_gemv_m<2>(a, stream)
+                           : mm == 3 ? launch_gemv_m<3>(a, stream)
+                                     : launch_gemv_m<4>(a, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

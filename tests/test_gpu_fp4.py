@@ -93,6 +93,11 @@ LINEAR_CASES = [
     (3, 37, 13824, True, True),     # pipelined, four weight rows per workgroup, the last workgroup partial
     (2, 9, 9216, False, True),      # pipelined at m = 2, the last workgroup partial
     (1, 1000, 5120, True, False),
+    # one row of x: x staged in LDS, 2, 4 and 8 code chunks per lane, rows past the grid's waves
+    (1, 77, 13824, True, True),
+    (1, 4100, 4096, False, True),
+    (1, 9, 16384, False, False),
+    (1, 5, 16448, True, False),     # past 16384: the four-row kernel
 ]
 
 
