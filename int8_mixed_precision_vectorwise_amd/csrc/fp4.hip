@@ -404,6 +404,157 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
     }
 }
 
+// Two to four rows of x: the same staging of x in LDS, but a wave takes
+// groups of four weight rows (group v of the grid's nw waves: rows 4v .. 4v +
+// 3, then group v + nw, ...), and a lane the same code chunk of all four, so
+// each chunk of x read from LDS (64 bytes per row of x) serves four weight
+// rows.  A row's chunks go in segments of 256 (S = 4 per lane); a lane keeps
+// the current segment's codes of the four rows in registers and, as each
+// chunk slot is used, requests that slot of the next segment (of the same
+// group, or the first of its next group).
+template <int M, int NSEG, bool kDq>
+__global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
+    constexpr int R = 4, S = 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[NSEG * S * M * 4096];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t chunks = a.k / 32, kb = a.k / kBlk;
+    const int nseg = (int)((chunks + 255) / 256);
+    const int64_t groups = (a.n + R - 1) / R;
+    const int64_t nw = (int64_t)gridDim.x * kFp4Waves;
+    int64_t g = (int64_t)blockIdx.x * kFp4Waves + wave;
+    int sg = 0;
+
+    // x -> LDS in 4 KB blocks: block (J, m) holds bytes [4096 J, 4096 J + 4096)
+    // of row m (the x of chunks 64 J .. 64 J + 63), zeros past the row
+    for (int q = wave; q < NSEG * S * M * 4; q += kFp4Waves) {
+        const int blk = q >> 2, part = q & 3;
+        const int J = blk / M, m = blk % M;
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + m * a.ldx, a.k * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void*)(xs + q * 1024), 16, J * 4096 + part * 1024 + lane * 16, 0,
+            0, 0);
+    }
+    uint4 cv[R][S];
+    float sa[R][S];
+    uint32_t c8[R][S];
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const Fp4RowSrc src = fp4_row_src<kDq>(a, g * R + r, chunks, kb);
+#pragma unroll
+            for (int j = 0; j < S; ++j) fp4_chunk_load<kDq>(src, lane + 64 * j, cv[r][j], sa[r][j], c8[r][j]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first segment) landed
+    __syncthreads();                      // ... and every wave's
+
+    const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias, a.bias ? a.n * 2 : 0);
+    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.out, ((M - 1) * a.ldout + a.n) * 2);
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    while (g < groups) {
+        int64_t gn = g;
+        int sn = sg + 1;
+        if (sn == nseg) {
+            sn = 0;
+            gn = g + nw;
+        }
+        Fp4RowSrc nsrc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) nsrc[r] = fp4_row_src<kDq>(a, gn * R + r, chunks, kb);   // past n: nothing
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int c = sg * 256 + lane + 64 * j;
+            // this chunk's x, 64 bytes per row of x, read once for the four
+            // weight rows (the base is made opaque so that the reads stay here)
+            uint32_t xb = (uint32_t)lane * 64u;
+            asm volatile("" : "+v"(xb));
+            const __attribute__((address_space(3))) uint8_t* const xl =
+                (const __attribute__((address_space(3))) uint8_t*)xs + xb + (sg * S + j) * M * 4096;
+            uint32_t xq[M][16];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4u_l v = *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(xl + m * 4096 + q * 16);
+                    xq[m][4 * q] = v.x;
+                    xq[m][4 * q + 1] = v.y;
+                    xq[m][4 * q + 2] = v.z;
+                    xq[m][4 * q + 3] = v.w;
+                }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float A = kDq ? (float)c8[r][j] * (sa[r][j] / 255.0f) : sa[r][j];
+                const float d = A * (1.0f / 6.0f);
+                const uint32_t cw[4] = {cv[r][j].x, cv[r][j].y, cv[r][j].z, cv[r][j].w};
+                hh2 wv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    wv[4 * q] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 0);
+                    wv[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 1);
+                    wv[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 2);
+                    wv[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[q], 1.0f, 3);
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        part = __builtin_amdgcn_fdot2(wv[e], __builtin_bit_cast(hh2, xq[m][e]), part, false);
+                    acc[r][m] = fmaf(part, d, acc[r][m]);
+                }
+            }
+            // the slot's registers are free: request it for the next segment
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                fp4_chunk_load<kDq>(nsrc[r], sn * 256 + lane + 64 * j, cv[r][j], sa[r][j], c8[r][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (sn == 0) {
+            // group g done: its 4 x M sums, lane 0 stores (other lanes' offsets
+            // are out of range)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = g * R + r;
+                const float bias =
+                    h2f((half_bits)__builtin_amdgcn_raw_buffer_load_b16(rbias, (int)row * 2, 0, 0));
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const float sum = wave_sum_f32(acc[r][m]);
+                    const int off = lane == 0 && row < a.n ? (int)(m * a.ldout + row) * 2 : (int)0x80000000;
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2h(sum + bias), ro, off, 0, 0);
+                    acc[r][m] = 0.0f;
+                }
+            }
+        }
+        g = gn;
+        sg = sn;
+    }
+}
+
+template <int M, int NSEG>
+hipError_t launch_rows4_seg(const Fp4Args& a, hipStream_t stream) {
+    const int64_t groups = (a.n + 3) / 4;
+    int64_t grid = 256;
+    const int64_t need = (groups + kFp4Waves - 1) / kFp4Waves;
+    if (need < grid) grid = need;
+    if (a.absmax)
+        hipLaunchKernelGGL((fp4_rows4_kernel<M, NSEG, false>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fp4_rows4_kernel<M, NSEG, true>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a);
+    return hipGetLastError();
+}
+
+// two to four rows of x, k <= 16384
+template <int M>
+hipError_t launch_rows4_m(const Fp4Args& a, hipStream_t stream) {
+    return a.k / 32 <= 256 ? launch_rows4_seg<M, 1>(a, stream) : launch_rows4_seg<M, 2>(a, stream);
+}
+
 template <int M, int CPL>
 hipError_t launch_rows_cpl(const Fp4Args& a, hipStream_t stream) {
     constexpr int kLds = CPL * M * 4096;
@@ -480,10 +631,11 @@ hipError_t launch_fp4_linear(const Fp4Args& in, hipStream_t stream) {
         // x for every 16 code bytes, outrun the LDS (13B m = 4: 1487 -> 1238
         // GB/s), and the four-row kernel, which reuses each x chunk for four
         // weight rows from registers, stays.
-        const hipError_t e = mm == 1 ? (a.k <= kFp4LdsMaxK ? launch_rows_m<1>(a, stream) : launch_gemv_m<1>(a, stream))
-                           : mm == 2 ? launch_gemv_m<2>(a, stream)
-                           : mm == 3 ? launch_gemv_m<3>(a, stream)
-                                     : launch_gemv_m<4>(a, stream);
+        const bool lds = a.k <= kFp4LdsMaxK;
+        const hipError_t e = mm == 1 ? (lds ? launch_rows_m<1>(a, stream) : launch_gemv_m<1>(a, stream))
+                           : mm == 2 ? (lds ? launch_rows4_m<2>(a, stream) : launch_gemv_m<2>(a, stream))
+                           : mm == 3 ? (lds ? launch_rows4_m<3>(a, stream) : launch_gemv_m<3>(a, stream))
+                                     : (lds ? launch_rows4_m<4>(a, stream) : launch_gemv_m<4>(a, stream));
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

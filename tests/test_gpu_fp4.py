@@ -98,6 +98,11 @@ LINEAR_CASES = [
     (1, 4100, 4096, False, True),
     (1, 9, 16384, False, False),
     (1, 5, 16448, True, False),     # past 16384: the four-row kernel
+    # two to four rows of x: x staged in LDS, groups of four weight rows per wave
+    (4, 9001, 1024, True, True),    # more groups than the grid's waves, the last group partial
+    (3, 4099, 13824, False, True),  # two segments of 256 chunks per row
+    (2, 4098, 8192, True, False),   # one full segment
+    (4, 30, 16448, False, True),    # past 16384: the four-row kernel
 ]
 
 
