@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
 }
 
 // The decode linear: out[i, n] = fp16(sum_k x[i, k] * w'[n, k] + bias[n]) for
-// M rows of x.  A workgroup takes kRows weight rows; its 256 lanes split each
+// M rows of x, where x is too long for LDS (k > 16384; shorter rows take the
+// LDS-x kernels below).  A workgroup takes kRows weight rows; its 256 lanes split each
 // row into 16-byte code chunks (32 weights, half a block), lane t taking chunks
 // t, t + 256, ..., the same chunks of all kRows rows, so the lane's x chunk is
 // read once for them.  The next chunk's codes are requested before the current
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void fp4_dequant_kernel(Fp4Args a) {
 // reduced in the wave (DPP), then over the 4 waves in LDS.
 // weight rows per workgroup: 4 for three or more rows of x (fewer registers,
 // two waves per SIMD at four rows of x), 8 otherwise
-template <int M, bool kOne>
+template <int M>
 constexpr int fp4_rows() { return M >= 3 ? 4 : 8; }
 
 // Everything one chunk needs, loaded together: the codes of the kRows rows,
@@ -197,13 +198,9 @@ __device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M, R>& t, in
     }
 }
 
-// kOne: every lane has at most one chunk (k <= 8192): no next-chunk buffer,
-// fewer registers, more workgroups resident.  Taken for two or more rows of x
-// (13B up layer, m = 4: 40.7 -> 30.6 us); for one row the pipelined form
-// measured faster (14.0 against 16.6 us).
-template <int M, bool kOne>
+template <int M>
 __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
-    constexpr int kRows = fp4_rows<M, kOne>();
+    constexpr int kRows = fp4_rows<M>();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t chunks = a.k / 32, kb = a.k / kBlk;
     const int64_t n0 = (int64_t)blockIdx.x * kRows;
@@ -213,13 +210,7 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
     int64_t c = tid;
-    if (kOne) {
-        if (c < chunks) {
-            Fp4Chunk<M, kRows> cur;
-            fp4_load(a, n0, c, kb, cur);
-            fp4_compute(a, cur, n0, acc);
-        }
-    } else if (c < chunks) {
+    if (c < chunks) {
         Fp4Chunk<M, kRows> cur, nxt;
         fp4_load(a, n0, c, kb, cur);
         for (;;) {
@@ -581,12 +572,7 @@ constexpr int64_t kFp4LdsMaxK = 16384;
 
 template <int M>
 hipError_t launch_gemv_m(const Fp4Args& a, hipStream_t stream) {
-    if (M > 1 && a.k / 32 <= 256)
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, true>), dim3((unsigned)ceil_div(a.n, fp4_rows<M, true>())),
-                           dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((fp4_gemv_kernel<M, false>), dim3((unsigned)ceil_div(a.n, fp4_rows<M, false>())),
-                           dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fp4_gemv_kernel<M>), dim3((unsigned)ceil_div(a.n, fp4_rows<M>())), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -89,20 +89,23 @@ LINEAR_CASES = [
     (4, 64, 4096, True, True),
     (5, 31, 2048, False, False),    # two launches: rows 0-3, then row 4
     (9, 100, 1024, True, True),
-    (4, 50, 13824, False, False),   # more than 256 chunks of 32 weights per row: the pipelined form
-    (3, 37, 13824, True, True),     # pipelined, four weight rows per workgroup, the last workgroup partial
-    (2, 9, 9216, False, True),      # pipelined at m = 2, the last workgroup partial
+    (4, 50, 13824, False, False),   # more than 256 chunks of 32 weights per row: two segments
+    (3, 37, 13824, True, True),     # two segments, the last group of four weight rows partial
+    (2, 9, 9216, False, True),      # two segments at m = 2, the last group partial
     (1, 1000, 5120, True, False),
     # one row of x: x staged in LDS, 2, 4 and 8 code chunks per lane, rows past the grid's waves
     (1, 77, 13824, True, True),
     (1, 4100, 4096, False, True),
     (1, 9, 16384, False, False),
-    (1, 5, 16448, True, False),     # past 16384: the four-row kernel
+    (1, 5, 16448, True, False),     # past 16384: x from L2
     # two to four rows of x: x staged in LDS, groups of four weight rows per wave
     (4, 9001, 1024, True, True),    # more groups than the grid's waves, the last group partial
     (3, 4099, 13824, False, True),  # two segments of 256 chunks per row
     (2, 4098, 8192, True, False),   # one full segment
-    (4, 30, 16448, False, True),    # past 16384: the four-row kernel
+    # past 16384 (x does not fit LDS): the kernel that reads x from L2 for 4 or 8 weight rows
+    (4, 30, 16448, False, True),
+    (3, 9, 16448, True, True),
+    (2, 7, 16448, True, False),
 ]
 
 
