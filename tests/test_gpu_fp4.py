@@ -98,10 +98,16 @@ LINEAR_CASES = [
     (1, 4100, 4096, False, True),
     (1, 9, 16384, False, False),
     (1, 5, 16448, True, False),     # past 16384: x from L2
-    # two to four rows of x: x staged in LDS, groups of four weight rows per wave
-    (4, 9001, 1024, True, True),    # more groups than the grid's waves, the last group partial
+    # two to four rows of x: x staged in LDS, the workgroups' shares of the weight rows
+    (4, 9001, 1024, True, True),    # two tiles of 32 rows per workgroup, the last share partial
     (3, 4099, 13824, False, True),  # two segments of 256 chunks per row
     (2, 4098, 8192, True, False),   # one full segment
+    # two to four rows of x on the matrix cores up to k = 14336 and n = 16384; past them
+    # the four-row LDS-x kernel
+    (4, 33, 16384, True, True),
+    (2, 5000, 15360, False, False),
+    (2, 16500, 1024, False, True),
+    (3, 300, 64, True, False),      # one block per row: waves past the last block
     # past 16384 (x does not fit LDS): the kernel that reads x from L2 for 4 or 8 weight rows
     (4, 30, 16448, False, True),
     (3, 9, 16448, True, True),
