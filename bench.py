@@ -741,7 +741,7 @@ def fp4_traffic_summary(directory: str, workload: str, launches: int) -> int:
     copy_wr give the factors)."""
     specs, _ = workload_specs(workload)
     f_scale, w_scale = _copy_scales(directory)
-    k4 = ("fp4_gemv_kernel", "fp4_rows_kernel", "fp4_rows4_kernel")
+    k4 = ("fp4_gemv_kernel", "fp4_rows_kernel", "fp4_rows4_kernel", "fp4_mfma16_kernel")
     n32, n64, n128 = (_per_layer(directory, "fp4_rd", c, launches, k4) for c in RD_COUNTERS[:3])
     w64, wall = (_per_layer(directory, "fp4_wr", c, launches, k4) for c in WR_COUNTERS)
     if min(len(n32), len(w64)) < len(specs):
@@ -890,8 +890,8 @@ def fp4_run(args) -> int:
                    "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": traffic,
-                     "kernel": "fp4_rows_kernel (one row of x) / fp4_rows4_kernel (two to four) for k <= 16384, "
-                               "fp4_gemv_kernel past it", "per_launch_us": {k: round(v, 3) for k, v in per_us.items()},
+                     "kernel": "fp4_rows_kernel (one row of x, k <= 16384) / fp4_mfma16_kernel (two to four, "
+                               "k <= 14336) / fp4_rows4_kernel / fp4_gemv_kernel (k > 16384)", "per_launch_us": {k: round(v, 3) for k, v in per_us.items()},
                      "timing": "HIP events around graph replays of each layer's launches"},
         "cpu_baseline": cpu}), flush=True)
     return 0

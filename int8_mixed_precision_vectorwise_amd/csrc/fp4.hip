@@ -528,38 +528,40 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
 }
 
 // Two to four rows of x on the matrix cores.  Every workgroup takes the same
-// number of weight rows, R = ceil(n / grid) (held as T tiles of 32 rows, rows
+// number of weight rows, R = ceil(n / grid) (held as T tiles of 16 rows, rows
 // past R masked), so every CU streams the same bytes; its 8 waves split the
-// blocks of 64 weights (wave w: blocks w, w + 8, ...) and meet in LDS at the
-// end.  x sits in LDS as for the kernels above, in 4 KB blocks, with one more
-// block of zeros per 4 KB slice for the rows past M.
+// chunks of 128 weights (wave w: chunks w, w + 8, ...) and meet in LDS at the
+// end, summed in wave order.  x sits in LDS as for the kernels above, in 4 KB
+// blocks, with one more block of zeros per 4 KB slice for the rows past M.
 //
-// For block b a lane (row i = lane % 32, half h = lane / 32) holds 16 code
-// bytes of weight row lane % 32 of the tile: weights 64 b + 32 h .. + 31.
-// Step s of v_mfma_f32_32x32x16_f16 takes weights 64 b + 32 h + 8 s .. + 7 of
-// both operands (the same relabelling of k in x and in the weights, so the
-// dot product is unchanged), so all four steps stay inside the block and its
-// scale applies to their sum: acc += fl32(A / 6) * P_b.  Lanes 0-31 hold the
-// outputs of rows 0-3 of x (accumulators 0-3).
+// A chunk is two blocks of 64.  Lane (n, g) (n = lane % 16, g = lane / 16)
+// holds 16 code bytes of weight row n of the tile: weights 128 c + 32 g .. +
+// 31, so a load is 64 bytes of each of 16 rows.  Step s of
+// v_mfma_f32_16x16x32_f16 takes weights 128 c + 32 g + 8 s .. + 7 of both
+// operands (the same relabelling of k in x and in the weights, so the dot
+// product is unchanged).  Lanes g = 0, 1 then carry block 2 c and lanes g = 2,
+// 3 block 2 c + 1: each step runs twice, with the x operand of the other
+// block's lanes read from the zero row, into one sum per block, and each
+// block's scale applies to its sum: acc += fl32(A / 6) * P_b.  Lanes 0-15
+// hold the outputs of rows 0-3 of x.
+typedef float v4f_16 __attribute__((ext_vector_type(4)));
 constexpr int kFp4MfmaJ = 7;    // 4 KB x blocks per row of x: k <= 14336
 
 template <int M, int T, bool kDq>
-__global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma_kernel(Fp4Args a, int64_t rows_per_wg) {
-    // blocks per wave in flight: 8 KB of codes per wave (twice as many
-    // measured slower: 13B m = 4 1735 -> 1546 GB/s)
-    constexpr int W = kFp4Waves, D = T == 1 ? 8 : 4;
+__global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, int64_t rows_per_wg) {
+    constexpr int W = kFp4Waves, D = T <= 2 ? 4 : 2;   // chunks per wave in flight: 8 KB of codes
     __shared__ __attribute__((aligned(1024))) uint8_t xs[kFp4MfmaJ * (M + 1) * 4096];
-    __shared__ float red[W][T][4][32];
+    __shared__ float red[W][T][4][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t kb = a.k / kBlk;
+    const int64_t kb = a.k / kBlk, kc = (a.k + 127) / 128;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
     int64_t valid = a.n - r0;
-    if (valid > rows_per_wg) valid = rows_per_wg;   // >= 1: the grid covers n exactly
+    if (valid > rows_per_wg) valid = rows_per_wg;
 
-    // x -> LDS: block (J, m) at (J (M + 1) + m) * 4096 holds bytes [4096 J,
-    // 4096 J + 4096) of row m of x; m = M is zeros
-    for (int q = wave; q < kFp4MfmaJ * (M + 1) * 4; q += W) {
+    // only the blocks that x reaches (the reads never go past them)
+    const int jx = (int)((a.k * 2 + 4095) / 4096);
+    for (int q = wave; q < jx * (M + 1) * 4; q += W) {
         const int blk = q >> 2, part = q & 3;
         const int J = blk / (M + 1), m = blk % (M + 1);
         const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + (m < M ? m : 0) * a.ldx, m < M ? a.k * 2 : 0);
@@ -567,68 +569,71 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma_kernel(Fp4Args a, int
             rx, (__attribute__((address_space(3))) void*)(xs + q * 1024), 16, J * 4096 + part * 1024 + lane * 16, 0,
             0, 0);
     }
-    const int l32 = lane & 31, h = lane >> 5;
-    const int ir = l32 < M ? l32 : M;               // x row of this lane's A operand (M: zeros)
-    // the workgroup's rows of codes and scales (rows past `valid` read zeros)
+    const int l16 = lane & 15, g = lane >> 4;
+    const int ir = l16 < M ? l16 : M;
+    const int ir_lo = g < 2 ? ir : M, ir_hi = g >= 2 ? ir : M;   // x rows of the two passes
     const __amdgpu_buffer_rsrc_t rc = buf_rsrc(a.codes + r0 * a.ldc, (valid - 1) * a.ldc + a.k / 2);
     const __amdgpu_buffer_rsrc_t rs =
         kDq ? buf_rsrc(a.c8 + r0 * kb, valid * kb) : buf_rsrc(a.absmax + r0 * kb, valid * kb * 4);
     const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(a.s2, kDq ? ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4 : 0);
 
     uint4 cv[D][T];
-    float sa[D][T];
-    uint32_t c8[D][T];
-    auto load = [&](int u, int64_t b) {   // block b into ring slot u (past kb: zeros)
-        const bool live = b < kb;
+    float sa[D][T][2];
+    uint32_t c8[D][T][2];
+    auto load = [&](int u, int64_t c) {   // chunk c into ring slot u (past the row: zeros)
+        const int64_t myblk = 2 * c + (g >> 1);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int rr = 32 * t + l32;
-            const int co = live ? (int)(rr * a.ldc + 32 * b + 16 * h) : (int)0x80000000;
+            const int rr = 16 * t + l16;
+            const int co = myblk < kb ? (int)(rr * a.ldc + 64 * c + 16 * g) : (int)0x80000000;
             cv[u][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 2));
-            if constexpr (kDq) {
-                const int so = live ? (int)(rr * kb + b) : (int)0x80000000;
-                c8[u][t] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
-                sa[u][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                         r2, (int)(((r0 + rr) * kb + b) / kDqGroup) * 4, 0, 0));
-            } else {
-                const int so = live ? (int)(rr * kb + b) * 4 : (int)0x80000000;
-                sa[u][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
-                c8[u][t] = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t b = 2 * c + e;
+                if constexpr (kDq) {
+                    const int so = b < kb ? (int)(rr * kb + b) : (int)0x80000000;
+                    c8[u][t][e] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
+                    sa[u][t][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                r2, (int)(((r0 + rr) * kb + b) / kDqGroup) * 4, 0, 0));
+                } else {
+                    const int so = b < kb ? (int)(rr * kb + b) * 4 : (int)0x80000000;
+                    sa[u][t][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
+                    c8[u][t][e] = 0;
+                }
             }
         }
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) load(u, wave + (int64_t)W * u);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first blocks) landed
-    __syncthreads();                      // ... and every wave's
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
 
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
-    for (int64_t b0 = wave; b0 < kb; b0 += (int64_t)W * D) {
+    for (int64_t c0 = wave; c0 < kc; c0 += (int64_t)W * D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            const int64_t b = b0 + (int64_t)W * u;
-            if (b < kb) {
-                // the four A steps of block b: x[ir, 64 b + 32 h + 8 s .. + 7]
-                uint32_t xb = (uint32_t)(((b >> 5) * (M + 1) + ir) * 4096 + 128 * (b & 31) + 64 * h);
-                asm volatile("" : "+v"(xb));
-                const __attribute__((address_space(3))) uint8_t* const xl =
-                    (const __attribute__((address_space(3))) uint8_t*)xs + xb;
-                v8h xa[4];
+            const int64_t c = c0 + (int64_t)W * u;
+            if (c < kc) {
+                // x of chunk c: bytes 256 c + 64 g + 16 s of row ir, in block J = c / 16
+                const uint32_t off = (uint32_t)(256 * (c & 15) + 64 * g);
+                uint32_t xlo = (uint32_t)(((c >> 4) * (M + 1) + ir_lo) * 4096) + off;
+                uint32_t xhi = (uint32_t)(((c >> 4) * (M + 1) + ir_hi) * 4096) + off;
+                asm volatile("" : "+v"(xlo), "+v"(xhi));
+                typedef const __attribute__((address_space(3))) v8h lv8h;
+                v8h alo[4], ahi[4];
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    xa[st] = *reinterpret_cast<const __attribute__((address_space(3))) v8h*>(xl + 16 * st);
+                for (int st = 0; st < 4; ++st) {
+                    alo[st] = *reinterpret_cast<lv8h*>((const __attribute__((address_space(3))) uint8_t*)xs + xlo + 16 * st);
+                    ahi[st] = *reinterpret_cast<lv8h*>((const __attribute__((address_space(3))) uint8_t*)xs + xhi + 16 * st);
+                }
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const float A = kDq ? (float)c8[u][t] * (sa[u][t] / 255.0f) : sa[u][t];
-                    const float d = A * (1.0f / 6.0f);
                     const uint32_t cw[4] = {cv[u][t].x, cv[u][t].y, cv[u][t].z, cv[u][t].w};
-                    v16f p;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) p[r] = 0.0f;
+                    v4f_16 plo = {0.0f, 0.0f, 0.0f, 0.0f}, phi = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
                         const hh2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 0);
@@ -636,38 +641,44 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma_kernel(Fp4Args a, int
                         const hh2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 2);
                         const hh2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 3);
                         const v8h wb = {w0.x, w0.y, w1.x, w1.y, w2.x, w2.y, w3.x, w3.y};
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[st], wb, p, 0, 0, 0);
+                        plo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[st], wb, plo, 0, 0, 0);
+                        phi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[st], wb, phi, 0, 0, 0);
+                    }
+                    float d[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float A = kDq ? (float)c8[u][t][e] * (sa[u][t][e] / 255.0f) : sa[u][t][e];
+                        d[e] = A * (1.0f / 6.0f);
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(p[r], d, acc[t][r]);
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(phi[r], d[1], fmaf(plo[r], d[0], acc[t][r]));
                 }
             }
-            load(u, b + (int64_t)W * D);   // the slot's next block
+            load(u, c + (int64_t)W * D);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // the loads past the last block
-    // the 8 waves' sums meet in LDS; wave 0 adds them in wave order
-    if (lane < 32) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    if (lane < 16) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][t][r][l32] = acc[t][r];
+            for (int r = 0; r < 4; ++r) red[wave][t][r][l16] = acc[t][r];
     }
     __syncthreads();
-    if (wave == 0 && lane < 32) {
+    if (wave == 0 && lane < 16) {
         const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias, a.bias ? a.n * 2 : 0);
         const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.out, ((M - 1) * a.ldout + a.n) * 2);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int rr = 32 * t + l32;
+            const int rr = 16 * t + l16;
             const int64_t row = r0 + rr;
             const float bias = h2f((half_bits)__builtin_amdgcn_raw_buffer_load_b16(rbias, (int)row * 2, 0, 0));
 #pragma unroll
             for (int r = 0; r < M; ++r) {
                 float sum = 0.0f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) sum += red[w][t][r][l32];
+                for (int w = 0; w < W; ++w) sum += red[w][t][r][l16];
                 const int off = rr < valid ? (int)(r * a.ldout + row) * 2 : (int)0x80000000;
                 __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2h(sum + bias), ro, off, 0, 0);
             }
@@ -676,13 +687,13 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma_kernel(Fp4Args a, int
 }
 
 template <int M, int T>
-hipError_t launch_mfma_t(const Fp4Args& a, int64_t grid, int64_t rows, hipStream_t stream) {
+hipError_t launch_mfma16_t(const Fp4Args& a, int64_t grid, int64_t rows, hipStream_t stream) {
     if (a.absmax)
-        hipLaunchKernelGGL((fp4_mfma_kernel<M, T, false>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a,
-                           rows);
+        hipLaunchKernelGGL((fp4_mfma16_kernel<M, T, false>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream,
+                           a, rows);
     else
-        hipLaunchKernelGGL((fp4_mfma_kernel<M, T, true>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream, a,
-                           rows);
+        hipLaunchKernelGGL((fp4_mfma16_kernel<M, T, true>), dim3((unsigned)grid), dim3(64 * kFp4Waves), 0, stream,
+                           a, rows);
     return hipGetLastError();
 }
 
@@ -693,7 +704,7 @@ bool launch_mfma_m(const Fp4Args& a, hipStream_t stream, hipError_t* err) {
     if (a.k > kFp4MfmaJ * 2048 || a.n > 256 * 64) return false;
     const int64_t rows = (a.n + 255) / 256;          // weight rows per workgroup
     const int64_t grid = (a.n + rows - 1) / rows;    // every workgroup has at least one row
-    *err = rows <= 32 ? launch_mfma_t<M, 1>(a, grid, rows, stream) : launch_mfma_t<M, 2>(a, grid, rows, stream);
+    *err = rows <= 32 ? launch_mfma16_t<M, 2>(a, grid, rows, stream) : launch_mfma16_t<M, 4>(a, grid, rows, stream);
     return true;
 }
 
