@@ -532,7 +532,7 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
 // past R masked), so every CU streams the same bytes; its 8 waves split the
 // chunks of 128 weights (wave w: chunks w, w + 8, ...) and meet in LDS at the
 // end, summed in wave order.  x sits in LDS as for the kernels above, in 4 KB
-// blocks, with one more block of zeros per 4 KB slice for the rows past M.
+// blocks, and so do the workgroup's block scale factors fl32(A / 6), read once.
 //
 // A chunk is two blocks of 64.  Lane (n, g) (n = lane % 16, g = lane / 16)
 // holds 16 code bytes of weight row n of the tile: weights 128 c + 32 g .. +
@@ -541,16 +541,20 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
 // operands (the same relabelling of k in x and in the weights, so the dot
 // product is unchanged).  Lanes g = 0, 1 then carry block 2 c and lanes g = 2,
 // 3 block 2 c + 1: each step runs twice, with the x operand of the other
-// block's lanes read from the zero row, into one sum per block, and each
+// block's lanes zeroed, into one sum per block, and each
 // block's scale applies to its sum: acc += fl32(A / 6) * P_b.  Lanes 0-15
 // hold the outputs of rows 0-3 of x.
 typedef float v4f_16 __attribute__((ext_vector_type(4)));
-constexpr int kFp4MfmaJ = 7;    // 4 KB x blocks per row of x: k <= 14336
+constexpr int kFp4MfmaJ = 7;          // 4 KB x blocks per row of x: k <= 14336
+constexpr int kFp4MfmaScales = 8192;  // block scales per workgroup: rows_per_wg * k / 64 + 2
 
 template <int M, int T, bool kDq>
 __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, int64_t rows_per_wg) {
     constexpr int W = kFp4Waves, D = T <= 2 ? 4 : 2;   // chunks per wave in flight: 8 KB of codes
-    __shared__ __attribute__((aligned(1024))) uint8_t xs[kFp4MfmaJ * (M + 1) * 4096];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[kFp4MfmaJ * M * 4096];
+    // the workgroup's block scale factors fl32(A / 6) (read here once, with
+    // whole-line loads: in the loop each load would touch 16 rows' scales)
+    __shared__ float sd[kFp4MfmaScales];
     __shared__ float red[W][T][4][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -559,27 +563,19 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
     int64_t valid = a.n - r0;
     if (valid > rows_per_wg) valid = rows_per_wg;
 
-    // only the blocks that x reaches (the reads never go past them)
+    // x -> LDS: block (J, m) at (J M + m) * 4096, only the blocks x reaches
     const int jx = (int)((a.k * 2 + 4095) / 4096);
-    for (int q = wave; q < jx * (M + 1) * 4; q += W) {
+    for (int q = wave; q < jx * M * 4; q += W) {
         const int blk = q >> 2, part = q & 3;
-        const int J = blk / (M + 1), m = blk % (M + 1);
-        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + (m < M ? m : 0) * a.ldx, m < M ? a.k * 2 : 0);
+        const int J = blk / M, m = blk % M;
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + m * a.ldx, a.k * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rx, (__attribute__((address_space(3))) void*)(xs + q * 1024), 16, J * 4096 + part * 1024 + lane * 16, 0,
             0, 0);
     }
     const int l16 = lane & 15, g = lane >> 4;
-    const int ir = l16 < M ? l16 : M;
-    const int ir_lo = g < 2 ? ir : M, ir_hi = g >= 2 ? ir : M;   // x rows of the two passes
     const __amdgpu_buffer_rsrc_t rc = buf_rsrc(a.codes + r0 * a.ldc, (valid - 1) * a.ldc + a.k / 2);
-    const __amdgpu_buffer_rsrc_t rs =
-        kDq ? buf_rsrc(a.c8 + r0 * kb, valid * kb) : buf_rsrc(a.absmax + r0 * kb, valid * kb * 4);
-    const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(a.s2, kDq ? ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4 : 0);
-
     uint4 cv[D][T];
-    float sa[D][T][2];
-    uint32_t c8[D][T][2];
     auto load = [&](int u, int64_t c) {   // chunk c into ring slot u (past the row: zeros)
         const int64_t myblk = 2 * c + (g >> 1);
 #pragma unroll
@@ -587,27 +583,46 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
             const int rr = 16 * t + l16;
             const int co = myblk < kb ? (int)(rr * a.ldc + 64 * c + 16 * g) : (int)0x80000000;
             cv[u][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 2));
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int64_t b = 2 * c + e;
-                if constexpr (kDq) {
-                    const int so = b < kb ? (int)(rr * kb + b) : (int)0x80000000;
-                    c8[u][t][e] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
-                    sa[u][t][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                r2, (int)(((r0 + rr) * kb + b) / kDqGroup) * 4, 0, 0));
-                } else {
-                    const int so = b < kb ? (int)(rr * kb + b) * 4 : (int)0x80000000;
-                    sa[u][t][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
-                    c8[u][t][e] = 0;
-                }
-            }
         }
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) load(u, wave + (int64_t)W * u);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
+    // the scale factors fl32(A / 6) of rows r0 .. r0 + rows_per_wg, the whole
+    // area (zeros past the valid rows): every load goes out before the first
+    // is used.  A is the absmax, or fl32(c8 * fl32(s2 / 255)).
+    constexpr int kFill = kFp4MfmaScales / (64 * W);
+    {
+        float v[kFill];
+        if constexpr (kDq) {
+            const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.c8 + r0 * kb, valid * kb);
+            const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(a.s2, ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4);
+            uint32_t cq[kFill];
+            float s2v[kFill];
+#pragma unroll
+            for (int it = 0; it < kFill; ++it) {
+                const int i = tid + 64 * W * it;
+                cq[it] = __builtin_amdgcn_raw_buffer_load_b8(rs, i, 0, 0);
+                s2v[it] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(r2, (int)((r0 * kb + i) / kDqGroup) * 4, 0, 0));
+            }
+#pragma unroll
+            for (int it = 0; it < kFill; ++it) v[it] = (float)cq[it] * (s2v[it] / 255.0f);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.absmax + r0 * kb, valid * kb * 4);
+#pragma unroll
+            for (int it = 0; it < kFill; ++it)
+                v[it] = __builtin_bit_cast(float,
+                                           __builtin_amdgcn_raw_buffer_load_b32(rs, (tid + 64 * W * it) * 4, 0, 0));
+        }
+        // A / 6 as A * fl32(1 / 6), as in the kernels above
+#pragma unroll
+        for (int it = 0; it < kFill; ++it) sd[tid + 64 * W * it] = v[it] * (1.0f / 6.0f);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first chunks) landed
+    __syncthreads();                      // ... and every wave's
 
+    const int irc = l16 < M ? l16 : M - 1;                  // a valid x row; masked below
+    const bool lo_ok = g < 2 && l16 < M, hi_ok = g >= 2 && l16 < M;
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -618,17 +633,29 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
         for (int u = 0; u < D; ++u) {
             const int64_t c = c0 + (int64_t)W * u;
             if (c < kc) {
-                // x of chunk c: bytes 256 c + 64 g + 16 s of row ir, in block J = c / 16
-                const uint32_t off = (uint32_t)(256 * (c & 15) + 64 * g);
-                uint32_t xlo = (uint32_t)(((c >> 4) * (M + 1) + ir_lo) * 4096) + off;
-                uint32_t xhi = (uint32_t)(((c >> 4) * (M + 1) + ir_hi) * 4096) + off;
-                asm volatile("" : "+v"(xlo), "+v"(xhi));
-                typedef const __attribute__((address_space(3))) v8h lv8h;
+                // x of chunk c: bytes 256 c + 64 g + 16 s of row irc, in block J = c / 16;
+                // the two passes keep only block 2c's lanes (g < 2) or block 2c + 1's
+                uint32_t xo = (uint32_t)(((c >> 4) * M + irc) * 4096 + 256 * (c & 15) + 64 * g);
+                asm volatile("" : "+v"(xo));
+                typedef const __attribute__((address_space(3))) v4u_l lv4u;
                 v8h alo[4], ahi[4];
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    alo[st] = *reinterpret_cast<lv8h*>((const __attribute__((address_space(3))) uint8_t*)xs + xlo + 16 * st);
-                    ahi[st] = *reinterpret_cast<lv8h*>((const __attribute__((address_space(3))) uint8_t*)xs + xhi + 16 * st);
+                    const v4u_l v = *reinterpret_cast<lv4u*>((const __attribute__((address_space(3))) uint8_t*)xs + xo + 16 * st);
+                    const v4u_l z = {0u, 0u, 0u, 0u};
+                    alo[st] = __builtin_bit_cast(v8h, lo_ok ? v : z);
+                    ahi[st] = __builtin_bit_cast(v8h, hi_ok ? v : z);
+                }
+                // the scale factors of the chunk's two blocks for this lane's
+                // weight rows (a row past the share reads row 0's: its codes
+                // are zero), read before the MFMAs
+                float d[T][2];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int rr = 16 * t + l16;
+                    const int64_t si = (rr < valid ? rr : 0) * kb + 2 * c;
+                    d[t][0] = sd[si];
+                    d[t][1] = sd[si + 1];
                 }
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
@@ -644,14 +671,8 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
                         plo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[st], wb, plo, 0, 0, 0);
                         phi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[st], wb, phi, 0, 0, 0);
                     }
-                    float d[2];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float A = kDq ? (float)c8[u][t][e] * (sa[u][t][e] / 255.0f) : sa[u][t][e];
-                        d[e] = A * (1.0f / 6.0f);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(phi[r], d[1], fmaf(plo[r], d[0], acc[t][r]));
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(phi[r], d[t][1], fmaf(plo[r], d[t][0], acc[t][r]));
                 }
             }
             load(u, c + (int64_t)W * D);
@@ -703,6 +724,7 @@ template <int M>
 bool launch_mfma_m(const Fp4Args& a, hipStream_t stream, hipError_t* err) {
     if (a.k > kFp4MfmaJ * 2048 || a.n > 256 * 64) return false;
     const int64_t rows = (a.n + 255) / 256;          // weight rows per workgroup
+    if (rows * (a.k / kBlk) + 2 > kFp4MfmaScales) return false;
     const int64_t grid = (a.n + rows - 1) / rows;    // every workgroup has at least one row
     *err = rows <= 32 ? launch_mfma16_t<M, 2>(a, grid, rows, stream) : launch_mfma16_t<M, 4>(a, grid, rows, stream);
     return true;
