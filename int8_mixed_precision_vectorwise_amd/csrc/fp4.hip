@@ -576,28 +576,29 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
     const int l16 = lane & 15, g = lane >> 4;
     const __amdgpu_buffer_rsrc_t rc = buf_rsrc(a.codes + r0 * a.ldc, (valid - 1) * a.ldc + a.k / 2);
     uint4 cv[D][T];
+    const int lane_off = (int)(l16 * a.ldc) + 16 * g;   // this lane's row and 16 bytes in a chunk
     auto load = [&](int u, int64_t c) {   // chunk c into ring slot u (past the row: zeros)
-        const int64_t myblk = 2 * c + (g >> 1);
+        const bool live = 2 * c + (g >> 1) < kb;
+        const int base = (int)(64 * c) + lane_off;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int rr = 16 * t + l16;
-            const int co = myblk < kb ? (int)(rr * a.ldc + 64 * c + 16 * g) : (int)0x80000000;
+            const int co = live ? base + (int)(16 * t * a.ldc) : (int)0x80000000;
             cv[u][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 2));
         }
     };
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(u, wave + (int64_t)W * u);
     // the scale factors fl32(A / 6) of rows r0 .. r0 + rows_per_wg, the whole
     // area (zeros past the valid rows): every load goes out before the first
     // is used.  A is the absmax, or fl32(c8 * fl32(s2 / 255)).
+    // The first D chunks are requested after these loads, and only the
+    // copies and the scales are waited for (loads complete in order).
     constexpr int kFill = kFp4MfmaScales / (64 * W);
     {
         float v[kFill];
+        uint32_t cq[kFill];
+        float s2v[kFill];
         if constexpr (kDq) {
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.c8 + r0 * kb, valid * kb);
             const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(a.s2, ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4);
-            uint32_t cq[kFill];
-            float s2v[kFill];
 #pragma unroll
             for (int it = 0; it < kFill; ++it) {
                 const int i = tid + 64 * W * it;
@@ -605,8 +606,6 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
                 s2v[it] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(r2, (int)((r0 * kb + i) / kDqGroup) * 4, 0, 0));
             }
-#pragma unroll
-            for (int it = 0; it < kFill; ++it) v[it] = (float)cq[it] * (s2v[it] / 255.0f);
         } else {
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.absmax + r0 * kb, valid * kb * 4);
 #pragma unroll
@@ -614,12 +613,21 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
                 v[it] = __builtin_bit_cast(float,
                                            __builtin_amdgcn_raw_buffer_load_b32(rs, (tid + 64 * W * it) * 4, 0, 0));
         }
+        __builtin_amdgcn_sched_barrier(0);   // the scale loads go out before the chunks'
+#pragma unroll
+        for (int u = 0; u < D; ++u) load(u, wave + (int64_t)W * u);
+        __builtin_amdgcn_sched_barrier(0);
+        static_assert(D * T <= 15, "the wait below counts the chunk loads in four bits");
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (D * T));   // vmcnt(D T): the copies and the scales landed
+        if constexpr (kDq) {
+#pragma unroll
+            for (int it = 0; it < kFill; ++it) v[it] = (float)cq[it] * (s2v[it] / 255.0f);
+        }
         // A / 6 as A * fl32(1 / 6), as in the kernels above
 #pragma unroll
         for (int it = 0; it < kFill; ++it) sd[tid + 64 * W * it] = v[it] * (1.0f / 6.0f);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first chunks) landed
-    __syncthreads();                      // ... and every wave's
+    __syncthreads();   // every wave's copies and factors are in LDS
 
     const int irc = l16 < M ? l16 : M - 1;                  // a valid x row; masked below
     const bool lo_ok = g < 2 && l16 < M, hi_ok = g >= 2 && l16 < M;
