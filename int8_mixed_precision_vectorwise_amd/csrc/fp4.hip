@@ -41,6 +41,18 @@ __device__ inline float block_scale(const Fp4Args& a, int64_t blk) {
     return (float)a.c8[blk] * step;
 }
 
+// The factor fl32(A / 6) that the decode linear applies to a half block's fp32
+// sum, from the raw scale values: the absmax sa times fl32(1 / 6), or, when
+// double-quantized (A = c8 * s2 / 255, sa = s2), c8 * (s2 * fl32(1 / 1530)).
+// Three roundings of relative size 2^-24 each, so within a few ulp of
+// fl32(fl32(c8 * fl32(s2 / 255)) / 6), the weight the dequantize op builds: far
+// inside the rounding of the fp32 sums, and a few operations per chunk instead
+// of an IEEE division sequence.
+template <bool kDq>
+__device__ inline float fp4_factor(float sa, uint32_t c8) {
+    return kDq ? (float)c8 * (sa * (1.0f / 1530.0f)) : sa * (1.0f / 6.0f);
+}
+
 // One lane per 8 weights, 8 lanes per block: absmax, codes, packed nibbles
 // (element 2j in the low nibble of byte j).
 template <bool kVec>
@@ -168,12 +180,7 @@ __device__ inline void fp4_compute(const Fp4Args& a, const Fp4Chunk<M, R>& t, in
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (n0 + r >= a.n) break;  // the same for the whole workgroup
-        // block scale A (the absmax, or fl32(c8 * fl32(s2 / 255))), then A / 6 as
-        // A * fl32(1 / 6): within one ulp of the IEEE quotient the dequantize op
-        // uses, far inside the fp32 sums' rounding, and one multiply instead of a
-        // division sequence per row and chunk
-        const float A = a.absmax ? t.sa[r] : (float)t.c8[r] * (t.sa[r] / 255.0f);
-        const float d = A * (1.0f / 6.0f);
+        const float d = a.absmax ? fp4_factor<false>(t.sa[r], 0) : fp4_factor<true>(t.sa[r], t.c8[r]);
         const uint32_t cw[4] = {t.cv[r].x, t.cv[r].y, t.cv[r].z, t.cv[r].w};
         float part[M];
 #pragma unroll
@@ -264,6 +271,7 @@ typedef unsigned v4u_l __attribute__((ext_vector_type(4)));
 struct Fp4RowSrc {
     __amdgpu_buffer_rsrc_t codes, scales, s2;
     int64_t b0;   // first block of the row
+    uint32_t g0;  // the same, as the 32-bit base of the group index (n k / 64 < 2^32)
 };
 
 template <bool kDq>
@@ -271,6 +279,7 @@ __device__ inline Fp4RowSrc fp4_row_src(const Fp4Args& a, int64_t row, int64_t c
     const bool live = row < a.n;
     Fp4RowSrc r;
     r.b0 = live ? row * kb : 0;
+    r.g0 = (uint32_t)r.b0;
     r.codes = buf_rsrc(a.codes + (live ? row * a.ldc : 0), live ? chunks * 16 : 0);
     if constexpr (kDq) {
         r.scales = buf_rsrc(a.c8 + r.b0, live ? kb : 0);
@@ -291,7 +300,7 @@ __device__ inline void fp4_chunk_load(const Fp4RowSrc& r, int c, uint4& cv, floa
     if constexpr (kDq) {
         c8 = __builtin_amdgcn_raw_buffer_load_b8(r.scales, c >> 1, 0, 0);
         sa = __builtin_bit_cast(float,
-                                __builtin_amdgcn_raw_buffer_load_b32(r.s2, (int)((r.b0 + (c >> 1)) / kDqGroup) * 4, 0, 0));
+                                __builtin_amdgcn_raw_buffer_load_b32(r.s2, (int)(((r.g0 + (uint32_t)(c >> 1)) / kDqGroup) * 4), 0, 0));
     } else {
         sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r.scales, (c >> 1) * 4, 0, 0));
         c8 = 0;
@@ -337,9 +346,7 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = lane + 64 * j;
-            // A / 6 as A * fl32(1 / 6), as in the four-row kernel
-            const float A = kDq ? (float)c8[j] * (sa[j] / 255.0f) : sa[j];
-            const float d = A * (1.0f / 6.0f);
+            const float d = fp4_factor<kDq>(sa[j], c8[j]);
             const uint32_t cw[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
             hh2 wv[4][4];
 #pragma unroll
@@ -479,8 +486,7 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
                 }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float A = kDq ? (float)c8[r][j] * (sa[r][j] / 255.0f) : sa[r][j];
-                const float d = A * (1.0f / 6.0f);
+                const float d = fp4_factor<kDq>(sa[r][j], c8[r][j]);
                 const uint32_t cw[4] = {cv[r][j].x, cv[r][j].y, cv[r][j].z, cv[r][j].w};
                 hh2 wv[16];
 #pragma unroll
@@ -590,14 +596,13 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
     };
     // the scale factors fl32(A / 6) of rows r0 .. r0 + rows_per_wg, the whole
     // area (zeros past the valid rows): every load goes out before the first
-    // is used.  A is the absmax, or fl32(c8 * fl32(s2 / 255)).
+    // is used (the factor as in the kernels above).
     // The first D chunks are requested after these loads, and only the
     // copies and the scales are waited for (loads complete in order).
     constexpr int kFill = kFp4MfmaScales / (64 * W);
     {
-        float v[kFill];
-        uint32_t cq[kFill];
-        float s2v[kFill];
+        float v[kFill];        // absmax, or s2 when double-quantized
+        uint32_t cq[kFill];    // c8 when double-quantized
         if constexpr (kDq) {
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.c8 + r0 * kb, valid * kb);
             const __amdgpu_buffer_rsrc_t r2 = buf_rsrc(a.s2, ((a.n * kb + kDqGroup - 1) / kDqGroup) * 4);
@@ -605,15 +610,17 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
             for (int it = 0; it < kFill; ++it) {
                 const int i = tid + 64 * W * it;
                 cq[it] = __builtin_amdgcn_raw_buffer_load_b8(rs, i, 0, 0);
-                s2v[it] = __builtin_bit_cast(
+                v[it] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(r2, (int)((r0 * kb + i) / kDqGroup) * 4, 0, 0));
             }
         } else {
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.absmax + r0 * kb, valid * kb * 4);
 #pragma unroll
-            for (int it = 0; it < kFill; ++it)
+            for (int it = 0; it < kFill; ++it) {
                 v[it] = __builtin_bit_cast(float,
                                            __builtin_amdgcn_raw_buffer_load_b32(rs, (tid + 64 * W * it) * 4, 0, 0));
+                cq[it] = 0;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);   // the scale loads go out before the chunks'
 #pragma unroll
@@ -621,13 +628,8 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
         __builtin_amdgcn_sched_barrier(0);
         static_assert(D * T <= 15, "the wait below counts the chunk loads in four bits");
         __builtin_amdgcn_s_waitcnt(0x0f70 | (D * T));   // vmcnt(D T): the copies and the scales landed
-        if constexpr (kDq) {
 #pragma unroll
-            for (int it = 0; it < kFill; ++it) v[it] = (float)cq[it] * (s2v[it] / 255.0f);
-        }
-        // A / 6 as A * fl32(1 / 6), as in the kernels above
-#pragma unroll
-        for (int it = 0; it < kFill; ++it) sd[tid + 64 * W * it] = v[it] * (1.0f / 6.0f);
+        for (int it = 0; it < kFill; ++it) sd[tid + 64 * W * it] = fp4_factor<kDq>(v[it], cq[it]);
     }
     __syncthreads();   // every wave's copies and factors are in LDS
 
@@ -773,13 +775,22 @@ hipError_t launch_rows_cpl(const Fp4Args& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// k <= 16384 (at most 8 chunks per lane): the LDS-x kernel
+// k <= 16384 (at most 8 chunks per lane): the LDS-x kernel with the fewest
+// chunk slots per lane that cover a row (at least 2): a slot past the row
+// reads nothing but still costs its conversions and dot products
 template <int M>
 hipError_t launch_rows_m(const Fp4Args& a, hipStream_t stream) {
-    const int64_t chunks = a.k / 32;
-    if (chunks <= 128) return launch_rows_cpl<M, 2>(a, stream);
-    if (chunks <= 256) return launch_rows_cpl<M, 4>(a, stream);
-    return launch_rows_cpl<M, 8>(a, stream);
+    switch ((a.k / 32 + 63) / 64) {
+        case 0:
+        case 1:
+        case 2: return launch_rows_cpl<M, 2>(a, stream);
+        case 3: return launch_rows_cpl<M, 3>(a, stream);
+        case 4: return launch_rows_cpl<M, 4>(a, stream);
+        case 5: return launch_rows_cpl<M, 5>(a, stream);
+        case 6: return launch_rows_cpl<M, 6>(a, stream);
+        case 7: return launch_rows_cpl<M, 7>(a, stream);
+        default: return launch_rows_cpl<M, 8>(a, stream);
+    }
 }
 constexpr int64_t kFp4LdsMaxK = 16384;
 

@@ -93,9 +93,13 @@ LINEAR_CASES = [
     (3, 37, 13824, True, True),     # two segments, the last group of four weight rows partial
     (2, 9, 9216, False, True),      # two segments at m = 2, the last group partial
     (1, 1000, 5120, True, False),
-    # one row of x: x staged in LDS, 2, 4 and 8 code chunks per lane, rows past the grid's waves
+    # one row of x: x staged in LDS, 2 to 8 code chunks per lane (the fewest that cover a
+    # row: 2, 3, 5, 6, 7, 8 here, the last slot partly past the row), rows past the grid's waves
     (1, 77, 13824, True, True),
     (1, 4100, 4096, False, True),
+    (1, 50, 4160, False, False),
+    (1, 37, 10240, False, True),
+    (1, 129, 12224, True, False),
     (1, 9, 16384, False, False),
     (1, 5, 16448, True, False),     # past 16384: x from L2
     # two to four rows of x: x staged in LDS, the workgroups' shares of the weight rows
