@@ -564,6 +564,8 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
     // whole-line loads: in the loop each load would touch 16 rows' scales)
     __shared__ float sd[kFp4MfmaScales];
     __shared__ float red[W][T][4][16];
+    // zeros: the x operand of the lanes a pass leaves out
+    __shared__ __attribute__((aligned(16))) uint32_t xz[16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t kb = a.k / kBlk, kc = (a.k + 127) / 128;
@@ -631,6 +633,7 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
 #pragma unroll
         for (int it = 0; it < kFill; ++it) sd[tid + 64 * W * it] = fp4_factor<kDq>(v[it], cq[it]);
     }
+    if (tid < 16) xz[tid] = 0u;
     __syncthreads();   // every wave's copies and factors are in LDS
 
     const int irc = l16 < M ? l16 : M - 1;                  // a valid x row; masked below
@@ -646,17 +649,21 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
             const int64_t c = c0 + (int64_t)W * u;
             if (c < kc) {
                 // x of chunk c: bytes 256 c + 64 g + 16 s of row irc, in block J = c / 16;
-                // the two passes keep only block 2c's lanes (g < 2) or block 2c + 1's
+                // the two passes keep only block 2c's lanes (g < 2) or block 2c + 1's:
+                // the lanes a pass leaves out (and rows past M) read the zero area
                 uint32_t xo = (uint32_t)(((c >> 4) * M + irc) * 4096 + 256 * (c & 15) + 64 * g);
                 asm volatile("" : "+v"(xo));
+                typedef const __attribute__((address_space(3))) uint8_t lu8;
                 typedef const __attribute__((address_space(3))) v4u_l lv4u;
+                lu8* const px = (lu8*)xs + xo;
+                lu8* const pz = (lu8*)xz;
+                lu8* const pxl = lo_ok ? px : pz;
+                lu8* const pxh = hi_ok ? px : pz;
                 v8h alo[4], ahi[4];
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    const v4u_l v = *reinterpret_cast<lv4u*>((const __attribute__((address_space(3))) uint8_t*)xs + xo + 16 * st);
-                    const v4u_l z = {0u, 0u, 0u, 0u};
-                    alo[st] = __builtin_bit_cast(v8h, lo_ok ? v : z);
-                    ahi[st] = __builtin_bit_cast(v8h, hi_ok ? v : z);
+                    alo[st] = __builtin_bit_cast(v8h, *reinterpret_cast<lv4u*>(pxl + 16 * st));
+                    ahi[st] = __builtin_bit_cast(v8h, *reinterpret_cast<lv4u*>(pxh + 16 * st));
                 }
                 // the scale factors of the chunk's two blocks for this lane's
                 // weight rows (a row past the share reads row 0's: its codes
