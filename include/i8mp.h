@@ -396,6 +396,9 @@ i8mp_status i8mp_fp4_dequantize(const uint8_t* codes, int64_t ldc, int64_t n, in
 
 /* The 4-bit linear for decode-sized batches:
  *   out[i, r] = fp16( sum_j x[i, j] * w'[r, j] + bias[r] )   (fp32 sums)
+ * where each half block's fp32 sum of x times the E2M1 values is scaled once by
+ * the block's A / 6, computed from the raw scales within a few ulp of the
+ * dequantized weight's scale (far inside the sums' rounding).
  * x fp16 [m x ldx] 16-byte aligned with ldx a multiple of 8; codes 16-byte
  * aligned with ldc a multiple of 16; scales as for the dequantize; bias
  * optional fp16 [n]; out fp16 [m x ldout], ldout >= n.  Any m >= 0: every four
