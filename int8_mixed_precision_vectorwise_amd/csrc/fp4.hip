@@ -271,7 +271,8 @@ typedef unsigned v4u_l __attribute__((ext_vector_type(4)));
 struct Fp4RowSrc {
     __amdgpu_buffer_rsrc_t codes, scales, s2;
     int64_t b0;   // first block of the row
-    uint32_t g0;  // the same, as the 32-bit base of the group index (n k / 64 < 2^32)
+    uint32_t g0;  // the same, as the 32-bit base of the group index: the launcher
+                  // takes the kernels that use it only where n k / 64 < 2^32
 };
 
 template <bool kDq>
@@ -847,7 +848,9 @@ hipError_t launch_fp4_linear(const Fp4Args& in, hipStream_t stream) {
         // 2986 GB/s); two to four rows: the MFMA kernel where it applies
         // (13B m = 4: 1604 -> 1752 GB/s against the four-row LDS-x kernel,
         // 1491 with the x-from-L2 kernel), else the four-row LDS-x kernel
-        const bool lds = a.k <= kFp4LdsMaxK;
+        // (and only while the block count n k / 64 fits the 32-bit group index
+        // of their double-quantized scales; past it the L2-x kernel)
+        const bool lds = a.k <= kFp4LdsMaxK && a.n * (a.k / kBlk) < ((int64_t)1 << 32);
         if (mm >= 2) {
             hipError_t em = hipSuccess;
             const bool took = mm == 2 ? launch_mfma_m<2>(a, stream, &em)
