@@ -547,10 +547,12 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows4_kernel(Fp4Args a) {
 // v_mfma_f32_16x16x32_f16 takes weights 128 c + 32 g + 8 s .. + 7 of both
 // operands (the same relabelling of k in x and in the weights, so the dot
 // product is unchanged).  Lanes g = 0, 1 then carry block 2 c and lanes g = 2,
-// 3 block 2 c + 1: each step runs twice, with the x operand of the other
-// block's lanes zeroed, into one sum per block, and each
-// block's scale applies to its sum: acc += fl32(A / 6) * P_b.  Lanes 0-15
-// hold the outputs of rows 0-3 of x.
+// 3 block 2 c + 1.  The x operand puts x row r in MFMA row r for block 2 c's
+// lanes and in MFMA row 4 + r for block 2 c + 1's (zeros elsewhere), so one
+// step yields both blocks' sums apart: output rows 0-3 (lanes 0-15) hold
+// block 2 c's, rows 4-7 (lanes 16-31) block 2 c + 1's, and each lane scales
+// its sums by its block's factor: acc += fl32(A / 6) * P.  At the end lanes
+// 0-15 add lanes 16-31: the outputs of rows 0-3 of x.
 typedef float v4f_16 __attribute__((ext_vector_type(4)));
 constexpr int kFp4MfmaJ = 7;          // 4 KB x blocks per row of x: k <= 14336
 constexpr int kFp4MfmaScales = 8192;  // block scales per workgroup: rows_per_wg * k / 64 + 2
@@ -637,8 +639,10 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
     if (tid < 16) xz[tid] = 0u;
     __syncthreads();   // every wave's copies and factors are in LDS
 
-    const int irc = l16 < M ? l16 : M - 1;                  // a valid x row; masked below
-    const bool lo_ok = g < 2 && l16 < M, hi_ok = g >= 2 && l16 < M;
+    // MFMA row l16 of this lane's x operand: x row l16 (block 2c's lanes, g < 2)
+    // or l16 - 4 (block 2c + 1's), else zeros
+    const bool x_ok = g < 2 ? l16 < M : (l16 >= 4 && l16 < 4 + M);
+    const int xrow = x_ok ? (l16 & 3) : 0;
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -649,38 +653,29 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
         for (int u = 0; u < D; ++u) {
             const int64_t c = c0 + (int64_t)W * u;
             if (c < kc) {
-                // x of chunk c: bytes 256 c + 64 g + 16 s of row irc, in block J = c / 16;
-                // the two passes keep only block 2c's lanes (g < 2) or block 2c + 1's:
-                // the lanes a pass leaves out (and rows past M) read the zero area
-                uint32_t xo = (uint32_t)(((c >> 4) * M + irc) * 4096 + 256 * (c & 15) + 64 * g);
+                // x of chunk c: bytes 256 c + 64 g + 16 s of row xrow, in block J = c / 16;
+                // the lanes outside the x rows read the zero area
+                uint32_t xo = (uint32_t)(((c >> 4) * M + xrow) * 4096 + 256 * (c & 15) + 64 * g);
                 asm volatile("" : "+v"(xo));
                 typedef const __attribute__((address_space(3))) uint8_t lu8;
                 typedef const __attribute__((address_space(3))) v4u_l lv4u;
-                lu8* const px = (lu8*)xs + xo;
-                lu8* const pz = (lu8*)xz;
-                lu8* const pxl = lo_ok ? px : pz;
-                lu8* const pxh = hi_ok ? px : pz;
-                v8h alo[4], ahi[4];
+                lu8* const px = x_ok ? (lu8*)xs + xo : (lu8*)xz;
+                v8h ax[4];
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    alo[st] = __builtin_bit_cast(v8h, *reinterpret_cast<lv4u*>(pxl + 16 * st));
-                    ahi[st] = __builtin_bit_cast(v8h, *reinterpret_cast<lv4u*>(pxh + 16 * st));
-                }
-                // the scale factors of the chunk's two blocks for this lane's
-                // weight rows (a row past the share reads row 0's: its codes
-                // are zero), read before the MFMAs
-                float d[T][2];
+                for (int st = 0; st < 4; ++st) ax[st] = __builtin_bit_cast(v8h, *reinterpret_cast<lv4u*>(px + 16 * st));
+                // the factor of the block whose sums this lane holds (2c + g for
+                // g < 2; lanes g >= 2 hold zeros) for its weight row (a row past
+                // the share reads row 0's: its codes are zero), read before the MFMAs
+                float d[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const int rr = 16 * t + l16;
-                    const int64_t si = (rr < valid ? rr : 0) * kb + 2 * c;
-                    d[t][0] = sd[si];
-                    d[t][1] = sd[si + 1];
+                    d[t] = sd[(rr < valid ? rr : 0) * kb + 2 * c + (g & 1)];
                 }
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const uint32_t cw[4] = {cv[u][t].x, cv[u][t].y, cv[u][t].z, cv[u][t].w};
-                    v4f_16 plo = {0.0f, 0.0f, 0.0f, 0.0f}, phi = {0.0f, 0.0f, 0.0f, 0.0f};
+                    v4f_16 p = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
                         const hh2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 0);
@@ -688,11 +683,10 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
                         const hh2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 2);
                         const hh2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[st], 1.0f, 3);
                         const v8h wb = {w0.x, w0.y, w1.x, w1.y, w2.x, w2.y, w3.x, w3.y};
-                        plo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[st], wb, plo, 0, 0, 0);
-                        phi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[st], wb, phi, 0, 0, 0);
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[st], wb, p, 0, 0, 0);
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(phi[r], d[t][1], fmaf(plo[r], d[t][0], acc[t][r]));
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(p[r], d[t], acc[t][r]);
                 }
             }
             load(u, c + (int64_t)W * D);
@@ -700,6 +694,11 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_mfma16_kernel(Fp4Args a, i
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
+    // lanes 0-15: block 2c's sums plus block 2c + 1's from lanes 16-31
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] += __shfl_down(acc[t][r], 16, 64);
     if (lane < 16) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
