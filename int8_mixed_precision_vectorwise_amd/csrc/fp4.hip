@@ -256,14 +256,15 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
 // blocks, zero past the row); then every wave takes whole weight rows (wave v
 // of the grid: rows v, v + nw, ...), so the grid sweeps a band of neighbouring
 // rows at a time.  A lane takes the 16-byte code chunks lane, lane + 64, ...
-// (CPL of them, 32 weights each, half a block) and reads the matching x from
-// LDS; per row the 64 lane sums meet in a DPP reduction and lane 0 writes the
-// M outputs.  As soon as a chunk of the current row has been converted, the
-// same chunk of the wave's next row is requested into its registers, so CPL
-// chunks are always in flight.  Each code byte is read once from HBM and x
-// once per workgroup from L2 (the four-row kernel above reads x from L2 again
-// for every group of weight rows).  Chunks past the row read zero codes
-// through the row's buffer range, against the zeros of the x block's tail.
+// (CPL of them, the fewest that cover the row; 32 weights each, half a block)
+// and reads the matching x from LDS; per row the 64 lane sums meet in a DPP
+// reduction and lane 0 writes the M outputs.  As soon as a chunk of the
+// current row has been converted, the same chunk of the wave's next row is
+// requested into its registers, so CPL chunks are always in flight.  Each code
+// byte is read once from HBM and x once per workgroup from L2 (the L2-x kernel
+// above reads x again for every group of 4 or 8 weight rows).  Chunks past the
+// row read zero codes through the row's buffer range, against the zeros of
+// the x block's tail.
 constexpr int kFp4Waves = 8;
 typedef unsigned v4u_l __attribute__((ext_vector_type(4)));
 
