@@ -339,6 +339,23 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first row) landed
     __syncthreads();                      // ... and every wave's
+    // one row of x and at most 3 slots: the lane's x chunks stay in registers
+    // across the weight rows (16 per slot, within 128 VGPRs)
+    constexpr bool kXReg = M == 1 && CPL <= 3;
+    uint32_t xr[kXReg ? CPL : 1][16];
+    if constexpr (kXReg) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4u_l xv = *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(
+                    (const __attribute__((address_space(3))) uint8_t*)xs + lane * 64 + j * 4096 + q * 16);
+                xr[j][4 * q] = xv.x;
+                xr[j][4 * q + 1] = xv.y;
+                xr[j][4 * q + 2] = xv.z;
+                xr[j][4 * q + 3] = xv.w;
+            }
+    }
 
     for (; row < a.n; row += nw) {
         const Fp4RowSrc rn = fp4_row_src<kDq>(a, row + nw, chunks, kb);   // past n: nothing is read
@@ -374,8 +391,18 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
                 float part = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const v4u_l xv = *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(xl + m * 4096 + q * 16);
-                    const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+                    uint32_t xq[4];
+                    if constexpr (kXReg) {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) xq[b] = xr[j][4 * q + b];
+                    } else {
+                        const v4u_l xv =
+                            *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(xl + m * 4096 + q * 16);
+                        xq[0] = xv.x;
+                        xq[1] = xv.y;
+                        xq[2] = xv.z;
+                        xq[3] = xv.w;
+                    }
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
                         part = __builtin_amdgcn_fdot2(wv[q][b], __builtin_bit_cast(hh2, xq[b]), part, false);
