@@ -340,13 +340,13 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies (and its first row) landed
     __syncthreads();                      // ... and every wave's
-    // one row of x and at most 3 slots: the lane's x chunks stay in registers
-    // across the weight rows (16 per slot, within 128 VGPRs)
-    constexpr bool kXReg = M == 1 && CPL <= 3;
-    uint32_t xr[kXReg ? CPL : 1][16];
-    if constexpr (kXReg) {
+    // one row of x: the lane's x chunks of the first kXS slots stay in
+    // registers across the weight rows (16 per slot, within 128 VGPRs)
+    constexpr int kXS = M != 1 ? 0 : CPL <= 3 ? CPL : CPL <= 5 ? 3 : CPL <= 7 ? 2 : 1;
+    uint32_t xr[kXS > 0 ? kXS : 1][16];
+    if constexpr (kXS > 0) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j)
+        for (int j = 0; j < kXS; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const v4u_l xv = *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(
@@ -392,9 +392,9 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t xq[4];
-                    if constexpr (kXReg) {
+                    if (j < kXS) {   // resolved at compile time: j is unrolled
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) xq[b] = xr[j][4 * q + b];
+                        for (int b = 0; b < 4; ++b) xq[b] = xr[j < kXS ? j : 0][4 * q + b];
                     } else {
                         const v4u_l xv =
                             *reinterpret_cast<const __attribute__((address_space(3))) v4u_l*>(xl + m * 4096 + q * 16);

@@ -94,10 +94,12 @@ LINEAR_CASES = [
     (2, 9, 9216, False, True),      # two segments at m = 2, the last group partial
     (1, 1000, 5120, True, False),
     # one row of x: x staged in LDS, 2 to 8 code chunks per lane (the fewest that cover a
-    # row: 2, 3, 5, 6, 7, 8 here, the last slot partly past the row), rows past the grid's waves
+    # row: 2 to 8 here, the last slot partly past the row; the first 1 to 3 slots' x held in
+    # registers), rows past the grid's waves
     (1, 77, 13824, True, True),
     (1, 4100, 4096, False, True),
     (1, 50, 4160, False, False),
+    (1, 300, 7168, True, True),
     (1, 37, 10240, False, True),
     (1, 129, 12224, True, False),
     (1, 9, 16384, False, False),
