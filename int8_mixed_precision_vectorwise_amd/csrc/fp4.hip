@@ -257,8 +257,8 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(Fp4Args a) {
 // of the grid: rows v, v + nw, ...), so the grid sweeps a band of neighbouring
 // rows at a time.  A lane takes the 16-byte code chunks lane, lane + 64, ...
 // (CPL of them, the fewest that cover the row; 32 weights each, half a block)
-// and reads the matching x from LDS (at up to 3 slots, from registers loaded
-// from there once); per row the 64 lane sums meet in a DPP
+// and reads the matching x from LDS (for its first 1 to 3 slots from registers
+// loaded from there once); per row the 64 lane sums meet in a DPP
 // reduction and lane 0 writes the M outputs.  As soon as a chunk of the
 // current row has been converted, the same chunk of the wave's next row is
 // requested into its registers, so CPL chunks are always in flight.  Each code
@@ -379,9 +379,10 @@ __global__ __launch_bounds__(64 * kFp4Waves) void fp4_rows_kernel(Fp4Args a) {
             // the chunk's registers are free: request the same chunk of the next row
             fp4_chunk_load<kDq>(rn, c, cv[j], sa[j], c8[j]);
             // this chunk's x: 64 bytes per row at lane * 64 of blocks (j, m),
-            // the same for every weight row (held in registers above at up to
-            // 3 slots; otherwise read from LDS here, with more rows of x
-            // through a base made opaque per chunk so that the reads stay here)
+            // the same for every weight row (for the first kXS slots held in
+            // registers above; the others read from LDS here, with more rows
+            // of x through a base made opaque per chunk so that the reads stay
+            // here)
             uint32_t xb = (uint32_t)lane * 64u;
             if constexpr (M > 1) asm volatile("" : "+v"(xb));
             const __attribute__((address_space(3))) uint8_t* const xl =
